@@ -1,0 +1,393 @@
+"""CPU oracle for the DSpark semi-autoregressive drafting hot path.
+
+TEST INFRASTRUCTURE.  Only the test suite, the package smoke check and the
+benchmark's CPU-baseline leg may import or run this module.  The product path
+never does, and this module shares no code with it (no kernels, headers,
+helpers, tables or constants): it is a plain, slow, obviously correct fp64
+restatement of what the pages define, used to judge the HIP path.
+
+Sources, cited by page title and section (no other source defines the method):
+  [P1] "DSpark" -- rainlin-net.pages.dev/llm-inference/dspark (sections 1-9).
+  [P2] "投机解码的新做法：整块草稿、按负载验证与 PD 分离" -- anrans.github.io
+       ai-infra-handbooks, serving/frontier/spec-next (headings "负载越高，K 越要小",
+       "一次前向给出一整块草稿", "按负载决定验证多少", "练习").
+  [P3] "DSpark: Speculative decodingを活用したLLM推論の高速化" -- ja.news.hada.io
+       topic 30902 (headings アーキテクチャ, 実験分析, 実サービス配備).
+
+What each function follows, and what pins it (tests/test_oracle_pins.py):
+  markov_bias / draft_logits   P1 §2.3 eq. B, P1 §2.2 eq. p_k.  Pinned by the
+        identity-W1 special case, the full-matrix B = W1 W2 row, the P2 Markov
+        toy printout (0.62 / 0.81) and a two-token closed form.
+  draft_distribution           P1 §2.2 eq. p_k and eq. P(X|x0).  Pinned by
+        brute-force enumeration (sum over all blocks = 1) and closed forms.
+  draft_step (Gumbel-argmax)   sampling of p_k.  Pinned by a chi-square test of
+        sampled blocks against the enumerated P(X|x0), and T=0 -> argmax.
+  confidence                   P1 §3.1 eq. c_k.  Pinned by closed forms.
+  survival / expected_tau      P1 §1.1 eq. a_j and eq. tau.  Pinned by the P2
+        Markov toy printout and closed forms.
+  theta_of_ell / schedule      P1 §4.1 eqs. B, tau, Theta and the global sort;
+        P1 §4.2 early stop.  Pinned by the P2 cost-model and plan() printouts,
+        exhaustive search over ell vectors, prefix contiguity and closed forms.
+  verify                       P1 §3.1 eq. c*, standard rejection sampling (P1
+        intro and §2.2; P3 問題定義).  Pinned by the c* = overlap identity,
+        special cases, losslessness (output law = p_t) and acceptance-rate = c*.
+
+Parity unpinned: the bits of the counter-based random number generator.  The
+pages do not fix a generator; the one used here (and, written separately, on
+the GPU) is the PCG hash of Jarzynski & Olano, "Hash Functions for GPU
+Rendering", JCGT 9(3), 2020, keyed as described at `stream_key`.  Only its
+statistical behaviour is pinned (uniformity of u and the sampler tests above).
+
+Readings taken where the pages are silent (each also listed in the design doc):
+  * sampling is Gumbel-argmax with the counter generator; ties -> lowest id;
+  * s = (U_k + bias) / T; p_d and p_t use the same T; T = 0 means argmax
+    (point mass, p = 1, lse reported as max z);
+  * the confidence head has no bias term; w = [w_h (d); w_e (rank)]; c_1 uses
+    W1[x_0] (the anchor);
+  * a is an fp32 running product of fp32 c (left to right); tau in the
+    scheduler is fixed point with unit 2^-32, Theta = float64(tau_fix) * SPS;
+  * the global sort key is (a descending, flat index req*gamma+j ascending);
+    the early stop admits candidate b+1 only if Theta strictly increases;
+    Theta(0) = R * SPS(R);
+  * verification: accept iff u < p_t(x)/p_d(x), with p_d(x) the kept draft
+    probability (1 under greedy drafting, whose law is the point mass on the
+    drafted token); the first rejection resamples
+    from max(0, p_t - p_d) by Gumbel-argmax of log(p_t - p_d); all accepted ->
+    bonus sampled from p_t at position ell+1 (none when ell = gamma, id -1);
+    realised tau per request = accepted + 1.
+"""
+from __future__ import annotations
+
+import itertools
+
+import numpy as np
+
+# ----------------------------------------------------------------------------
+# Counter-based random numbers (written from the JCGT 2020 definition).
+# ----------------------------------------------------------------------------
+STREAM_DRAFT, STREAM_ACCEPT, STREAM_RESID, STREAM_BONUS = 1, 2, 3, 4
+
+_U32 = np.uint32
+
+
+def pcg_hash(x):
+    """pcg(v): state = v*747796405 + 2891336453; word = ((state >> ((state >> 28) + 4))
+    ^ state) * 277803737; return (word >> 22) ^ word  -- all mod 2^32."""
+    x = np.asarray(x, dtype=np.uint32)
+    with np.errstate(over="ignore"):
+        state = x * _U32(747796405) + _U32(2891336453)
+        word = ((state >> ((state >> _U32(28)) + _U32(4))) ^ state) * _U32(277803737)
+    return (word >> _U32(22)) ^ word
+
+
+def stream_key(seed, stream, req, k):
+    """32-bit key of one (seed, stream, request, position) row: the seed's low and
+    high words, the stream id, the request index and the position are folded in,
+    one pcg round each, in that order."""
+    seed = np.asarray(seed, dtype=np.uint64)
+    lo = (seed & np.uint64(0xFFFFFFFF)).astype(np.uint32)
+    hi = (seed >> np.uint64(32)).astype(np.uint32)
+    h = pcg_hash(lo)
+    h = pcg_hash(h ^ hi)
+    h = pcg_hash(h ^ _U32(stream))
+    h = pcg_hash(h ^ np.asarray(req, dtype=np.uint32))
+    h = pcg_hash(h ^ np.asarray(k, dtype=np.uint32))
+    return h
+
+
+def uniforms(seed, stream, req, k, v):
+    """u in (0,1) for element v of a row: bits = pcg(key + v mod 2^32);
+    u = ((bits >> 8) + 0.5) * 2^-24 (exact in fp64 and in fp32)."""
+    key = stream_key(seed, stream, req, k)
+    with np.errstate(over="ignore"):
+        bits = pcg_hash(key + np.asarray(v, dtype=np.uint32))
+    return ((bits >> _U32(8)).astype(np.float64) + 0.5) * 2.0 ** -24
+
+
+def gumbel(u):
+    """Standard Gumbel variate from a uniform: G = -ln(-ln u)."""
+    return -np.log(-np.log(u))
+
+
+def bf16_to_f64(bits):
+    """Exact value of bf16 bit patterns: (bits << 16) reinterpreted as fp32."""
+    return (np.asarray(bits, dtype=np.uint32) << _U32(16)).view(np.float32).astype(np.float64)
+
+
+def as_f64(store):
+    """Weights/hidden states as stored (uint16 bf16 bits or float32) -> exact fp64."""
+    store = np.asarray(store)
+    return bf16_to_f64(store) if store.dtype == np.uint16 else store.astype(np.float64)
+
+
+# ----------------------------------------------------------------------------
+# Sequential head: Markov bias, logits, distribution, sampling   [P1 §2.2-2.3]
+# ----------------------------------------------------------------------------
+def markov_bias(W1, W2t, x_prev):
+    """B(x_{k-1}, .) = W1[x_{k-1}] W2  [P1 §2.3, eq. B], with W2 (rank x V) stored
+    as its transpose W2t (V x rank).  One embedding lookup, then one rank->vocab
+    projection per request."""
+    E = W1[np.asarray(x_prev)]            # [n, rank]
+    return E @ W2t.T                      # [n, V]
+
+
+def draft_logits(U_k, W1, W2t, x_prev):
+    """Exponent of p_k: U_k(v) + B_k(x_{k-1}, v)  [P1 §2.2, eq. p_k]."""
+    return np.asarray(U_k, dtype=np.float64) + markov_bias(W1, W2t, x_prev)
+
+
+def log_softmax_rows(s):
+    m = s.max(axis=-1, keepdims=True)
+    lse = m + np.log(np.exp(s - m).sum(axis=-1, keepdims=True))
+    return s - lse, lse[..., 0]
+
+
+def draft_distribution(z, T):
+    """p_k(. | x0, x<k) = softmax(z / T) over the vocabulary  [P1 §2.2, eq. p_k].
+    T = 0: point mass on the lowest-id maximiser of z."""
+    z = np.asarray(z, dtype=np.float64)
+    if T > 0:
+        logp, _ = log_softmax_rows(z / T)
+        return np.exp(logp)
+    p = np.zeros_like(z)
+    idx = np.argmax(z, axis=-1)
+    np.put_along_axis(p, idx[..., None], 1.0, axis=-1)
+    return p
+
+
+def _top2(keys):
+    """(argmax with lowest index on ties, top1 - top2 gap) per row."""
+    x = np.argmax(keys, axis=-1)
+    top1 = np.take_along_axis(keys, x[:, None], axis=-1)[:, 0]
+    rest = keys.copy()
+    np.put_along_axis(rest, x[:, None], -np.inf, axis=-1)
+    top2 = rest.max(axis=-1)
+    return x, top1 - top2
+
+
+def draft_step(U_k, W1, W2t, x_prev, T, seed, k, req_ids):
+    """One sequential step k for a set of requests (rows of U_k).
+
+    z = U_k + W1[x_{k-1}] W2; for T > 0: s = z/T, lse = log sum_v exp(s_v),
+    x_k = lowest v maximising s_v + G_v with G from the DRAFT stream at
+    (req, k, v), p_k(x_k) = exp(s_{x_k} - lse).  T = 0: x_k = argmax z, p = 1,
+    lse := max z.  Also returns the gap between the top two perturbed scores
+    (natural-log units of s), used to count near ties.
+    """
+    z = draft_logits(U_k, W1, W2t, x_prev)
+    n, V = z.shape
+    req_ids = np.asarray(req_ids)
+    if T > 0:
+        s = z / T
+        m = s.max(axis=1)
+        lse = m + np.log(np.exp(s - m[:, None]).sum(axis=1))
+        v = np.arange(V, dtype=np.uint32)[None, :]
+        u = uniforms(np.asarray(seed)[..., None] if np.ndim(seed) else seed,
+                     STREAM_DRAFT, req_ids[:, None], k, v)
+        keys = s + gumbel(u)
+        x, gap = _top2(keys)
+        p = np.exp(s[np.arange(n), x] - lse)
+    else:
+        x, gap = _top2(z)
+        p = np.ones(n)
+        lse = z.max(axis=1)
+    return {"z": z, "x": x.astype(np.int64), "p": p, "lse": lse, "gap": gap}
+
+
+# ----------------------------------------------------------------------------
+# Confidence head and survival                               [P1 §1.1, §3.1]
+# ----------------------------------------------------------------------------
+def sigmoid(t):
+    return 1.0 / (1.0 + np.exp(-t))
+
+
+def confidence(h_k, w, W1, x_prev):
+    """c_k = sigma(w^T [h_k ; W1[x_{k-1}]])  [P1 §3.1, eq. c_k]; no bias term,
+    w[:d] weights h_k and w[d:] weights the Markov embedding."""
+    h_k = np.asarray(h_k, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    d = h_k.shape[-1]
+    e = W1[np.asarray(x_prev)]
+    return sigmoid(h_k @ w[:d] + e @ w[d:])
+
+
+def survival(c32):
+    """a_{r,j} = prod_{i<=j} c_{r,i}  [P1 §1.1 eq. a_j; §4.1 eq. tau], as an fp32
+    running product of fp32 c taken left to right (one rounding per factor)."""
+    c32 = np.asarray(c32, dtype=np.float32)
+    a = np.empty_like(c32)
+    run = np.ones(c32.shape[:-1], dtype=np.float32)
+    for j in range(c32.shape[-1]):
+        run = (run * c32[..., j]).astype(np.float32)
+        a[..., j] = run
+    return a
+
+
+def expected_tau(a, ell=None):
+    """tau = 1 + sum_{j<=ell} a_j per request (bonus token included)
+    [P1 §1.1 eq. tau; §4.1 eq. tau].  ell=None means the whole block."""
+    a = np.asarray(a, dtype=np.float64)
+    if ell is None:
+        return 1.0 + a.sum(axis=-1)
+    j = np.arange(a.shape[-1])
+    return 1.0 + np.where(j[None, :] < np.asarray(ell)[:, None], a, 0.0).sum(axis=-1)
+
+
+# ----------------------------------------------------------------------------
+# Hardware-aware prefix scheduler                                  [P1 §4]
+# ----------------------------------------------------------------------------
+TAU_ONE = 2 ** 32   # fixed-point unit of tau
+
+
+def tau_fixed_units(a):
+    """q(a) = round-half-even(a * 2^32) as int64 (exact scaling in fp64)."""
+    return np.rint(np.asarray(a, dtype=np.float32).astype(np.float64) * TAU_ONE).astype(np.int64)
+
+
+def theta_of_ell(a, ell, sps):
+    """Theta = tau * SPS(B) for a vector of verify lengths  [P1 §4.1, eqs. B, tau,
+    Theta]: B = sum_r (1 + ell_r), tau = sum_r (1 + sum_{j<=ell_r} a_{r,j}).
+    tau is accumulated in fixed point (unit 2^-32); returns Theta in tokens/s."""
+    a = np.asarray(a, dtype=np.float32)
+    R, g = a.shape
+    ell = np.asarray(ell, dtype=np.int64)
+    q = tau_fixed_units(a)
+    mask = np.arange(g)[None, :] < ell[:, None]
+    tau_fix = R * TAU_ONE + int(q[mask].sum())
+    B = R + int(ell.sum())
+    return float(np.float64(tau_fix) * np.float64(sps[B])) * 2.0 ** -32
+
+
+def schedule(a, sps):
+    """Global sort of all (request, position) candidates by survival, then admit
+    them one by one while Theta strictly increases  [P1 §4.1 global sort, §4.2
+    early stop; P3 スケジューラ].
+
+    Returns (ell[R], budget b*, Theta(b*) in tokens/s, sorted flat order,
+    Theta_fixed[0..N] before the 2^-32 scaling)."""
+    a = np.asarray(a, dtype=np.float32)
+    R, g = a.shape
+    N = R * g
+    flat = a.reshape(-1)
+    order = np.argsort(-flat.astype(np.float64), kind="stable")      # a desc, index asc
+    q = tau_fixed_units(flat[order])
+    G = np.concatenate([[0], np.cumsum(q)]).astype(np.int64)
+    tau_fix = np.int64(R) * TAU_ONE + G
+    theta_fix = tau_fix.astype(np.float64) * np.asarray(sps, dtype=np.float64)[R + np.arange(N + 1)]
+    b = 0
+    while b < N and theta_fix[b + 1] > theta_fix[b]:
+        b += 1
+    ell = np.bincount(order[:b] // g, minlength=R).astype(np.int64)
+    return ell, b, float(theta_fix[b]) * 2.0 ** -32, order, theta_fix
+
+
+def schedule_exhaustive(a, sps):
+    """max over all ell in {0..gamma}^R of Theta(ell) (tiny R, gamma only)."""
+    a = np.asarray(a, dtype=np.float32)
+    R, g = a.shape
+    best, arg = -np.inf, None
+    for ell in itertools.product(range(g + 1), repeat=R):
+        th = theta_of_ell(a, ell, sps)
+        if th > best:
+            best, arg = th, np.array(ell)
+    return best, arg
+
+
+# ----------------------------------------------------------------------------
+# Verification: c* and lossless rejection sampling      [P1 §3.1, §2.2; P3]
+# ----------------------------------------------------------------------------
+def tv_acceptance(p_d, p_t):
+    """c* = 1 - 1/2 ||p_d - p_t||_1  [P1 §3.1, eq. c*]."""
+    return 1.0 - 0.5 * np.abs(np.asarray(p_d) - np.asarray(p_t)).sum(axis=-1)
+
+
+def verify(U, Tl, W1, W2t, x, ell, T, seed, req_ids):
+    """Per-position c* for all gamma positions, then standard rejection sampling
+    over each request's admitted prefix (positions 1..ell_r).
+
+    U, Tl: [n, gamma, V] draft base logits and target logits; x: [n, gamma+1]
+    token block (x[:,0] = anchor); ell: [n].  Returns a dict with c_star
+    [n,gamma], overlap [n,gamma] (= sum min(p_d, p_t)), n_accept [n],
+    next_token [n], tau [n] and per-request diagnostics for near-tie counting.
+    """
+    U = np.asarray(U)
+    n, g, V = U.shape
+    x = np.asarray(x, dtype=np.int64)
+    ell = np.asarray(ell, dtype=np.int64)
+    v = np.arange(V, dtype=np.uint32)
+    out = {k: [] for k in ("c_star", "overlap", "n_accept", "next_token", "tau",
+                           "accept_margin", "sample_gap", "p_d_x", "p_t_x")}
+    for i in range(n):
+        req = int(req_ids[i])
+        z_d = draft_logits(U[i], W1, W2t, x[i, :g])              # rows k = 1..gamma
+        z_t = np.asarray(Tl[i], dtype=np.float64)
+        p_d = draft_distribution(z_d, T)
+        p_t = draft_distribution(z_t, T)
+        out["c_star"].append(tv_acceptance(p_d, p_t))
+        out["overlap"].append(np.minimum(p_d, p_t).sum(axis=-1))
+        rows = np.arange(g)
+        # the kept draft probability of each drafted token; under greedy drafting
+        # the draft law at position j is the point mass on the drafted x_j itself
+        pdx = p_d[rows, x[i, 1:]] if T > 0 else np.ones(g)
+        ptx = p_t[rows, x[i, 1:]]
+        out["p_d_x"].append(pdx)
+        out["p_t_x"].append(ptx)
+        n_acc, nxt, margin, gap = 0, None, [], np.inf
+        for j in range(1, ell[i] + 1):
+            ratio = np.inf if pdx[j - 1] == 0 else ptx[j - 1] / pdx[j - 1]
+            u = float(uniforms(seed, STREAM_ACCEPT, req, j, 0))
+            margin.append(abs(u - ratio) if np.isfinite(ratio) else np.inf)
+            if u < ratio:
+                n_acc += 1
+                continue
+            law_d = p_d[j - 1] if T > 0 else np.eye(V)[x[i, j]]
+            r = np.maximum(p_t[j - 1] - law_d, 0.0)
+            G = gumbel(uniforms(seed, STREAM_RESID, req, j, v))
+            if np.any(r > 0):
+                with np.errstate(divide="ignore"):
+                    keys = np.where(r > 0, np.log(r), -np.inf) + G
+            else:
+                keys = (z_t[j - 1] / T if T > 0 else np.where(p_t[j - 1] > 0, 0.0, -np.inf)) + G
+            xs, gp = _top2(keys[None, :])
+            nxt, gap = int(xs[0]), float(gp[0])
+            break
+        if nxt is None:
+            if ell[i] < g:
+                row = ell[i]
+                if T > 0:
+                    keys = z_t[row] / T + gumbel(uniforms(seed, STREAM_BONUS, req, row + 1, v))
+                else:
+                    keys = z_t[row]
+                xs, gp = _top2(keys[None, :])
+                nxt, gap = int(xs[0]), float(gp[0])
+            else:
+                nxt = -1
+        out["n_accept"].append(n_acc)
+        out["next_token"].append(nxt)
+        out["tau"].append(n_acc + 1)
+        out["accept_margin"].append(min(margin) if margin else np.inf)
+        out["sample_gap"].append(gap)
+    res = {k: np.array(vv) for k, vv in out.items()}
+    res["tau_mean"] = float(np.mean(res["tau"])) if n else 0.0
+    return res
+
+
+# ----------------------------------------------------------------------------
+# A whole draft round (free running), for the smoke check and the CPU baseline
+# ----------------------------------------------------------------------------
+def draft_round(U, h, w, W1, W2t, anchor, T, seed, req_ids):
+    """gamma sequential steps [P1 §6.2 loop semantics: prev = sampled token],
+    confidence and survival for each position.  Inputs in fp64/fp32 arrays:
+    U [n,gamma,V], h [n,gamma,d], W1/W2t [V,rank]."""
+    n, g, V = U.shape
+    x = np.empty((n, g + 1), dtype=np.int64)
+    x[:, 0] = anchor
+    p = np.empty((n, g))
+    lse = np.empty((n, g))
+    c = np.empty((n, g))
+    for k in range(1, g + 1):
+        st = draft_step(U[:, k - 1], W1, W2t, x[:, k - 1], T, seed, k, req_ids)
+        c[:, k - 1] = confidence(h[:, k - 1], w, W1, x[:, k - 1])
+        x[:, k], p[:, k - 1], lse[:, k - 1] = st["x"], st["p"], st["lse"]
+    c32 = c.astype(np.float32)
+    return {"x": x, "p": p, "lse": lse, "c": c, "a": survival(c32)}
