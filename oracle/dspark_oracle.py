@@ -97,11 +97,12 @@ def stream_key(seed, stream, req, k):
 
 def uniforms(seed, stream, req, k, v):
     """u in (0,1) for element v of a row: bits = pcg(key + v mod 2^32);
-    u = ((bits >> 8) + 0.5) * 2^-24 (exact in fp64 and in fp32)."""
+    u = ((bits >> 9) + 0.5) * 2^-23, an odd multiple of 2^-24 with at most 24
+    significant bits, hence exact in fp32 as well as fp64."""
     key = stream_key(seed, stream, req, k)
     with np.errstate(over="ignore"):
         bits = pcg_hash(key + np.asarray(v, dtype=np.uint32))
-    return ((bits >> _U32(8)).astype(np.float64) + 0.5) * 2.0 ** -24
+    return ((bits >> _U32(9)).astype(np.float64) + 0.5) * 2.0 ** -23
 
 
 def gumbel(u):

@@ -276,14 +276,16 @@ def test_sampler_probability_and_greedy():
 
 
 def test_uniforms_are_uniform_and_exact():
-    """u lies strictly inside (0,1) on the 2^-24 grid offset by half a step, and
+    """u lies strictly inside (0,1) on the 2^-23 grid offset by half a step (so
+    it is exactly representable in fp32), and
     is uniform (chi-square over 256 buckets, KS test), with no visible lag-1
     correlation along v."""
     v = np.arange(1 << 20, dtype=np.uint32)
     u = O.uniforms(12345, O.STREAM_DRAFT, 3, 5, v)
     assert u.min() > 0 and u.max() < 1
-    scaled = u * 2.0 ** 25
+    scaled = u * 2.0 ** 24
     assert np.all(scaled == np.round(scaled)) and np.all(scaled.astype(np.int64) % 2 == 1)
+    assert np.all(u.astype(np.float32).astype(np.float64) == u)
     counts = np.bincount((u * 256).astype(int), minlength=256)
     chi2 = ((counts - len(u) / 256) ** 2 / (len(u) / 256)).sum()
     assert chi2 < stats.chi2.ppf(1 - 1e-6, 255)
