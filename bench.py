@@ -1,0 +1,174 @@
+#!/usr/bin/env python3
+"""Benchmark of the DSpark drafting hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch: gamma sequential
+Markov draft steps (gather, MFMA bias, base-logit add, online softmax,
+Gumbel-argmax, confidence head, survival product), the prefix scheduler and
+verification (c*, rejection sampling).  Workload: R = 128 requests, gamma = 16,
+V = 151936, rank 256, d = 4096, bf16 weights, fp32 logits (the Qwen3-8B-shaped
+long-block workload), plus synthetic target logits U + N(0, 1) for the
+verification pass.  All inputs are resident in GPU memory before timing starts.
+
+Prints one JSON line.  `value` = draft tokens per second of the whole round
+(R * gamma / wall-clock time per round).  `roofline` covers the draft step
+(markov_partial + markov_combine), timed with events on the stream it runs on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+WORKLOAD = "qwen3_8b_r128_g16"
+HBM_PEAK_GBS = 8000.0
+TEMPERATURE = 1.0
+
+
+def draft_step_bytes(R, V, rank, d):
+    """Algorithmic HBM bytes of one draft step: W2 once (rank*V bf16), U_k
+    (R*V fp32), the gathered W1 rows (R*rank bf16), h_k (R*d bf16) and the
+    per-request outputs (token, p, lse, c, a: 20 bytes)."""
+    return rank * V * 2 + R * V * 4 + R * rank * 2 + R * d * 2 + R * 20
+
+
+def verify_bytes(R, V, rank, gamma):
+    """Algorithmic bytes of verification: the target logits twice (normaliser
+    pass, then the fused pass), U and W2 once."""
+    return 2 * R * gamma * V * 4 + R * gamma * V * 4 + rank * V * 2
+
+
+def cpu_baseline(inp, seed):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload:
+    32 requests (16 easy, 16 hard) through the whole round (gamma draft steps
+    with confidence and survival, schedule, verify), one BLAS thread."""
+    from threadpoolctl import threadpool_limits
+    from oracle import dspark_oracle as O
+
+    wl = inp.wl
+    reqs = np.concatenate([np.arange(16), np.arange(wl.R // 2, wl.R // 2 + 16)])
+    W1, W2t = O.as_f64(inp.W1_store), O.as_f64(inp.W2t_store)
+    h = O.as_f64(inp.h_store[reqs])
+    U = inp.U[reqs].astype(np.float64)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        rnd = O.draft_round(U, h, inp.w, W1, W2t, inp.anchor[reqs], TEMPERATURE, seed, reqs)
+        ell, b, th, _, _ = O.schedule(rnd["a"], inp.sps[: len(reqs) * (1 + wl.gamma) + 1])
+        O.verify(inp.U[reqs], inp.target[reqs], W1, W2t, rnd["x"], ell, TEMPERATURE, seed, reqs)
+        dt = time.perf_counter() - t0
+    tokens = len(reqs) * wl.gamma
+    return {"value": tokens / dt, "unit": "draft tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(reqs)} of {wl.R} requests (16 easy, 16 hard), full round "
+                      f"(gamma={wl.gamma} draft steps + schedule + verify), fp64 NumPy, "
+                      f"1 BLAS thread, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from semi_autoregressive_drafting_amd import runner, synth
+
+    t_gen = time.perf_counter()
+    inp = synth.generate(WORKLOAD, seed=0, target=True)
+    di = runner.DeviceInputs.upload(inp)
+    buf = runner.RoundBuffers.allocate(di)
+    torch.cuda.synchronize()
+    print(f"# inputs ready in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+    R, g, V, rank, d = di.R, di.gamma, di.V, di.rank, di.d
+
+    def one_round(seed, ev=None):
+        buf.x[:, 0].copy_(di.anchor)
+        if ev is not None:
+            ev[0].record()
+        for k in range(1, g + 1):
+            runner.draft_step(di, buf, k, TEMPERATURE, seed)
+            if ev is not None:
+                ev[k].record()
+        runner.schedule(di, buf)
+        if ev is not None:
+            ev[g + 1].record()
+        runner.verify(di, buf, TEMPERATURE, seed)
+        if ev is not None:
+            ev[g + 2].record()
+
+    for w in range(args.warmup):
+        one_round(10_000 + w)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(g + 3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        one_round(s, evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    step_ms = np.array([[evs[s][k - 1].elapsed_time(evs[s][k]) for k in range(1, g + 1)]
+                        for s in range(K)])
+    sched_ms = np.array([evs[s][g].elapsed_time(evs[s][g + 1]) for s in range(K)])
+    ver_ms = np.array([evs[s][g + 1].elapsed_time(evs[s][g + 2]) for s in range(K)])
+    gpu_round_ms = np.array([evs[s][0].elapsed_time(evs[s][g + 2]) for s in range(K)])
+    ms_round = wall / K * 1e3
+    value = R * g / (wall / K)
+
+    sb = draft_step_bytes(R, V, rank, d)
+    step_s = float(step_ms.mean()) * 1e-3
+    achieved = sb / step_s / 1e9
+    vb = verify_bytes(R, V, rank, g)
+    out = {
+        "metric": "Markov-head draft tokens/s at R=128,γ=16,V=152k; % of HBM roofline",
+        "value": round(value, 1),
+        "unit": "draft tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_round, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{WORKLOAD}: R={R}, gamma={g}, V={V}, rank={rank}, d={d}, "
+                               "bf16 W1/W2/h, fp32 logits, T=1, verify target U+N(0,1)",
+                   "R": R, "gamma": g, "V": V, "rank": rank, "d": d,
+                   "temperature": TEMPERATURE},
+        "roofline": {"kernel": "dspark_draft_step (markov_partial_shared + markov_combine)",
+                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "bytes_per_launch": sb,
+                     "avg_launch_us": round(step_s * 1e6, 2)},
+        "breakdown_us": {"draft_step_mean": round(float(step_ms.mean()) * 1e3, 2),
+                         "draft_step_min": round(float(step_ms.min()) * 1e3, 2),
+                         "draft_total": round(float(step_ms.sum(1).mean()) * 1e3, 2),
+                         "schedule": round(float(sched_ms.mean()) * 1e3, 2),
+                         "verify": round(float(ver_ms.mean()) * 1e3, 2),
+                         "round_gpu": round(float(gpu_round_ms.mean()) * 1e3, 2),
+                         "round_wall": round(ms_round * 1e3, 2)},
+        "verify_roofline": {"bytes": vb, "achieved_GBps": round(vb / (ver_ms.mean() * 1e-3) / 1e9, 1)},
+        "draft_only_tokens_per_s": round(R * g / (step_ms.sum(1).mean() * 1e-3), 1),
+        "budget_last_round": int(buf.budget.item()),
+        "tau_mean_last_round": round(float(buf.tau_mean.item()), 4),
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline and os.environ.get("RANK", "0") == "0":
+        print("# timing the CPU oracle on a bounded sample ...", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(inp, 0)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,169 @@
+/*
+ * dspark.h -- C ABI of the DSpark semi-autoregressive drafting hot path for
+ * AMD MI355X (gfx950).  Library: libdspark.so (hand-written HIP kernels).
+ *
+ * Sources (cited by page title and section):
+ *   [P1] "DSpark" (rainlin-net.pages.dev/llm-inference/dspark)
+ *   [P2] "投机解码的新做法：整块草稿、按负载验证与 PD 分离" (anrans.github.io
+ *        ai-infra-handbooks, serving/frontier/spec-next)
+ *   [P3] "DSpark: Speculative decodingを活用したLLM推論の高速化" (ja.news.hada.io)
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless stated otherwise.  Every buffer is
+ *     owned by the caller; the library never allocates, frees or
+ *     synchronises.  Each call only enqueues kernels on `stream` (0 = the
+ *     default stream) and returns.
+ *   - Arguments are validated on the host before any HIP call; a failed check
+ *     returns an error status and enqueues nothing.  Launch failures return
+ *     DSPARK_ERR_LAUNCH.  Faults inside kernels surface at the caller's next
+ *     synchronisation.  Device data (token ids, NaNs) is not checked.
+ *   - Outputs are overwritten; outputs must not alias inputs.
+ *   - Layouts are row-major and dense:
+ *       W1   [V][rank]       Markov embedding table (P1 §2.3, W1 in R^{V x r})
+ *       W2t  [V][rank]       the Markov projection W2 in R^{r x V} (P1 §2.3)
+ *                            stored vocabulary-major, i.e. W2t[v][i] = W2[i][v]
+ *                            (the weight layout of a rank->vocab linear layer)
+ *       U    [R][gamma][V]   backbone base logits U_1..U_gamma, fp32 (P1 §2.1)
+ *       h    [R][gamma][d]   backbone hidden states h_1..h_gamma (P1 §2.1)
+ *       w    [d + rank]      confidence weights, fp32: w[0:d] for h_k,
+ *                            w[d:] for W1[x_{k-1}] (P1 §3.1, eq. c_k)
+ *       x    [R][gamma+1]    int32 token block; x[r][0] is the anchor x_0,
+ *                            x[r][k] the token drafted at position k
+ *       p, lse, c, a  [R][gamma] fp32, position k stored at column k-1
+ *   - W1, W2t and h share one element type `dt`: DSPARK_BF16 (raw bf16 bits)
+ *     or DSPARK_F32.
+ *   - Random numbers come from a counter-based generator (the PCG hash of
+ *     Jarzynski & Olano, JCGT 2020): for stream s, request r, position k and
+ *     vocabulary entry v, key = pcg folded over (seed low word, seed high
+ *     word, s, r, k); bits = pcg(key + v); u = ((bits >> 9) + 0.5) * 2^-23.
+ *     Streams: 1 draft sampling, 2 acceptance tests, 3 residual resampling,
+ *     4 bonus sampling.  Outputs are therefore a deterministic function of
+ *     (inputs, seed), and repeated calls give bit-identical results.
+ *
+ * Limits: 1 <= R <= 512; 1 <= gamma <= 16; 2 <= V <= 2^24;
+ *         bf16: rank multiple of 16, 16 <= rank <= 256;
+ *         fp32: rank multiple of 4, 4 <= rank <= 128;  1 <= d <= 65536;
+ *         W1, W2t, ws (and U, target when V % 4 == 0) 16-byte aligned;
+ *         R * gamma <= 8192 for dspark_schedule.
+ */
+#ifndef DSPARK_H
+#define DSPARK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* dspark_stream_t; /* a hipStream_t */
+
+typedef enum {
+  DSPARK_OK = 0,
+  DSPARK_ERR_NULL = 1,      /* a required pointer is NULL */
+  DSPARK_ERR_SHAPE = 2,     /* a size is out of range or inconsistent */
+  DSPARK_ERR_DTYPE = 3,     /* unknown element type */
+  DSPARK_ERR_VALUE = 4,     /* bad scalar (temperature < 0 or NaN, k out of range) */
+  DSPARK_ERR_WORKSPACE = 5, /* workspace NULL or smaller than dspark_workspace_bytes() */
+  DSPARK_ERR_LAUNCH = 6     /* a kernel launch failed */
+} dspark_status;
+
+typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
+
+typedef enum {
+  DSPARK_OP_DRAFT_STEP = 0,
+  DSPARK_OP_SCHEDULE = 1,
+  DSPARK_OP_VERIFY = 2
+} dspark_op;
+
+/* Bytes of device workspace entry point `op` needs for these sizes (0 if the
+ * sizes are invalid).  Host-only; makes no HIP call. */
+size_t dspark_workspace_bytes(int op, int R, int V, int rank, int gamma);
+
+/* Human-readable name of a status code (static string). Host-only. */
+const char* dspark_status_string(int status);
+
+/*
+ * One sequential draft step k (1 <= k <= gamma) for all R requests
+ * [P1 §2.2 eq. p_k; §2.3 eq. B; P1 §6.2 loop; P3 アーキテクチャ]:
+ *   e_r   = W1[x[r][k-1]]                         gather (one lookup)
+ *   z_r,v = U[r][k-1][v] + e_r . W2t[v]           bias + base logits
+ *   T > 0: s = z / T, lse = log sum_v exp(s_v),
+ *          x[r][k] = lowest v maximising s_v + G_v, G_v = -ln(-ln u_v) from
+ *          stream 1 at (r, k, v); p[r][k-1] = exp(s_x - lse).
+ *   T = 0: x[r][k] = lowest argmax_v z; p = 1; lse := max_v z.
+ * If h and w are both non-NULL, also the confidence head and survival
+ * product [P1 §3.1 eq. c_k; §1.1 eq. a_j]:
+ *   c[r][k-1] = sigma(w[0:d] . h[r][k-1] + w[d:] . e_r)       (fp32)
+ *   a[r][k-1] = (k == 1 ? 1 : a[r][k-2]) * c[r][k-1]           (one fp32 multiply)
+ * (c and a must then be non-NULL; with h == w == NULL they are not touched.)
+ * z_debug, if non-NULL, receives z as fp32 [R][V] (testing only).
+ * Reads x[:, k-1]; writes x[:, k], p, lse (and c, a) at column k-1.
+ * ws: dspark_workspace_bytes(DSPARK_OP_DRAFT_STEP, ...) bytes of device memory.
+ */
+dspark_status dspark_draft_step(int R, int V, int rank, int d, int gamma, int k, int dt,
+                                const void* W1, const void* W2t, const float* U,
+                                const void* h, const float* w, float temperature,
+                                uint64_t seed, int32_t* x, float* p, float* lse, float* c,
+                                float* a, float* z_debug, void* ws, size_t ws_bytes,
+                                dspark_stream_t stream);
+
+/*
+ * Confidence head and survival for a whole drafted block
+ * [P1 §3.1 eq. c_k; P1 §1.1 eq. a_j; §4.1 eq. tau]:
+ *   c[r][k-1] = sigma(w[0:d] . h[r][k-1] + w[d:] . W1[x[r][k-1]]),  k = 1..gamma
+ *   a[r][j]   = fp32 running product c[r][0] * ... * c[r][j], left to right.
+ * Same arithmetic as the fused path of dspark_draft_step.
+ */
+dspark_status dspark_confidence(int R, int gamma, int d, int rank, int V, int dt,
+                                const void* h, const void* W1, const int32_t* x,
+                                const float* w, float* c, float* a, dspark_stream_t stream);
+
+/*
+ * Hardware-aware prefix scheduler [P1 §4.1 eqs. B, tau, Theta and the global
+ * sort; P1 §4.2 early stop; P3 スケジューラ; P2 "按负载决定验证多少"]:
+ *   sort all N = R*gamma candidates (r, j) by key (a[r][j] descending, flat
+ *   index r*gamma + j ascending); q_i = round-half-even(a_i * 2^32) (int64);
+ *   G_b = q_1 + ... + q_b; tau_fix(b) = R*2^32 + G_b;
+ *   Theta_fix(b) = (double)tau_fix(b) * sps[R + b];
+ *   admit b+1 while Theta_fix(b+1) > Theta_fix(b) (strictly); stop at the first
+ *   non-increase.  Outputs (device): ell[R] = admitted positions of request r
+ *   (always a prefix), *budget = b*, *theta = Theta_fix(b*) * 2^-32 (tokens/s;
+ *   may be NULL).
+ * sps: fp64 [sps_len], steps/s at B verified tokens, B = 0..R*(1+gamma)
+ * (sps_len >= R*(1+gamma)+1).  a: fp32 [R][gamma], values in [0, 1].
+ * One workgroup; R*gamma <= 8192.
+ */
+dspark_status dspark_schedule(int R, int gamma, const float* a, const double* sps, int sps_len,
+                              int32_t* ell, int32_t* budget, double* theta, void* ws,
+                              size_t ws_bytes, dspark_stream_t stream);
+
+/*
+ * Verification of drafted blocks against target logits [P1 §3.1 eq. c*;
+ * standard rejection sampling: P1 opening and §2.2, P3 問題定義]:
+ *   for every (r, k): p_d = softmax((U[r][k-1] + W1[x[r][k-1]] . W2) / T),
+ *   p_t = softmax(target[r][k-1] / T);  c_star[r][k-1] = 1 - 1/2 |p_d - p_t|_1.
+ *   for j = 1..ell[r]: accept x[r][j] iff u(stream 2, r, j, v=0) <
+ *   p_t(x_j) / p_d_x[r][j-1]  (p_d_x = the draft probabilities kept by
+ *   dspark_draft_step).  At the first rejection next_token[r] = Gumbel-argmax of
+ *   log(p_t - p_d) over {v : p_t(v) > p_d(v)} (stream 3 at (r, j)); if all are
+ *   accepted, next_token[r] = Gumbel sample of p_t at row ell[r]+1 (stream 4),
+ *   or -1 when ell[r] = gamma.  n_accept[r] = accepted count; tau[r] =
+ *   n_accept[r] + 1; *tau_mean = mean of tau over requests (fp32).
+ *   T = 0: both laws are point masses (draft: on x_j; target: lowest argmax).
+ * lse_d: [R][gamma] fp32 draft log-normalisers from dspark_draft_step.
+ * target: fp32 [R][gamma][V].  ws: dspark_workspace_bytes(DSPARK_OP_VERIFY,...).
+ */
+dspark_status dspark_verify(int R, int V, int rank, int gamma, int dt, const void* W1,
+                            const void* W2t, const float* U, const float* target,
+                            const int32_t* x, const float* lse_d, const float* p_d_x,
+                            const int32_t* ell, float temperature, uint64_t seed,
+                            float* c_star, int32_t* n_accept, int32_t* next_token,
+                            int32_t* tau, float* tau_mean, void* ws, size_t ws_bytes,
+                            dspark_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSPARK_H */

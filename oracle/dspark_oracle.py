@@ -49,9 +49,9 @@ Readings taken where the pages are silent (each also listed in the design doc):
   * the global sort key is (a descending, flat index req*gamma+j ascending);
     the early stop admits candidate b+1 only if Theta strictly increases;
     Theta(0) = R * SPS(R);
-  * verification: accept iff u < p_t(x)/p_d(x), with p_d(x) the kept draft
-    probability (1 under greedy drafting, whose law is the point mass on the
-    drafted token); the first rejection resamples
+  * verification: accept iff u < p_t(x)/p_d(x); under greedy drafting (T = 0)
+    the draft law at position k is the point mass on the drafted x_k (so
+    p_d(x) = 1 and c*_k = p_t(x_k)); the first rejection resamples
     from max(0, p_t - p_d) by Gumbel-argmax of log(p_t - p_d); all accepted ->
     bonus sampled from p_t at position ell+1 (none when ell = gamma, id -1);
     realised tau per request = accepted + 1.
@@ -322,14 +322,15 @@ def verify(U, Tl, W1, W2t, x, ell, T, seed, req_ids):
         req = int(req_ids[i])
         z_d = draft_logits(U[i], W1, W2t, x[i, :g])              # rows k = 1..gamma
         z_t = np.asarray(Tl[i], dtype=np.float64)
-        p_d = draft_distribution(z_d, T)
+        # greedy drafting's law at position k is the point mass on its drafted token
+        p_d = draft_distribution(z_d, T) if T > 0 else np.eye(V)[x[i, 1:]]
         p_t = draft_distribution(z_t, T)
         out["c_star"].append(tv_acceptance(p_d, p_t))
         out["overlap"].append(np.minimum(p_d, p_t).sum(axis=-1))
         rows = np.arange(g)
         # the kept draft probability of each drafted token; under greedy drafting
         # the draft law at position j is the point mass on the drafted x_j itself
-        pdx = p_d[rows, x[i, 1:]] if T > 0 else np.ones(g)
+        pdx = p_d[rows, x[i, 1:]]
         ptx = p_t[rows, x[i, 1:]]
         out["p_d_x"].append(pdx)
         out["p_t_x"].append(ptx)
@@ -341,8 +342,7 @@ def verify(U, Tl, W1, W2t, x, ell, T, seed, req_ids):
             if u < ratio:
                 n_acc += 1
                 continue
-            law_d = p_d[j - 1] if T > 0 else np.eye(V)[x[i, j]]
-            r = np.maximum(p_t[j - 1] - law_d, 0.0)
+            r = np.maximum(p_t[j - 1] - p_d[j - 1], 0.0)
             G = gumbel(uniforms(seed, STREAM_RESID, req, j, v))
             if np.any(r > 0):
                 with np.errstate(divide="ignore"):

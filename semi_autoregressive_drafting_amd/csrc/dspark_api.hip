@@ -1,0 +1,202 @@
+// C ABI of the DSpark drafting hot path (declared in include/dspark.h).
+//
+// Every entry point validates its arguments on the host before touching HIP,
+// so each error status can be produced on a machine without a GPU.  The
+// library never allocates, frees or synchronises; it only enqueues kernels on
+// the caller's stream.
+#include <math.h>
+#include <stdint.h>
+
+#include "dspark.h"
+#include "dspark_kernels.h"
+
+using namespace dspark;
+
+namespace {
+
+constexpr int kMaxR = 512;
+constexpr int kMaxGamma = 16;
+constexpr int kMaxV = 1 << 24;
+constexpr int kMaxD = 65536;
+constexpr int kMaxSched = 8192;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+dspark_status check_rank(int dt, int rank) {
+  if (dt == DSPARK_BF16) {
+    if (rank < 16 || rank > 256 || rank % 16 != 0) return DSPARK_ERR_SHAPE;
+  } else if (dt == DSPARK_F32) {
+    if (rank < 4 || rank > 128 || rank % 4 != 0) return DSPARK_ERR_SHAPE;
+  } else {
+    return DSPARK_ERR_DTYPE;
+  }
+  return DSPARK_OK;
+}
+
+bool bad_temperature(float T) { return !(T >= 0.0f) || isinf(T); }
+
+float kscale_of(float T) { return T > 0.0f ? (float)(1.4426950408889634 / (double)T) : 1.0f; }
+
+}  // namespace
+
+extern "C" {
+
+const char* dspark_status_string(int status) {
+  switch (status) {
+    case DSPARK_OK: return "ok";
+    case DSPARK_ERR_NULL: return "required pointer is NULL";
+    case DSPARK_ERR_SHAPE: return "size out of range, inconsistent or misaligned";
+    case DSPARK_ERR_DTYPE: return "unknown element type";
+    case DSPARK_ERR_VALUE: return "bad scalar argument";
+    case DSPARK_ERR_WORKSPACE: return "workspace missing or too small";
+    case DSPARK_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t dspark_workspace_bytes(int op, int R, int V, int rank, int gamma) {
+  (void)rank;
+  if (R < 1 || R > kMaxR || V < 2 || V > kMaxV || gamma < 1 || gamma > kMaxGamma) return 0;
+  switch (op) {
+    case DSPARK_OP_DRAFT_STEP: return plan_draft_step(R, V).ws_bytes;
+    case DSPARK_OP_SCHEDULE: return 0;
+    case DSPARK_OP_VERIFY: return plan_verify(R, V, gamma).ws_bytes;
+    default: return 0;
+  }
+}
+
+dspark_status dspark_draft_step(int R, int V, int rank, int d, int gamma, int k, int dt,
+                                const void* W1, const void* W2t, const float* U,
+                                const void* h, const float* w, float temperature,
+                                uint64_t seed, int32_t* x, float* p, float* lse, float* c,
+                                float* a, float* z_debug, void* ws, size_t ws_bytes,
+                                dspark_stream_t stream) {
+  if (dt != DSPARK_F32 && dt != DSPARK_BF16) return DSPARK_ERR_DTYPE;
+  if (!W1 || !W2t || !U || !x || !p || !lse) return DSPARK_ERR_NULL;
+  if ((h == nullptr) != (w == nullptr)) return DSPARK_ERR_NULL;
+  if (h && (!c || !a)) return DSPARK_ERR_NULL;
+  if (R < 1 || R > kMaxR || V < 2 || V > kMaxV || gamma < 1 || gamma > kMaxGamma)
+    return DSPARK_ERR_SHAPE;
+  dspark_status s = check_rank(dt, rank);
+  if (s != DSPARK_OK) return s;
+  if (h && (d < 1 || d > kMaxD)) return DSPARK_ERR_SHAPE;
+  if (!aligned16(W1) || !aligned16(W2t) || ((V % 4) == 0 && !aligned16(U)))
+    return DSPARK_ERR_SHAPE;
+  if (k < 1 || k > gamma || bad_temperature(temperature)) return DSPARK_ERR_VALUE;
+  const StepPlan plan = plan_draft_step(R, V);
+  if (!ws || ws_bytes < plan.ws_bytes || !aligned16(ws)) return DSPARK_ERR_WORKSPACE;
+
+  StepArgs args{};
+  args.R = R;
+  args.V = V;
+  args.rank = rank;
+  args.d = d;
+  args.gamma = gamma;
+  args.k = k;
+  args.bf16 = dt == DSPARK_BF16;
+  args.greedy = temperature == 0.0f;
+  args.W1 = W1;
+  args.W2t = W2t;
+  args.U = U;
+  args.h = h;
+  args.w = w;
+  args.kscale = kscale_of(temperature);
+  args.seed = seed;
+  args.x = x;
+  args.p = p;
+  args.lse = lse;
+  args.c = c;
+  args.a = a;
+  args.z_debug = z_debug;
+  args.part = static_cast<float*>(ws);
+  args.n_parts = plan.n_parts;
+  args.n_vtiles = plan.n_vtiles;
+  args.n_slabs = plan.n_slabs;
+  args.n_groups = plan.n_groups;
+  if (launch_draft_step(args, plan, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return DSPARK_ERR_LAUNCH;
+  return DSPARK_OK;
+}
+
+dspark_status dspark_confidence(int R, int gamma, int d, int rank, int V, int dt,
+                                const void* h, const void* W1, const int32_t* x,
+                                const float* w, float* c, float* a, dspark_stream_t stream) {
+  if (dt != DSPARK_F32 && dt != DSPARK_BF16) return DSPARK_ERR_DTYPE;
+  if (!h || !W1 || !x || !w || !c || !a) return DSPARK_ERR_NULL;
+  if (R < 1 || R > kMaxR || gamma < 1 || gamma > kMaxGamma || d < 1 || d > kMaxD || V < 2 ||
+      V > kMaxV)
+    return DSPARK_ERR_SHAPE;
+  dspark_status s = check_rank(dt, rank);
+  if (s != DSPARK_OK) return s;
+  ConfArgs args{R, gamma, d, rank, V, dt == DSPARK_BF16, h, W1, x, w, c, a};
+  if (launch_confidence(args, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return DSPARK_ERR_LAUNCH;
+  return DSPARK_OK;
+}
+
+dspark_status dspark_schedule(int R, int gamma, const float* a, const double* sps, int sps_len,
+                              int32_t* ell, int32_t* budget, double* theta, void* ws,
+                              size_t ws_bytes, dspark_stream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (!a || !sps || !ell || !budget) return DSPARK_ERR_NULL;
+  if (R < 1 || R > kMaxR || gamma < 1 || gamma > kMaxGamma || R * gamma > kMaxSched)
+    return DSPARK_ERR_SHAPE;
+  if (sps_len < R * (1 + gamma) + 1) return DSPARK_ERR_SHAPE;
+  SchedArgs args{R, gamma, a, sps, ell, budget, theta};
+  if (launch_schedule(args, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return DSPARK_ERR_LAUNCH;
+  return DSPARK_OK;
+}
+
+dspark_status dspark_verify(int R, int V, int rank, int gamma, int dt, const void* W1,
+                            const void* W2t, const float* U, const float* target,
+                            const int32_t* x, const float* lse_d, const float* p_d_x,
+                            const int32_t* ell, float temperature, uint64_t seed,
+                            float* c_star, int32_t* n_accept, int32_t* next_token,
+                            int32_t* tau, float* tau_mean, void* ws, size_t ws_bytes,
+                            dspark_stream_t stream) {
+  if (dt != DSPARK_F32 && dt != DSPARK_BF16) return DSPARK_ERR_DTYPE;
+  if (!W1 || !W2t || !U || !target || !x || !lse_d || !p_d_x || !ell || !c_star || !n_accept ||
+      !next_token || !tau || !tau_mean)
+    return DSPARK_ERR_NULL;
+  if (R < 1 || R > kMaxR || V < 2 || V > kMaxV || gamma < 1 || gamma > kMaxGamma)
+    return DSPARK_ERR_SHAPE;
+  dspark_status s = check_rank(dt, rank);
+  if (s != DSPARK_OK) return s;
+  if (!aligned16(W1) || !aligned16(W2t) ||
+      ((V % 4) == 0 && (!aligned16(U) || !aligned16(target))))
+    return DSPARK_ERR_SHAPE;
+  if (bad_temperature(temperature)) return DSPARK_ERR_VALUE;
+  const VerifyPlan plan = plan_verify(R, V, gamma);
+  if (!ws || ws_bytes < plan.ws_bytes || !aligned16(ws)) return DSPARK_ERR_WORKSPACE;
+
+  VerifyArgs args{};
+  args.R = R;
+  args.V = V;
+  args.rank = rank;
+  args.gamma = gamma;
+  args.bf16 = dt == DSPARK_BF16;
+  args.greedy = temperature == 0.0f;
+  args.W1 = W1;
+  args.W2t = W2t;
+  args.U = U;
+  args.target = target;
+  args.x = x;
+  args.lse_d = lse_d;
+  args.p_d_x = p_d_x;
+  args.ell = ell;
+  args.kscale = kscale_of(temperature);
+  args.seed = seed;
+  args.c_star = c_star;
+  args.n_accept = n_accept;
+  args.next_token = next_token;
+  args.tau = tau;
+  args.tau_mean = tau_mean;
+  args.ws = static_cast<unsigned char*>(ws);
+  if (launch_verify(args, plan, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return DSPARK_ERR_LAUNCH;
+  return DSPARK_OK;
+}
+
+}  // extern "C"

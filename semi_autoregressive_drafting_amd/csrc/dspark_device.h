@@ -1,0 +1,188 @@
+// Device-side building blocks shared by the DSpark kernels (gfx950 only).
+//
+//  * Counter-based generator: the PCG hash of Jarzynski & Olano ("Hash Functions
+//    for GPU Rendering", JCGT 9(3), 2020) -- one step of the 32-bit LCG with
+//    multiplier 747796405 and increment 2891336453, then PCG's RXS-M-XS output
+//    permutation with multiplier 277803737.  A row (seed, stream, request,
+//    position) gets a key by folding the seed's low word, its high word, the
+//    stream id, the request and the position into the hash one after another;
+//    element v of the row draws bits = pcg(key + v) and u = ((bits >> 9) + 0.5)
+//    * 2^-23, an odd multiple of 2^-24 that fp32 holds exactly.
+//  * MFMA fragment traits for bf16 (v_mfma_f32_32x32x16_bf16) and fp32
+//    (v_mfma_f32_32x32x2f32) weights.  Both produce the 32x32 fp32 tile in the
+//    same lane layout: lane l holds column l % 32 and, in accumulator i, row
+//    8*(i/4) + 4*(l/32) + i%4.
+//  * The partial-result record of the online softmax + Gumbel race and its
+//    merge (commutative; callers fix the merge order so results are
+//    bit-reproducible).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dspark {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+
+constexpr uint32_t kLcgMul = 747796405u;
+constexpr uint32_t kLcgInc = 2891336453u;
+constexpr uint32_t kRxsMul = 277803737u;
+
+constexpr uint32_t kStreamDraft = 1, kStreamAccept = 2, kStreamResid = 3, kStreamBonus = 4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Output permutation applied to an LCG state.
+__device__ __forceinline__ uint32_t rxs_m_xs(uint32_t state) {
+  uint32_t word = ((state >> ((state >> 28u) + 4u)) ^ state) * kRxsMul;
+  return (word >> 22u) ^ word;
+}
+
+__device__ __forceinline__ uint32_t pcg(uint32_t v) { return rxs_m_xs(v * kLcgMul + kLcgInc); }
+
+__device__ __forceinline__ uint32_t row_key(uint64_t seed, uint32_t stream, uint32_t req,
+                                            uint32_t k) {
+  uint32_t h = pcg((uint32_t)(seed & 0xFFFFFFFFull));
+  h = pcg(h ^ (uint32_t)(seed >> 32));
+  h = pcg(h ^ stream);
+  h = pcg(h ^ req);
+  return pcg(h ^ k);
+}
+
+// LCG state of element v of a row with key `key`: (key + v) * mul + inc.  For
+// consecutive v the states differ by kLcgMul, so the first multiply is hoisted.
+__device__ __forceinline__ uint32_t row_state(uint32_t key, uint32_t v) {
+  return (key + v) * kLcgMul + kLcgInc;
+}
+
+__device__ __forceinline__ float bits_to_uniform(uint32_t bits) {
+  return fmaf((float)(bits >> 9), 0x1p-23f, 0x1p-24f);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// ---------------------------------------------------------------------------
+// MFMA weight traits.  `row` points at one rank-vector (a row of W1 or W2t).
+// ---------------------------------------------------------------------------
+struct WBf16 {
+  using store_t = uint16_t;
+  using frag_t = bf16x8_t;
+  static constexpr int kKStep = 16;  // k per MFMA
+  static constexpr int kHalf = 8;    // k per lane half
+  static constexpr int kMaxKs = 16;  // rank <= 256
+  __device__ static frag_t load(const store_t* row, int ks, int half) {
+    return *reinterpret_cast<const bf16x8_t*>(row + ks * kKStep + half * kHalf);
+  }
+  __device__ static frag_t zero() { return frag_t{}; }
+  __device__ static f32x16_t mma(frag_t a, frag_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static float to_f32(store_t v) { return __uint_as_float((uint32_t)v << 16); }
+};
+
+struct WF32 {
+  using store_t = float;
+  using frag_t = float;
+  static constexpr int kKStep = 2;
+  static constexpr int kHalf = 1;
+  static constexpr int kMaxKs = 64;  // rank <= 128
+  __device__ static frag_t load(const store_t* row, int ks, int half) {
+    return row[ks * kKStep + half * kHalf];
+  }
+  __device__ static frag_t zero() { return 0.0f; }
+  __device__ static f32x16_t mma(frag_t a, frag_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+  __device__ static float to_f32(store_t v) { return v; }
+};
+
+// MFMA row m of a 32-wide vocabulary tile is mapped to tile column perm(m) so
+// that accumulator i of lane l holds vocabulary entry 16*(l/32) + i: each lane
+// then owns 16 consecutive entries of one request.
+__device__ __forceinline__ int tile_perm(int m) {
+  return 16 * ((m >> 2) & 1) + 4 * (m >> 3) + (m & 3);
+}
+
+// ---------------------------------------------------------------------------
+// Partial result of the online softmax + Gumbel race over a vocabulary range,
+// in log2 units of s = z / T (t = s * log2 e):
+//   m     running maximum of t          S     sum of 2^(t - m)
+//   key   t_best - log2(L_best), L = -log2(u) (an exponential variate up to
+//         the factor ln 2): the winner's Gumbel-perturbed score in log2 units,
+//         up to a constant common to all entries; larger wins, ties -> lower id
+//   tbest t of the winner               idx   winner's vocabulary id (-1: none)
+// Greedy (T = 0) reuses the record with t = z, key = z, S unused.
+// ---------------------------------------------------------------------------
+struct Rec {
+  float m, S, key, tbest;
+  int idx;
+};
+
+__device__ __forceinline__ bool rec_beats(float k1, int i1, float k2, int i2) {
+  if (i2 < 0) return i1 >= 0;
+  if (i1 < 0) return false;
+  return (k1 > k2) || (k1 == k2 && i1 < i2);
+}
+
+__device__ __forceinline__ Rec rec_merge(const Rec& a, const Rec& b) {
+  Rec r;
+  r.m = fmaxf(a.m, b.m);
+  if (r.m == -INFINITY) {
+    r.S = 0.0f;
+  } else {
+    r.S = a.S * fast_exp2(a.m - r.m) + b.S * fast_exp2(b.m - r.m);
+  }
+  bool take_a = rec_beats(a.key, a.idx, b.key, b.idx);
+  r.key = take_a ? a.key : b.key;
+  r.tbest = take_a ? a.tbest : b.tbest;
+  r.idx = take_a ? a.idx : b.idx;
+  return r;
+}
+
+__device__ __forceinline__ Rec rec_shfl_xor(const Rec& a, int mask) {
+  Rec r;
+  r.m = __shfl_xor(a.m, mask);
+  r.S = __shfl_xor(a.S, mask);
+  r.key = __shfl_xor(a.key, mask);
+  r.tbest = __shfl_xor(a.tbest, mask);
+  r.idx = __shfl_xor(a.idx, mask);
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// Confidence head c = sigma(w[0:d] . h + w[d:] . e)  [P1 §3.1, eq. c_k].  The
+// fused draft-step combine and the batched confidence kernel both use these two
+// functions with 256 threads, so their c values are bit-identical.
+// ---------------------------------------------------------------------------
+template <class W>
+__device__ __forceinline__ float conf_partial(const typename W::store_t* hrow,
+                                              const typename W::store_t* erow, const float* w,
+                                              int d, int rank, int t) {
+  float dot = 0.0f;
+  for (int j = t; j < d; j += 256) dot = fmaf(w[j], W::to_f32(hrow[j]), dot);
+  for (int j = t; j < rank; j += 256) dot = fmaf(w[d + j], W::to_f32(erow[j]), dot);
+  return dot;
+}
+
+// Fixed-order tree sum over 256 threads (all threads call it; result in all).
+__device__ __forceinline__ float block_sum256(float v, float* sbuf) {
+  const int t = threadIdx.x;
+  sbuf[t] = v;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (t < s) sbuf[t] = sbuf[t] + sbuf[t + s];
+    __syncthreads();
+  }
+  const float r = sbuf[0];
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ float sigmoid_f32(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+}  // namespace dspark

@@ -1,0 +1,102 @@
+// Internal interface between the C-ABI host layer (dspark_api.hip) and the
+// kernel launchers.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dspark {
+
+// Launch shape of one draft step (see markov_step.hip).
+struct StepPlan {
+  bool shared;     // 4 waves = 4 request tiles sharing an LDS W2t tile
+  int grid_x, grid_y;
+  int n_parts;     // partial records per request
+  int n_slabs;     // shared: vocabulary slabs per request group
+  int n_groups;    // shared: groups of 128 requests
+  int n_vtiles;    // 32-wide vocabulary tiles
+  size_t ws_bytes; // workspace: 5 planes of R x n_parts 32-bit words
+};
+
+struct StepArgs {
+  int R, V, rank, d, gamma, k;
+  bool bf16, greedy;
+  const void* W1;
+  const void* W2t;
+  const float* U;
+  const void* h;
+  const float* w;
+  float kscale;  // log2(e) / T
+  uint64_t seed;
+  int32_t* x;
+  float* p;
+  float* lse;
+  float* c;
+  float* a;
+  float* z_debug;
+  float* part;
+  int n_parts, n_vtiles, n_slabs, n_groups;
+};
+
+StepPlan plan_draft_step(int R, int V);
+hipError_t launch_draft_step(const StepArgs& a, const StepPlan& plan, hipStream_t stream);
+
+struct ConfArgs {
+  int R, gamma, d, rank, V;
+  bool bf16;
+  const void* h;
+  const void* W1;
+  const int32_t* x;
+  const float* w;
+  float* c;
+  float* a;
+};
+hipError_t launch_confidence(const ConfArgs& a, hipStream_t stream);
+
+struct SchedArgs {
+  int R, gamma;
+  const float* a;
+  const double* sps;
+  int32_t* ell;
+  int32_t* budget;
+  double* theta;
+};
+hipError_t launch_schedule(const SchedArgs& a, hipStream_t stream);
+
+// Verification (see verify.hip).
+struct VerifyPlan {
+  int n_rows;       // R * gamma
+  int n_rtiles;     // ceil(n_rows / 32)
+  int n_groups;     // groups of 4 row tiles
+  int n_slabs;      // vocabulary slabs per group
+  int n_vtiles;
+  int lse_chunks;   // vocabulary chunks per row in the target normaliser pass
+  size_t off_lse_t, off_tx, off_flag, off_lsepart, off_part, ws_bytes;
+};
+
+struct VerifyArgs {
+  int R, V, rank, gamma;
+  bool bf16, greedy;
+  const void* W1;
+  const void* W2t;
+  const float* U;
+  const float* target;
+  const int32_t* x;
+  const float* lse_d;
+  const float* p_d_x;
+  const int32_t* ell;
+  float kscale;
+  uint64_t seed;
+  float* c_star;
+  int32_t* n_accept;
+  int32_t* next_token;
+  int32_t* tau;
+  float* tau_mean;
+  unsigned char* ws;
+};
+
+VerifyPlan plan_verify(int R, int V, int gamma);
+hipError_t launch_verify(const VerifyArgs& a, const VerifyPlan& plan, hipStream_t stream);
+
+}  // namespace dspark

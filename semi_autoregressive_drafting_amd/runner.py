@@ -1,0 +1,121 @@
+"""Device-side orchestration of one DSpark round through the C ABI.
+
+Uploads a workload's inputs to GPU memory and enqueues the entry points of
+libdspark.so in order (gamma draft steps, schedule, verify).  It only moves
+buffers and calls the library; every step of the method runs in its kernels.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from . import dspark as D
+from .synth import Inputs
+
+
+@dataclass
+class DeviceInputs:
+    R: int
+    V: int
+    rank: int
+    d: int
+    gamma: int
+    dt: int
+    W1: torch.Tensor
+    W2t: torch.Tensor
+    U: torch.Tensor
+    h: torch.Tensor
+    w: torch.Tensor
+    anchor: torch.Tensor
+    sps: torch.Tensor
+    target: torch.Tensor | None
+
+    @staticmethod
+    def upload(inp: Inputs, device="cuda") -> "DeviceInputs":
+        def dev(a):
+            a = np.ascontiguousarray(a)
+            if a.dtype == np.uint16:
+                a = a.view(np.int16)
+            return torch.from_numpy(a).to(device)
+        wl = inp.wl
+        return DeviceInputs(
+            R=len(inp.req_ids), V=wl.V, rank=wl.rank, d=wl.d, gamma=wl.gamma,
+            dt=D.DSPARK_BF16 if wl.dtype == "bf16" else D.DSPARK_F32,
+            W1=dev(inp.W1_store), W2t=dev(inp.W2t_store), U=dev(inp.U), h=dev(inp.h_store),
+            w=dev(inp.w), anchor=dev(inp.anchor.astype(np.int32)), sps=dev(inp.sps),
+            target=dev(inp.target) if inp.target is not None else None)
+
+
+@dataclass
+class RoundBuffers:
+    x: torch.Tensor        # [R, gamma+1] int32
+    p: torch.Tensor        # [R, gamma] f32
+    lse: torch.Tensor
+    c: torch.Tensor
+    a: torch.Tensor
+    ws: torch.Tensor       # draft-step workspace
+    ell: torch.Tensor      # [R] int32
+    budget: torch.Tensor   # [1] int32
+    theta: torch.Tensor    # [1] f64
+    c_star: torch.Tensor   # [R, gamma] f32
+    n_accept: torch.Tensor
+    next_token: torch.Tensor
+    tau: torch.Tensor
+    tau_mean: torch.Tensor
+    vws: torch.Tensor      # verify workspace
+
+    @staticmethod
+    def allocate(di: DeviceInputs, device="cuda") -> "RoundBuffers":
+        R, g = di.R, di.gamma
+        f32 = dict(dtype=torch.float32, device=device)
+        i32 = dict(dtype=torch.int32, device=device)
+        ws = D.dspark_workspace_bytes(D.DSPARK_OP_DRAFT_STEP, R, di.V, di.rank, g)
+        vws = D.dspark_workspace_bytes(D.DSPARK_OP_VERIFY, R, di.V, di.rank, g)
+        return RoundBuffers(
+            x=torch.zeros((R, g + 1), **i32), p=torch.zeros((R, g), **f32),
+            lse=torch.zeros((R, g), **f32), c=torch.zeros((R, g), **f32),
+            a=torch.zeros((R, g), **f32), ws=torch.empty(max(ws, 16), dtype=torch.uint8, device=device),
+            ell=torch.zeros(R, **i32), budget=torch.zeros(1, **i32),
+            theta=torch.zeros(1, dtype=torch.float64, device=device),
+            c_star=torch.zeros((R, g), **f32), n_accept=torch.zeros(R, **i32),
+            next_token=torch.zeros(R, **i32), tau=torch.zeros(R, **i32),
+            tau_mean=torch.zeros(1, **f32),
+            vws=torch.empty(max(vws, 16), dtype=torch.uint8, device=device))
+
+
+def draft_step(di: DeviceInputs, buf: RoundBuffers, k: int, temperature: float, seed: int,
+               z_debug: torch.Tensor | None = None, confidence: bool = True):
+    D.dspark_draft_step(di.R, di.V, di.rank, di.d, di.gamma, k, di.dt, di.W1, di.W2t, di.U,
+                        di.h if confidence else None, di.w if confidence else None,
+                        temperature, seed, buf.x, buf.p, buf.lse,
+                        buf.c if confidence else None, buf.a if confidence else None,
+                        z_debug, buf.ws)
+
+
+def draft(di: DeviceInputs, buf: RoundBuffers, temperature: float, seed: int):
+    """gamma sequential draft steps (with confidence and survival)."""
+    buf.x[:, 0].copy_(di.anchor)
+    for k in range(1, di.gamma + 1):
+        draft_step(di, buf, k, temperature, seed)
+
+
+def schedule(di: DeviceInputs, buf: RoundBuffers):
+    D.dspark_schedule(di.R, di.gamma, buf.a, di.sps, di.sps.numel(), buf.ell, buf.budget,
+                      buf.theta)
+
+
+def verify(di: DeviceInputs, buf: RoundBuffers, temperature: float, seed: int):
+    D.dspark_verify(di.R, di.V, di.rank, di.gamma, di.dt, di.W1, di.W2t, di.U, di.target,
+                    buf.x, buf.lse, buf.p, buf.ell, temperature, seed, buf.c_star,
+                    buf.n_accept, buf.next_token, buf.tau, buf.tau_mean, buf.vws)
+
+
+def full_round(di: DeviceInputs, buf: RoundBuffers, temperature: float, seed: int):
+    """One pass of the whole hot path: draft (gamma steps, confidence, survival),
+    schedule, verify."""
+    draft(di, buf, temperature, seed)
+    schedule(di, buf)
+    if di.target is not None:
+        verify(di, buf, temperature, seed)

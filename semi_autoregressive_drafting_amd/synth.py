@@ -8,7 +8,8 @@ so the two sides always see the same bytes.
 Workloads (shapes follow the Qwen3 family the pages evaluate on: vocabulary
 151936, Markov rank 256, block lengths 7 and 16, batches up to 512):
 
-  tiny_v1024_r4_g4         V=1024, rank 32, d 64, gamma 4, R 4, all fp32
+  tiny_v1024_r4_g4         V=1024, rank 32, d 64, gamma 4, R 4, all fp32,
+                           plus target logits = U + N(0, 1)
   qwen3_4b_r32_g7          V=151936, rank 256, d 2560, gamma 7,  R 32,  bf16
   qwen3_8b_r128_g16        V=151936, rank 256, d 4096, gamma 16, R 128, bf16,
                            requests 0..R/2-1 "easy", R/2..R-1 "hard"
@@ -31,7 +32,7 @@ arrays, so any subset of requests can be regenerated on its own):
           (easy) or -1 (hard), so that w_h . h = w_h . z + mu.
   w       N(0, 1/(d + rank)) fp32, ordered [w_h (d); w_e (rank)].
   anchor  uniform token ids (int32).
-  target  U + N(0, 1) fp32 (full-round workload only).
+  target  U + N(0, 1) fp32 (full-round and tiny workloads).
   sps     SPS(B) = 1 / max(5.97e-3, 3.24e-5 * B) steps/s for B = 0..R(1+gamma).
 """
 from __future__ import annotations
@@ -69,7 +70,7 @@ WORKLOADS = {
     w.name: w
     for w in [
         Workload("tiny_v1024_r4_g4", V=1024, rank=32, d=64, gamma=4, R=4, dtype="f32",
-                 peak="three", temperatures=(1.0, 0.0),
+                 peak="three", temperatures=(1.0, 0.0), target=True,
                  description="tiny CPU-checkable instance, all fp32"),
         Workload("qwen3_4b_r32_g7", V=151936, rank=256, d=2560, gamma=7, R=32, dtype="bf16",
                  description="Qwen3-4B-shaped draft round"),
@@ -87,6 +88,13 @@ WORKLOADS = {
                  description="brute-force enumeration instance"),
     ]
 }
+
+
+def custom(name: str, **kw) -> Workload:
+    """Register an ad-hoc workload (edge and ragged shapes for tests)."""
+    wl = Workload(name=name, **kw)
+    WORKLOADS[name] = wl
+    return wl
 
 
 def _rng(seed: int, *tags: int) -> np.random.Generator:
@@ -174,10 +182,14 @@ def _request_rows(wl: Workload, seed: int, req: int, w_h: np.ndarray):
     return U, hz, T
 
 
-def generate(name: str, seed: int = 0, requests=None, threads: int | None = None) -> Inputs:
+def generate(name: str, seed: int = 0, requests=None, threads: int | None = None,
+             target: bool | None = None) -> Inputs:
     """Build the inputs of workload `name`.  `requests` (optional) selects a subset
-    of request indices; each request's rows do not depend on which others are made."""
+    of request indices; each request's rows do not depend on which others are made.
+    `target` overrides whether target logits (U + N(0, 1)) are drawn."""
     wl = WORKLOADS[name]
+    if target is not None and target != wl.target:
+        wl = Workload(**{**wl.__dict__, "target": target})
     req_ids = np.arange(wl.R) if requests is None else np.asarray(requests, dtype=np.int64)
     n = len(req_ids)
     w = (_rng(seed, _TAG_W).standard_normal(wl.d + wl.rank, dtype=np.float32)

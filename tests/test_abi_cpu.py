@@ -1,0 +1,150 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, sizes its workspaces, and rejects bad arguments on the host
+before any HIP call (fake non-NULL addresses are never dereferenced)."""
+import os
+import re
+
+import pytest
+
+from semi_autoregressive_drafting_amd import dspark as D
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dspark.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(D.LIB_PATH),
+                                reason="libdspark.so not built (run __graft_entry__.build())")
+
+FAKE = 0x10000  # 16-byte aligned, non-NULL, never dereferenced by a failing call
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:dspark_status|size_t|const char\*)\s+(dspark_\w+)\(",
+                                 text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    lib = D.load()
+    names = declared_functions()
+    assert set(names) == set(D.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_nm_lists_the_c_symbols():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", D.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    for n in declared_functions():
+        assert re.search(rf"\bT {n}$", out, flags=re.M), n
+
+
+def test_status_strings():
+    assert D.status_string(0) == "ok"
+    assert "NULL" in D.status_string(D.DSPARK_ERR_NULL)
+    assert D.status_string(99) == "unknown status"
+
+
+def test_workspace_sizes():
+    f = D.dspark_workspace_bytes
+    assert f(D.DSPARK_OP_DRAFT_STEP, 0, 1024, 32, 4) == 0
+    assert f(D.DSPARK_OP_DRAFT_STEP, 513, 1024, 32, 4) == 0
+    assert f(D.DSPARK_OP_DRAFT_STEP, 4, 1, 32, 4) == 0
+    assert f(D.DSPARK_OP_DRAFT_STEP, 4, 1024, 32, 17) == 0
+    assert f(D.DSPARK_OP_SCHEDULE, 128, 151936, 256, 16) == 0
+    assert f(99, 4, 1024, 32, 4) == 0
+    # 5 planes of R x partials 32-bit words; grows with R
+    w128 = f(D.DSPARK_OP_DRAFT_STEP, 128, 151936, 256, 16)
+    assert w128 > 0 and w128 % (5 * 128 * 4) == 0
+    assert f(D.DSPARK_OP_DRAFT_STEP, 512, 151936, 256, 7) > 0
+    assert f(D.DSPARK_OP_VERIFY, 128, 151936, 256, 7) > 128 * 7 * 8
+
+
+def _step(**kw):
+    a = dict(R=4, V=1024, rank=32, d=64, gamma=4, k=1, dt=D.DSPARK_F32, W1=FAKE, W2t=FAKE,
+             U=FAKE, h=FAKE, w=FAKE, temperature=1.0, seed=0, x=FAKE, p=FAKE, lse=FAKE, c=FAKE,
+             a=FAKE, z_debug=None, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    lib = D.load()
+    return lib.dspark_draft_step(a["R"], a["V"], a["rank"], a["d"], a["gamma"], a["k"], a["dt"],
+                                 a["W1"], a["W2t"], a["U"], a["h"], a["w"], a["temperature"],
+                                 a["seed"], a["x"], a["p"], a["lse"], a["c"], a["a"],
+                                 a["z_debug"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(W1=None), D.DSPARK_ERR_NULL),
+    (dict(U=None), D.DSPARK_ERR_NULL),
+    (dict(x=None), D.DSPARK_ERR_NULL),
+    (dict(h=None), D.DSPARK_ERR_NULL),              # h without w
+    (dict(c=None), D.DSPARK_ERR_NULL),              # confidence needs c and a
+    (dict(dt=7), D.DSPARK_ERR_DTYPE),
+    (dict(R=0), D.DSPARK_ERR_SHAPE),
+    (dict(R=513), D.DSPARK_ERR_SHAPE),
+    (dict(V=1), D.DSPARK_ERR_SHAPE),
+    (dict(gamma=17, k=1), D.DSPARK_ERR_SHAPE),
+    (dict(rank=30), D.DSPARK_ERR_SHAPE),            # fp32 rank multiple of 4
+    (dict(rank=132), D.DSPARK_ERR_SHAPE),
+    (dict(rank=24, dt=D.DSPARK_BF16), D.DSPARK_ERR_SHAPE),   # bf16 rank multiple of 16
+    (dict(rank=272, dt=D.DSPARK_BF16), D.DSPARK_ERR_SHAPE),
+    (dict(d=0), D.DSPARK_ERR_SHAPE),
+    (dict(W2t=FAKE + 4), D.DSPARK_ERR_SHAPE),       # misaligned weights
+    (dict(U=FAKE + 4), D.DSPARK_ERR_SHAPE),         # misaligned logits with V % 4 == 0
+    (dict(k=0), D.DSPARK_ERR_VALUE),
+    (dict(k=5), D.DSPARK_ERR_VALUE),
+    (dict(temperature=-1.0), D.DSPARK_ERR_VALUE),
+    (dict(temperature=float("nan")), D.DSPARK_ERR_VALUE),
+    (dict(temperature=float("inf")), D.DSPARK_ERR_VALUE),
+    (dict(ws=None), D.DSPARK_ERR_WORKSPACE),
+    (dict(ws_bytes=16), D.DSPARK_ERR_WORKSPACE),
+])
+def test_draft_step_validation(kw, status):
+    assert _step(**kw) == status
+
+
+def test_schedule_validation():
+    lib = D.load()
+    f = lib.dspark_schedule
+    assert f(4, 4, None, FAKE, 21, FAKE, FAKE, FAKE, None, 0, None) == D.DSPARK_ERR_NULL
+    assert f(4, 4, FAKE, FAKE, 21, None, FAKE, FAKE, None, 0, None) == D.DSPARK_ERR_NULL
+    assert f(4, 4, FAKE, FAKE, 20, FAKE, FAKE, FAKE, None, 0, None) == D.DSPARK_ERR_SHAPE
+    assert f(512, 17, FAKE, FAKE, 10 ** 6, FAKE, FAKE, FAKE, None, 0, None) == D.DSPARK_ERR_SHAPE
+    assert f(600, 4, FAKE, FAKE, 10 ** 6, FAKE, FAKE, FAKE, None, 0, None) == D.DSPARK_ERR_SHAPE
+
+
+def test_confidence_validation():
+    f = D.load().dspark_confidence
+    assert f(4, 4, 64, 32, 1024, 0, None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == D.DSPARK_ERR_NULL
+    assert f(4, 4, 64, 32, 1024, 5, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == D.DSPARK_ERR_DTYPE
+    assert f(4, 4, 0, 32, 1024, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == D.DSPARK_ERR_SHAPE
+    assert f(4, 4, 64, 31, 1024, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == D.DSPARK_ERR_SHAPE
+
+
+def _verify(**kw):
+    a = dict(R=4, V=1024, rank=32, gamma=4, dt=0, W1=FAKE, W2t=FAKE, U=FAKE, target=FAKE,
+             x=FAKE, lse_d=FAKE, p_d_x=FAKE, ell=FAKE, temperature=1.0, seed=0, c_star=FAKE,
+             n_accept=FAKE, next_token=FAKE, tau=FAKE, tau_mean=FAKE, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    return D.load().dspark_verify(*[a[k] for k in (
+        "R", "V", "rank", "gamma", "dt", "W1", "W2t", "U", "target", "x", "lse_d", "p_d_x",
+        "ell", "temperature", "seed", "c_star", "n_accept", "next_token", "tau", "tau_mean",
+        "ws", "ws_bytes")], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(target=None), D.DSPARK_ERR_NULL),
+    (dict(tau_mean=None), D.DSPARK_ERR_NULL),
+    (dict(dt=3), D.DSPARK_ERR_DTYPE),
+    (dict(gamma=0), D.DSPARK_ERR_SHAPE),
+    (dict(target=FAKE + 8), D.DSPARK_ERR_SHAPE),
+    (dict(temperature=-0.5), D.DSPARK_ERR_VALUE),
+    (dict(ws_bytes=0), D.DSPARK_ERR_WORKSPACE),
+])
+def test_verify_validation(kw, status):
+    assert _verify(**kw) == status
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        D._ptr(torch.zeros(4))

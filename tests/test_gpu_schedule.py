@@ -1,0 +1,78 @@
+"""GPU parity of the single-workgroup prefix scheduler: budgets, admitted
+prefixes and Theta must equal the oracle's bit for bit on identical a."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import dspark_oracle as O
+from semi_autoregressive_drafting_amd import dspark as D
+from semi_autoregressive_drafting_amd import synth
+from tests.gpu_parity import say
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_schedule(a, sps):
+    R, g = a.shape
+    ta = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+    ts = torch.from_numpy(np.ascontiguousarray(sps, dtype=np.float64)).cuda()
+    ell = torch.full((R,), -7, dtype=torch.int32, device="cuda")
+    budget = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    theta = torch.zeros(1, dtype=torch.float64, device="cuda")
+    D.dspark_schedule(R, g, ta, ts, ts.numel(), ell, budget, theta)
+    torch.cuda.synchronize()
+    return ell.cpu().numpy(), int(budget.item()), float(theta.item())
+
+
+def assert_same(a, sps, tag=""):
+    ell_g, b_g, th_g = gpu_schedule(a, sps)
+    ell_o, b_o, th_o, _, _ = O.schedule(a, sps)
+    assert b_g == b_o, (tag, b_g, b_o)
+    np.testing.assert_array_equal(ell_g, ell_o)
+    assert th_g == th_o, (tag, th_g, th_o)
+    return b_g
+
+
+def _tables(rng, R, g):
+    yield "workload", synth.sps_table(R, g)
+    knee = rng.uniform(R, R * (1 + g))
+    yield "knee", synth.sps_table(R, g, 1e-4 * knee, 1e-4)
+    B = np.arange(R * (1 + g) + 1)
+    yield "steps", 1.0 / np.maximum(2e-3, 3e-6 * np.ceil(np.maximum(B, 1) / 16) * 16)
+
+
+@pytest.mark.parametrize("R,g", [(1, 1), (1, 16), (3, 5), (4, 4), (7, 13), (32, 7),
+                                 (128, 16), (128, 7), (512, 7), (512, 16), (300, 9)])
+def test_schedule_random(R, g):
+    rng = np.random.default_rng(R * 100 + g)
+    for trial in range(3):
+        c = rng.uniform(0.0, 1.0, (R, g)).astype(np.float32)
+        c[rng.uniform(size=(R, g)) < 0.1] = 1.0          # ties along a row
+        c[rng.uniform(size=(R, g)) < 0.02] = 0.0         # zero survival
+        a = O.survival(c)
+        for name, sps in _tables(rng, R, g):
+            assert_same(a, sps, f"{R}x{g} {name} #{trial}")
+    say(f"[schedule] {R}x{g} ok")
+
+
+def test_schedule_all_equal_keys():
+    """Every candidate ties: order falls back to the flat index."""
+    a = np.full((16, 8), 0.5, dtype=np.float32)
+    assert_same(a, synth.sps_table(16, 8, 1e-3, 1e-5))
+    assert_same(np.ones((8, 8), dtype=np.float32), synth.sps_table(8, 8))
+
+
+def test_schedule_reproduces_the_plan_demo():
+    """The handbook's adaptive-verification demo inputs (torch seed 0) give the
+    printed budgets 112 / 57 / 7 on the GPU as well."""
+    from tests.test_oracle_pins import _golden, _h100_step_time, _plan_confidences
+    g = _golden("p2_plan_printout.json")
+    st = _h100_step_time(_golden("p2_cost_model_printout.json")["model"])
+    torch.manual_seed(0)
+    for row in g["rows"]:
+        batch = row["batch"]
+        a = O.survival(_plan_confidences(batch, g["gamma"]))
+        N = batch * (1 + g["gamma"])
+        sps = np.array([1.0 / (0.25e-3 + st(B)) for B in range(N + 1)])
+        assert assert_same(a, sps) == row["admitted"]
+        assert round(gpu_schedule(a, sps)[2]) == row["adaptive_tok_s"]

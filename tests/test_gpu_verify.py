@@ -1,0 +1,65 @@
+"""GPU parity of verification (per-position c*, acceptance chain, residual /
+bonus resampling, realised tau) against the oracle, fed the GPU's own drafted
+block and admitted lengths."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import dspark_oracle as O
+from semi_autoregressive_drafting_amd import runner
+from tests.gpu_parity import Case, NEAR_TIE, say
+
+pytestmark = pytest.mark.gpu
+
+CSTAR_RTOL, CSTAR_ATOL = 1e-3, 1e-5
+ACCEPT_NEAR_TIE = 1e-5
+
+
+def run_and_check(case, T, seed, ell_override=None, reqs=None):
+    di = case.di
+    buf, host, _ = case.run_draft(T, seed)
+    runner.schedule(di, buf)
+    if ell_override is not None:
+        buf.ell.copy_(torch.as_tensor(ell_override, dtype=torch.int32))
+    runner.verify(di, buf, T, seed)
+    torch.cuda.synchronize()
+    g = {n: getattr(buf, n).cpu().numpy() for n in ("ell", "c_star", "n_accept", "next_token",
+                                                    "tau", "tau_mean")}
+    R = case.wl.R
+    reqs = np.arange(R) if reqs is None else np.asarray(reqs)
+    x = host["x"].astype(np.int64)
+    res = O.verify(case.inp.U[reqs], case.inp.target[reqs], case.W1, case.W2t, x[reqs],
+                   g["ell"][reqs], T, seed, reqs)
+    # c* for every position
+    cs_g, cs_o = g["c_star"][reqs], res["c_star"]
+    assert np.all(np.abs(cs_g - cs_o) <= np.maximum(CSTAR_ATOL, CSTAR_RTOL * np.abs(cs_o))), \
+        np.abs(cs_g - cs_o).max()
+    # accept decisions / tokens: exact unless the oracle saw a near tie
+    near = (res["accept_margin"] < ACCEPT_NEAR_TIE) | (res["sample_gap"] < NEAR_TIE)
+    ok = ((g["n_accept"][reqs] == res["n_accept"]) & (g["next_token"][reqs] == res["next_token"])
+          & (g["tau"][reqs] == res["tau"]))
+    assert np.all(ok | near), np.nonzero(~ok & ~near)
+    assert (~ok).sum() <= 1e-3 * len(reqs)
+    if len(reqs) == R:
+        assert abs(float(g["tau_mean"][0]) - res["tau_mean"]) <= 1e-6 * res["tau_mean"]
+    return g, res
+
+
+@pytest.mark.parametrize("T", [1.0, 0.0])
+def test_verify_tiny(T):
+    case = Case("tiny_v1024_r4_g4")
+    g, res = run_and_check(case, T, 21)
+    say(f"[verify] tiny T={T} ell={g['ell']} n_acc={g['n_accept']} tau_mean={g['tau_mean']}")
+    # every position admitted (exercises the no-bonus case) and nothing admitted
+    run_and_check(case, T, 22, ell_override=[4, 4, 4, 4])
+    run_and_check(case, T, 23, ell_override=[0, 1, 2, 3])
+
+
+def test_verify_full_round():
+    """The full draft + schedule + verify round at R = 128, gamma = 7."""
+    case = Case("round_4b_r128_g7")
+    g, res = run_and_check(case, 1.0, 5)
+    say(f"[verify] round budget={g['ell'].sum()} tau_mean={g['tau_mean'][0]:.4f} "
+        f"c* mean={g['c_star'].mean():.4f}")
+    g, res = run_and_check(case, 1.0, 6, ell_override=np.full(128, 7), reqs=np.arange(0, 128, 4))
+    say(f"[verify] round ell=7 tau_mean={g['tau_mean'][0]:.4f}")
