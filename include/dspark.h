@@ -99,7 +99,10 @@ const char* dspark_status_string(int status);
  * (c and a must then be non-NULL; with h == w == NULL they are not touched.)
  * z_debug, if non-NULL, receives z as fp32 [R][V] (testing only).
  * Reads x[:, k-1]; writes x[:, k], p, lse (and c, a) at column k-1.
- * ws: dspark_workspace_bytes(DSPARK_OP_DRAFT_STEP, ...) bytes of device memory.
+ * ws: dspark_workspace_bytes(DSPARK_OP_DRAFT_STEP, ...) bytes of device memory,
+ * ZERO-FILLED before its first use (it holds arrival counters that every call
+ * leaves at zero again).  Calls that may run concurrently need separate
+ * workspaces.
  */
 dspark_status dspark_draft_step(int R, int V, int rank, int d, int gamma, int k, int dt,
                                 const void* W1, const void* W2t, const float* U,
@@ -107,6 +110,17 @@ dspark_status dspark_draft_step(int R, int V, int rank, int d, int gamma, int k,
                                 uint64_t seed, int32_t* x, float* p, float* lse, float* c,
                                 float* a, float* z_debug, void* ws, size_t ws_bytes,
                                 dspark_stream_t stream);
+
+/*
+ * The whole draft block: dspark_draft_step for k = 1..gamma in order on
+ * `stream` (x[:, 0] must hold the anchors), without z_debug.  Same arguments,
+ * results and workspace as the single step.
+ */
+dspark_status dspark_draft_block(int R, int V, int rank, int d, int gamma, int dt,
+                                 const void* W1, const void* W2t, const float* U,
+                                 const void* h, const float* w, float temperature,
+                                 uint64_t seed, int32_t* x, float* p, float* lse, float* c,
+                                 float* a, void* ws, size_t ws_bytes, dspark_stream_t stream);
 
 /*
  * Confidence head and survival for a whole drafted block

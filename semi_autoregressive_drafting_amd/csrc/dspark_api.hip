@@ -65,12 +65,17 @@ size_t dspark_workspace_bytes(int op, int R, int V, int rank, int gamma) {
   }
 }
 
-dspark_status dspark_draft_step(int R, int V, int rank, int d, int gamma, int k, int dt,
-                                const void* W1, const void* W2t, const float* U,
-                                const void* h, const float* w, float temperature,
-                                uint64_t seed, int32_t* x, float* p, float* lse, float* c,
-                                float* a, float* z_debug, void* ws, size_t ws_bytes,
-                                dspark_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation shared by dspark_draft_step and dspark_draft_block (k = 0 means
+// "any step"); fills `args` for step 1 on success.
+dspark_status check_draft(int R, int V, int rank, int d, int gamma, int k, int dt, const void* W1,
+                          const void* W2t, const float* U, const void* h, const float* w,
+                          float temperature, uint64_t seed, int32_t* x, float* p, float* lse,
+                          float* c, float* a, float* z_debug, void* ws, size_t ws_bytes,
+                          StepArgs& args, StepPlan& plan) {
   if (dt != DSPARK_F32 && dt != DSPARK_BF16) return DSPARK_ERR_DTYPE;
   if (!W1 || !W2t || !U || !x || !p || !lse) return DSPARK_ERR_NULL;
   if ((h == nullptr) != (w == nullptr)) return DSPARK_ERR_NULL;
@@ -82,17 +87,17 @@ dspark_status dspark_draft_step(int R, int V, int rank, int d, int gamma, int k,
   if (h && (d < 1 || d > kMaxD)) return DSPARK_ERR_SHAPE;
   if (!aligned16(W1) || !aligned16(W2t) || ((V % 4) == 0 && !aligned16(U)))
     return DSPARK_ERR_SHAPE;
-  if (k < 1 || k > gamma || bad_temperature(temperature)) return DSPARK_ERR_VALUE;
-  const StepPlan plan = plan_draft_step(R, V);
+  if (k < 0 || k > gamma || bad_temperature(temperature)) return DSPARK_ERR_VALUE;
+  plan = plan_draft_step(R, V);
   if (!ws || ws_bytes < plan.ws_bytes || !aligned16(ws)) return DSPARK_ERR_WORKSPACE;
 
-  StepArgs args{};
+  args = StepArgs{};
   args.R = R;
   args.V = V;
   args.rank = rank;
   args.d = d;
   args.gamma = gamma;
-  args.k = k;
+  args.k = k < 1 ? 1 : k;
   args.bf16 = dt == DSPARK_BF16;
   args.greedy = temperature == 0.0f;
   args.W1 = W1;
@@ -109,12 +114,52 @@ dspark_status dspark_draft_step(int R, int V, int rank, int d, int gamma, int k,
   args.a = a;
   args.z_debug = z_debug;
   args.part = static_cast<float*>(ws);
-  args.n_parts = plan.n_parts;
+  args.part2 = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) + plan.off_part2);
+  args.counters = reinterpret_cast<unsigned*>(static_cast<unsigned char*>(ws) + plan.off_counters);
   args.n_vtiles = plan.n_vtiles;
   args.n_slabs = plan.n_slabs;
   args.n_groups = plan.n_groups;
+  args.team_size = plan.team_size;
+  args.n_teams = plan.n_teams;
+  return DSPARK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dspark_status dspark_draft_step(int R, int V, int rank, int d, int gamma, int k, int dt,
+                                const void* W1, const void* W2t, const float* U,
+                                const void* h, const float* w, float temperature,
+                                uint64_t seed, int32_t* x, float* p, float* lse, float* c,
+                                float* a, float* z_debug, void* ws, size_t ws_bytes,
+                                dspark_stream_t stream) {
+  if (k < 1) return DSPARK_ERR_VALUE;
+  StepArgs args;
+  StepPlan plan;
+  const dspark_status s = check_draft(R, V, rank, d, gamma, k, dt, W1, W2t, U, h, w, temperature,
+                                      seed, x, p, lse, c, a, z_debug, ws, ws_bytes, args, plan);
+  if (s != DSPARK_OK) return s;
   if (launch_draft_step(args, plan, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return DSPARK_ERR_LAUNCH;
+  return DSPARK_OK;
+}
+
+dspark_status dspark_draft_block(int R, int V, int rank, int d, int gamma, int dt,
+                                 const void* W1, const void* W2t, const float* U,
+                                 const void* h, const float* w, float temperature,
+                                 uint64_t seed, int32_t* x, float* p, float* lse, float* c,
+                                 float* a, void* ws, size_t ws_bytes, dspark_stream_t stream) {
+  StepArgs args;
+  StepPlan plan;
+  const dspark_status s = check_draft(R, V, rank, d, gamma, 0, dt, W1, W2t, U, h, w, temperature,
+                                      seed, x, p, lse, c, a, nullptr, ws, ws_bytes, args, plan);
+  if (s != DSPARK_OK) return s;
+  for (int k = 1; k <= gamma; ++k) {
+    args.k = k;
+    if (launch_draft_step(args, plan, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+      return DSPARK_ERR_LAUNCH;
+  }
   return DSPARK_OK;
 }
 

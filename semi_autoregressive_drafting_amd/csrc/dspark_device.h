@@ -155,34 +155,56 @@ __device__ __forceinline__ Rec rec_shfl_xor(const Rec& a, int mask) {
 }
 
 // ---------------------------------------------------------------------------
-// Confidence head c = sigma(w[0:d] . h + w[d:] . e)  [P1 §3.1, eq. c_k].  The
-// fused draft-step combine and the batched confidence kernel both use these two
-// functions with 256 threads, so their c values are bit-identical.
+// Confidence head c = sigma(w[0:d] . h + w[d:] . e)  [P1 §3.1, eq. c_k], one
+// wave per (request, position): lane-strided fp32 partial dot products (16-byte
+// chunks per lane), then a butterfly over the 64 lanes (every lane ends with
+// the same bits).  The fused
+// draft step and the batched confidence kernel both use this function, so
+// their c values are bit-identical.
 // ---------------------------------------------------------------------------
 template <class W>
-__device__ __forceinline__ float conf_partial(const typename W::store_t* hrow,
-                                              const typename W::store_t* erow, const float* w,
-                                              int d, int rank, int t) {
+__device__ __forceinline__ float conf_dot_wave(const typename W::store_t* hrow,
+                                               const typename W::store_t* erow, const float* w,
+                                               int d, int rank, int lane) {
+  using store_t = typename W::store_t;
+  constexpr int kV = 16 / sizeof(store_t);  // elements per 16-byte load (8 bf16 / 4 fp32)
   float dot = 0.0f;
-  for (int j = t; j < d; j += 256) dot = fmaf(w[j], W::to_f32(hrow[j]), dot);
-  for (int j = t; j < rank; j += 256) dot = fmaf(w[d + j], W::to_f32(erow[j]), dot);
+  // h part: each lane takes kV consecutive elements per step (16-byte loads)
+  // when the row allows it, else one element per step.
+  const bool vec = (d % kV) == 0 && ((reinterpret_cast<uintptr_t>(hrow) | reinterpret_cast<uintptr_t>(w)) & 15u) == 0;
+  if (vec) {
+#pragma unroll 4
+    for (int j = lane * kV; j < d; j += 64 * kV) {
+      const u32x4_t hv = *reinterpret_cast<const u32x4_t*>(hrow + j);
+      const store_t* hs = reinterpret_cast<const store_t*>(&hv);
+#pragma unroll
+      for (int i = 0; i < kV; ++i) dot = fmaf(w[j + i], W::to_f32(hs[i]), dot);
+    }
+  } else {
+    for (int j = lane; j < d; j += 64) dot = fmaf(w[j], W::to_f32(hrow[j]), dot);
+  }
+  // Markov-embedding part (rank is a multiple of kV, rows 16-byte aligned)
+  for (int j = lane * kV; j < rank; j += 64 * kV) {
+    const u32x4_t ev = *reinterpret_cast<const u32x4_t*>(erow + j);
+    const store_t* es = reinterpret_cast<const store_t*>(&ev);
+#pragma unroll
+    for (int i = 0; i < kV; ++i) dot = fmaf(w[d + j + i], W::to_f32(es[i]), dot);
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) dot += __shfl_xor(dot, m);
   return dot;
 }
 
-// Fixed-order tree sum over 256 threads (all threads call it; result in all).
-__device__ __forceinline__ float block_sum256(float v, float* sbuf) {
-  const int t = threadIdx.x;
-  sbuf[t] = v;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (t < s) sbuf[t] = sbuf[t] + sbuf[t + s];
-    __syncthreads();
-  }
-  const float r = sbuf[0];
-  __syncthreads();
-  return r;
-}
-
 __device__ __forceinline__ float sigmoid_f32(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+__device__ __forceinline__ int clamp_token(int x, int V) { return x < 0 ? 0 : (x >= V ? V - 1 : x); }
+
+// Balanced split of T tiles over n slabs: the first n - T%n slabs get T/n
+// tiles, the rest one more (so low slab ids carry the lighter share).
+__host__ __device__ inline void slab_range(int s, int n, int T, int& b, int& e) {
+  const int q = T / n, rem = T % n, lo = n - rem;
+  b = s * q + (s > lo ? s - lo : 0);
+  e = b + q + (s >= lo ? 1 : 0);
+}
 
 }  // namespace dspark

@@ -10,13 +10,16 @@ namespace dspark {
 
 // Launch shape of one draft step (see markov_step.hip).
 struct StepPlan {
-  bool shared;     // 4 waves = 4 request tiles sharing an LDS W2t tile
+  bool shared;        // 4 waves = 4 request tiles sharing an LDS W2t tile
   int grid_x, grid_y;
-  int n_parts;     // partial records per request
-  int n_slabs;     // shared: vocabulary slabs per request group
-  int n_groups;    // shared: groups of 128 requests
-  int n_vtiles;    // 32-wide vocabulary tiles
-  size_t ws_bytes; // workspace: 5 planes of R x n_parts 32-bit words
+  int n_slabs;        // vocabulary slabs (workgroups) per request group
+  int n_groups;       // request groups (128 requests shared, 32 private)
+  int n_vtiles;       // 32-wide vocabulary tiles
+  int team_size;      // slabs merged by one team closer
+  int n_teams;        // teams per group
+  size_t off_part2;   // workspace: level-1 records at 0, level-2 records,
+  size_t off_counters;//   then n_groups x (n_teams + 1) arrival counters
+  size_t ws_bytes;
 };
 
 struct StepArgs {
@@ -35,8 +38,10 @@ struct StepArgs {
   float* c;
   float* a;
   float* z_debug;
-  float* part;
-  int n_parts, n_vtiles, n_slabs, n_groups;
+  float* part;       // level-1 records [n_slabs][5][R]
+  float* part2;      // level-2 records [n_teams][5][R]
+  unsigned* counters;
+  int n_vtiles, n_slabs, n_groups, team_size, n_teams;
 };
 
 StepPlan plan_draft_step(int R, int V);

@@ -1,28 +1,36 @@
-// Fused DSpark Markov draft step for gfx950.
+// Fused DSpark Markov draft step for gfx950: one kernel per sequential step.
 //
-// One sequential step k over R requests [P1 "DSpark" §2.2 eq. p_k, §2.3 eq. B,
-// §3.1 eq. c_k, §1.1 eq. a_j; the §6.2 vLLM loop fixes the per-position order]:
+// Step k over R requests [P1 "DSpark" §2.2 eq. p_k, §2.3 eq. B, §3.1 eq. c_k,
+// §1.1 eq. a_j; the §6.2 vLLM loop fixes the per-position order]:
 //
-//   pass 1 (markov_partial_*): for a vocabulary slab, gather E = W1[x_{k-1}],
-//     form the bias tile E . W2 with bf16 (or fp32) MFMA, add the base logits
-//     U_k, and fold the tile into an online max / sum-exp and a Gumbel race,
-//     so the R x V bias never reaches HBM.  The race is argmax_v s_v + G_v in
-//     its exponential-race form: the winner maximises e_v / L_v with
-//     e_v = 2^(t_v - m) (already needed for the sum) and L_v = -log2 u_v, which
-//     costs one logarithm per entry.  Each workgroup (shared shape) or wave
-//     (private shape) writes one partial record per request.
-//   pass 2 (markov_combine): one workgroup per request merges the records in a
-//     fixed order -> x_k, p_k(x_k), lse_k; then the confidence head and the
-//     survival product.
+//  1. Confidence head (waves of the first workgroups of each request group, one
+//     wave per request): c_k = sigma(w . [h_k; W1[x_{k-1}]]), a_k = a_{k-1} c_k.
+//  2. Stream a vocabulary slab: gather E = W1[x_{k-1}] once into VGPRs, form
+//     each 32 x 32 bias tile E . W2 with bf16 (or fp32) MFMA, add the base
+//     logits U_k and fold the tile into an online max / sum-exp and a Gumbel
+//     race, so the R x V bias never reaches HBM.  The race is argmax_v s_v + G_v
+//     in its exponential-race form: the winner maximises e_v / L_v with
+//     e_v = 2^(t_v - m) (already needed for the sum) and L_v = -log2 u_v, one
+//     logarithm per entry.
+//  3. Write one partial record per request (slab-major, device-scope atomic
+//     writes), then merge in two levels without a second kernel: the last
+//     workgroup of a team of slabs to arrive (device-scope counter) merges the
+//     team's records; the last team to arrive merges the team records in a
+//     fixed order and writes x_k, p_k(x_k) and lse_k.  Nobody waits on anybody:
+//     a workgroup that is not last simply exits.  No L2-wide fence is needed
+//     because every cross-workgroup value travels through device-scope
+//     atomics.  Counters are reset by their last user, so the workspace must
+//     be zero-filled once before its first use.
 //
 // Launch shapes (see mfma_stream.h):
-//   shared : R > 96.  4 waves = 4 request tiles (128 requests); each wave keeps
-//            its E fragments in VGPRs for the whole step and the W2t tile is
-//            staged once per workgroup in LDS.  W2t leaves HBM once per group of
-//            128 requests; the groups of one slab share an XCD (blockIdx % 8)
-//            so that their repeated W2t reads hit that XCD's L2.
-//   private: R <= 96.  Every wave streams its own vocabulary tiles with the W2t
-//            fragment loaded straight into VGPRs; grid.y = request tile.
+//   shared : R > 96.  A workgroup = 4 waves = 4 request tiles (a group of 128
+//            requests); each wave keeps its E fragments in VGPRs for the whole
+//            step and each W2t tile is staged once per workgroup in LDS.  W2t
+//            leaves HBM once per request group; the groups of one slab share an
+//            XCD (blockIdx % 8) so repeated W2t reads hit that XCD's L2.
+//   private: R <= 96.  A group = one request tile; the 4 waves of a workgroup
+//            stream interleaved tiles of the slab with W2t fragments loaded
+//            straight into VGPRs, then merge their records in LDS.
 #include "dspark_kernels.h"
 #include "mfma_stream.h"
 
@@ -31,6 +39,8 @@ namespace dspark {
 namespace {
 
 constexpr int kWaves = 4;
+constexpr int kTeamSize = 32;  // slabs merged by one team closer
+constexpr int kMaxTeams = 16;  // teams per request group (n_slabs <= 512)
 
 // Per-lane online state over the lane's vocabulary entries of one request.
 struct LaneState {
@@ -144,18 +154,147 @@ struct DraftEpi {
   }
 };
 
-__device__ __forceinline__ void store_rec(float* part, int R, int P, int r, int slot, const Rec& q) {
-  const size_t plane = (size_t)R * P;
-  const size_t o = (size_t)r * P + slot;
-  part[o] = q.m;
-  part[plane + o] = q.S;
-  part[2 * plane + o] = q.key;
-  part[3 * plane + o] = q.tbest;
-  reinterpret_cast<int*>(part)[4 * plane + o] = q.idx;
+// Records live in slab-major planes: rec[(slot * 5 + field) * R + r], so the
+// 32 or 128 requests a workgroup writes for one slot are contiguous.
+//
+// Records cross workgroups (and XCDs) inside one launch, so they are written
+// and read with device-scope atomics, which the hardware keeps coherent
+// without writing back or invalidating whole L2 caches.  Each write is an
+// exchange whose returned old value the caller folds into `chk`: using `chk`
+// before the workgroup barrier makes every write complete at the coherence
+// point before the arrival counter is incremented.
+__device__ __forceinline__ unsigned xchg(float* p, float v) {
+  return __float_as_uint(
+      __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+__device__ __forceinline__ unsigned put_rec(float* base, int R, int slot, int r, const Rec& q) {
+  float* p = base + (size_t)slot * 5 * R + r;
+  unsigned chk = xchg(p, q.m);
+  chk ^= xchg(p + R, q.S);
+  chk ^= xchg(p + 2 * R, q.key);
+  chk ^= xchg(p + 3 * R, q.tbest);
+  chk ^= xchg(p + 4 * R, __int_as_float(q.idx));
+  return chk;
+}
+
+__device__ __forceinline__ float ld(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ Rec get_rec(const float* base, int R, int slot, int r) {
+  const float* p = base + (size_t)slot * 5 * R + r;
+  return Rec{ld(p), ld(p + R), ld(p + 2 * R), ld(p + 3 * R), __float_as_int(ld(p + 4 * R))};
+}
+
+__device__ __forceinline__ Rec empty_rec() { return Rec{-INFINITY, 0.0f, -INFINITY, -INFINITY, -1}; }
+
+// Fixed-order merge of records [j0, j1) of request r by kTpr consecutive
+// threads (a power of two <= 64, inside one wave): each thread loads its
+// contiguous chunk of at most kChunk records at once (one memory round trip),
+// folds it in order, then a butterfly over the kTpr lanes.
+template <int kTpr, int kChunk>
+__device__ __forceinline__ Rec merge_range(const float* base, int R, int r, int j0, int j1,
+                                           int sub) {
+  const int n = j1 - j0;
+  const int chunk = (n + kTpr - 1) / kTpr;  // <= kChunk by construction of the plan
+  const int b = j0 + sub * chunk;
+  const int e = min(j1, b + chunk);
+  Rec buf[kChunk];
+#pragma unroll
+  for (int i = 0; i < kChunk; ++i)
+    if (b + i < e) buf[i] = get_rec(base, R, b + i, r);
+  Rec acc = empty_rec();
+#pragma unroll
+  for (int i = 0; i < kChunk; ++i)
+    if (b + i < e) acc = rec_merge(acc, buf[i]);
+#pragma unroll
+  for (int m = 1; m < kTpr; m <<= 1) {
+    const Rec o = rec_shfl_xor(acc, m);
+    acc = (sub & m) ? rec_merge(o, acc) : rec_merge(acc, o);
+  }
+  return acc;
+}
+
+// Final outputs of request r from its merged record.
+__device__ __forceinline__ void write_outputs(const StepArgs& a, int r, const Rec& f) {
+  const size_t o = (size_t)r * a.gamma + (a.k - 1);
+  a.x[(size_t)r * (a.gamma + 1) + a.k] = f.idx;
+  if (a.greedy) {
+    a.p[o] = 1.0f;
+    a.lse[o] = f.m;
+  } else {
+    const float lse2 = f.m + log2f(f.S);
+    a.p[o] = exp2f(f.tbest - lse2);
+    a.lse[o] = lse2 * kLn2;
+  }
+}
+
+// Confidence head for request r, computed by one whole wave.
+template <class W>
+__device__ __forceinline__ void confidence_wave(const StepArgs& a, int r, int lane) {
+  using store_t = typename W::store_t;
+  const size_t o = (size_t)r * a.gamma + (a.k - 1);
+  const int xp = clamp_token(a.x[(size_t)r * (a.gamma + 1) + (a.k - 1)], a.V);
+  const store_t* hrow = reinterpret_cast<const store_t*>(a.h) + o * a.d;
+  const store_t* erow = reinterpret_cast<const store_t*>(a.W1) + (size_t)xp * a.rank;
+  const float dot = conf_dot_wave<W>(hrow, erow, a.w, a.d, a.rank, lane);
+  if (lane == 0) {
+    const float c = sigmoid_f32(dot);
+    const float prev = (a.k == 1) ? 1.0f : a.a[o - 1];
+    a.c[o] = c;
+    a.a[o] = __fmul_rn(prev, c);
+  }
+}
+
+// Arrival at a device-scope counter; returns true in every thread of the last
+// workgroup to arrive.  `chk` (the folded exchange results of this thread's
+// record writes) is consumed before the barrier, so all writes of the
+// workgroup are complete before thread 0 increments the counter.  The last
+// arriver resets the counter for the next call.
+__device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned expected, unsigned chk,
+                                            int* sflag) {
+  if (chk == 0x7FC00001u) *sflag = 2;  // never true in practice; forces the wait on chk
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned old =
+        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = old + 1u == expected;
+    if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *sflag = last ? 1 : 0;
+  }
+  __syncthreads();
+  return *sflag == 1;
+}
+
+// Level-1 records of this workgroup are at slot `slab`; the group covers
+// requests [r0, r0 + nr) (nr <= kNr).
+template <int kNr>
+__device__ __forceinline__ void merge_levels(const StepArgs& a, int grp, int slab, int r0, int nr,
+                                             unsigned chk) {
+  __shared__ int sflag;
+  const int team = slab / a.team_size;
+  const int t0 = team * a.team_size;
+  const int t1 = min(a.n_slabs, t0 + a.team_size);
+  unsigned* cnt = a.counters + (size_t)grp * (a.n_teams + 1);
+  if (!arrive_last(cnt + team, (unsigned)(t1 - t0), chk, &sflag)) return;
+
+  constexpr int kTpr = kStreamThreads / kNr;  // threads per request
+  constexpr int kChunk = (kTeamSize + kTpr - 1) / kTpr;
+  const int rl = threadIdx.x / kTpr, sub = threadIdx.x % kTpr;
+  const int r = r0 + rl;
+  const int rr = (rl < nr) ? r : r0;  // idle threads shadow request r0, never stored
+  Rec q = merge_range<kTpr, kChunk>(a.part, a.R, rr, t0, t1, sub);
+  chk = 0u;
+  if (sub == 0 && rl < nr) chk = put_rec(a.part2, a.R, team, r, q);
+
+  if (!arrive_last(cnt + a.n_teams, (unsigned)a.n_teams, chk, &sflag)) return;
+  q = merge_range<kTpr, (kMaxTeams + kTpr - 1) / kTpr>(a.part2, a.R, rr, 0, a.n_teams, sub);
+  if (sub == 0 && rl < nr) write_outputs(a, r, q);
 }
 
 template <class W, bool kGreedy, bool kDebug, bool kVec>
-__global__ __launch_bounds__(kStreamThreads) void markov_partial_shared(StepArgs a) {
+__global__ __launch_bounds__(kStreamThreads) void markov_step_shared(StepArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = lane >> 5, col = lane & 31;
@@ -170,10 +309,15 @@ __global__ __launch_bounds__(kStreamThreads) void markov_partial_shared(StepArgs
     grp = (b >> 3) % a.n_groups;
     slab = (b / (8 * a.n_groups)) * 8 + (b & 7);
   }
-  const int t_begin = (int)(((long long)slab * a.n_vtiles) / a.n_slabs);
-  const int t_end = (int)(((long long)(slab + 1) * a.n_vtiles) / a.n_slabs);
+  const int r0 = grp * kWaves * kVTile;
+  if (a.h != nullptr && slab < kVTile) {  // 32 workgroups x 4 waves cover the group
+    const int rq = r0 + slab * kWaves + wave;
+    if (rq < a.R) confidence_wave<W>(a, rq, lane);
+  }
+  int t_begin, t_end;
+  slab_range(slab, a.n_slabs, a.n_vtiles, t_begin, t_end);
 
-  const int r = (grp * kWaves + wave) * kVTile + col;
+  const int r = r0 + wave * kVTile + col;
   const int rc = r < a.R ? r : a.R - 1;  // padded lanes recompute row R-1, never stored
   typename W::frag_t e[W::kMaxKs];
   load_e_frags<W>(e, a.W1, a.x[(size_t)rc * (a.gamma + 1) + (a.k - 1)], a.rank, a.V, half);
@@ -183,116 +327,77 @@ __global__ __launch_bounds__(kStreamThreads) void markov_partial_shared(StepArgs
 
   Rec q = epi.record();
   q = rec_merge(q, rec_shfl_xor(q, 32));
-  if (half == 0 && r < a.R) store_rec(a.part, a.R, a.n_parts, r, slab, q);
+  unsigned chk = 0u;
+  if (half == 0 && r < a.R) chk = put_rec(a.part, a.R, slab, r, q);
+  merge_levels<kWaves * kVTile>(a, grp, slab, r0, min(kWaves * kVTile, a.R - r0), chk);
 }
 
 template <class W, bool kGreedy, bool kDebug, bool kVec>
-__global__ __launch_bounds__(kStreamThreads) void markov_partial_private(StepArgs a) {
+__global__ __launch_bounds__(kStreamThreads) void markov_step_private(StepArgs a) {
+  __shared__ Rec srec[kWaves][kVTile];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = lane >> 5, col = lane & 31;
-  const int ws = blockIdx.x * kWaves + wave;
-  const int t_begin = (int)(((long long)ws * a.n_vtiles) / a.n_parts);
-  const int t_end = (int)(((long long)(ws + 1) * a.n_vtiles) / a.n_parts);
+  const int slab = blockIdx.x % a.n_slabs;
+  const int grp = blockIdx.x / a.n_slabs;  // request tile
+  const int r0 = grp * kVTile;
+  if (a.h != nullptr && slab < kVTile / kWaves) {  // 8 workgroups x 4 waves
+    const int rq = r0 + slab * kWaves + wave;
+    if (rq < a.R) confidence_wave<W>(a, rq, lane);
+  }
+  int t_begin, t_end;
+  slab_range(slab, a.n_slabs, a.n_vtiles, t_begin, t_end);
 
-  const int r = blockIdx.y * kVTile + col;
+  const int r = r0 + col;
   const int rc = r < a.R ? r : a.R - 1;
   typename W::frag_t e[W::kMaxKs];
   load_e_frags<W>(e, a.W1, a.x[(size_t)rc * (a.gamma + 1) + (a.k - 1)], a.rank, a.V, half);
 
   DraftEpi<kGreedy, kDebug, kVec> epi(a, r, rc, half);
-  private_a_stream<W>(a.W2t, a.V, a.rank, t_begin, t_end, e, epi);
+  private_a_stream<W>(a.W2t, a.V, a.rank, t_begin + wave, t_end, kWaves, e, epi);
 
   Rec q = epi.record();
   q = rec_merge(q, rec_shfl_xor(q, 32));
-  if (half == 0 && r < a.R) store_rec(a.part, a.R, a.n_parts, r, ws, q);
-}
-
-// One workgroup per request: fixed-order merge of the partial records, then
-// the confidence head and the survival product.
-template <class W>
-__global__ __launch_bounds__(256) void markov_combine(StepArgs a) {
-  using store_t = typename W::store_t;
-  __shared__ Rec srec[256];
-  __shared__ float sbuf[256];
-  const int r = blockIdx.x, t = threadIdx.x;
-  const size_t plane = (size_t)a.R * a.n_parts;
-  const float* pm = a.part + (size_t)r * a.n_parts;
-  const int* pidx = reinterpret_cast<const int*>(a.part) + 4 * plane + (size_t)r * a.n_parts;
-
-  Rec acc{-INFINITY, 0.0f, -INFINITY, -INFINITY, -1};
-  for (int j = t; j < a.n_parts; j += 256) {
-    const Rec q{pm[j], pm[plane + j], pm[2 * plane + j], pm[3 * plane + j], pidx[j]};
-    acc = rec_merge(acc, q);
-  }
-  srec[t] = acc;
+  if (half == 0) srec[wave][col] = q;
   __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (t < s) srec[t] = rec_merge(srec[t], srec[t + s]);
-    __syncthreads();
+  unsigned chk = 0u;
+  if (wave == 0 && half == 0) {
+    Rec m = srec[0][col];
+    for (int w = 1; w < kWaves; ++w) m = rec_merge(m, srec[w][col]);
+    if (r < a.R) chk = put_rec(a.part, a.R, slab, r, m);
   }
-
-  const size_t o = (size_t)r * a.gamma + (a.k - 1);
-  int xp = a.x[(size_t)r * (a.gamma + 1) + (a.k - 1)];
-  xp = xp < 0 ? 0 : (xp >= a.V ? a.V - 1 : xp);
-  const bool conf = a.h != nullptr && a.w != nullptr;
-  float dot = 0.0f;
-  if (conf) {
-    const store_t* hrow = reinterpret_cast<const store_t*>(a.h) + o * a.d;
-    const store_t* erow = reinterpret_cast<const store_t*>(a.W1) + (size_t)xp * a.rank;
-    dot = block_sum256(conf_partial<W>(hrow, erow, a.w, a.d, a.rank, t), sbuf);
-  }
-  if (t == 0) {
-    const Rec f = srec[0];
-    a.x[(size_t)r * (a.gamma + 1) + a.k] = f.idx;
-    if (a.greedy) {
-      a.p[o] = 1.0f;
-      a.lse[o] = f.m;
-    } else {
-      const float lse2 = f.m + log2f(f.S);
-      a.p[o] = exp2f(f.tbest - lse2);
-      a.lse[o] = lse2 * kLn2;
-    }
-    if (conf) {
-      const float c = sigmoid_f32(dot);
-      const float prev = (a.k == 1) ? 1.0f : a.a[o - 1];
-      a.c[o] = c;
-      a.a[o] = __fmul_rn(prev, c);
-    }
-  }
+  merge_levels<kVTile>(a, grp, slab, r0, min(kVTile, a.R - r0), chk);
 }
 
 template <class W, bool kGreedy, bool kDebug, bool kVec>
-void launch_partial(const StepArgs& a, const StepPlan& plan, hipStream_t stream) {
-  if (plan.shared) {
-    hipLaunchKernelGGL((markov_partial_shared<W, kGreedy, kDebug, kVec>), dim3(plan.grid_x),
+void launch_one(const StepArgs& a, const StepPlan& plan, hipStream_t stream) {
+  if (plan.shared)
+    hipLaunchKernelGGL((markov_step_shared<W, kGreedy, kDebug, kVec>), dim3(plan.grid_x),
                        dim3(kStreamThreads), stream_lds_bytes<W>(a.rank), stream, a);
-  } else {
-    hipLaunchKernelGGL((markov_partial_private<W, kGreedy, kDebug, kVec>),
-                       dim3(plan.grid_x, plan.grid_y), dim3(kStreamThreads), 0, stream, a);
-  }
+  else
+    hipLaunchKernelGGL((markov_step_private<W, kGreedy, kDebug, kVec>), dim3(plan.grid_x),
+                       dim3(kStreamThreads), 0, stream, a);
 }
 
 template <class W, bool kGreedy>
-void launch_partial_g(const StepArgs& a, const StepPlan& plan, hipStream_t stream) {
+void launch_g(const StepArgs& a, const StepPlan& plan, hipStream_t stream) {
   const bool vec = (a.V % 4) == 0;
   if (a.z_debug != nullptr) {
-    if (vec) launch_partial<W, kGreedy, true, true>(a, plan, stream);
-    else launch_partial<W, kGreedy, true, false>(a, plan, stream);
+    if (vec) launch_one<W, kGreedy, true, true>(a, plan, stream);
+    else launch_one<W, kGreedy, true, false>(a, plan, stream);
   } else {
-    if (vec) launch_partial<W, kGreedy, false, true>(a, plan, stream);
-    else launch_partial<W, kGreedy, false, false>(a, plan, stream);
+    if (vec) launch_one<W, kGreedy, false, true>(a, plan, stream);
+    else launch_one<W, kGreedy, false, false>(a, plan, stream);
   }
 }
 
 template <class W>
-hipError_t launch_step_w(const StepArgs& a, const StepPlan& plan, hipStream_t stream) {
-  if (a.greedy) launch_partial_g<W, true>(a, plan, stream);
-  else launch_partial_g<W, false>(a, plan, stream);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((markov_combine<W>), dim3(a.R), dim3(256), 0, stream, a);
+hipError_t launch_w(const StepArgs& a, const StepPlan& plan, hipStream_t stream) {
+  if (a.greedy) launch_g<W, true>(a, plan, stream);
+  else launch_g<W, false>(a, plan, stream);
   return hipGetLastError();
 }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
@@ -305,37 +410,31 @@ StepPlan plan_draft_step(int R, int V) {
   if (rt >= 4) {
     p.shared = true;
     p.n_groups = (rt + kWaves - 1) / kWaves;
-    // Two resident workgroups on each of the 256 CUs (the T > 0 kernel needs
-    // about 230 registers per lane, so two waves per SIMD).
     int slabs = kResidentWgs / p.n_groups;
     if (p.n_groups > 1) slabs = (slabs / 8) * 8;
-    if (slabs < 8 && p.n_groups > 1) slabs = 8;
-    if (slabs > p.n_vtiles) slabs = p.n_vtiles;
-    if (slabs < 1) slabs = 1;
-    if (p.n_groups > 1 && slabs % 8 != 0 && p.n_vtiles >= 8) slabs = (p.n_vtiles / 8) * 8;
-    // (fewer than 8 tiles: plain slab-major order, see markov_partial_shared)
+    if (slabs < kVTile) slabs = kVTile;  // the confidence head uses 32 slabs per group
     p.n_slabs = slabs;
-    p.n_parts = slabs;
-    p.grid_x = slabs * p.n_groups;
-    p.grid_y = 1;
   } else {
     p.shared = false;
-    p.n_groups = 1;
-    int wgs = 512 / rt;
-    const int max_wgs = (p.n_vtiles + kWaves - 1) / kWaves;
-    if (wgs > max_wgs) wgs = max_wgs;
-    if (wgs < 1) wgs = 1;
-    p.n_slabs = wgs * kWaves;
-    p.n_parts = wgs * kWaves;
-    p.grid_x = wgs;
-    p.grid_y = rt;
+    p.n_groups = rt;
+    int slabs = kResidentWgs / rt;
+    const int max_slabs = (p.n_vtiles + kWaves - 1) / kWaves;
+    if (slabs > max_slabs) slabs = max_slabs;
+    if (slabs < kVTile / kWaves) slabs = kVTile / kWaves;  // 8 slabs carry the confidence head
+    p.n_slabs = slabs;
   }
-  p.ws_bytes = (size_t)5 * (size_t)R * (size_t)p.n_parts * 4u;
+  p.grid_x = p.n_slabs * p.n_groups;
+  p.grid_y = 1;
+  p.team_size = kTeamSize;
+  p.n_teams = (p.n_slabs + p.team_size - 1) / p.team_size;  // <= kMaxTeams
+  p.off_part2 = align256((size_t)p.n_slabs * 5 * R * 4);
+  p.off_counters = p.off_part2 + align256((size_t)p.n_teams * 5 * R * 4);
+  p.ws_bytes = p.off_counters + align256((size_t)p.n_groups * (p.n_teams + 1) * 4);
   return p;
 }
 
 hipError_t launch_draft_step(const StepArgs& a, const StepPlan& plan, hipStream_t stream) {
-  return a.bf16 ? launch_step_w<WBf16>(a, plan, stream) : launch_step_w<WF32>(a, plan, stream);
+  return a.bf16 ? launch_w<WBf16>(a, plan, stream) : launch_w<WF32>(a, plan, stream);
 }
 
 }  // namespace dspark

@@ -108,11 +108,11 @@ __device__ __forceinline__ void shared_a_stream(const void* W2t, int V, int rank
   }
 }
 
-// A single wave streams its own tiles; the W2t fragment goes straight from
-// global memory into VGPRs.
+// A single wave streams tiles t_begin, t_begin + t_stride, ... < t_end; the
+// W2t fragment goes straight from global memory into VGPRs.
 template <class W, class Epi>
 __device__ __forceinline__ void private_a_stream(const void* W2t, int V, int rank, int t_begin,
-                                                 int t_end,
+                                                 int t_end, int t_stride,
                                                  const typename W::frag_t (&e)[W::kMaxKs],
                                                  Epi& epi) {
   using store_t = typename W::store_t;
@@ -120,7 +120,7 @@ __device__ __forceinline__ void private_a_stream(const void* W2t, int V, int ran
   const int half = lane >> 5;
   const int nks = rank / W::kKStep;
   const int prow = tile_perm(lane & 31);
-  for (int vt = t_begin; vt < t_end; ++vt) {
+  for (int vt = t_begin; vt < t_end; vt += t_stride) {
     epi.prefetch(vt);
     epi.advance();
     const int vv = vt * kVTile + prow;

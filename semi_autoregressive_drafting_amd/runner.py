@@ -76,7 +76,8 @@ class RoundBuffers:
         return RoundBuffers(
             x=torch.zeros((R, g + 1), **i32), p=torch.zeros((R, g), **f32),
             lse=torch.zeros((R, g), **f32), c=torch.zeros((R, g), **f32),
-            a=torch.zeros((R, g), **f32), ws=torch.empty(max(ws, 16), dtype=torch.uint8, device=device),
+            a=torch.zeros((R, g), **f32),
+            ws=torch.zeros(max(ws, 16), dtype=torch.uint8, device=device),  # zero-filled once
             ell=torch.zeros(R, **i32), budget=torch.zeros(1, **i32),
             theta=torch.zeros(1, dtype=torch.float64, device=device),
             c_star=torch.zeros((R, g), **f32), n_accept=torch.zeros(R, **i32),
@@ -95,10 +96,10 @@ def draft_step(di: DeviceInputs, buf: RoundBuffers, k: int, temperature: float, 
 
 
 def draft(di: DeviceInputs, buf: RoundBuffers, temperature: float, seed: int):
-    """gamma sequential draft steps (with confidence and survival)."""
+    """gamma sequential draft steps (with confidence and survival) in one call."""
     buf.x[:, 0].copy_(di.anchor)
-    for k in range(1, di.gamma + 1):
-        draft_step(di, buf, k, temperature, seed)
+    D.dspark_draft_block(di.R, di.V, di.rank, di.d, di.gamma, di.dt, di.W1, di.W2t, di.U, di.h,
+                         di.w, temperature, seed, buf.x, buf.p, buf.lse, buf.c, buf.a, buf.ws)
 
 
 def schedule(di: DeviceInputs, buf: RoundBuffers):

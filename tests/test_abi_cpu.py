@@ -53,9 +53,9 @@ def test_workspace_sizes():
     assert f(D.DSPARK_OP_DRAFT_STEP, 4, 1024, 32, 17) == 0
     assert f(D.DSPARK_OP_SCHEDULE, 128, 151936, 256, 16) == 0
     assert f(99, 4, 1024, 32, 4) == 0
-    # 5 planes of R x partials 32-bit words; grows with R
+    # at least one 5-field record per request and slab; 256-byte aligned regions
     w128 = f(D.DSPARK_OP_DRAFT_STEP, 128, 151936, 256, 16)
-    assert w128 > 0 and w128 % (5 * 128 * 4) == 0
+    assert w128 >= 5 * 128 * 4 * 32 and w128 % 256 == 0
     assert f(D.DSPARK_OP_DRAFT_STEP, 512, 151936, 256, 7) > 0
     assert f(D.DSPARK_OP_VERIFY, 128, 151936, 256, 7) > 128 * 7 * 8
 
@@ -100,6 +100,20 @@ def _step(**kw):
 ])
 def test_draft_step_validation(kw, status):
     assert _step(**kw) == status
+
+
+def test_draft_block_validation():
+    f = D.load().dspark_draft_block
+    args = [4, 1024, 32, 64, 4, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 1.0, 0, FAKE, FAKE, FAKE,
+            FAKE, FAKE, FAKE, 1 << 30, None]
+    bad = list(args); bad[6] = None
+    assert f(*bad) == D.DSPARK_ERR_NULL
+    bad = list(args); bad[4] = 0
+    assert f(*bad) == D.DSPARK_ERR_SHAPE
+    bad = list(args); bad[11] = -2.0
+    assert f(*bad) == D.DSPARK_ERR_VALUE
+    bad = list(args); bad[19] = 8
+    assert f(*bad) == D.DSPARK_ERR_WORKSPACE
 
 
 def test_schedule_validation():

@@ -74,6 +74,20 @@ def test_draft_is_deterministic():
         np.testing.assert_array_equal(h1[n], h2[n])
 
 
+def test_draft_block_matches_single_steps():
+    """dspark_draft_block gives the same bits as gamma dspark_draft_step calls."""
+    from semi_autoregressive_drafting_amd import dspark as D
+    for name in ("qwen3_4b_r32_g7", "edge_v1000_r100_g2", "tiny_v1024_r4_g4"):
+        case = Case(name)
+        _, h1, _ = case.run_draft(1.0, 11)
+        di = case.di
+        buf = runner.RoundBuffers.allocate(di)
+        runner.draft(di, buf, 1.0, 11)
+        torch.cuda.synchronize()
+        for n in ("x", "p", "lse", "c", "a"):
+            np.testing.assert_array_equal(getattr(buf, n).cpu().numpy(), h1[n], err_msg=name + n)
+
+
 def test_batched_confidence_matches_fused():
     """dspark_confidence over a drafted block reproduces the c and a that the
     draft steps computed, bit for bit."""
