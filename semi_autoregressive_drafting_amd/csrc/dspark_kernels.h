@@ -73,11 +73,13 @@ hipError_t launch_schedule(const SchedArgs& a, hipStream_t stream);
 struct VerifyPlan {
   int n_rows;       // R * gamma
   int n_rtiles;     // ceil(n_rows / 32)
-  int n_groups;     // groups of 4 row tiles
-  int n_slabs;      // vocabulary slabs per group
+  int n_groups;     // c* pass: groups of 4 row tiles
+  int n_slabs;      // c* pass: vocabulary slabs per group
+  int s_groups;     // sampling pass: groups of 128 requests
+  int s_slabs;      // sampling pass: vocabulary slabs per group
   int n_vtiles;
   int lse_chunks;   // vocabulary chunks per row in the target normaliser pass
-  size_t off_lse_t, off_tx, off_flag, off_lsepart, off_part, ws_bytes;
+  size_t off_lse_t, off_tv, off_best, off_srow, off_skind, off_lsepart, ws_bytes;
 };
 
 struct VerifyArgs {

@@ -58,7 +58,7 @@ struct DraftEpi {
   int V, R, r, half;
   float kscale;
   uint32_t state_row;  // LCG state of vocabulary entry 0 of this row
-  float ucur[16], unext[16];
+  float ubuf[2][16];  // U of the current and the prefetched tile (alternating)
   LaneState st;
 
   __device__ DraftEpi(const StepArgs& a, int r_, int rc, int half_)
@@ -71,10 +71,9 @@ struct DraftEpi {
     st.bLn = -1.0f;
     st.bV = -1;
   }
-  __device__ void prefetch(int vt) { load16<kVec>(unext, urow, vt * kVTile + 16 * half, V); }
-  __device__ void advance() {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) ucur[i] = unext[i];
+  template <int S>
+  __device__ void prefetch(int vt) {
+    load16<kVec>(ubuf[S], urow, vt * kVTile + 16 * half, V, (vt + 1) * kVTile <= V);
   }
 
   template <bool kMasked>
@@ -112,11 +111,12 @@ struct DraftEpi {
     }
   }
 
+  template <int S>
   __device__ void consume(const f32x16_t& acc, int vt) {
     const int vb = vt * kVTile + 16 * half;
     float z[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) z[i] = ucur[i] + acc[i];
+    for (int i = 0; i < 16; ++i) z[i] = ubuf[S][i] + acc[i];
     if constexpr (kDebug) {
       if (r < R) {
         for (int i = 0; i < 16; ++i)
@@ -293,7 +293,7 @@ __device__ __forceinline__ void merge_levels(const StepArgs& a, int grp, int sla
   if (sub == 0 && rl < nr) write_outputs(a, r, q);
 }
 
-template <class W, bool kGreedy, bool kDebug, bool kVec>
+template <class W, int kKs, bool kGreedy, bool kDebug, bool kVec>
 __global__ __launch_bounds__(kStreamThreads) void markov_step_shared(StepArgs a) {
   extern __shared__ __align__(16) unsigned char lds[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -320,10 +320,10 @@ __global__ __launch_bounds__(kStreamThreads) void markov_step_shared(StepArgs a)
   const int r = r0 + wave * kVTile + col;
   const int rc = r < a.R ? r : a.R - 1;  // padded lanes recompute row R-1, never stored
   typename W::frag_t e[W::kMaxKs];
-  load_e_frags<W>(e, a.W1, a.x[(size_t)rc * (a.gamma + 1) + (a.k - 1)], a.rank, a.V, half);
+  load_e_frags<W, kKs>(e, a.W1, a.x[(size_t)rc * (a.gamma + 1) + (a.k - 1)], a.rank, a.V, half);
 
   DraftEpi<kGreedy, kDebug, kVec> epi(a, r, rc, half);
-  shared_a_stream<W>(a.W2t, a.V, a.rank, t_begin, t_end, e, lds, epi);
+  shared_a_stream<W, kKs>(a.W2t, a.V, a.rank, t_begin, t_end, e, lds, epi);
 
   Rec q = epi.record();
   q = rec_merge(q, rec_shfl_xor(q, 32));
@@ -332,7 +332,7 @@ __global__ __launch_bounds__(kStreamThreads) void markov_step_shared(StepArgs a)
   merge_levels<kWaves * kVTile>(a, grp, slab, r0, min(kWaves * kVTile, a.R - r0), chk);
 }
 
-template <class W, bool kGreedy, bool kDebug, bool kVec>
+template <class W, int kKs, bool kGreedy, bool kDebug, bool kVec>
 __global__ __launch_bounds__(kStreamThreads) void markov_step_private(StepArgs a) {
   __shared__ Rec srec[kWaves][kVTile];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -350,10 +350,10 @@ __global__ __launch_bounds__(kStreamThreads) void markov_step_private(StepArgs a
   const int r = r0 + col;
   const int rc = r < a.R ? r : a.R - 1;
   typename W::frag_t e[W::kMaxKs];
-  load_e_frags<W>(e, a.W1, a.x[(size_t)rc * (a.gamma + 1) + (a.k - 1)], a.rank, a.V, half);
+  load_e_frags<W, kKs>(e, a.W1, a.x[(size_t)rc * (a.gamma + 1) + (a.k - 1)], a.rank, a.V, half);
 
   DraftEpi<kGreedy, kDebug, kVec> epi(a, r, rc, half);
-  private_a_stream<W>(a.W2t, a.V, a.rank, t_begin + wave, t_end, kWaves, e, epi);
+  private_a_stream<W, kKs>(a.W2t, a.V, a.rank, t_begin + wave, t_end, kWaves, e, epi);
 
   Rec q = epi.record();
   q = rec_merge(q, rec_shfl_xor(q, 32));
@@ -368,33 +368,40 @@ __global__ __launch_bounds__(kStreamThreads) void markov_step_private(StepArgs a
   merge_levels<kVTile>(a, grp, slab, r0, min(kVTile, a.R - r0), chk);
 }
 
-template <class W, bool kGreedy, bool kDebug, bool kVec>
+template <class W, int kKs, bool kGreedy, bool kDebug, bool kVec>
 void launch_one(const StepArgs& a, const StepPlan& plan, hipStream_t stream) {
   if (plan.shared)
-    hipLaunchKernelGGL((markov_step_shared<W, kGreedy, kDebug, kVec>), dim3(plan.grid_x),
+    hipLaunchKernelGGL((markov_step_shared<W, kKs, kGreedy, kDebug, kVec>), dim3(plan.grid_x),
                        dim3(kStreamThreads), stream_lds_bytes<W>(a.rank), stream, a);
   else
-    hipLaunchKernelGGL((markov_step_private<W, kGreedy, kDebug, kVec>), dim3(plan.grid_x),
+    hipLaunchKernelGGL((markov_step_private<W, kKs, kGreedy, kDebug, kVec>), dim3(plan.grid_x),
                        dim3(kStreamThreads), 0, stream, a);
 }
 
-template <class W, bool kGreedy>
+template <class W, int kKs, bool kGreedy>
 void launch_g(const StepArgs& a, const StepPlan& plan, hipStream_t stream) {
   const bool vec = (a.V % 4) == 0;
   if (a.z_debug != nullptr) {
-    if (vec) launch_one<W, kGreedy, true, true>(a, plan, stream);
-    else launch_one<W, kGreedy, true, false>(a, plan, stream);
+    if (vec) launch_one<W, kKs, kGreedy, true, true>(a, plan, stream);
+    else launch_one<W, kKs, kGreedy, true, false>(a, plan, stream);
   } else {
-    if (vec) launch_one<W, kGreedy, false, true>(a, plan, stream);
-    else launch_one<W, kGreedy, false, false>(a, plan, stream);
+    if (vec) launch_one<W, kKs, kGreedy, false, true>(a, plan, stream);
+    else launch_one<W, kKs, kGreedy, false, false>(a, plan, stream);
   }
 }
 
+template <class W, int kKs>
+hipError_t launch_k(const StepArgs& a, const StepPlan& plan, hipStream_t stream) {
+  if (a.greedy) launch_g<W, kKs, true>(a, plan, stream);
+  else launch_g<W, kKs, false>(a, plan, stream);
+  return hipGetLastError();
+}
+
+// The Qwen3-family rank (256 bf16 = 16 MFMA K-steps) gets a branch-free MFMA loop.
 template <class W>
 hipError_t launch_w(const StepArgs& a, const StepPlan& plan, hipStream_t stream) {
-  if (a.greedy) launch_g<W, true>(a, plan, stream);
-  else launch_g<W, false>(a, plan, stream);
-  return hipGetLastError();
+  if (W::kKStep * W::kMaxKs == a.rank) return launch_k<W, W::kMaxKs>(a, plan, stream);
+  return launch_k<W, 0>(a, plan, stream);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }

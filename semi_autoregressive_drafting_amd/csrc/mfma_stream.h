@@ -7,11 +7,16 @@
 // Lane l owns row 32*tile + l%32 and vocabulary entries 16*(l/32) .. +15 of the
 // tile (tile_perm), matching the accumulator layout of the 32x32 MFMAs.
 //
-// Epilogue interface (Epi):
-//   void prefetch(int vt)   issue the global loads the epilogue needs for tile vt
-//   void advance()          make the prefetched tile current
-//   void consume(const f32x16_t& acc, int vt)
+// Epilogue interface (Epi), with a compile-time register slot S in {0, 1}
+// (tiles alternate between two register buffers, so nothing is copied):
+//   template <int S> void prefetch(int vt)   issue the loads of tile vt into slot S
+//   template <int S> void consume(const f32x16_t& acc, int vt)   fold tile vt (slot S)
+//
+// kKs > 0 fixes the number of MFMA K-steps at compile time (rank = kKs * K
+// per MFMA); kKs = 0 reads it at run time.
 #pragma once
+
+#include <type_traits>
 
 #include "dspark_device.h"
 
@@ -24,13 +29,13 @@ constexpr int kStreamThreads = 256;
 constexpr int kResidentWgs = 512;
 
 // E fragments (MFMA B operand) of this lane's row: W1[token], K split in steps.
-template <class W>
+template <class W, int kKs = 0>
 __device__ __forceinline__ void load_e_frags(typename W::frag_t (&e)[W::kMaxKs], const void* W1,
                                              int token, int rank, int V, int half) {
   token = token < 0 ? 0 : (token >= V ? V - 1 : token);  // device ids are not validated
   const typename W::store_t* row = reinterpret_cast<const typename W::store_t*>(W1) +
                                    (size_t)token * rank;
-  const int nks = rank / W::kKStep;
+  const int nks = kKs > 0 ? kKs : rank / W::kKStep;
 #pragma unroll
   for (int ks = 0; ks < W::kMaxKs; ++ks) e[ks] = (ks < nks) ? W::load(row, ks, half) : W::zero();
 }
@@ -43,8 +48,9 @@ __host__ __device__ inline size_t stream_lds_bytes(int rank) {
 
 // Workgroup of 4 waves: each W2t tile is loaded from HBM once (256 threads x
 // up to 4 x 16 bytes, prefetched one tile ahead in registers), staged in LDS and
-// multiplied by every wave with its own E fragments.
-template <class W, class Epi>
+// multiplied by every wave with its own E fragments.  The loop is unrolled by
+// two so the epilogue's prefetch buffers alternate without copies.
+template <class W, int kKs, class Epi>
 __device__ __forceinline__ void shared_a_stream(const void* W2t, int V, int rank, int t_begin,
                                                 int t_end,
                                                 const typename W::frag_t (&e)[W::kMaxKs],
@@ -52,7 +58,7 @@ __device__ __forceinline__ void shared_a_stream(const void* W2t, int V, int rank
   using store_t = typename W::store_t;
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5;
-  const int nks = rank / W::kKStep;
+  const int nks = kKs > 0 ? kKs : rank / W::kKStep;
   const int row_bytes = rank * (int)sizeof(store_t);
   const int rs = row_bytes + 16;
   const int cpr = row_bytes / 16;
@@ -84,33 +90,44 @@ __device__ __forceinline__ void shared_a_stream(const void* W2t, int V, int rank
       }
     }
   };
-
   const store_t* arow = reinterpret_cast<const store_t*>(lds + tile_perm(lane & 31) * rs);
-  if (t_begin < t_end) {
-    fetch(t_begin);
-    epi.prefetch(t_begin);
-    epi.advance();
-  }
-  for (int vt = t_begin; vt < t_end; ++vt) {
-    __syncthreads();
+  auto mma = [&]() {
+    f32x16_t acc = {};
+    if constexpr (kKs > 0) {
+#pragma unroll
+      for (int ks = 0; ks < kKs; ++ks) acc = W::mma(W::load(arow, ks, half), e[ks], acc);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < W::kMaxKs; ++ks)
+        if (ks < nks) acc = W::mma(W::load(arow, ks, half), e[ks], acc);
+    }
+    return acc;
+  };
+  auto step = [&](auto slot, int vt) {
+    constexpr int S = decltype(slot)::value;
+    __syncthreads();  // previous tile's LDS reads are done
     stash();
-    __syncthreads();
+    __syncthreads();  // this tile is visible
     if (vt + 1 < t_end) {
       fetch(vt + 1);
-      epi.prefetch(vt + 1);
+      epi.template prefetch<1 - S>(vt + 1);
     }
-    f32x16_t acc = {};
-#pragma unroll
-    for (int ks = 0; ks < W::kMaxKs; ++ks)
-      if (ks < nks) acc = W::mma(W::load(arow, ks, half), e[ks], acc);
-    epi.consume(acc, vt);
-    epi.advance();
+    const f32x16_t acc = mma();
+    epi.template consume<S>(acc, vt);
+  };
+  if (t_begin >= t_end) return;
+  fetch(t_begin);
+  epi.template prefetch<0>(t_begin);
+  for (int vt = t_begin; vt < t_end; vt += 2) {
+    step(std::integral_constant<int, 0>{}, vt);
+    if (vt + 1 >= t_end) break;
+    step(std::integral_constant<int, 1>{}, vt + 1);
   }
 }
 
 // A single wave streams tiles t_begin, t_begin + t_stride, ... < t_end; the
 // W2t fragment goes straight from global memory into VGPRs.
-template <class W, class Epi>
+template <class W, int kKs, class Epi>
 __device__ __forceinline__ void private_a_stream(const void* W2t, int V, int rank, int t_begin,
                                                  int t_end, int t_stride,
                                                  const typename W::frag_t (&e)[W::kMaxKs],
@@ -118,11 +135,10 @@ __device__ __forceinline__ void private_a_stream(const void* W2t, int V, int ran
   using store_t = typename W::store_t;
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5;
-  const int nks = rank / W::kKStep;
+  const int nks = kKs > 0 ? kKs : rank / W::kKStep;
   const int prow = tile_perm(lane & 31);
   for (int vt = t_begin; vt < t_end; vt += t_stride) {
-    epi.prefetch(vt);
-    epi.advance();
+    epi.template prefetch<0>(vt);
     const int vv = vt * kVTile + prow;
     const store_t* wrow = reinterpret_cast<const store_t*>(W2t) + (size_t)(vv < V ? vv : V - 1) * rank;
     f32x16_t acc = {};
@@ -133,16 +149,17 @@ __device__ __forceinline__ void private_a_stream(const void* W2t, int V, int ran
         acc = W::mma(af, e[ks], acc);
       }
     }
-    epi.consume(acc, vt);
+    epi.template consume<0>(acc, vt);
   }
 }
 
 // Load 16 consecutive fp32 values row[vb .. vb+15]; entries >= V read as 0.
-// kVec: rows are 16-byte aligned (V % 4 == 0), so a range that lies fully
-// inside the row is read with four 16-byte loads.
+// `full` (uniform across the wave) says the whole 32-wide tile lies inside the
+// row; with kVec (rows 16-byte aligned, V % 4 == 0) it is read with four
+// 16-byte loads.
 template <bool kVec>
-__device__ __forceinline__ void load16(float (&u)[16], const float* row, int vb, int V) {
-  if (kVec && vb + 16 <= V) {
+__device__ __forceinline__ void load16(float (&u)[16], const float* row, int vb, int V, bool full) {
+  if (kVec && full) {
     const f32x4_t* p = reinterpret_cast<const f32x4_t*>(row + vb);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {

@@ -10,14 +10,20 @@
 //      (greedy: max and lowest argmax).
 //   V2 verify_accept      one workgroup, one thread per request: merge V1's
 //      chunks -> lse_t per row; run the acceptance chain over the admitted
-//      prefix (u < p_t(x_j) / p_d(x_j)); flag the row that needs a sample
-//      (1 = residual at the first rejection, 2 = bonus at row ell+1); write
-//      n_accept, tau and tau_mean.  Greedy: also c* and the correction token.
-//   V3 verify_main        (T > 0) one pass over W2t, U and the target logits
-//      for all rows: bias tile by MFMA, p_d and p_t, sum |p_d - p_t|, and for
-//      flagged rows the Gumbel race over max(p_t - p_d, 0) or p_t.
-//   V4 verify_finalize    (T > 0) per row: fixed-order merge of V3's slab
-//      partials -> c* = 1 - sum/2; the flagged row's winner -> next_token.
+//      prefix (u < p_t(x_j) / p_d(x_j)); pick the one row per request that
+//      needs a sample (residual at the first rejection, or bonus at row
+//      ell+1); write n_accept, tau and tau_mean; clear the accumulators of
+//      V3 and V5.  Greedy: also c* and the correction token (V3-V5 skipped).
+//   V3 verify_tv          (T > 0) one pass over W2t, U and the target logits
+//      for all rows: bias tile by MFMA, p_d and p_t, sum |p_d - p_t| per row,
+//      accumulated across workgroups as exact fixed-point (2^-40) integers so
+//      the result does not depend on the order of arrival.
+//   V5 verify_sample      (T > 0) the same stream over only the sampled rows
+//      (at most one per request): Gumbel race over max(p_t - p_d, 0)
+//      (residual) or p_t (bonus), merged across workgroups with a 64-bit
+//      atomic max of (order-preserving key, ~id), which is order-independent
+//      and keeps the lowest id on ties.
+//   V4 verify_finalize    (T > 0) c* = 1 - sum/2 per row; winner -> next_token.
 #include "dspark_kernels.h"
 #include "mfma_stream.h"
 
@@ -26,10 +32,17 @@ namespace dspark {
 namespace {
 
 constexpr int kWaves = 4;
+constexpr double kFix = 1099511627776.0;  // 2^40, fixed-point unit of sum |p_d - p_t|
 
 __device__ __forceinline__ int chunk_size(int V, int chunks) {
   const int cs = (V + chunks - 1) / chunks;
   return (cs + 3) & ~3;
+}
+
+// Order-preserving map of a float to uint32 (larger float -> larger code).
+__device__ __forceinline__ uint32_t ordered(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
 // ---------------------------------------------------------------------------
@@ -64,7 +77,7 @@ __global__ __launch_bounds__(256) void verify_target_lse(VerifyArgs a, VerifyPla
         idx = win ? v + i : idx;
       }
     } else {
-      float xm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      const float xm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
       const float mn = fmaxf(m, xm * a.kscale);
       S *= (mn == -INFINITY) ? 1.0f : fast_exp2(m - mn);
       m = mn;
@@ -109,7 +122,10 @@ __global__ __launch_bounds__(512) void verify_accept(VerifyArgs a, VerifyPlan p)
   const int r = threadIdx.x;
   float* lse_t2 = reinterpret_cast<float*>(a.ws + p.off_lse_t);
   int* targmax = reinterpret_cast<int*>(a.ws + p.off_lse_t);  // greedy reuses the slot
-  int* flag = reinterpret_cast<int*>(a.ws + p.off_flag);
+  int* srow = reinterpret_cast<int*>(a.ws + p.off_srow);      // sampled k (1-based) or 0
+  int* skind = reinterpret_cast<int*>(a.ws + p.off_skind);    // 1 residual, 2 bonus
+  unsigned long long* tvsum = reinterpret_cast<unsigned long long*>(a.ws + p.off_tv);
+  unsigned long long* best = reinterpret_cast<unsigned long long*>(a.ws + p.off_best);
   const float* lp = reinterpret_cast<const float*>(a.ws + p.off_lsepart);
   int tau = 0;
   if (r < a.R) {
@@ -137,17 +153,16 @@ __global__ __launch_bounds__(512) void verify_accept(VerifyArgs a, VerifyPlan p)
           m = M;
         }
         lse_t2[row] = m + log2f(S);
+        tvsum[row] = 0ull;
       }
-      flag[row] = 0;
     }
-    int n_acc = 0, nxt = -1;
-    bool rejected = false;
+    best[r] = 0ull;
+    int n_acc = 0, nxt = -1, kind = 0, ks = 0;
     int ell = a.ell[r];
     ell = ell < 0 ? 0 : (ell > a.gamma ? a.gamma : ell);  // device values are not validated
     for (int j = 1; j <= ell; ++j) {
       const int row = r * a.gamma + (j - 1);
-      int xj = a.x[(size_t)r * (a.gamma + 1) + j];
-      xj = xj < 0 ? 0 : (xj >= a.V ? a.V - 1 : xj);
+      const int xj = clamp_token(a.x[(size_t)r * (a.gamma + 1) + j], a.V);
       float ratio;
       if (a.greedy) {
         ratio = (xj == targmax[row]) ? 1.0f : 0.0f;
@@ -159,17 +174,18 @@ __global__ __launch_bounds__(512) void verify_accept(VerifyArgs a, VerifyPlan p)
       if (u < ratio) {
         ++n_acc;
       } else {
-        flag[row] = 1;
-        if (a.greedy) nxt = targmax[row];
-        rejected = true;
+        kind = 1;
+        ks = j;
         break;
       }
     }
-    if (!rejected && ell < a.gamma) {
-      const int row = r * a.gamma + ell;
-      flag[row] = 2;
-      if (a.greedy) nxt = targmax[row];
+    if (kind == 0 && ell < a.gamma) {
+      kind = 2;
+      ks = ell + 1;
     }
+    if (a.greedy && kind != 0) nxt = targmax[r * a.gamma + (ks - 1)];
+    srow[r] = ks;
+    skind[r] = kind;
     a.n_accept[r] = n_acc;
     a.tau[r] = n_acc + 1;
     a.next_token[r] = nxt;
@@ -184,83 +200,68 @@ __global__ __launch_bounds__(512) void verify_accept(VerifyArgs a, VerifyPlan p)
   if (r == 0) *a.tau_mean = (float)stau[0] / (float)a.R;
 }
 
+// Map blockIdx to (slab, group); the groups of one slab share an XCD.
+__device__ __forceinline__ void slab_group(int b, int n_slabs, int n_groups, int& slab, int& grp) {
+  if (n_groups == 1 || n_slabs % 8 != 0) {
+    slab = b % n_slabs;
+    grp = b / n_slabs;
+  } else {
+    grp = (b >> 3) % n_groups;
+    slab = (b / (8 * n_groups)) * 8 + (b & 7);
+  }
+}
+
 // ---------------------------------------------------------------------------
-// V3: the fused pass over all rows (T > 0).
+// V3: sum |p_d - p_t| over all rows (T > 0).
 // ---------------------------------------------------------------------------
 template <bool kVec>
-struct VerifyEpi {
+struct TvEpi {
   const float* urow;
   const float* trow;
   int V, half;
   float kscale, lse2_d, lse2_t;
-  int flag;
-  uint32_t state_row;
-  float ucur[16], unext[16], tcur[16], tnext[16];
-  float sabs, bE, bLn;
-  int bV;
+  float ubuf[2][16], tbuf[2][16];
+  float sabs;
 
+  template <int S>
   __device__ void prefetch(int vt) {
-    load16<kVec>(unext, urow, vt * kVTile + 16 * half, V);
-    load16<kVec>(tnext, trow, vt * kVTile + 16 * half, V);
+    const bool full = (vt + 1) * kVTile <= V;
+    load16<kVec>(ubuf[S], urow, vt * kVTile + 16 * half, V, full);
+    load16<kVec>(tbuf[S], trow, vt * kVTile + 16 * half, V, full);
   }
-  __device__ void advance() {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      ucur[i] = unext[i];
-      tcur[i] = tnext[i];
-    }
-  }
+  template <int S>
   __device__ void consume(const f32x16_t& acc, int vt) {
+    const float* ucur = ubuf[S];
+    const float* tcur = tbuf[S];
     const int vb = vt * kVTile + 16 * half;
     const bool full = (vt + 1) * kVTile <= V;
-    float pd[16], pt[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const bool ok = full || (vb + i < V);
-      pd[i] = ok ? fast_exp2(fmaf(ucur[i] + acc[i], kscale, -lse2_d)) : 0.0f;
-      pt[i] = ok ? fast_exp2(fmaf(tcur[i], kscale, -lse2_t)) : 0.0f;
-      sabs += fabsf(pd[i] - pt[i]);
-    }
-    if (__ballot(flag != 0) != 0ull) {
-      const uint32_t s0 = state_row + (uint32_t)vb * kLcgMul;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float e = (flag == 1) ? fmaxf(pt[i] - pd[i], 0.0f) : pt[i];
-        const float ln = fast_log2(bits_to_uniform(rxs_m_xs(s0 + (uint32_t)i * kLcgMul)));
-        const bool win = e * bLn < bE * ln;
-        bE = win ? e : bE;
-        bLn = win ? ln : bLn;
-        bV = win ? vb + i : bV;
-      }
+      const float pd = fast_exp2(fmaf(ucur[i] + acc[i], kscale, -lse2_d));
+      const float pt = fast_exp2(fmaf(tcur[i], kscale, -lse2_t));
+      const float d = (full || vb + i < V) ? fabsf(pd - pt) : 0.0f;
+      sabs += d;
     }
   }
 };
 
-template <class W, bool kVec>
-__global__ __launch_bounds__(kStreamThreads) void verify_main(VerifyArgs a, VerifyPlan p) {
+template <class W, int kKs, bool kVec>
+__global__ __launch_bounds__(kStreamThreads) void verify_tv(VerifyArgs a, VerifyPlan p) {
   extern __shared__ __align__(16) unsigned char lds[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = lane >> 5, col = lane & 31;
-  const int b = blockIdx.x;
   int slab, grp;
-  if (p.n_groups == 1 || p.n_slabs % 8 != 0) {
-    slab = b % p.n_slabs;
-    grp = b / p.n_slabs;
-  } else {
-    grp = (b >> 3) % p.n_groups;
-    slab = (b / (8 * p.n_groups)) * 8 + (b & 7);
-  }
-  const int t_begin = (int)(((long long)slab * p.n_vtiles) / p.n_slabs);
-  const int t_end = (int)(((long long)(slab + 1) * p.n_vtiles) / p.n_slabs);
+  slab_group(blockIdx.x, p.n_slabs, p.n_groups, slab, grp);
+  int t_begin, t_end;
+  slab_range(slab, p.n_slabs, p.n_vtiles, t_begin, t_end);
 
   const int row = (grp * kWaves + wave) * kVTile + col;
   const int rowc = row < p.n_rows ? row : p.n_rows - 1;
   const int r = rowc / a.gamma, k = rowc % a.gamma + 1;
   typename W::frag_t e[W::kMaxKs];
-  load_e_frags<W>(e, a.W1, a.x[(size_t)r * (a.gamma + 1) + (k - 1)], a.rank, a.V, half);
+  load_e_frags<W, kKs>(e, a.W1, a.x[(size_t)r * (a.gamma + 1) + (k - 1)], a.rank, a.V, half);
 
-  const int* flag = reinterpret_cast<const int*>(a.ws + p.off_flag);
-  VerifyEpi<kVec> epi;
+  TvEpi<kVec> epi;
   epi.urow = a.U + (size_t)rowc * a.V;
   epi.trow = a.target + (size_t)rowc * a.V;
   epi.V = a.V;
@@ -268,17 +269,95 @@ __global__ __launch_bounds__(kStreamThreads) void verify_main(VerifyArgs a, Veri
   epi.kscale = a.kscale;
   epi.lse2_d = a.lse_d[rowc] * kLog2e;
   epi.lse2_t = reinterpret_cast<const float*>(a.ws + p.off_lse_t)[rowc];
-  epi.flag = row < p.n_rows ? flag[rowc] : 0;
-  const uint32_t stream = epi.flag == 1 ? kStreamResid : kStreamBonus;
-  epi.state_row = row_key(a.seed, stream, (uint32_t)r, (uint32_t)k) * kLcgMul + kLcgInc;
   epi.sabs = 0.0f;
+  shared_a_stream<W, kKs>(a.W2t, a.V, a.rank, t_begin, t_end, e, lds, epi);
+
+  const float s = epi.sabs + __shfl_xor(epi.sabs, 32);
+  if (half == 0 && row < p.n_rows) {
+    const unsigned long long q = (unsigned long long)llrint((double)s * kFix);
+    atomicAdd(reinterpret_cast<unsigned long long*>(a.ws + p.off_tv) + row, q);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// V5: Gumbel race over the sampled rows (T > 0), one virtual row per request.
+// ---------------------------------------------------------------------------
+template <bool kVec>
+struct SampleEpi {
+  const float* urow;
+  const float* trow;
+  int V, half, kind;
+  float kscale, lse2_d, lse2_t;
+  uint32_t state_row;
+  float ubuf[2][16], tbuf[2][16];
+  float bE, bLn;
+  int bV;
+
+  template <int S>
+  __device__ void prefetch(int vt) {
+    const bool full = (vt + 1) * kVTile <= V;
+    load16<kVec>(ubuf[S], urow, vt * kVTile + 16 * half, V, full);
+    load16<kVec>(tbuf[S], trow, vt * kVTile + 16 * half, V, full);
+  }
+  template <int S>
+  __device__ void consume(const f32x16_t& acc, int vt) {
+    const float* ucur = ubuf[S];
+    const float* tcur = tbuf[S];
+    const int vb = vt * kVTile + 16 * half;
+    const bool full = (vt + 1) * kVTile <= V;
+    const uint32_t s0 = state_row + (uint32_t)vb * kLcgMul;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float pd = fast_exp2(fmaf(ucur[i] + acc[i], kscale, -lse2_d));
+      const float pt = fast_exp2(fmaf(tcur[i], kscale, -lse2_t));
+      float e = (kind == 1) ? fmaxf(pt - pd, 0.0f) : pt;
+      e = (full || vb + i < V) ? e : 0.0f;
+      const float ln = fast_log2(bits_to_uniform(rxs_m_xs(s0 + (uint32_t)i * kLcgMul)));
+      // e / L > bE / bL  <=>  e * bLn < bE * ln     (L = -ln > 0)
+      const bool win = e * bLn < bE * ln;
+      bE = win ? e : bE;
+      bLn = win ? ln : bLn;
+      bV = win ? vb + i : bV;
+    }
+  }
+};
+
+template <class W, int kKs, bool kVec>
+__global__ __launch_bounds__(kStreamThreads) void verify_sample(VerifyArgs a, VerifyPlan p) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int half = lane >> 5, col = lane & 31;
+  int slab, grp;
+  slab_group(blockIdx.x, p.s_slabs, p.s_groups, slab, grp);
+  int t_begin, t_end;
+  slab_range(slab, p.s_slabs, p.n_vtiles, t_begin, t_end);
+
+  const int r = (grp * kWaves + wave) * kVTile + col;
+  const int rc = r < a.R ? r : a.R - 1;
+  const int* srow = reinterpret_cast<const int*>(a.ws + p.off_srow);
+  const int* skind = reinterpret_cast<const int*>(a.ws + p.off_skind);
+  const int ks = srow[rc];
+  const int k = ks > 0 ? ks : 1;  // lanes without a sample run row 1 and never store
+  const int row = rc * a.gamma + (k - 1);
+  typename W::frag_t e[W::kMaxKs];
+  load_e_frags<W, kKs>(e, a.W1, a.x[(size_t)rc * (a.gamma + 1) + (k - 1)], a.rank, a.V, half);
+
+  SampleEpi<kVec> epi;
+  epi.urow = a.U + (size_t)row * a.V;
+  epi.trow = a.target + (size_t)row * a.V;
+  epi.V = a.V;
+  epi.half = half;
+  epi.kind = skind[rc];
+  epi.kscale = a.kscale;
+  epi.lse2_d = a.lse_d[row] * kLog2e;
+  epi.lse2_t = reinterpret_cast<const float*>(a.ws + p.off_lse_t)[row];
+  const uint32_t stream = epi.kind == 1 ? kStreamResid : kStreamBonus;
+  epi.state_row = row_key(a.seed, stream, (uint32_t)rc, (uint32_t)k) * kLcgMul + kLcgInc;
   epi.bE = 0.0f;
   epi.bLn = -1.0f;
   epi.bV = -1;
-  shared_a_stream<W>(a.W2t, a.V, a.rank, t_begin, t_end, e, lds, epi);
+  shared_a_stream<W, kKs>(a.W2t, a.V, a.rank, t_begin, t_end, e, lds, epi);
 
-  // merge the two lane halves of each row
-  const float s_o = __shfl_xor(epi.sabs, 32);
   float key = (epi.bV >= 0 && epi.bE > 0.0f) ? fast_log2(epi.bE) - fast_log2(-epi.bLn) : -INFINITY;
   int idx = (epi.bV >= 0 && epi.bE > 0.0f) ? epi.bV : -1;
   const float key_o = __shfl_xor(key, 32);
@@ -287,64 +366,57 @@ __global__ __launch_bounds__(kStreamThreads) void verify_main(VerifyArgs a, Veri
     key = key_o;
     idx = idx_o;
   }
-  if (half == 0 && row < p.n_rows) {
-    const size_t plane = (size_t)p.n_rows * p.n_slabs;
-    float* part = reinterpret_cast<float*>(a.ws + p.off_part);
-    const size_t o = (size_t)row * p.n_slabs + slab;
-    part[o] = epi.sabs + s_o;
-    part[plane + o] = key;
-    reinterpret_cast<int*>(part)[2 * plane + o] = idx;
+  if (half == 0 && r < a.R && ks > 0 && idx >= 0) {
+    const unsigned long long packed =
+        ((unsigned long long)ordered(key) << 32) | (unsigned long long)(~(uint32_t)idx);
+    atomicMax(reinterpret_cast<unsigned long long*>(a.ws + p.off_best) + r, packed);
   }
 }
 
 // ---------------------------------------------------------------------------
-// V4: per-row finalisation (T > 0).
+// V4: finalisation (T > 0): c* for every row, the sampled token per request.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void verify_finalize(VerifyArgs a, VerifyPlan p) {
-  const int row = blockIdx.x, t = threadIdx.x;
-  const size_t plane = (size_t)p.n_rows * p.n_slabs;
-  const float* part = reinterpret_cast<const float*>(a.ws + p.off_part) + (size_t)row * p.n_slabs;
-  const int* pidx = reinterpret_cast<const int*>(a.ws + p.off_part) + 2 * plane + (size_t)row * p.n_slabs;
-  float s = 0.0f, key = -INFINITY;
-  int idx = -1;
-  for (int j = t; j < p.n_slabs; j += 64) {
-    s += part[j];
-    const float kj = part[plane + j];
-    const int ij = pidx[j];
-    if (rec_beats(kj, ij, key, idx)) {
-      key = kj;
-      idx = ij;
-    }
+__global__ __launch_bounds__(256) void verify_finalize(VerifyArgs a, VerifyPlan p) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < p.n_rows) {
+    const unsigned long long q = reinterpret_cast<const unsigned long long*>(a.ws + p.off_tv)[i];
+    a.c_star[i] = (float)(1.0 - 0.5 * ((double)q / kFix));
   }
-  for (int m = 32; m > 0; m >>= 1) {
-    s += __shfl_xor(s, m);
-    const float ko = __shfl_xor(key, m);
-    const int io = __shfl_xor(idx, m);
-    if (rec_beats(ko, io, key, idx)) {
-      key = ko;
-      idx = io;
-    }
-  }
-  if (t == 0) {
-    a.c_star[row] = 1.0f - 0.5f * s;
-    const int f = reinterpret_cast<const int*>(a.ws + p.off_flag)[row];
-    if (f != 0) a.next_token[row / a.gamma] = idx;
+  if (i < a.R) {
+    const int ks = reinterpret_cast<const int*>(a.ws + p.off_srow)[i];
+    const unsigned long long b = reinterpret_cast<const unsigned long long*>(a.ws + p.off_best)[i];
+    if (ks > 0 && b != 0ull) a.next_token[i] = (int)(~(uint32_t)(b & 0xFFFFFFFFull));
   }
 }
 
-template <class W>
-hipError_t launch_main(const VerifyArgs& a, const VerifyPlan& p, hipStream_t stream) {
-  const int grid = p.n_slabs * p.n_groups;
-  if (a.V % 4 == 0)
-    hipLaunchKernelGGL((verify_main<W, true>), dim3(grid), dim3(kStreamThreads),
-                       stream_lds_bytes<W>(a.rank), stream, a, p);
-  else
-    hipLaunchKernelGGL((verify_main<W, false>), dim3(grid), dim3(kStreamThreads),
-                       stream_lds_bytes<W>(a.rank), stream, a, p);
+template <class W, int kKs, bool kVec>
+hipError_t launch_passes(const VerifyArgs& a, const VerifyPlan& p, hipStream_t stream) {
+  const size_t lds = stream_lds_bytes<W>(a.rank);
+  hipLaunchKernelGGL((verify_tv<W, kKs, kVec>), dim3(p.n_slabs * p.n_groups), dim3(kStreamThreads),
+                     lds, stream, a, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((verify_sample<W, kKs, kVec>), dim3(p.s_slabs * p.s_groups),
+                     dim3(kStreamThreads), lds, stream, a, p);
   return hipGetLastError();
 }
 
+template <class W, bool kVec>
+hipError_t launch_w(const VerifyArgs& a, const VerifyPlan& p, hipStream_t stream) {
+  if (W::kKStep * W::kMaxKs == a.rank) return launch_passes<W, W::kMaxKs, kVec>(a, p, stream);
+  return launch_passes<W, 0, kVec>(a, p, stream);
+}
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int plan_slabs(int n_groups, int n_vtiles) {
+  int slabs = kResidentWgs / n_groups;
+  if (n_groups > 1) slabs = (slabs / 8) * 8;
+  if (slabs < 8) slabs = 8;
+  if (slabs > n_vtiles) slabs = n_vtiles;
+  if (n_groups > 1 && slabs % 8 != 0 && n_vtiles >= 8) slabs = (n_vtiles / 8) * 8;
+  return slabs;
+}
 
 }  // namespace
 
@@ -354,12 +426,9 @@ VerifyPlan plan_verify(int R, int V, int gamma) {
   p.n_rtiles = (p.n_rows + kVTile - 1) / kVTile;
   p.n_groups = (p.n_rtiles + kWaves - 1) / kWaves;
   p.n_vtiles = (V + kVTile - 1) / kVTile;
-  int slabs = kResidentWgs / p.n_groups;
-  if (p.n_groups > 1) slabs = (slabs / 8) * 8;
-  if (slabs < 8) slabs = 8;
-  if (slabs > p.n_vtiles) slabs = p.n_vtiles;
-  if (p.n_groups > 1 && slabs % 8 != 0 && p.n_vtiles >= 8) slabs = (p.n_vtiles / 8) * 8;
-  p.n_slabs = slabs;
+  p.n_slabs = plan_slabs(p.n_groups, p.n_vtiles);
+  p.s_groups = ((R + kVTile - 1) / kVTile + kWaves - 1) / kWaves;
+  p.s_slabs = plan_slabs(p.s_groups, p.n_vtiles);
   int chunks = (2048 + p.n_rows - 1) / p.n_rows;
   const int max_chunks = (V + 1023) / 1024;
   if (chunks > max_chunks) chunks = max_chunks;
@@ -369,13 +438,16 @@ VerifyPlan plan_verify(int R, int V, int gamma) {
   size_t off = 0;
   p.off_lse_t = off;
   off = align256(off + (size_t)p.n_rows * 4);
-  p.off_tx = off;  // reserved
-  p.off_flag = off;
-  off = align256(off + (size_t)p.n_rows * 4);
+  p.off_tv = off;
+  off = align256(off + (size_t)p.n_rows * 8);
+  p.off_best = off;
+  off = align256(off + (size_t)R * 8);
+  p.off_srow = off;
+  off = align256(off + (size_t)R * 4);
+  p.off_skind = off;
+  off = align256(off + (size_t)R * 4);
   p.off_lsepart = off;
   off = align256(off + (size_t)p.n_rows * p.lse_chunks * 8);
-  p.off_part = off;
-  off = align256(off + (size_t)3 * p.n_rows * p.n_slabs * 4);
   p.ws_bytes = off;
   return p;
 }
@@ -395,9 +467,11 @@ hipError_t launch_verify(const VerifyArgs& a, const VerifyPlan& p, hipStream_t s
   hipLaunchKernelGGL(verify_accept, dim3(1), dim3(512), 0, stream, a, p);
   e = hipGetLastError();
   if (e != hipSuccess || a.greedy) return e;
-  e = a.bf16 ? launch_main<WBf16>(a, p, stream) : launch_main<WF32>(a, p, stream);
+  if (a.bf16) e = vec ? launch_w<WBf16, true>(a, p, stream) : launch_w<WBf16, false>(a, p, stream);
+  else e = vec ? launch_w<WF32, true>(a, p, stream) : launch_w<WF32, false>(a, p, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(verify_finalize, dim3(p.n_rows), dim3(64), 0, stream, a, p);
+  const int n = p.n_rows > a.R ? p.n_rows : a.R;
+  hipLaunchKernelGGL(verify_finalize, dim3((n + 255) / 256), dim3(256), 0, stream, a, p);
   return hipGetLastError();
 }
 
