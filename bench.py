@@ -41,6 +41,41 @@ def verify_bytes(R, V, rank, gamma):
     return 2 * R * gamma * V * 4 + R * gamma * V * 4 + rank * V * 2
 
 
+PROFILE_COUNTERS = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                                "dspark_round_qwen3_8b_r128_g16_hbm_counters.txt")
+
+
+def sources_sha256():
+    """Hash of the kernel sources (every file under csrc/, by name and bytes)."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                        "semi_autoregressive_drafting_amd", "csrc")
+    for f in sorted(glob.glob(os.path.join(csrc, "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the draft kernel from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary (both scaled by a plain-copy calibration),
+    or None when the kernel sources have changed since it was taken."""
+    try:
+        with open(PROFILE_COUNTERS) as fh:
+            lines = [l for l in fh if l.startswith("traffic markov_step_shared ")]
+    except OSError:
+        return None
+    if not lines:
+        return None
+    kv = dict(t.split("=", 1) for t in lines[-1].split()[2:])
+    if kv.get("source_sha256") != sources_sha256():
+        return None
+    return int(kv["read_bytes"]) + int(kv["write_bytes"])
+
+
 def cpu_baseline(inp, seed):
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
     32 requests (16 easy, 16 hard) through the whole round (gamma draft steps
@@ -162,7 +197,7 @@ def main():
                                "gamma launches of a draft block, launch gaps included)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "bytes_per_launch": sb,
+                     "traffic": measured_traffic(), "bytes_per_launch": sb,
                      "avg_launch_us": round(step_s * 1e6, 2)},
         "breakdown_us": {"draft_step_mean": round(float(step_ms.mean()) * 1e3, 2),
                          "draft_step_min": round(float(step_ms.min()) * 1e3, 2),

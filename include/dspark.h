@@ -99,10 +99,13 @@ const char* dspark_status_string(int status);
  * (c and a must then be non-NULL; with h == w == NULL they are not touched.)
  * z_debug, if non-NULL, receives z as fp32 [R][V] (testing only).
  * Reads x[:, k-1]; writes x[:, k], p, lse (and c, a) at column k-1.
- * ws: dspark_workspace_bytes(DSPARK_OP_DRAFT_STEP, ...) bytes of device memory,
- * ZERO-FILLED before its first use (it holds arrival counters that every call
- * leaves at zero again).  Calls that may run concurrently need separate
- * workspaces.
+ * ws: dspark_workspace_bytes(DSPARK_OP_DRAFT_STEP, ...) bytes of device memory
+ * (per-workgroup partial records for gamma steps, then gamma x R 64-bit winner
+ * words), ZERO-FILLED before its first use: the winner words are atomic-max
+ * targets that every call leaves at zero again.  Calls that may run
+ * concurrently need separate workspaces.
+ * Enqueues two kernels: the streaming step and the finalisation (record merge,
+ * confidence head, survival product).
  */
 dspark_status dspark_draft_step(int R, int V, int rank, int d, int gamma, int k, int dt,
                                 const void* W1, const void* W2t, const float* U,
@@ -114,7 +117,9 @@ dspark_status dspark_draft_step(int R, int V, int rank, int d, int gamma, int k,
 /*
  * The whole draft block: dspark_draft_step for k = 1..gamma in order on
  * `stream` (x[:, 0] must hold the anchors), without z_debug.  Same arguments,
- * results and workspace as the single step.
+ * results and workspace as the single step.  Step k takes x_{k-1} straight
+ * from step k-1's winner word, and one finalisation for all gamma positions
+ * runs after the last step (gamma + 1 kernels).
  */
 dspark_status dspark_draft_block(int R, int V, int rank, int d, int gamma, int dt,
                                  const void* W1, const void* W2t, const float* U,

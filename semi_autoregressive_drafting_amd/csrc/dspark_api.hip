@@ -58,7 +58,7 @@ size_t dspark_workspace_bytes(int op, int R, int V, int rank, int gamma) {
   (void)rank;
   if (R < 1 || R > kMaxR || V < 2 || V > kMaxV || gamma < 1 || gamma > kMaxGamma) return 0;
   switch (op) {
-    case DSPARK_OP_DRAFT_STEP: return plan_draft_step(R, V).ws_bytes;
+    case DSPARK_OP_DRAFT_STEP: return plan_draft_step(R, V, gamma).ws_bytes;
     case DSPARK_OP_SCHEDULE: return 0;
     case DSPARK_OP_VERIFY: return plan_verify(R, V, gamma).ws_bytes;
     default: return 0;
@@ -88,7 +88,7 @@ dspark_status check_draft(int R, int V, int rank, int d, int gamma, int k, int d
   if (!aligned16(W1) || !aligned16(W2t) || ((V % 4) == 0 && !aligned16(U)))
     return DSPARK_ERR_SHAPE;
   if (k < 0 || k > gamma || bad_temperature(temperature)) return DSPARK_ERR_VALUE;
-  plan = plan_draft_step(R, V);
+  plan = plan_draft_step(R, V, gamma);
   if (!ws || ws_bytes < plan.ws_bytes || !aligned16(ws)) return DSPARK_ERR_WORKSPACE;
 
   args = StepArgs{};
@@ -113,14 +113,13 @@ dspark_status check_draft(int R, int V, int rank, int d, int gamma, int k, int d
   args.c = c;
   args.a = a;
   args.z_debug = z_debug;
-  args.part = static_cast<float*>(ws);
-  args.part2 = reinterpret_cast<float*>(static_cast<unsigned char*>(ws) + plan.off_part2);
-  args.counters = reinterpret_cast<unsigned*>(static_cast<unsigned char*>(ws) + plan.off_counters);
+  args.rec = static_cast<float*>(ws);
+  args.rec_step_f = plan.rec_step / sizeof(float);
+  args.best = reinterpret_cast<unsigned long long*>(static_cast<unsigned char*>(ws) + plan.off_best);
+  args.prev_from_best = false;
   args.n_vtiles = plan.n_vtiles;
   args.n_slabs = plan.n_slabs;
   args.n_groups = plan.n_groups;
-  args.team_size = plan.team_size;
-  args.n_teams = plan.n_teams;
   return DSPARK_OK;
 }
 
@@ -140,7 +139,9 @@ dspark_status dspark_draft_step(int R, int V, int rank, int d, int gamma, int k,
   const dspark_status s = check_draft(R, V, rank, d, gamma, k, dt, W1, W2t, U, h, w, temperature,
                                       seed, x, p, lse, c, a, z_debug, ws, ws_bytes, args, plan);
   if (s != DSPARK_OK) return s;
-  if (launch_draft_step(args, plan, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (launch_draft_step(args, plan, st) != hipSuccess ||
+      launch_draft_finalize(args, plan, k, 1, st) != hipSuccess)
     return DSPARK_ERR_LAUNCH;
   return DSPARK_OK;
 }
@@ -155,11 +156,15 @@ dspark_status dspark_draft_block(int R, int V, int rank, int d, int gamma, int d
   const dspark_status s = check_draft(R, V, rank, d, gamma, 0, dt, W1, W2t, U, h, w, temperature,
                                       seed, x, p, lse, c, a, nullptr, ws, ws_bytes, args, plan);
   if (s != DSPARK_OK) return s;
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   for (int k = 1; k <= gamma; ++k) {
     args.k = k;
-    if (launch_draft_step(args, plan, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
-      return DSPARK_ERR_LAUNCH;
+    args.prev_from_best = k > 1;  // x_{k-1} straight from step k-1's winner word
+    if (launch_draft_step(args, plan, st) != hipSuccess) return DSPARK_ERR_LAUNCH;
   }
+  args.k = 1;
+  args.prev_from_best = true;  // x_{k-1} of positions 2..gamma from the winner words
+  if (launch_draft_finalize(args, plan, 1, gamma, st) != hipSuccess) return DSPARK_ERR_LAUNCH;
   return DSPARK_OK;
 }
 

@@ -155,43 +155,67 @@ __device__ __forceinline__ Rec rec_shfl_xor(const Rec& a, int mask) {
 }
 
 // ---------------------------------------------------------------------------
-// Confidence head c = sigma(w[0:d] . h + w[d:] . e)  [P1 §3.1, eq. c_k], one
-// wave per (request, position): lane-strided fp32 partial dot products (16-byte
-// chunks per lane), then a butterfly over the 64 lanes (every lane ends with
-// the same bits).  The fused
-// draft step and the batched confidence kernel both use this function, so
-// their c values are bit-identical.
+// Confidence head c = sigma(w[0:d] . h + w[d:] . e)  [P1 §3.1, eq. c_k] of one
+// (request, position), computed by the 4 waves of a workgroup: over the
+// concatenated vector v = [h; e] of length n = d + rank, wave q takes the
+// quarter [q * n4, (q + 1) * n4) (n4 a multiple of the 16-byte chunk), its
+// lanes accumulate lane-strided fp32 partial sums, a butterfly reduces the
+// wave, and the four wave sums are added in wave order.  The draft step and
+// the batched confidence kernel both call conf_dot_wg, so their c values are
+// bit-identical.
 // ---------------------------------------------------------------------------
 template <class W>
-__device__ __forceinline__ float conf_dot_wave(const typename W::store_t* hrow,
+__device__ __forceinline__ float conf_dot_part(const typename W::store_t* hrow,
                                                const typename W::store_t* erow, const float* w,
-                                               int d, int rank, int lane) {
+                                               int d, int rank, int j0, int j1, int lane) {
   using store_t = typename W::store_t;
-  constexpr int kV = 16 / sizeof(store_t);  // elements per 16-byte load (8 bf16 / 4 fp32)
+  constexpr int kV = 16 / sizeof(store_t);  // elements per 16-byte chunk (8 bf16 / 4 fp32)
   float dot = 0.0f;
-  // h part: each lane takes kV consecutive elements per step (16-byte loads)
-  // when the row allows it, else one element per step.
-  const bool vec = (d % kV) == 0 && ((reinterpret_cast<uintptr_t>(hrow) | reinterpret_cast<uintptr_t>(w)) & 15u) == 0;
+  // 16-byte chunks when no chunk straddles h and e and every row is aligned.
+  const bool vec = (d % kV) == 0 &&
+                   ((reinterpret_cast<uintptr_t>(hrow) | reinterpret_cast<uintptr_t>(erow) |
+                     reinterpret_cast<uintptr_t>(w)) & 15u) == 0;
   if (vec) {
 #pragma unroll 4
-    for (int j = lane * kV; j < d; j += 64 * kV) {
-      const u32x4_t hv = *reinterpret_cast<const u32x4_t*>(hrow + j);
-      const store_t* hs = reinterpret_cast<const store_t*>(&hv);
+    for (int j = j0 + lane * kV; j < j1; j += 64 * kV) {
+      const store_t* src = j < d ? hrow + j : erow + (j - d);
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(src);
+      const store_t* vs = reinterpret_cast<const store_t*>(&v);
 #pragma unroll
-      for (int i = 0; i < kV; ++i) dot = fmaf(w[j + i], W::to_f32(hs[i]), dot);
+      for (int i = 0; i < kV; i += 4) {
+        const f32x4_t wv = *reinterpret_cast<const f32x4_t*>(w + j + i);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dot = fmaf(wv[q], W::to_f32(vs[i + q]), dot);
+      }
     }
   } else {
-    for (int j = lane; j < d; j += 64) dot = fmaf(w[j], W::to_f32(hrow[j]), dot);
+    for (int j = j0 + lane; j < j1; j += 64) {
+      const float v = W::to_f32(j < d ? hrow[j] : erow[j - d]);
+      dot = fmaf(w[j], v, dot);
+    }
   }
-  // Markov-embedding part (rank is a multiple of kV, rows 16-byte aligned)
-  for (int j = lane * kV; j < rank; j += 64 * kV) {
-    const u32x4_t ev = *reinterpret_cast<const u32x4_t*>(erow + j);
-    const store_t* es = reinterpret_cast<const store_t*>(&ev);
-#pragma unroll
-    for (int i = 0; i < kV; ++i) dot = fmaf(w[d + j + i], W::to_f32(es[i]), dot);
-  }
+  (void)rank;
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) dot += __shfl_xor(dot, m);
+  return dot;
+}
+
+// All 256 threads of the workgroup must call it; every thread gets c.
+// `red` is 4 floats of LDS.
+template <class W>
+__device__ __forceinline__ float conf_dot_wg(const typename W::store_t* hrow,
+                                             const typename W::store_t* erow, const float* w,
+                                             int d, int rank, float* red) {
+  constexpr int kV = 16 / sizeof(typename W::store_t);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = d + rank;
+  const int n4 = ((n + 3) / 4 + kV - 1) / kV * kV;
+  const int j0 = min(n, wave * n4), j1 = min(n, j0 + n4);
+  const float part = conf_dot_part<W>(hrow, erow, w, d, rank, j0, j1, lane);
+  if (lane == 0) red[wave] = part;
+  __syncthreads();
+  const float dot = ((red[0] + red[1]) + red[2]) + red[3];
+  __syncthreads();  // red may be reused
   return dot;
 }
 

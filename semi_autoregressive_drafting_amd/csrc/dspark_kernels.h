@@ -15,16 +15,15 @@ struct StepPlan {
   int n_slabs;        // vocabulary slabs (workgroups) per request group
   int n_groups;       // request groups (128 requests shared, 32 private)
   int n_vtiles;       // 32-wide vocabulary tiles
-  int team_size;      // slabs merged by one team closer
-  int n_teams;        // teams per group
-  size_t off_part2;   // workspace: level-1 records at 0, level-2 records,
-  size_t off_counters;//   then n_groups x (n_teams + 1) arrival counters
+  size_t rec_step;    // workspace: per-step record planes [gamma][n_slabs][5][R]
+  size_t off_best;    //   then the winner words [gamma][R] (u64)
   size_t ws_bytes;
 };
 
 struct StepArgs {
   int R, V, rank, d, gamma, k;
   bool bf16, greedy;
+  bool prev_from_best;  // x_{k-1} comes from step k-1's winner word (inside a block)
   const void* W1;
   const void* W2t;
   const float* U;
@@ -38,14 +37,17 @@ struct StepArgs {
   float* c;
   float* a;
   float* z_debug;
-  float* part;       // level-1 records [n_slabs][5][R]
-  float* part2;      // level-2 records [n_teams][5][R]
-  unsigned* counters;
-  int n_vtiles, n_slabs, n_groups, team_size, n_teams;
+  float* rec;                // records of step 1; step k at rec + (k-1) * rec_step_f
+  size_t rec_step_f;         // floats per step plane
+  unsigned long long* best;  // winner words [gamma][R]
+  int n_vtiles, n_slabs, n_groups;
 };
 
-StepPlan plan_draft_step(int R, int V);
+StepPlan plan_draft_step(int R, int V, int gamma);
 hipError_t launch_draft_step(const StepArgs& a, const StepPlan& plan, hipStream_t stream);
+// Merge records, write x/p/lse and (if h is set) c/a for steps k0 .. k0+nk-1.
+hipError_t launch_draft_finalize(const StepArgs& a, const StepPlan& plan, int k0, int nk,
+                                 hipStream_t stream);
 
 struct ConfArgs {
   int R, gamma, d, rank, V;

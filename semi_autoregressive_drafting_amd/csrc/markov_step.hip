@@ -1,28 +1,34 @@
-// Fused DSpark Markov draft step for gfx950: one kernel per sequential step.
+// DSpark Markov draft step for gfx950: a streaming kernel per sequential step
+// and one finalisation kernel per call.
 //
-// Step k over R requests [P1 "DSpark" §2.2 eq. p_k, §2.3 eq. B, §3.1 eq. c_k,
-// §1.1 eq. a_j; the §6.2 vLLM loop fixes the per-position order]:
+// Step k over R requests [P1 "DSpark" §2.2 eq. p_k, §2.3 eq. B; the §6.2 vLLM
+// loop fixes the per-position order]:
 //
-//  1. Confidence head (waves of the first workgroups of each request group, one
-//     wave per request): c_k = sigma(w . [h_k; W1[x_{k-1}]]), a_k = a_{k-1} c_k.
-//  2. Stream a vocabulary slab: gather E = W1[x_{k-1}] once into VGPRs, form
-//     each 32 x 32 bias tile E . W2 with bf16 (or fp32) MFMA, add the base
-//     logits U_k and fold the tile into an online max / sum-exp and a Gumbel
-//     race, so the R x V bias never reaches HBM.  The race is argmax_v s_v + G_v
-//     in its exponential-race form: the winner maximises e_v / L_v with
-//     e_v = 2^(t_v - m) (already needed for the sum) and L_v = -log2 u_v, one
-//     logarithm per entry.
-//  3. Write one partial record per request (slab-major, device-scope atomic
-//     writes), then merge in two levels without a second kernel: the last
-//     workgroup of a team of slabs to arrive (device-scope counter) merges the
-//     team's records; the last team to arrive merges the team records in a
-//     fixed order and writes x_k, p_k(x_k) and lse_k.  Nobody waits on anybody:
-//     a workgroup that is not last simply exits.  No L2-wide fence is needed
-//     because every cross-workgroup value travels through device-scope
-//     atomics.  Counters are reset by their last user, so the workspace must
-//     be zero-filled once before its first use.
+//  markov_step_*   Each workgroup streams one vocabulary slab: it gathers
+//     E = W1[x_{k-1}] into VGPRs, forms each 32 x 32 bias tile E . W2 with bf16
+//     (or fp32) MFMA, adds the base logits U_k and folds the tile into an
+//     online max / sum-exp and a Gumbel race, so the R x V bias never reaches
+//     HBM.  The race is argmax_v s_v + G_v in its exponential-race form: the
+//     winner maximises e_v / L_v with e_v = 2^(t_v - m) (already needed for
+//     the sum) and L_v = -log2 u_v, one logarithm per entry.  At the end the
+//     workgroup stores one partial record per request (m, S, key, t_best, id)
+//     with plain stores and publishes its winner with one 64-bit atomic max of
+//     (order-preserving key, ~id): the maximum is independent of the order in
+//     which workgroups arrive and keeps the lowest id on equal keys.  The next
+//     step reads x_k from that word, so nothing waits for a merge.
 //
-// Launch shapes (see mfma_stream.h):
+//     The first slabs (the ones with the lighter share of tiles) also run the
+//     confidence head for one request each after their stream:
+//     c_k = sigma(w . [h_k; W1[x_{k-1}]]) [P1 §3.1 eq. c_k] and the survival
+//     product a_k = a_{k-1} c_k [P1 §1.1 eq. a_j] (a_{k-1} comes from the
+//     previous launch).
+//
+//  draft_merge  One workgroup per (32 requests, position) merges the records
+//     of the step in a fixed tree order (so the result is bit-reproducible):
+//     x_k, p_k(x_k) = 2^(t_best - lse), lse_k.  It clears the atomic words it
+//     consumed, so the workspace stays zero between calls.
+//
+// Launch shapes of the streaming kernel (see mfma_stream.h):
 //   shared : R > 96.  A workgroup = 4 waves = 4 request tiles (a group of 128
 //            requests); each wave keeps its E fragments in VGPRs for the whole
 //            step and each W2t tile is staged once per workgroup in LDS.  W2t
@@ -39,8 +45,30 @@ namespace dspark {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kTeamSize = 32;  // slabs merged by one team closer
-constexpr int kMaxTeams = 16;  // teams per request group (n_slabs <= 512)
+
+// Prefetch distance of the shared stream: 2 for bf16 weights; fp32 weights
+// (E fragments twice as large) keep 1 to stay within the register budget.
+template <class W>
+constexpr int draft_dist() {
+  return std::is_same<W, WBf16>::value ? 2 : 1;
+}
+
+// Order-preserving map of a float to uint32 (larger float -> larger code).
+__device__ __forceinline__ uint32_t ordered(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// 64-bit word of a race winner: larger key first, then lower id.  0 = none.
+__device__ __forceinline__ unsigned long long pack_winner(float key, int idx) {
+  return idx < 0 ? 0ull
+                 : ((unsigned long long)ordered(key) << 32) |
+                       (unsigned long long)(~(uint32_t)idx);
+}
+
+__device__ __forceinline__ int winner_id(unsigned long long w) {
+  return w == 0ull ? -1 : (int)(~(uint32_t)(w & 0xFFFFFFFFull));
+}
 
 // Per-lane online state over the lane's vocabulary entries of one request.
 struct LaneState {
@@ -58,8 +86,9 @@ struct DraftEpi {
   int V, R, r, half;
   float kscale;
   uint32_t state_row;  // LCG state of vocabulary entry 0 of this row
-  float ubuf[2][16];  // U of the current and the prefetched tile (alternating)
+  float ubuf[kMaxDist + 1][16];  // U of the tile being folded and the prefetched ones
   LaneState st;
+  static constexpr int kLoads = kVec ? 4 : 16;
 
   __device__ DraftEpi(const StepArgs& a, int r_, int rc, int half_)
       : zdbg(a.z_debug), V(a.V), R(a.R), r(r_), half(half_), kscale(a.kscale) {
@@ -73,7 +102,7 @@ struct DraftEpi {
   }
   template <int S>
   __device__ void prefetch(int vt) {
-    load16<kVec>(ubuf[S], urow, vt * kVTile + 16 * half, V, (vt + 1) * kVTile <= V);
+    load16<kVec>(ubuf[S], urow, (vt < 0 ? 0 : vt * kVTile) + 16 * half);
   }
 
   template <bool kMasked>
@@ -111,22 +140,30 @@ struct DraftEpi {
     }
   }
 
-  template <int S>
-  __device__ void consume(const f32x16_t& acc, int vt) {
+  template <bool kMasked>
+  __device__ __forceinline__ void fold_tile(const float (&u)[16], const f32x16_t& acc, int vt) {
     const int vb = vt * kVTile + 16 * half;
     float z[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) z[i] = ubuf[S][i] + acc[i];
+    for (int i = 0; i < 16; ++i) z[i] = u[i] + acc[i];
     if constexpr (kDebug) {
       if (r < R) {
         for (int i = 0; i < 16; ++i)
           if (vb + i < V) zdbg[(size_t)r * V + vb + i] = z[i];
       }
     }
-    if ((vt + 1) * kVTile <= V)
-      fold<false>(z, vb);
-    else
-      fold<true>(z, vb);
+    fold<kMasked>(z, vb);
+  }
+
+  template <int S>
+  __device__ void consume(const f32x16_t& acc, int vt) {
+    fold_tile<false>(ubuf[S], acc, vt);
+  }
+
+  __device__ void tail(const f32x16_t& acc, int vt) {
+    float u[16];
+    load16_masked(u, urow, vt * kVTile + 16 * half, V, 0.0f);
+    fold_tile<true>(u, acc, vt);
   }
 
   __device__ Rec record() const {
@@ -154,143 +191,50 @@ struct DraftEpi {
   }
 };
 
-// Records live in slab-major planes: rec[(slot * 5 + field) * R + r], so the
-// 32 or 128 requests a workgroup writes for one slot are contiguous.
-//
-// Records cross workgroups (and XCDs) inside one launch, so they are written
-// and read with device-scope atomics, which the hardware keeps coherent
-// without writing back or invalidating whole L2 caches.  Each write is an
-// exchange whose returned old value the caller folds into `chk`: using `chk`
-// before the workgroup barrier makes every write complete at the coherence
-// point before the arrival counter is incremented.
-__device__ __forceinline__ unsigned xchg(float* p, float v) {
-  return __float_as_uint(
-      __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+// Token x_{k-1} of request rc: the anchor column, the column written by the
+// previous call's finalisation, or (inside a block) the previous step's
+// winner word.
+__device__ __forceinline__ int prev_token(const StepArgs& a, int rc) {
+  if (a.k > 1 && a.prev_from_best)
+    return winner_id(a.best[(size_t)(a.k - 2) * a.R + rc]);
+  return a.x[(size_t)rc * (a.gamma + 1) + (a.k - 1)];
 }
 
-__device__ __forceinline__ unsigned put_rec(float* base, int R, int slot, int r, const Rec& q) {
-  float* p = base + (size_t)slot * 5 * R + r;
-  unsigned chk = xchg(p, q.m);
-  chk ^= xchg(p + R, q.S);
-  chk ^= xchg(p + 2 * R, q.key);
-  chk ^= xchg(p + 3 * R, q.tbest);
-  chk ^= xchg(p + 4 * R, __int_as_float(q.idx));
-  return chk;
+// Records of step k live in slab-major planes: rec[(slab * 5 + field) * R + r].
+__device__ __forceinline__ void put_rec(float* base, int R, int slab, int r, const Rec& q) {
+  float* p = base + (size_t)slab * 5 * R + r;
+  p[0] = q.m;
+  p[R] = q.S;
+  p[2 * R] = q.key;
+  p[3 * R] = q.tbest;
+  p[4 * R] = __int_as_float(q.idx);
 }
 
-__device__ __forceinline__ float ld(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void publish(const StepArgs& a, int slab, int r, const Rec& q) {
+  put_rec(a.rec + (size_t)(a.k - 1) * a.rec_step_f, a.R, slab, r, q);
+  if (q.idx >= 0)
+    atomicMax(a.best + (size_t)(a.k - 1) * a.R + r, pack_winner(q.key, q.idx));
 }
 
-__device__ __forceinline__ Rec get_rec(const float* base, int R, int slot, int r) {
-  const float* p = base + (size_t)slot * 5 * R + r;
-  return Rec{ld(p), ld(p + R), ld(p + 2 * R), ld(p + 3 * R), __float_as_int(ld(p + 4 * R))};
-}
-
-__device__ __forceinline__ Rec empty_rec() { return Rec{-INFINITY, 0.0f, -INFINITY, -INFINITY, -1}; }
-
-// Fixed-order merge of records [j0, j1) of request r by kTpr consecutive
-// threads (a power of two <= 64, inside one wave): each thread loads its
-// contiguous chunk of at most kChunk records at once (one memory round trip),
-// folds it in order, then a butterfly over the kTpr lanes.
-template <int kTpr, int kChunk>
-__device__ __forceinline__ Rec merge_range(const float* base, int R, int r, int j0, int j1,
-                                           int sub) {
-  const int n = j1 - j0;
-  const int chunk = (n + kTpr - 1) / kTpr;  // <= kChunk by construction of the plan
-  const int b = j0 + sub * chunk;
-  const int e = min(j1, b + chunk);
-  Rec buf[kChunk];
-#pragma unroll
-  for (int i = 0; i < kChunk; ++i)
-    if (b + i < e) buf[i] = get_rec(base, R, b + i, r);
-  Rec acc = empty_rec();
-#pragma unroll
-  for (int i = 0; i < kChunk; ++i)
-    if (b + i < e) acc = rec_merge(acc, buf[i]);
-#pragma unroll
-  for (int m = 1; m < kTpr; m <<= 1) {
-    const Rec o = rec_shfl_xor(acc, m);
-    acc = (sub & m) ? rec_merge(o, acc) : rec_merge(acc, o);
-  }
-  return acc;
-}
-
-// Final outputs of request r from its merged record.
-__device__ __forceinline__ void write_outputs(const StepArgs& a, int r, const Rec& f) {
-  const size_t o = (size_t)r * a.gamma + (a.k - 1);
-  a.x[(size_t)r * (a.gamma + 1) + a.k] = f.idx;
-  if (a.greedy) {
-    a.p[o] = 1.0f;
-    a.lse[o] = f.m;
-  } else {
-    const float lse2 = f.m + log2f(f.S);
-    a.p[o] = exp2f(f.tbest - lse2);
-    a.lse[o] = lse2 * kLn2;
-  }
-}
-
-// Confidence head for request r, computed by one whole wave.
+// Confidence head and survival product of step k for requests r0 + slab,
+// r0 + slab + n_slabs, ... < r0 + nr.  Called by the whole workgroup.
 template <class W>
-__device__ __forceinline__ void confidence_wave(const StepArgs& a, int r, int lane) {
+__device__ __forceinline__ void step_confidence(const StepArgs& a, int slab, int r0, int nr) {
   using store_t = typename W::store_t;
-  const size_t o = (size_t)r * a.gamma + (a.k - 1);
-  const int xp = clamp_token(a.x[(size_t)r * (a.gamma + 1) + (a.k - 1)], a.V);
-  const store_t* hrow = reinterpret_cast<const store_t*>(a.h) + o * a.d;
-  const store_t* erow = reinterpret_cast<const store_t*>(a.W1) + (size_t)xp * a.rank;
-  const float dot = conf_dot_wave<W>(hrow, erow, a.w, a.d, a.rank, lane);
-  if (lane == 0) {
-    const float c = sigmoid_f32(dot);
-    const float prev = (a.k == 1) ? 1.0f : a.a[o - 1];
-    a.c[o] = c;
-    a.a[o] = __fmul_rn(prev, c);
+  __shared__ float red[4];
+  for (int q = slab; q < nr; q += a.n_slabs) {
+    const int r = r0 + q;
+    const size_t o = (size_t)r * a.gamma + (a.k - 1);
+    const int xp = clamp_token(prev_token(a, r), a.V);
+    const store_t* hrow = reinterpret_cast<const store_t*>(a.h) + o * a.d;
+    const store_t* erow = reinterpret_cast<const store_t*>(a.W1) + (size_t)xp * a.rank;
+    const float c = sigmoid_f32(conf_dot_wg<W>(hrow, erow, a.w, a.d, a.rank, red));
+    if (threadIdx.x == 0) {
+      const float prev = (a.k == 1) ? 1.0f : a.a[o - 1];
+      a.c[o] = c;
+      a.a[o] = __fmul_rn(prev, c);
+    }
   }
-}
-
-// Arrival at a device-scope counter; returns true in every thread of the last
-// workgroup to arrive.  `chk` (the folded exchange results of this thread's
-// record writes) is consumed before the barrier, so all writes of the
-// workgroup are complete before thread 0 increments the counter.  The last
-// arriver resets the counter for the next call.
-__device__ __forceinline__ bool arrive_last(unsigned* counter, unsigned expected, unsigned chk,
-                                            int* sflag) {
-  if (chk == 0x7FC00001u) *sflag = 2;  // never true in practice; forces the wait on chk
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned old =
-        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const bool last = old + 1u == expected;
-    if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *sflag = last ? 1 : 0;
-  }
-  __syncthreads();
-  return *sflag == 1;
-}
-
-// Level-1 records of this workgroup are at slot `slab`; the group covers
-// requests [r0, r0 + nr) (nr <= kNr).
-template <int kNr>
-__device__ __forceinline__ void merge_levels(const StepArgs& a, int grp, int slab, int r0, int nr,
-                                             unsigned chk) {
-  __shared__ int sflag;
-  const int team = slab / a.team_size;
-  const int t0 = team * a.team_size;
-  const int t1 = min(a.n_slabs, t0 + a.team_size);
-  unsigned* cnt = a.counters + (size_t)grp * (a.n_teams + 1);
-  if (!arrive_last(cnt + team, (unsigned)(t1 - t0), chk, &sflag)) return;
-
-  constexpr int kTpr = kStreamThreads / kNr;  // threads per request
-  constexpr int kChunk = (kTeamSize + kTpr - 1) / kTpr;
-  const int rl = threadIdx.x / kTpr, sub = threadIdx.x % kTpr;
-  const int r = r0 + rl;
-  const int rr = (rl < nr) ? r : r0;  // idle threads shadow request r0, never stored
-  Rec q = merge_range<kTpr, kChunk>(a.part, a.R, rr, t0, t1, sub);
-  chk = 0u;
-  if (sub == 0 && rl < nr) chk = put_rec(a.part2, a.R, team, r, q);
-
-  if (!arrive_last(cnt + a.n_teams, (unsigned)a.n_teams, chk, &sflag)) return;
-  q = merge_range<kTpr, (kMaxTeams + kTpr - 1) / kTpr>(a.part2, a.R, rr, 0, a.n_teams, sub);
-  if (sub == 0 && rl < nr) write_outputs(a, r, q);
 }
 
 template <class W, int kKs, bool kGreedy, bool kDebug, bool kVec>
@@ -310,26 +254,26 @@ __global__ __launch_bounds__(kStreamThreads) void markov_step_shared(StepArgs a)
     slab = (b / (8 * a.n_groups)) * 8 + (b & 7);
   }
   const int r0 = grp * kWaves * kVTile;
-  if (a.h != nullptr && slab < kVTile) {  // 32 workgroups x 4 waves cover the group
-    const int rq = r0 + slab * kWaves + wave;
-    if (rq < a.R) confidence_wave<W>(a, rq, lane);
-  }
   int t_begin, t_end;
   slab_range(slab, a.n_slabs, a.n_vtiles, t_begin, t_end);
 
   const int r = r0 + wave * kVTile + col;
   const int rc = r < a.R ? r : a.R - 1;  // padded lanes recompute row R-1, never stored
   typename W::frag_t e[W::kMaxKs];
-  load_e_frags<W, kKs>(e, a.W1, a.x[(size_t)rc * (a.gamma + 1) + (a.k - 1)], a.rank, a.V, half);
-
   DraftEpi<kGreedy, kDebug, kVec> epi(a, r, rc, half);
-  shared_a_stream<W, kKs>(a.W2t, a.V, a.rank, t_begin, t_end, e, lds, epi);
+  auto gather = [&](typename W::frag_t(&ef)[W::kMaxKs]) {
+    load_e_frags<W, kKs>(ef, a.W1, prev_token(a, rc), a.rank, a.V, half);
+  };
+  if constexpr (kKs > 0)
+    shared_a_stream_skew<W, kKs>(a.W2t, a.V, t_begin, t_end, e, gather, lds, epi);
+  else
+    shared_a_stream<W, kKs, draft_dist<W>()>(a.W2t, a.V, a.rank, t_begin, t_end, e, gather, lds,
+                                             epi);
 
   Rec q = epi.record();
   q = rec_merge(q, rec_shfl_xor(q, 32));
-  unsigned chk = 0u;
-  if (half == 0 && r < a.R) chk = put_rec(a.part, a.R, slab, r, q);
-  merge_levels<kWaves * kVTile>(a, grp, slab, r0, min(kWaves * kVTile, a.R - r0), chk);
+  if (half == 0 && r < a.R) publish(a, slab, r, q);
+  if (a.h != nullptr) step_confidence<W>(a, slab, r0, min(kWaves * kVTile, a.R - r0));
 }
 
 template <class W, int kKs, bool kGreedy, bool kDebug, bool kVec>
@@ -340,39 +284,117 @@ __global__ __launch_bounds__(kStreamThreads) void markov_step_private(StepArgs a
   const int slab = blockIdx.x % a.n_slabs;
   const int grp = blockIdx.x / a.n_slabs;  // request tile
   const int r0 = grp * kVTile;
-  if (a.h != nullptr && slab < kVTile / kWaves) {  // 8 workgroups x 4 waves
-    const int rq = r0 + slab * kWaves + wave;
-    if (rq < a.R) confidence_wave<W>(a, rq, lane);
-  }
   int t_begin, t_end;
   slab_range(slab, a.n_slabs, a.n_vtiles, t_begin, t_end);
 
   const int r = r0 + col;
   const int rc = r < a.R ? r : a.R - 1;
   typename W::frag_t e[W::kMaxKs];
-  load_e_frags<W, kKs>(e, a.W1, a.x[(size_t)rc * (a.gamma + 1) + (a.k - 1)], a.rank, a.V, half);
-
   DraftEpi<kGreedy, kDebug, kVec> epi(a, r, rc, half);
-  private_a_stream<W, kKs>(a.W2t, a.V, a.rank, t_begin + wave, t_end, kWaves, e, epi);
+  private_a_stream<W, kKs>(
+      a.W2t, a.V, a.rank, t_begin + wave, t_end, kWaves, e,
+      [&](typename W::frag_t(&ef)[W::kMaxKs]) {
+        load_e_frags<W, kKs>(ef, a.W1, prev_token(a, rc), a.rank, a.V, half);
+      },
+      epi);
 
   Rec q = epi.record();
   q = rec_merge(q, rec_shfl_xor(q, 32));
   if (half == 0) srec[wave][col] = q;
   __syncthreads();
-  unsigned chk = 0u;
-  if (wave == 0 && half == 0) {
+  if (wave == 0 && half == 0 && r < a.R) {
     Rec m = srec[0][col];
     for (int w = 1; w < kWaves; ++w) m = rec_merge(m, srec[w][col]);
-    if (r < a.R) chk = put_rec(a.part, a.R, slab, r, m);
+    publish(a, slab, r, m);
   }
-  merge_levels<kVTile>(a, grp, slab, r0, min(kVTile, a.R - r0), chk);
+  if (a.h != nullptr) step_confidence<W>(a, slab, r0, min(kVTile, a.R - r0));
+}
+
+// ---------------------------------------------------------------------------
+// Merge of the records of step k = k0 + blockIdx.y for requests
+// r0 = 32 * blockIdx.x .. r0 + 31.  Wave w takes slabs [w * spw, (w+1) * spw);
+// lane (h, rl) = (lane / 32, lane % 32) folds slabs w * spw + h, + 2, + 4, ...
+// of request r0 + rl in order (each load instruction reads 32 consecutive
+// requests of two slabs), the two halves merge (h = 0 first), then thread rl
+// merges the 16 wave results in wave order.
+// ---------------------------------------------------------------------------
+constexpr int kMergeWaves = 16;
+constexpr int kMergeRounds = kResidentWgs / kMergeWaves / 2;  // load rounds per lane
+
+struct MergeAcc {
+  float m, S, tb;
+  unsigned long long wb;  // largest winner word seen
+};
+
+__device__ __forceinline__ MergeAcc macc_merge(const MergeAcc& x, const MergeAcc& y) {
+  MergeAcc o;
+  o.m = fmaxf(x.m, y.m);
+  o.S = (o.m == -INFINITY) ? 0.0f : x.S * fast_exp2(x.m - o.m) + y.S * fast_exp2(y.m - o.m);
+  const bool ty = y.wb > x.wb;
+  o.wb = ty ? y.wb : x.wb;
+  o.tb = ty ? y.tb : x.tb;
+  return o;
+}
+
+__global__ __launch_bounds__(64 * kMergeWaves) void draft_merge(StepArgs a, int k0) {
+  __shared__ MergeAcc sacc[kMergeWaves][kVTile];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = lane >> 5, rl = lane & 31;
+  const int k = k0 + blockIdx.y;
+  const int r = blockIdx.x * kVTile + rl;
+  const int rc = r < a.R ? r : a.R - 1;
+  const float* base = a.rec + (size_t)(k - 1) * a.rec_step_f + rc;
+  const int spw = (a.n_slabs + kMergeWaves - 1) / kMergeWaves;
+  const int s0 = wave * spw, s1 = min(a.n_slabs, s0 + spw);
+
+  float rm[kMergeRounds], rS[kMergeRounds], rkey[kMergeRounds], rt[kMergeRounds];
+  int rid[kMergeRounds];
+#pragma unroll
+  for (int i = 0; i < kMergeRounds; ++i) {
+    const int sl = s0 + 2 * i + h;
+    const bool ok = sl < s1;
+    const float* p = base + (size_t)(ok ? sl : 0) * 5 * a.R;
+    rm[i] = ok ? p[0] : -INFINITY;
+    rS[i] = ok ? p[a.R] : 0.0f;
+    rkey[i] = ok ? p[2 * a.R] : -INFINITY;
+    rt[i] = ok ? p[3 * a.R] : -INFINITY;
+    rid[i] = ok ? __float_as_int(p[4 * a.R]) : -1;
+  }
+  MergeAcc acc{-INFINITY, 0.0f, -INFINITY, 0ull};
+#pragma unroll
+  for (int i = 0; i < kMergeRounds; ++i)
+    acc = macc_merge(acc, MergeAcc{rm[i], rS[i], rt[i], pack_winner(rkey[i], rid[i])});
+  MergeAcc o;
+  o.m = __shfl_xor(acc.m, 32);
+  o.S = __shfl_xor(acc.S, 32);
+  o.tb = __shfl_xor(acc.tb, 32);
+  o.wb = __shfl_xor(acc.wb, 32);
+  acc = h == 0 ? macc_merge(acc, o) : macc_merge(o, acc);
+  if (h == 0) sacc[wave][rl] = acc;
+  __syncthreads();
+  if (wave == 0 && h == 0 && r < a.R) {
+    MergeAcc f = sacc[0][rl];
+    for (int w = 1; w < kMergeWaves; ++w) f = macc_merge(f, sacc[w][rl]);
+    const size_t oi = (size_t)r * a.gamma + (k - 1);
+    a.x[(size_t)r * (a.gamma + 1) + k] = winner_id(f.wb);
+    if (a.greedy) {
+      a.p[oi] = 1.0f;
+      a.lse[oi] = f.m;
+    } else {
+      const float lse2 = f.m + log2f(f.S);
+      a.p[oi] = exp2f(f.tb - lse2);
+      a.lse[oi] = lse2 * kLn2;
+    }
+    a.best[(size_t)(k - 1) * a.R + r] = 0ull;  // leave the workspace zeroed for the next call
+  }
 }
 
 template <class W, int kKs, bool kGreedy, bool kDebug, bool kVec>
 void launch_one(const StepArgs& a, const StepPlan& plan, hipStream_t stream) {
   if (plan.shared)
     hipLaunchKernelGGL((markov_step_shared<W, kKs, kGreedy, kDebug, kVec>), dim3(plan.grid_x),
-                       dim3(kStreamThreads), stream_lds_bytes<W>(a.rank), stream, a);
+                       dim3(kStreamThreads),
+                       stream_lds_bytes<W>(a.rank, kKs > 0 ? 1 : draft_dist<W>()), stream, a);
   else
     hipLaunchKernelGGL((markov_step_private<W, kKs, kGreedy, kDebug, kVec>), dim3(plan.grid_x),
                        dim3(kStreamThreads), 0, stream, a);
@@ -410,7 +432,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Launch planning depends only on the sizes (never on the device), so every
 // run of a given problem merges its partial results in the same order.
-StepPlan plan_draft_step(int R, int V) {
+StepPlan plan_draft_step(int R, int V, int gamma) {
   StepPlan p{};
   p.n_vtiles = (V + kVTile - 1) / kVTile;
   const int rt = (R + kVTile - 1) / kVTile;
@@ -419,7 +441,7 @@ StepPlan plan_draft_step(int R, int V) {
     p.n_groups = (rt + kWaves - 1) / kWaves;
     int slabs = kResidentWgs / p.n_groups;
     if (p.n_groups > 1) slabs = (slabs / 8) * 8;
-    if (slabs < kVTile) slabs = kVTile;  // the confidence head uses 32 slabs per group
+    if (slabs < 8) slabs = 8;
     p.n_slabs = slabs;
   } else {
     p.shared = false;
@@ -427,21 +449,26 @@ StepPlan plan_draft_step(int R, int V) {
     int slabs = kResidentWgs / rt;
     const int max_slabs = (p.n_vtiles + kWaves - 1) / kWaves;
     if (slabs > max_slabs) slabs = max_slabs;
-    if (slabs < kVTile / kWaves) slabs = kVTile / kWaves;  // 8 slabs carry the confidence head
     p.n_slabs = slabs;
   }
   p.grid_x = p.n_slabs * p.n_groups;
   p.grid_y = 1;
-  p.team_size = kTeamSize;
-  p.n_teams = (p.n_slabs + p.team_size - 1) / p.team_size;  // <= kMaxTeams
-  p.off_part2 = align256((size_t)p.n_slabs * 5 * R * 4);
-  p.off_counters = p.off_part2 + align256((size_t)p.n_teams * 5 * R * 4);
-  p.ws_bytes = p.off_counters + align256((size_t)p.n_groups * (p.n_teams + 1) * 4);
+  p.rec_step = align256((size_t)p.n_slabs * 5 * R * 4);
+  p.off_best = p.rec_step * gamma;
+  p.ws_bytes = p.off_best + align256((size_t)gamma * R * 8);
   return p;
 }
 
 hipError_t launch_draft_step(const StepArgs& a, const StepPlan& plan, hipStream_t stream) {
   return a.bf16 ? launch_w<WBf16>(a, plan, stream) : launch_w<WF32>(a, plan, stream);
+}
+
+hipError_t launch_draft_finalize(const StepArgs& a, const StepPlan& plan, int k0, int nk,
+                                 hipStream_t stream) {
+  (void)plan;
+  const dim3 grid((a.R + kVTile - 1) / kVTile, nk), block(64 * kMergeWaves);
+  hipLaunchKernelGGL(draft_merge, grid, block, 0, stream, a, k0);
+  return hipGetLastError();
 }
 
 }  // namespace dspark

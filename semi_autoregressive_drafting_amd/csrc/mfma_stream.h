@@ -7,10 +7,17 @@
 // Lane l owns row 32*tile + l%32 and vocabulary entries 16*(l/32) .. +15 of the
 // tile (tile_perm), matching the accumulator layout of the 32x32 MFMAs.
 //
-// Epilogue interface (Epi), with a compile-time register slot S in {0, 1}
-// (tiles alternate between two register buffers, so nothing is copied):
-//   template <int S> void prefetch(int vt)   issue the loads of tile vt into slot S
-//   template <int S> void consume(const f32x16_t& acc, int vt)   fold tile vt (slot S)
+// Epilogue interface (Epi), with a compile-time register slot S in
+// {0 .. kDist} (kDist = the prefetch distance chosen by the kernel):
+//   static constexpr int kLoads   load instructions one prefetch issues
+//   template <int S> void prefetch(int vt)
+//       issue the loads of full tile vt into slot S; vt < 0 asks for the same
+//       loads from an address that is always valid and cached (the start of the
+//       lane's row), whose values are never used.  Prefetches are therefore
+//       never conditional, which keeps the compiler's load counting exact.
+//   template <int S> void consume(const f32x16_t& acc, int vt)   fold full tile vt
+//   void tail(const f32x16_t& acc, int vt)
+//       load (masked) and fold the last, partial tile of the vocabulary.
 //
 // kKs > 0 fixes the number of MFMA K-steps at compile time (rank = kKs * K
 // per MFMA); kKs = 0 reads it at run time.
@@ -27,6 +34,32 @@ constexpr int kStreamThreads = 256;
 // Workgroups of kStreamThreads that the 256 CUs of an MI355X hold at once for
 // the streaming kernels (two per CU at their register footprint).
 constexpr int kResidentWgs = 512;
+// Largest prefetch distance of the shared stream (tile i is multiplied while
+// tiles i+1 .. i+kDist are in flight); buffers rotate with period kDist + 1.
+constexpr int kMaxDist = 2;
+
+template <int S>
+using slot_t = std::integral_constant<int, S>;
+
+// Workgroup barrier for LDS hand-offs.  It waits only for this wave's LDS
+// operations; a __syncthreads() would also wait for every outstanding global
+// load of the wave and so drain the prefetch pipeline at each tile.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Wait until every global load this wave has issued so far has returned.
+__device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Wait until at most N of this wave's global loads are outstanding (vmcnt(N);
+// expcnt and lgkmcnt left alone).  Stating the wait explicitly keeps the
+// compiler from assuming, at a loop header, that older loads are still
+// pending.
+template <int N>
+__device__ __forceinline__ void wait_loads_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
 
 // E fragments (MFMA B operand) of this lane's row: W1[token], K split in steps.
 template <class W, int kKs = 0>
@@ -42,19 +75,35 @@ __device__ __forceinline__ void load_e_frags(typename W::frag_t (&e)[W::kMaxKs],
 
 // LDS bytes of one staged W2t tile (32 rows, row stride padded by 16 bytes).
 template <class W>
-__host__ __device__ inline size_t stream_lds_bytes(int rank) {
+__host__ __device__ inline size_t stream_tile_bytes(int rank) {
   return (size_t)kVTile * (rank * sizeof(typename W::store_t) + 16);
 }
+template <class W>
+__host__ __device__ inline size_t stream_lds_bytes(int rank, int dist) {
+  return (size_t)(dist + 1) * stream_tile_bytes<W>(rank);
+}
 
-// Workgroup of 4 waves: each W2t tile is loaded from HBM once (256 threads x
-// up to 4 x 16 bytes, prefetched one tile ahead in registers), staged in LDS and
-// multiplied by every wave with its own E fragments.  The loop is unrolled by
-// two so the epilogue's prefetch buffers alternate without copies.
-template <class W, int kKs, class Epi>
+// Workgroup of 4 waves over tiles [t_begin, t_end) of the vocabulary.  Each
+// W2t tile leaves HBM once per workgroup (256 threads x up to 4 x 16 bytes),
+// is staged in LDS and multiplied by every wave with its own E fragments.
+//
+// Iteration i, with prefetch distance D = kDist and slot S = i mod (D + 1):
+//   1. issue the loads of tile i+D: W2t into registers, the epilogue's rows;
+//   2. MFMA tile i from LDS slot S;
+//   3. epilogue of tile i (its rows were loaded during iteration i-D);
+//   4. store W2t of tile i+1 (loaded during iteration i+1-D) into LDS slot S+1;
+//   5. LDS barrier.
+// D = 2 hides two iterations of load latency; epilogues that stream two rows
+// per entry (verification) use D = 1 to stay within the register budget.
+// Only full tiles go through the pipeline; a partial last tile of the
+// vocabulary is handled after it without prefetching.
+// load_e(e) fills the E fragments; it runs after the first tiles' loads are
+// issued, so the row gather (which depends on a token id read from memory)
+// overlaps them.
+template <class W, int kKs, int kDist, class LoadE, class Epi>
 __device__ __forceinline__ void shared_a_stream(const void* W2t, int V, int rank, int t_begin,
-                                                int t_end,
-                                                const typename W::frag_t (&e)[W::kMaxKs],
-                                                unsigned char* lds, Epi& epi) {
+                                                int t_end, typename W::frag_t (&e)[W::kMaxKs],
+                                                LoadE&& load_e, unsigned char* lds, Epi& epi) {
   using store_t = typename W::store_t;
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5;
@@ -62,40 +111,78 @@ __device__ __forceinline__ void shared_a_stream(const void* W2t, int V, int rank
   const int row_bytes = rank * (int)sizeof(store_t);
   const int rs = row_bytes + 16;
   const int cpr = row_bytes / 16;
-  const int nchunks = kVTile * cpr;
+  const int nchunks = kVTile * cpr;  // 16-byte chunks per tile
+  const int tile_lds = kVTile * rs;
+  const unsigned char* wbase = reinterpret_cast<const unsigned char*>(W2t);
+  const int t_full = min(t_end, V / kVTile);
 
-  u32x4_t pre[4];
-  auto fetch = [&](int vt) {
+  // Chunk j of this thread: c = tid + 256 j.  Threads past the tile's chunk
+  // count load a duplicate of the last chunk (never stored), so the loads are
+  // unconditional.
+  int coff[4], loff[4];
+  bool cst[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = threadIdx.x + j * kStreamThreads;
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (c < nchunks) {
-        const int row = c / cpr, ch = c - row * cpr;
-        const int vv = vt * kVTile + row;
-        if (vv < V)
-          v = *reinterpret_cast<const u32x4_t*>(reinterpret_cast<const unsigned char*>(W2t) +
-                                                (size_t)vv * row_bytes + (size_t)ch * 16);
-      }
-      pre[j] = v;
-    }
-  };
-  auto stash = [&]() {
+  for (int j = 0; j < 4; ++j) {
+    const int c = threadIdx.x + j * kStreamThreads;
+    cst[j] = c < nchunks;
+    const int cc = cst[j] ? c : nchunks - 1;
+    coff[j] = cc * 16;
+    const int row = cc / cpr;
+    loff[j] = row * rs + (cc - row * cpr) * 16;
+  }
+
+  static_assert(kDist >= 1 && kDist <= kMaxDist, "prefetch distance");
+  constexpr int P = kDist + 1;
+  u32x4_t wreg[P][4];
+  auto fetch = [&](auto slot, int vt) {
+    constexpr int S = decltype(slot)::value;
+    const bool real = vt < t_full;
+    const unsigned char* tile = wbase + (real ? (size_t)vt * nchunks * 16 : 0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = threadIdx.x + j * kStreamThreads;
-      if (c < nchunks) {
-        const int row = c / cpr, ch = c - row * cpr;
-        *reinterpret_cast<u32x4_t*>(lds + row * rs + ch * 16) = pre[j];
-      }
-    }
+    for (int j = 0; j < 4; ++j) wreg[S][j] = *reinterpret_cast<const u32x4_t*>(tile + coff[j]);
+    epi.template prefetch<S>(real ? vt : -1);
   };
-  const store_t* arow = reinterpret_cast<const store_t*>(lds + tile_perm(lane & 31) * rs);
-  auto mma = [&]() {
+  auto stash = [&](auto slot) {
+    constexpr int S = decltype(slot)::value;
+    unsigned char* dst = lds + S * tile_lds;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (cst[j]) *reinterpret_cast<u32x4_t*>(dst + loff[j]) = wreg[S][j];
+  };
+  const int arow_off = tile_perm(lane & 31) * rs;
+  auto mma = [&](const unsigned char* slot_base) {
+    const store_t* arow = reinterpret_cast<const store_t*>(slot_base + arow_off);
     f32x16_t acc = {};
     if constexpr (kKs > 0) {
+      // A fragments come from LDS in groups of kG, double-buffered, so each
+      // group's reads are in flight while the previous group's MFMAs run
+      // (one shared register set would expose an LDS round trip per MFMA).
+      constexpr int kG = 4;
+      constexpr int kGroups = (kKs + kG - 1) / kG;
+      typename W::frag_t af[2][kG];
 #pragma unroll
-      for (int ks = 0; ks < kKs; ++ks) acc = W::mma(W::load(arow, ks, half), e[ks], acc);
+      for (int q = 0; q < kG; ++q)
+        if (q < kKs) af[0][q] = W::load(arow, q, half);
+#pragma unroll
+      for (int g = 0; g < kGroups; ++g) {
+        if (g + 1 < kGroups) {
+#pragma unroll
+          for (int q = 0; q < kG; ++q)
+            if ((g + 1) * kG + q < kKs) af[(g + 1) & 1][q] = W::load(arow, (g + 1) * kG + q, half);
+        }
+#pragma unroll
+        for (int q = 0; q < kG; ++q)
+          if (g * kG + q < kKs) acc = W::mma(af[g & 1][q], e[g * kG + q], acc);
+      }
+      // Pin that order for the scheduler (it would otherwise sink each read
+      // next to its MFMA to save registers): reads of group 0, then per group
+      // the next group's reads followed by this group's MFMAs.
+      __builtin_amdgcn_sched_group_barrier(0x100, kG, 0);
+#pragma unroll
+      for (int g = 0; g < kGroups; ++g) {
+        if (g + 1 < kGroups) __builtin_amdgcn_sched_group_barrier(0x100, kG, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, kG, 0);
+      }
     } else {
 #pragma unroll
       for (int ks = 0; ks < W::kMaxKs; ++ks)
@@ -103,63 +190,250 @@ __device__ __forceinline__ void shared_a_stream(const void* W2t, int V, int rank
     }
     return acc;
   };
-  auto step = [&](auto slot, int vt) {
+  auto body = [&](auto slot, int vt) {
     constexpr int S = decltype(slot)::value;
-    __syncthreads();  // previous tile's LDS reads are done
-    stash();
-    __syncthreads();  // this tile is visible
-    if (vt + 1 < t_end) {
-      fetch(vt + 1);
-      epi.template prefetch<1 - S>(vt + 1);
-    }
-    const f32x16_t acc = mma();
+    fetch(slot_t<(S + kDist) % P>{}, vt + kDist);
+    const f32x16_t acc = mma(lds + S * tile_lds);
     epi.template consume<S>(acc, vt);
+    stash(slot_t<(S + 1) % P>{});
+    lds_barrier();
   };
-  if (t_begin >= t_end) return;
-  fetch(t_begin);
-  epi.template prefetch<0>(t_begin);
-  for (int vt = t_begin; vt < t_end; vt += 2) {
-    step(std::integral_constant<int, 0>{}, vt);
-    if (vt + 1 >= t_end) break;
-    step(std::integral_constant<int, 1>{}, vt + 1);
+
+  // Prologue: only the first tile is waited for (with the E fragments, which
+  // then never stay pending into the loop); with distance 2 the second tile
+  // is issued just before the loop, where the loop expects one tile in flight.
+  if (t_begin < t_full) fetch(slot_t<0>{}, t_begin);
+  load_e(e);
+  wait_all_loads();
+  if (t_begin < t_full) {
+    stash(slot_t<0>{});
+    if constexpr (kDist == 2) fetch(slot_t<1>{}, t_begin + 1);
+    lds_barrier();
+    int vt = t_begin;
+    for (;;) {
+      body(slot_t<0>{}, vt);
+      if (++vt >= t_full) break;
+      body(slot_t<1>{}, vt);
+      if (++vt >= t_full) break;
+      if constexpr (P > 2) {
+        body(slot_t<2>{}, vt);
+        if (++vt >= t_full) break;
+      }
+    }
+  }
+  if (t_end > t_full) {  // the partial last tile (rows >= V read as zero)
+    const int vt = t_full;
+    const int valid = (V - vt * kVTile) * cpr;
+    unsigned char* dst = lds;  // slot 0: every wave is past its last read (barrier above)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = threadIdx.x + j * kStreamThreads;
+      if (c < nchunks) {
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (c < valid) v = *reinterpret_cast<const u32x4_t*>(wbase + (size_t)vt * nchunks * 16 + c * 16);
+        *reinterpret_cast<u32x4_t*>(dst + loff[j]) = v;
+      }
+    }
+    lds_barrier();
+    const f32x16_t acc = mma(lds);
+    epi.tail(acc, vt);
+  }
+}
+
+// Skewed variant of the shared stream for a compile-time rank (kKs > 0): the
+// MFMAs of tile i+1 are issued interleaved with the epilogue of tile i, so
+// the matrix core and the LDS reads that feed it work underneath the
+// epilogue's VALU instead of in front of it.  Two accumulators, two LDS
+// slots, two W2t register buffers and two epilogue slots (period 2).
+//
+// Iteration i (S = i mod 2):
+//   a. store W2t of tile i+1 (loaded during iteration i-1) into LDS slot S^1;
+//   b. LDS barrier;
+//   c. issue the W2t loads of tile i+2 into register buffer S;
+//   d. acc_next = MFMA of tile i+1 from LDS slot S^1   } interleaved by the
+//   e. epilogue of tile i with acc_cur                 } scheduler groups below
+//   f. issue the epilogue's loads of tile i+2 into slot S (tile i is folded).
+// A partial last tile of the vocabulary is handled after the loop.
+template <class W, int kKs, class LoadE, class Epi>
+__device__ __forceinline__ void shared_a_stream_skew(const void* W2t, int V, int t_begin,
+                                                     int t_end,
+                                                     typename W::frag_t (&e)[W::kMaxKs],
+                                                     LoadE&& load_e, unsigned char* lds,
+                                                     Epi& epi) {
+  static_assert(kKs > 0, "compile-time rank");
+  using store_t = typename W::store_t;
+  constexpr int kRowBytes = kKs * W::kKStep * (int)sizeof(store_t);
+  constexpr int kRs = kRowBytes + 16;
+  constexpr int kCpr = kRowBytes / 16;
+  constexpr int kChunks = kVTile * kCpr;          // 16-byte chunks per tile
+  constexpr int kPer = (kChunks + kStreamThreads - 1) / kStreamThreads;
+  static_assert(kChunks % kStreamThreads == 0, "whole chunks per thread");
+  constexpr int kTileLds = kVTile * kRs;
+  const int lane = threadIdx.x & 63;
+  const int half = lane >> 5;
+  const unsigned char* wbase = reinterpret_cast<const unsigned char*>(W2t);
+  const int t_full = min(t_end, V / kVTile);
+
+  int coff[kPer], loff[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int c = threadIdx.x + j * kStreamThreads;
+    coff[j] = c * 16;
+    const int row = c / kCpr;
+    loff[j] = row * kRs + (c - row * kCpr) * 16;
+  }
+  u32x4_t wreg[2][kPer];
+  auto fetch_w = [&](auto slot, int vt) {
+    constexpr int S = decltype(slot)::value;
+    const unsigned char* tile = wbase + (vt < t_full ? (size_t)vt * kChunks * 16 : 0);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) wreg[S][j] = *reinterpret_cast<const u32x4_t*>(tile + coff[j]);
+  };
+  auto stash = [&](auto slot, unsigned char* dst) {
+    constexpr int S = decltype(slot)::value;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) *reinterpret_cast<u32x4_t*>(dst + loff[j]) = wreg[S][j];
+  };
+  const int arow_off = tile_perm(lane & 31) * kRs;
+  // 16 A-fragment reads and MFMAs; reads run up to kAhead fragments ahead.
+  auto mma = [&](const unsigned char* slot_base) {
+    const store_t* arow = reinterpret_cast<const store_t*>(slot_base + arow_off);
+    typename W::frag_t af[kKs];
+#pragma unroll
+    for (int ks = 0; ks < kKs; ++ks) af[ks] = W::load(arow, ks, half);
+    f32x16_t acc = {};
+#pragma unroll
+    for (int ks = 0; ks < kKs; ++ks) acc = W::mma(af[ks], e[ks], acc);
+    return acc;
+  };
+  // Scheduler groups for one iteration body: the first kAhead A reads, then
+  // per MFMA one more read and a share of the epilogue's VALU work.
+  constexpr int kAhead = 4;
+  constexpr int kValuPerMfma = 24;
+  auto pin = [&]() {
+    __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 1);
+#pragma unroll
+    for (int ks = 0; ks < kKs; ++ks) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      if (ks + kAhead < kKs) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 1);
+    }
+  };
+
+  f32x16_t acc_cur = {};
+  auto body = [&](auto slot, int vt) {
+    constexpr int S = decltype(slot)::value;
+    // Everything but the epilogue loads of tile i+1 has arrived: the W2t of
+    // tile i+1 (stored next) and the epilogue rows of tile i.
+    wait_loads_le<Epi::kLoads>();
+    stash(slot_t<S ^ 1>{}, lds + (S ^ 1) * kTileLds);
+    lds_barrier();
+    fetch_w(slot_t<S>{}, vt + 2);
+    const f32x16_t acc_next = mma(lds + (S ^ 1) * kTileLds);
+    epi.template consume<S>(acc_cur, vt);
+    epi.template prefetch<S>(vt + 2 < t_full ? vt + 2 : -1);
+    pin();
+    acc_cur = acc_next;
+  };
+
+  if (t_begin < t_full) {
+    fetch_w(slot_t<0>{}, t_begin);
+    epi.template prefetch<0>(t_begin);
+  }
+  load_e(e);
+  wait_all_loads();  // the E fragments never stay pending into the loop
+  if (t_begin < t_full) {
+    stash(slot_t<0>{}, lds);
+    fetch_w(slot_t<1>{}, t_begin + 1);
+    epi.template prefetch<1>(t_begin + 1 < t_full ? t_begin + 1 : -1);
+    lds_barrier();
+    acc_cur = mma(lds);
+    int vt = t_begin;
+    for (;;) {
+      body(slot_t<0>{}, vt);
+      if (++vt >= t_full) break;
+      body(slot_t<1>{}, vt);
+      if (++vt >= t_full) break;
+    }
+  }
+  if (t_end > t_full) {  // the partial last tile (rows >= V read as zero)
+    const int vt = t_full;
+    const int valid = (V - vt * kVTile) * kCpr;
+    lds_barrier();  // every wave is past its last LDS read
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int c = threadIdx.x + j * kStreamThreads;
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (c < valid) v = *reinterpret_cast<const u32x4_t*>(wbase + (size_t)vt * kChunks * 16 + c * 16);
+      *reinterpret_cast<u32x4_t*>(lds + loff[j]) = v;
+    }
+    lds_barrier();
+    const f32x16_t acc = mma(lds);
+    epi.tail(acc, vt);
   }
 }
 
 // A single wave streams tiles t_begin, t_begin + t_stride, ... < t_end; the
-// W2t fragment goes straight from global memory into VGPRs.
-template <class W, int kKs, class Epi>
+// W2t fragment goes straight from global memory into VGPRs.  The epilogue's
+// loads of the next tile are issued before the current tile's MFMAs.
+template <class W, int kKs, class LoadE, class Epi>
 __device__ __forceinline__ void private_a_stream(const void* W2t, int V, int rank, int t_begin,
                                                  int t_end, int t_stride,
-                                                 const typename W::frag_t (&e)[W::kMaxKs],
-                                                 Epi& epi) {
+                                                 typename W::frag_t (&e)[W::kMaxKs],
+                                                 LoadE&& load_e, Epi& epi) {
   using store_t = typename W::store_t;
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5;
   const int nks = kKs > 0 ? kKs : rank / W::kKStep;
   const int prow = tile_perm(lane & 31);
-  for (int vt = t_begin; vt < t_end; vt += t_stride) {
-    epi.template prefetch<0>(vt);
+  const int t_full = min(t_end, V / kVTile);
+  auto mma = [&](int vt, bool masked) {
     const int vv = vt * kVTile + prow;
-    const store_t* wrow = reinterpret_cast<const store_t*>(W2t) + (size_t)(vv < V ? vv : V - 1) * rank;
+    const bool ok = !masked || vv < V;
+    const store_t* wrow = reinterpret_cast<const store_t*>(W2t) + (size_t)(ok ? vv : 0) * rank;
     f32x16_t acc = {};
 #pragma unroll
     for (int ks = 0; ks < W::kMaxKs; ++ks) {
-      if (ks < nks) {
-        typename W::frag_t af = (vv < V) ? W::load(wrow, ks, half) : W::zero();
+      if (kKs > 0 ? ks < kKs : ks < nks) {
+        typename W::frag_t af = W::load(wrow, ks, half);
+        if (masked && !ok) af = W::zero();
         acc = W::mma(af, e[ks], acc);
       }
     }
-    epi.template consume<0>(acc, vt);
+    return acc;
+  };
+  auto body = [&](auto slot, int vt) {
+    constexpr int S = decltype(slot)::value;
+    const int nxt = vt + t_stride;
+    epi.template prefetch<(S + 1) % 2>(nxt < t_full ? nxt : -1);
+    const f32x16_t acc = mma(vt, false);
+    epi.template consume<S>(acc, vt);
+  };
+  int vt = t_begin;
+  if (vt < t_full) epi.template prefetch<0>(vt);
+  load_e(e);
+  wait_all_loads();
+  if (vt < t_full) {
+    for (;;) {
+      body(slot_t<0>{}, vt);
+      vt += t_stride;
+      if (vt >= t_full) break;
+      body(slot_t<1>{}, vt);
+      vt += t_stride;
+      if (vt >= t_full) break;
+    }
+  }
+  if (vt < t_end) {  // at most one partial tile remains (the last of the vocabulary)
+    const f32x16_t acc = mma(vt, true);
+    epi.tail(acc, vt);
   }
 }
 
-// Load 16 consecutive fp32 values row[vb .. vb+15]; entries >= V read as 0.
-// `full` (uniform across the wave) says the whole 32-wide tile lies inside the
-// row; with kVec (rows 16-byte aligned, V % 4 == 0) it is read with four
-// 16-byte loads.
+// Load 16 consecutive fp32 values row[vb .. vb+15] of a full tile; with kVec
+// (rows 16-byte aligned) as four 16-byte non-temporal loads.
 template <bool kVec>
-__device__ __forceinline__ void load16(float (&u)[16], const float* row, int vb, int V, bool full) {
-  if (kVec && full) {
+__device__ __forceinline__ void load16(float (&u)[16], const float* row, int vb) {
+  if constexpr (kVec) {
     const f32x4_t* p = reinterpret_cast<const f32x4_t*>(row + vb);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -171,8 +445,15 @@ __device__ __forceinline__ void load16(float (&u)[16], const float* row, int vb,
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) u[i] = (vb + i < V) ? row[vb + i] : 0.0f;
+    for (int i = 0; i < 16; ++i) u[i] = row[vb + i];
   }
+}
+
+// Masked variant for the partial last tile: entries >= V read as `fill`.
+__device__ __forceinline__ void load16_masked(float (&u)[16], const float* row, int vb, int V,
+                                              float fill) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) u[i] = (vb + i < V) ? row[vb + i] : fill;
 }
 
 }  // namespace dspark

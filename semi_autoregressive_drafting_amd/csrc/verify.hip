@@ -32,6 +32,7 @@ namespace dspark {
 namespace {
 
 constexpr int kWaves = 4;
+constexpr int kVerifyDist = 1;  // prefetch distance of the shared stream (two rows per entry)
 constexpr double kFix = 1099511627776.0;  // 2^40, fixed-point unit of sum |p_d - p_t|
 
 __device__ __forceinline__ int chunk_size(int V, int chunks) {
@@ -220,28 +221,37 @@ struct TvEpi {
   const float* trow;
   int V, half;
   float kscale, lse2_d, lse2_t;
-  float ubuf[2][16], tbuf[2][16];
+  float ubuf[kVerifyDist + 1][16], tbuf[kVerifyDist + 1][16];
+  static constexpr int kLoads = kVec ? 8 : 32;
   float sabs;
 
   template <int S>
   __device__ void prefetch(int vt) {
-    const bool full = (vt + 1) * kVTile <= V;
-    load16<kVec>(ubuf[S], urow, vt * kVTile + 16 * half, V, full);
-    load16<kVec>(tbuf[S], trow, vt * kVTile + 16 * half, V, full);
+    const int vb = (vt < 0 ? 0 : vt * kVTile) + 16 * half;
+    load16<kVec>(ubuf[S], urow, vb);
+    load16<kVec>(tbuf[S], trow, vb);
+  }
+  template <bool kMasked>
+  __device__ __forceinline__ void fold(const float (&u)[16], const float (&t)[16],
+                                       const f32x16_t& acc, int vt) {
+    const int vb = vt * kVTile + 16 * half;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float pd = fast_exp2(fmaf(u[i] + acc[i], kscale, -lse2_d));
+      const float pt = fast_exp2(fmaf(t[i], kscale, -lse2_t));
+      const float d = fabsf(pd - pt);
+      sabs += (!kMasked || vb + i < V) ? d : 0.0f;
+    }
   }
   template <int S>
   __device__ void consume(const f32x16_t& acc, int vt) {
-    const float* ucur = ubuf[S];
-    const float* tcur = tbuf[S];
-    const int vb = vt * kVTile + 16 * half;
-    const bool full = (vt + 1) * kVTile <= V;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float pd = fast_exp2(fmaf(ucur[i] + acc[i], kscale, -lse2_d));
-      const float pt = fast_exp2(fmaf(tcur[i], kscale, -lse2_t));
-      const float d = (full || vb + i < V) ? fabsf(pd - pt) : 0.0f;
-      sabs += d;
-    }
+    fold<false>(ubuf[S], tbuf[S], acc, vt);
+  }
+  __device__ void tail(const f32x16_t& acc, int vt) {
+    float u[16], t[16];
+    load16_masked(u, urow, vt * kVTile + 16 * half, V, 0.0f);
+    load16_masked(t, trow, vt * kVTile + 16 * half, V, 0.0f);
+    fold<true>(u, t, acc, vt);
   }
 };
 
@@ -259,8 +269,6 @@ __global__ __launch_bounds__(kStreamThreads) void verify_tv(VerifyArgs a, Verify
   const int rowc = row < p.n_rows ? row : p.n_rows - 1;
   const int r = rowc / a.gamma, k = rowc % a.gamma + 1;
   typename W::frag_t e[W::kMaxKs];
-  load_e_frags<W, kKs>(e, a.W1, a.x[(size_t)r * (a.gamma + 1) + (k - 1)], a.rank, a.V, half);
-
   TvEpi<kVec> epi;
   epi.urow = a.U + (size_t)rowc * a.V;
   epi.trow = a.target + (size_t)rowc * a.V;
@@ -270,7 +278,13 @@ __global__ __launch_bounds__(kStreamThreads) void verify_tv(VerifyArgs a, Verify
   epi.lse2_d = a.lse_d[rowc] * kLog2e;
   epi.lse2_t = reinterpret_cast<const float*>(a.ws + p.off_lse_t)[rowc];
   epi.sabs = 0.0f;
-  shared_a_stream<W, kKs>(a.W2t, a.V, a.rank, t_begin, t_end, e, lds, epi);
+  shared_a_stream<W, kKs, kVerifyDist>(
+      a.W2t, a.V, a.rank, t_begin, t_end, e,
+      [&](typename W::frag_t(&ef)[W::kMaxKs]) {
+        load_e_frags<W, kKs>(ef, a.W1, a.x[(size_t)r * (a.gamma + 1) + (k - 1)], a.rank, a.V,
+                             half);
+      },
+      lds, epi);
 
   const float s = epi.sabs + __shfl_xor(epi.sabs, 32);
   if (half == 0 && row < p.n_rows) {
@@ -289,29 +303,28 @@ struct SampleEpi {
   int V, half, kind;
   float kscale, lse2_d, lse2_t;
   uint32_t state_row;
-  float ubuf[2][16], tbuf[2][16];
+  float ubuf[kVerifyDist + 1][16], tbuf[kVerifyDist + 1][16];
+  static constexpr int kLoads = kVec ? 8 : 32;
   float bE, bLn;
   int bV;
 
   template <int S>
   __device__ void prefetch(int vt) {
-    const bool full = (vt + 1) * kVTile <= V;
-    load16<kVec>(ubuf[S], urow, vt * kVTile + 16 * half, V, full);
-    load16<kVec>(tbuf[S], trow, vt * kVTile + 16 * half, V, full);
+    const int vb = (vt < 0 ? 0 : vt * kVTile) + 16 * half;
+    load16<kVec>(ubuf[S], urow, vb);
+    load16<kVec>(tbuf[S], trow, vb);
   }
-  template <int S>
-  __device__ void consume(const f32x16_t& acc, int vt) {
-    const float* ucur = ubuf[S];
-    const float* tcur = tbuf[S];
+  template <bool kMasked>
+  __device__ __forceinline__ void fold(const float (&u)[16], const float (&t)[16],
+                                       const f32x16_t& acc, int vt) {
     const int vb = vt * kVTile + 16 * half;
-    const bool full = (vt + 1) * kVTile <= V;
     const uint32_t s0 = state_row + (uint32_t)vb * kLcgMul;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float pd = fast_exp2(fmaf(ucur[i] + acc[i], kscale, -lse2_d));
-      const float pt = fast_exp2(fmaf(tcur[i], kscale, -lse2_t));
+      const float pd = fast_exp2(fmaf(u[i] + acc[i], kscale, -lse2_d));
+      const float pt = fast_exp2(fmaf(t[i], kscale, -lse2_t));
       float e = (kind == 1) ? fmaxf(pt - pd, 0.0f) : pt;
-      e = (full || vb + i < V) ? e : 0.0f;
+      if constexpr (kMasked) e = (vb + i < V) ? e : 0.0f;
       const float ln = fast_log2(bits_to_uniform(rxs_m_xs(s0 + (uint32_t)i * kLcgMul)));
       // e / L > bE / bL  <=>  e * bLn < bE * ln     (L = -ln > 0)
       const bool win = e * bLn < bE * ln;
@@ -319,6 +332,16 @@ struct SampleEpi {
       bLn = win ? ln : bLn;
       bV = win ? vb + i : bV;
     }
+  }
+  template <int S>
+  __device__ void consume(const f32x16_t& acc, int vt) {
+    fold<false>(ubuf[S], tbuf[S], acc, vt);
+  }
+  __device__ void tail(const f32x16_t& acc, int vt) {
+    float u[16], t[16];
+    load16_masked(u, urow, vt * kVTile + 16 * half, V, 0.0f);
+    load16_masked(t, trow, vt * kVTile + 16 * half, V, 0.0f);
+    fold<true>(u, t, acc, vt);
   }
 };
 
@@ -340,8 +363,6 @@ __global__ __launch_bounds__(kStreamThreads) void verify_sample(VerifyArgs a, Ve
   const int k = ks > 0 ? ks : 1;  // lanes without a sample run row 1 and never store
   const int row = rc * a.gamma + (k - 1);
   typename W::frag_t e[W::kMaxKs];
-  load_e_frags<W, kKs>(e, a.W1, a.x[(size_t)rc * (a.gamma + 1) + (k - 1)], a.rank, a.V, half);
-
   SampleEpi<kVec> epi;
   epi.urow = a.U + (size_t)row * a.V;
   epi.trow = a.target + (size_t)row * a.V;
@@ -356,7 +377,13 @@ __global__ __launch_bounds__(kStreamThreads) void verify_sample(VerifyArgs a, Ve
   epi.bE = 0.0f;
   epi.bLn = -1.0f;
   epi.bV = -1;
-  shared_a_stream<W, kKs>(a.W2t, a.V, a.rank, t_begin, t_end, e, lds, epi);
+  shared_a_stream<W, kKs, kVerifyDist>(
+      a.W2t, a.V, a.rank, t_begin, t_end, e,
+      [&](typename W::frag_t(&ef)[W::kMaxKs]) {
+        load_e_frags<W, kKs>(ef, a.W1, a.x[(size_t)rc * (a.gamma + 1) + (k - 1)], a.rank, a.V,
+                             half);
+      },
+      lds, epi);
 
   float key = (epi.bV >= 0 && epi.bE > 0.0f) ? fast_log2(epi.bE) - fast_log2(-epi.bLn) : -INFINITY;
   int idx = (epi.bV >= 0 && epi.bE > 0.0f) ? epi.bV : -1;
@@ -391,7 +418,7 @@ __global__ __launch_bounds__(256) void verify_finalize(VerifyArgs a, VerifyPlan 
 
 template <class W, int kKs, bool kVec>
 hipError_t launch_passes(const VerifyArgs& a, const VerifyPlan& p, hipStream_t stream) {
-  const size_t lds = stream_lds_bytes<W>(a.rank);
+  const size_t lds = stream_lds_bytes<W>(a.rank, kVerifyDist);
   hipLaunchKernelGGL((verify_tv<W, kKs, kVec>), dim3(p.n_slabs * p.n_groups), dim3(kStreamThreads),
                      lds, stream, a, p);
   hipError_t e = hipGetLastError();
