@@ -53,6 +53,12 @@ constexpr int draft_dist() {
   return std::is_same<W, WBf16>::value ? 2 : 1;
 }
 
+// LDS bytes of the shared draft stream (the skewed stream keeps two W2t slots).
+template <class W, int kKs>
+__host__ __device__ inline size_t draft_stream_lds(int rank) {
+  return stream_lds_bytes<W>(rank, kKs > 0 ? 1 : draft_dist<W>());
+}
+
 // Order-preserving map of a float to uint32 (larger float -> larger code).
 __device__ __forceinline__ uint32_t ordered(float f) {
   const uint32_t u = __float_as_uint(f);
@@ -79,20 +85,32 @@ struct LaneState {
   int bV;     // winner id, -1 if none
 };
 
+// U rows of the wave's 32 requests: with kVec (16-byte aligned rows) read as
+// whole lines and passed through the wave's LDS patch (RowTiles); otherwise
+// each lane loads its own row's 16 entries.
 template <bool kGreedy, bool kDebug, bool kVec>
 struct DraftEpi {
   const float* urow;
   float* zdbg;
+  float* patch;  // this wave's LDS patch (kVec)
   int V, R, r, half;
   float kscale;
   uint32_t state_row;  // LCG state of vocabulary entry 0 of this row
-  float ubuf[kMaxDist + 1][16];  // U of the tile being folded and the prefetched ones
+  float ubuf[kVec ? 1 : kMaxDist + 1][16];       // own-row U (scalar path)
+  RowTiles<1, kVec ? kMaxDist + 1 : 1> rows;     // line-coalesced U (kVec)
   LaneState st;
   static constexpr int kLoads = kVec ? 4 : 16;
 
-  __device__ DraftEpi(const StepArgs& a, int r_, int rc, int half_)
-      : zdbg(a.z_debug), V(a.V), R(a.R), r(r_), half(half_), kscale(a.kscale) {
+  // r0w: first request of the wave's 32-row tile.
+  __device__ DraftEpi(const StepArgs& a, int r_, int rc, int half_, int r0w, float* patch_)
+      : zdbg(a.z_debug), patch(patch_), V(a.V), R(a.R), r(r_), half(half_), kscale(a.kscale) {
     urow = a.U + ((size_t)rc * a.gamma + (a.k - 1)) * a.V;
+    if constexpr (kVec) {
+      rows.base[0] = a.U + (size_t)(a.k - 1) * a.V;
+      const int jmax = a.R - 1 - r0w;
+      const size_t rstride = (size_t)a.gamma * a.V;
+      rows.init([&](int j) { return (size_t)(r0w + (j < jmax ? j : jmax)) * rstride; });
+    }
     state_row = row_key(a.seed, kStreamDraft, (uint32_t)rc, (uint32_t)a.k) * kLcgMul + kLcgInc;
     st.m = -INFINITY;
     st.S = 0.0f;
@@ -102,7 +120,10 @@ struct DraftEpi {
   }
   template <int S>
   __device__ void prefetch(int vt) {
-    load16<kVec>(ubuf[S], urow, (vt < 0 ? 0 : vt * kVTile) + 16 * half);
+    if constexpr (kVec)
+      rows.template load<S>(vt);
+    else
+      load16<false>(ubuf[S], urow, (vt < 0 ? 0 : vt * kVTile) + 16 * half);
   }
 
   template <bool kMasked>
@@ -157,7 +178,13 @@ struct DraftEpi {
 
   template <int S>
   __device__ void consume(const f32x16_t& acc, int vt) {
-    fold_tile<false>(ubuf[S], acc, vt);
+    if constexpr (kVec) {
+      float u[1][16];
+      rows.template to_lanes<S>(patch, u);
+      fold_tile<false>(u[0], acc, vt);
+    } else {
+      fold_tile<false>(ubuf[S], acc, vt);
+    }
   }
 
   __device__ void tail(const f32x16_t& acc, int vt) {
@@ -260,7 +287,9 @@ __global__ __launch_bounds__(kStreamThreads) void markov_step_shared(StepArgs a)
   const int r = r0 + wave * kVTile + col;
   const int rc = r < a.R ? r : a.R - 1;  // padded lanes recompute row R-1, never stored
   typename W::frag_t e[W::kMaxKs];
-  DraftEpi<kGreedy, kDebug, kVec> epi(a, r, rc, half);
+  float* patch = reinterpret_cast<float*>(lds + draft_stream_lds<W, kKs>(a.rank)) +
+                 wave * kPatchFloats;
+  DraftEpi<kGreedy, kDebug, kVec> epi(a, r, rc, half, r0 + wave * kVTile, patch);
   auto gather = [&](typename W::frag_t(&ef)[W::kMaxKs]) {
     load_e_frags<W, kKs>(ef, a.W1, prev_token(a, rc), a.rank, a.V, half);
   };
@@ -289,8 +318,9 @@ __global__ __launch_bounds__(kStreamThreads) void markov_step_private(StepArgs a
 
   const int r = r0 + col;
   const int rc = r < a.R ? r : a.R - 1;
+  __shared__ __align__(16) float patches[kVec ? kWaves : 1][kPatchFloats];
   typename W::frag_t e[W::kMaxKs];
-  DraftEpi<kGreedy, kDebug, kVec> epi(a, r, rc, half);
+  DraftEpi<kGreedy, kDebug, kVec> epi(a, r, rc, half, r0, patches[kVec ? wave : 0]);
   private_a_stream<W, kKs>(
       a.W2t, a.V, a.rank, t_begin + wave, t_end, kWaves, e,
       [&](typename W::frag_t(&ef)[W::kMaxKs]) {
@@ -394,7 +424,8 @@ void launch_one(const StepArgs& a, const StepPlan& plan, hipStream_t stream) {
   if (plan.shared)
     hipLaunchKernelGGL((markov_step_shared<W, kKs, kGreedy, kDebug, kVec>), dim3(plan.grid_x),
                        dim3(kStreamThreads),
-                       stream_lds_bytes<W>(a.rank, kKs > 0 ? 1 : draft_dist<W>()), stream, a);
+                       (draft_stream_lds<W, kKs>(a.rank) + kWaves * kPatchFloats * sizeof(float)),
+                       stream, a);
   else
     hipLaunchKernelGGL((markov_step_private<W, kKs, kGreedy, kDebug, kVec>), dim3(plan.grid_x),
                        dim3(kStreamThreads), 0, stream, a);

@@ -100,7 +100,7 @@ __host__ __device__ inline size_t stream_lds_bytes(int rank, int dist) {
 // load_e(e) fills the E fragments; it runs after the first tiles' loads are
 // issued, so the row gather (which depends on a token id read from memory)
 // overlaps them.
-template <class W, int kKs, int kDist, class LoadE, class Epi>
+template <class W, int kKs, int kDist, int kThreads = kStreamThreads, class LoadE, class Epi>
 __device__ __forceinline__ void shared_a_stream(const void* W2t, int V, int rank, int t_begin,
                                                 int t_end, typename W::frag_t (&e)[W::kMaxKs],
                                                 LoadE&& load_e, unsigned char* lds, Epi& epi) {
@@ -116,14 +116,15 @@ __device__ __forceinline__ void shared_a_stream(const void* W2t, int V, int rank
   const unsigned char* wbase = reinterpret_cast<const unsigned char*>(W2t);
   const int t_full = min(t_end, V / kVTile);
 
-  // Chunk j of this thread: c = tid + 256 j.  Threads past the tile's chunk
-  // count load a duplicate of the last chunk (never stored), so the loads are
-  // unconditional.
-  int coff[4], loff[4];
-  bool cst[4];
+  // Chunk j of this thread: c = tid + kThreads j.  Threads past the tile's
+  // chunk count load a duplicate of the last chunk (never stored), so the
+  // loads are unconditional.
+  constexpr int kPer = 1024 / kThreads;  // chunks of the largest tile (32 x 512 B)
+  int coff[kPer], loff[kPer];
+  bool cst[kPer];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int c = threadIdx.x + j * kStreamThreads;
+  for (int j = 0; j < kPer; ++j) {
+    const int c = threadIdx.x + j * kThreads;
     cst[j] = c < nchunks;
     const int cc = cst[j] ? c : nchunks - 1;
     coff[j] = cc * 16;
@@ -133,20 +134,20 @@ __device__ __forceinline__ void shared_a_stream(const void* W2t, int V, int rank
 
   static_assert(kDist >= 1 && kDist <= kMaxDist, "prefetch distance");
   constexpr int P = kDist + 1;
-  u32x4_t wreg[P][4];
+  u32x4_t wreg[P][kPer];
   auto fetch = [&](auto slot, int vt) {
     constexpr int S = decltype(slot)::value;
     const bool real = vt < t_full;
     const unsigned char* tile = wbase + (real ? (size_t)vt * nchunks * 16 : 0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) wreg[S][j] = *reinterpret_cast<const u32x4_t*>(tile + coff[j]);
+    for (int j = 0; j < kPer; ++j) wreg[S][j] = *reinterpret_cast<const u32x4_t*>(tile + coff[j]);
     epi.template prefetch<S>(real ? vt : -1);
   };
   auto stash = [&](auto slot) {
     constexpr int S = decltype(slot)::value;
     unsigned char* dst = lds + S * tile_lds;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < kPer; ++j)
       if (cst[j]) *reinterpret_cast<u32x4_t*>(dst + loff[j]) = wreg[S][j];
   };
   const int arow_off = tile_perm(lane & 31) * rs;
@@ -226,8 +227,8 @@ __device__ __forceinline__ void shared_a_stream(const void* W2t, int V, int rank
     const int valid = (V - vt * kVTile) * cpr;
     unsigned char* dst = lds;  // slot 0: every wave is past its last read (barrier above)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = threadIdx.x + j * kStreamThreads;
+    for (int j = 0; j < kPer; ++j) {
+      const int c = threadIdx.x + j * kThreads;
       if (c < nchunks) {
         u32x4_t v = {0u, 0u, 0u, 0u};
         if (c < valid) v = *reinterpret_cast<const u32x4_t*>(wbase + (size_t)vt * nchunks * 16 + c * 16);
@@ -254,7 +255,7 @@ __device__ __forceinline__ void shared_a_stream(const void* W2t, int V, int rank
 //   e. epilogue of tile i with acc_cur                 } scheduler groups below
 //   f. issue the epilogue's loads of tile i+2 into slot S (tile i is folded).
 // A partial last tile of the vocabulary is handled after the loop.
-template <class W, int kKs, class LoadE, class Epi>
+template <class W, int kKs, int kThreads = kStreamThreads, class LoadE, class Epi>
 __device__ __forceinline__ void shared_a_stream_skew(const void* W2t, int V, int t_begin,
                                                      int t_end,
                                                      typename W::frag_t (&e)[W::kMaxKs],
@@ -266,8 +267,8 @@ __device__ __forceinline__ void shared_a_stream_skew(const void* W2t, int V, int
   constexpr int kRs = kRowBytes + 16;
   constexpr int kCpr = kRowBytes / 16;
   constexpr int kChunks = kVTile * kCpr;          // 16-byte chunks per tile
-  constexpr int kPer = (kChunks + kStreamThreads - 1) / kStreamThreads;
-  static_assert(kChunks % kStreamThreads == 0, "whole chunks per thread");
+  constexpr int kPer = kChunks / kThreads;
+  static_assert(kChunks % kThreads == 0, "whole chunks per thread");
   constexpr int kTileLds = kVTile * kRs;
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5;
@@ -277,7 +278,7 @@ __device__ __forceinline__ void shared_a_stream_skew(const void* W2t, int V, int
   int coff[kPer], loff[kPer];
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
-    const int c = threadIdx.x + j * kStreamThreads;
+    const int c = threadIdx.x + j * kThreads;
     coff[j] = c * 16;
     const int row = c / kCpr;
     loff[j] = row * kRs + (c - row * kCpr) * 16;
@@ -362,7 +363,7 @@ __device__ __forceinline__ void shared_a_stream_skew(const void* W2t, int V, int
     lds_barrier();  // every wave is past its last LDS read
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-      const int c = threadIdx.x + j * kStreamThreads;
+      const int c = threadIdx.x + j * kThreads;
       u32x4_t v = {0u, 0u, 0u, 0u};
       if (c < valid) v = *reinterpret_cast<const u32x4_t*>(wbase + (size_t)vt * kChunks * 16 + c * 16);
       *reinterpret_cast<u32x4_t*>(lds + loff[j]) = v;
@@ -428,6 +429,68 @@ __device__ __forceinline__ void private_a_stream(const void* W2t, int V, int ran
     epi.tail(acc, vt);
   }
 }
+
+// ---------------------------------------------------------------------------
+// Rows of a vocabulary tile in fp32 (one wave: 32 rows x 32 entries = 4 KB per
+// array), read from global memory as whole 128-byte lines -- load instruction
+// q, lane l: row 8q + l/8, entries 4 (l%8) .. +3 -- and handed to the MFMA lane
+// layout (row l%32, entries 16 (l/32) .. +15) through a padded LDS patch of the
+// wave (row stride 36 floats, so both the stores and the 16-byte reads are
+// free of bank conflicts).  The lane layout would touch 32 lines per load
+// instruction; whole lines are what the memory system serves best.
+// kArrays row sets share the row offsets (e.g. U and the target logits).
+// ---------------------------------------------------------------------------
+constexpr int kPatchRowFloats = 36;
+constexpr int kPatchFloats = kVTile * kPatchRowFloats;  // per wave (4.5 KB)
+
+template <int kArrays, int kSlots>
+struct RowTiles {
+  const float* base[kArrays];  // vocabulary entry 0 of the row of offset 0
+  size_t off[4];               // floats from base to this lane's (row, entry) of load q
+  f32x4_t g[kSlots][kArrays][4];
+
+  // row_off(j): offset in floats of the wave's row j (0..31) from base.
+  template <class RowOff>
+  __device__ __forceinline__ void init(RowOff&& row_off) {
+    const int l = threadIdx.x & 63;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) off[q] = row_off(8 * q + (l >> 3)) + 4 * (l & 7);
+  }
+  // Issue the loads of tile vt (vt < 0: the same loads from tile 0, unused).
+  template <int S>
+  __device__ __forceinline__ void load(int vt) {
+    const int col = vt < 0 ? 0 : vt * kVTile;
+#pragma unroll
+    for (int a = 0; a < kArrays; ++a)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        g[S][a][q] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4_t*>(base[a] + off[q] + col));
+  }
+  // Slot S to lane layout: out[a][i] = row l%32, entry 16 (l/32) + i.  The
+  // arrays pass through the same patch one after another (a wave's LDS
+  // operations complete in order, so a read returns before the next store).
+  template <int S>
+  __device__ __forceinline__ void to_lanes(float* patch, float (&out)[kArrays][16]) {
+    const int l = threadIdx.x & 63;
+    float* wr = patch + (l >> 3) * kPatchRowFloats + 4 * (l & 7);
+    const float* rd = patch + (l & 31) * kPatchRowFloats + 16 * (l >> 5);
+#pragma unroll
+    for (int a = 0; a < kArrays; ++a) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<f32x4_t*>(wr + 8 * q * kPatchRowFloats) = g[S][a][q];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(rd + 4 * c);
+        out[a][4 * c + 0] = v[0];
+        out[a][4 * c + 1] = v[1];
+        out[a][4 * c + 2] = v[2];
+        out[a][4 * c + 3] = v[3];
+      }
+    }
+  }
+};
 
 // Load 16 consecutive fp32 values row[vb .. vb+15] of a full tile; with kVec
 // (rows 16-byte aligned) as four 16-byte non-temporal loads.

@@ -31,7 +31,10 @@ namespace dspark {
 
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;        // sampling pass: waves (row tiles) per workgroup
+constexpr int kTvWaves = 4;      // c* pass: waves (row tiles) per workgroup
+constexpr int kTvThreads = 64 * kTvWaves;
+constexpr int kTvResidentWgs = kResidentWgs * kStreamThreads / kTvThreads;  // one per CU
 constexpr int kVerifyDist = 1;  // prefetch distance of the shared stream (two rows per entry)
 constexpr double kFix = 1099511627776.0;  // 2^40, fixed-point unit of sum |p_d - p_t|
 
@@ -215,48 +218,78 @@ __device__ __forceinline__ void slab_group(int b, int n_slabs, int n_groups, int
 // ---------------------------------------------------------------------------
 // V3: sum |p_d - p_t| over all rows (T > 0).
 // ---------------------------------------------------------------------------
+// Rows of U and of the target logits: with kVec read as whole lines through
+// the wave's LDS patch (RowTiles), otherwise each lane loads its own row.
 template <bool kVec>
-struct TvEpi {
+struct UTRows {
   const float* urow;
   const float* trow;
+  float* patch;
   int V, half;
-  float kscale, lse2_d, lse2_t;
-  float ubuf[kVerifyDist + 1][16], tbuf[kVerifyDist + 1][16];
+  float ubuf[kVec ? 1 : kVerifyDist + 1][16], tbuf[kVec ? 1 : kVerifyDist + 1][16];
+  RowTiles<2, kVec ? kVerifyDist + 1 : 1> rows;
   static constexpr int kLoads = kVec ? 8 : 32;
-  float sabs;
 
   template <int S>
-  __device__ void prefetch(int vt) {
-    const int vb = (vt < 0 ? 0 : vt * kVTile) + 16 * half;
-    load16<kVec>(ubuf[S], urow, vb);
-    load16<kVec>(tbuf[S], trow, vb);
+  __device__ __forceinline__ void prefetch(int vt) {
+    if constexpr (kVec) {
+      rows.template load<S>(vt);
+    } else {
+      const int vb = (vt < 0 ? 0 : vt * kVTile) + 16 * half;
+      load16<false>(ubuf[S], urow, vb);
+      load16<false>(tbuf[S], trow, vb);
+    }
   }
+  // Lane-layout U and target of slot S.
+  template <int S>
+  __device__ __forceinline__ void get(float (&ut)[2][16]) {
+    if constexpr (kVec) {
+      rows.template to_lanes<S>(patch, ut);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        ut[0][i] = ubuf[S][i];
+        ut[1][i] = tbuf[S][i];
+      }
+    }
+  }
+  __device__ __forceinline__ void get_tail(float (&ut)[2][16], int vt) {
+    load16_masked(ut[0], urow, vt * kVTile + 16 * half, V, 0.0f);
+    load16_masked(ut[1], trow, vt * kVTile + 16 * half, V, 0.0f);
+  }
+};
+
+template <bool kVec>
+struct TvEpi : UTRows<kVec> {
+  float kscale, lse2_d, lse2_t;
+  float sabs;
+
   template <bool kMasked>
-  __device__ __forceinline__ void fold(const float (&u)[16], const float (&t)[16],
-                                       const f32x16_t& acc, int vt) {
-    const int vb = vt * kVTile + 16 * half;
+  __device__ __forceinline__ void fold(const float (&ut)[2][16], const f32x16_t& acc, int vt) {
+    const int vb = vt * kVTile + 16 * this->half;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float pd = fast_exp2(fmaf(u[i] + acc[i], kscale, -lse2_d));
-      const float pt = fast_exp2(fmaf(t[i], kscale, -lse2_t));
+      const float pd = fast_exp2(fmaf(ut[0][i] + acc[i], kscale, -lse2_d));
+      const float pt = fast_exp2(fmaf(ut[1][i], kscale, -lse2_t));
       const float d = fabsf(pd - pt);
-      sabs += (!kMasked || vb + i < V) ? d : 0.0f;
+      sabs += (!kMasked || vb + i < this->V) ? d : 0.0f;
     }
   }
   template <int S>
   __device__ void consume(const f32x16_t& acc, int vt) {
-    fold<false>(ubuf[S], tbuf[S], acc, vt);
+    float ut[2][16];
+    this->template get<S>(ut);
+    fold<false>(ut, acc, vt);
   }
   __device__ void tail(const f32x16_t& acc, int vt) {
-    float u[16], t[16];
-    load16_masked(u, urow, vt * kVTile + 16 * half, V, 0.0f);
-    load16_masked(t, trow, vt * kVTile + 16 * half, V, 0.0f);
-    fold<true>(u, t, acc, vt);
+    float ut[2][16];
+    this->get_tail(ut, vt);
+    fold<true>(ut, acc, vt);
   }
 };
 
 template <class W, int kKs, bool kVec>
-__global__ __launch_bounds__(kStreamThreads) void verify_tv(VerifyArgs a, VerifyPlan p) {
+__global__ __launch_bounds__(kTvThreads) void verify_tv(VerifyArgs a, VerifyPlan p) {
   extern __shared__ __align__(16) unsigned char lds[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = lane >> 5, col = lane & 31;
@@ -265,7 +298,7 @@ __global__ __launch_bounds__(kStreamThreads) void verify_tv(VerifyArgs a, Verify
   int t_begin, t_end;
   slab_range(slab, p.n_slabs, p.n_vtiles, t_begin, t_end);
 
-  const int row = (grp * kWaves + wave) * kVTile + col;
+  const int row = (grp * kTvWaves + wave) * kVTile + col;
   const int rowc = row < p.n_rows ? row : p.n_rows - 1;
   const int r = rowc / a.gamma, k = rowc % a.gamma + 1;
   typename W::frag_t e[W::kMaxKs];
@@ -274,17 +307,26 @@ __global__ __launch_bounds__(kStreamThreads) void verify_tv(VerifyArgs a, Verify
   epi.trow = a.target + (size_t)rowc * a.V;
   epi.V = a.V;
   epi.half = half;
+  epi.patch = reinterpret_cast<float*>(lds + stream_lds_bytes<W>(a.rank, kVerifyDist)) +
+              wave * kPatchFloats;
+  if constexpr (kVec) {
+    const int row0 = (grp * kTvWaves + wave) * kVTile;
+    epi.rows.base[0] = a.U;
+    epi.rows.base[1] = a.target;
+    epi.rows.init([&](int j) {
+      const int rr = row0 + j < p.n_rows ? row0 + j : p.n_rows - 1;
+      return (size_t)rr * a.V;
+    });
+  }
   epi.kscale = a.kscale;
   epi.lse2_d = a.lse_d[rowc] * kLog2e;
   epi.lse2_t = reinterpret_cast<const float*>(a.ws + p.off_lse_t)[rowc];
   epi.sabs = 0.0f;
-  shared_a_stream<W, kKs, kVerifyDist>(
-      a.W2t, a.V, a.rank, t_begin, t_end, e,
-      [&](typename W::frag_t(&ef)[W::kMaxKs]) {
-        load_e_frags<W, kKs>(ef, a.W1, a.x[(size_t)r * (a.gamma + 1) + (k - 1)], a.rank, a.V,
-                             half);
-      },
-      lds, epi);
+  auto gather = [&](typename W::frag_t(&ef)[W::kMaxKs]) {
+    load_e_frags<W, kKs>(ef, a.W1, a.x[(size_t)r * (a.gamma + 1) + (k - 1)], a.rank, a.V, half);
+  };
+  shared_a_stream<W, kKs, kVerifyDist, kTvThreads>(a.W2t, a.V, a.rank, t_begin, t_end, e, gather,
+                                                   lds, epi);
 
   const float s = epi.sabs + __shfl_xor(epi.sabs, 32);
   if (half == 0 && row < p.n_rows) {
@@ -297,34 +339,23 @@ __global__ __launch_bounds__(kStreamThreads) void verify_tv(VerifyArgs a, Verify
 // V5: Gumbel race over the sampled rows (T > 0), one virtual row per request.
 // ---------------------------------------------------------------------------
 template <bool kVec>
-struct SampleEpi {
-  const float* urow;
-  const float* trow;
-  int V, half, kind;
+struct SampleEpi : UTRows<kVec> {
+  int kind;
   float kscale, lse2_d, lse2_t;
   uint32_t state_row;
-  float ubuf[kVerifyDist + 1][16], tbuf[kVerifyDist + 1][16];
-  static constexpr int kLoads = kVec ? 8 : 32;
   float bE, bLn;
   int bV;
 
-  template <int S>
-  __device__ void prefetch(int vt) {
-    const int vb = (vt < 0 ? 0 : vt * kVTile) + 16 * half;
-    load16<kVec>(ubuf[S], urow, vb);
-    load16<kVec>(tbuf[S], trow, vb);
-  }
   template <bool kMasked>
-  __device__ __forceinline__ void fold(const float (&u)[16], const float (&t)[16],
-                                       const f32x16_t& acc, int vt) {
-    const int vb = vt * kVTile + 16 * half;
+  __device__ __forceinline__ void fold(const float (&ut)[2][16], const f32x16_t& acc, int vt) {
+    const int vb = vt * kVTile + 16 * this->half;
     const uint32_t s0 = state_row + (uint32_t)vb * kLcgMul;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float pd = fast_exp2(fmaf(u[i] + acc[i], kscale, -lse2_d));
-      const float pt = fast_exp2(fmaf(t[i], kscale, -lse2_t));
+      const float pd = fast_exp2(fmaf(ut[0][i] + acc[i], kscale, -lse2_d));
+      const float pt = fast_exp2(fmaf(ut[1][i], kscale, -lse2_t));
       float e = (kind == 1) ? fmaxf(pt - pd, 0.0f) : pt;
-      if constexpr (kMasked) e = (vb + i < V) ? e : 0.0f;
+      if constexpr (kMasked) e = (vb + i < this->V) ? e : 0.0f;
       const float ln = fast_log2(bits_to_uniform(rxs_m_xs(s0 + (uint32_t)i * kLcgMul)));
       // e / L > bE / bL  <=>  e * bLn < bE * ln     (L = -ln > 0)
       const bool win = e * bLn < bE * ln;
@@ -335,13 +366,14 @@ struct SampleEpi {
   }
   template <int S>
   __device__ void consume(const f32x16_t& acc, int vt) {
-    fold<false>(ubuf[S], tbuf[S], acc, vt);
+    float ut[2][16];
+    this->template get<S>(ut);
+    fold<false>(ut, acc, vt);
   }
   __device__ void tail(const f32x16_t& acc, int vt) {
-    float u[16], t[16];
-    load16_masked(u, urow, vt * kVTile + 16 * half, V, 0.0f);
-    load16_masked(t, trow, vt * kVTile + 16 * half, V, 0.0f);
-    fold<true>(u, t, acc, vt);
+    float ut[2][16];
+    this->get_tail(ut, vt);
+    fold<true>(ut, acc, vt);
   }
 };
 
@@ -368,6 +400,18 @@ __global__ __launch_bounds__(kStreamThreads) void verify_sample(VerifyArgs a, Ve
   epi.trow = a.target + (size_t)row * a.V;
   epi.V = a.V;
   epi.half = half;
+  epi.patch = reinterpret_cast<float*>(lds + stream_lds_bytes<W>(a.rank, kVerifyDist)) +
+              wave * kPatchFloats;
+  if constexpr (kVec) {
+    const int r0w = (grp * kWaves + wave) * kVTile;
+    epi.rows.base[0] = a.U;
+    epi.rows.base[1] = a.target;
+    epi.rows.init([&](int j) {
+      const int rq = r0w + j < a.R ? r0w + j : a.R - 1;
+      const int kq = srow[rq] > 0 ? srow[rq] : 1;
+      return ((size_t)rq * a.gamma + (kq - 1)) * a.V;
+    });
+  }
   epi.kind = skind[rc];
   epi.kscale = a.kscale;
   epi.lse2_d = a.lse_d[row] * kLog2e;
@@ -377,13 +421,10 @@ __global__ __launch_bounds__(kStreamThreads) void verify_sample(VerifyArgs a, Ve
   epi.bE = 0.0f;
   epi.bLn = -1.0f;
   epi.bV = -1;
-  shared_a_stream<W, kKs, kVerifyDist>(
-      a.W2t, a.V, a.rank, t_begin, t_end, e,
-      [&](typename W::frag_t(&ef)[W::kMaxKs]) {
-        load_e_frags<W, kKs>(ef, a.W1, a.x[(size_t)rc * (a.gamma + 1) + (k - 1)], a.rank, a.V,
-                             half);
-      },
-      lds, epi);
+  auto gather = [&](typename W::frag_t(&ef)[W::kMaxKs]) {
+    load_e_frags<W, kKs>(ef, a.W1, a.x[(size_t)rc * (a.gamma + 1) + (k - 1)], a.rank, a.V, half);
+  };
+  shared_a_stream<W, kKs, kVerifyDist>(a.W2t, a.V, a.rank, t_begin, t_end, e, gather, lds, epi);
 
   float key = (epi.bV >= 0 && epi.bE > 0.0f) ? fast_log2(epi.bE) - fast_log2(-epi.bLn) : -INFINITY;
   int idx = (epi.bV >= 0 && epi.bE > 0.0f) ? epi.bV : -1;
@@ -418,8 +459,9 @@ __global__ __launch_bounds__(256) void verify_finalize(VerifyArgs a, VerifyPlan 
 
 template <class W, int kKs, bool kVec>
 hipError_t launch_passes(const VerifyArgs& a, const VerifyPlan& p, hipStream_t stream) {
-  const size_t lds = stream_lds_bytes<W>(a.rank, kVerifyDist);
-  hipLaunchKernelGGL((verify_tv<W, kKs, kVec>), dim3(p.n_slabs * p.n_groups), dim3(kStreamThreads),
+  // W2t slots, then one LDS patch per wave (U and target rows pass in turn).
+  const size_t lds = stream_lds_bytes<W>(a.rank, kVerifyDist) + kWaves * kPatchFloats * 4;
+  hipLaunchKernelGGL((verify_tv<W, kKs, kVec>), dim3(p.n_slabs * p.n_groups), dim3(kTvThreads),
                      lds, stream, a, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -436,8 +478,8 @@ hipError_t launch_w(const VerifyArgs& a, const VerifyPlan& p, hipStream_t stream
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-int plan_slabs(int n_groups, int n_vtiles) {
-  int slabs = kResidentWgs / n_groups;
+int plan_slabs(int n_groups, int n_vtiles, int resident) {
+  int slabs = resident / n_groups;
   if (n_groups > 1) slabs = (slabs / 8) * 8;
   if (slabs < 8) slabs = 8;
   if (slabs > n_vtiles) slabs = n_vtiles;
@@ -451,11 +493,11 @@ VerifyPlan plan_verify(int R, int V, int gamma) {
   VerifyPlan p{};
   p.n_rows = R * gamma;
   p.n_rtiles = (p.n_rows + kVTile - 1) / kVTile;
-  p.n_groups = (p.n_rtiles + kWaves - 1) / kWaves;
+  p.n_groups = (p.n_rtiles + kTvWaves - 1) / kTvWaves;
   p.n_vtiles = (V + kVTile - 1) / kVTile;
-  p.n_slabs = plan_slabs(p.n_groups, p.n_vtiles);
+  p.n_slabs = plan_slabs(p.n_groups, p.n_vtiles, kTvResidentWgs);
   p.s_groups = ((R + kVTile - 1) / kVTile + kWaves - 1) / kWaves;
-  p.s_slabs = plan_slabs(p.s_groups, p.n_vtiles);
+  p.s_slabs = plan_slabs(p.s_groups, p.n_vtiles, kResidentWgs);
   int chunks = (2048 + p.n_rows - 1) / p.n_rows;
   const int max_chunks = (V + 1023) / 1024;
   if (chunks > max_chunks) chunks = max_chunks;
