@@ -291,7 +291,11 @@ __global__ __launch_bounds__(kStreamThreads) void markov_step_shared(StepArgs a)
                  wave * kPatchFloats;
   DraftEpi<kGreedy, kDebug, kVec> epi(a, r, rc, half, r0 + wave * kVTile, patch);
   auto gather = [&](typename W::frag_t(&ef)[W::kMaxKs]) {
-    load_e_frags<W, kKs>(ef, a.W1, prev_token(a, rc), a.rank, a.V, half);
+    if constexpr (std::is_same<W, WBf16>::value && kKs > 0 && kKs % 4 == 0 && kVec)
+      load_e_frags_lines<kKs>(ef, reinterpret_cast<const uint16_t*>(a.W1),
+                              clamp_token(prev_token(a, rc), a.V), patch);
+    else
+      load_e_frags<W, kKs>(ef, a.W1, prev_token(a, rc), a.rank, a.V, half);
   };
   if constexpr (kKs > 0)
     shared_a_stream_skew<W, kKs>(a.W2t, a.V, t_begin, t_end, e, gather, lds, epi);
@@ -324,7 +328,11 @@ __global__ __launch_bounds__(kStreamThreads) void markov_step_private(StepArgs a
   private_a_stream<W, kKs>(
       a.W2t, a.V, a.rank, t_begin + wave, t_end, kWaves, e,
       [&](typename W::frag_t(&ef)[W::kMaxKs]) {
-        load_e_frags<W, kKs>(ef, a.W1, prev_token(a, rc), a.rank, a.V, half);
+        if constexpr (std::is_same<W, WBf16>::value && kKs > 0 && kKs % 4 == 0 && kVec)
+          load_e_frags_lines<kKs>(ef, reinterpret_cast<const uint16_t*>(a.W1),
+                                  clamp_token(prev_token(a, rc), a.V), patches[kVec ? wave : 0]);
+        else
+          load_e_frags<W, kKs>(ef, a.W1, prev_token(a, rc), a.rank, a.V, half);
       },
       epi);
 

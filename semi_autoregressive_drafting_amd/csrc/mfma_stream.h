@@ -492,6 +492,47 @@ struct RowTiles {
   }
 };
 
+// E fragments (bf16, rank = 16 kKs with kKs a multiple of 4) of the wave's 32
+// rows, gathered as whole lines.  The fragment layout reads 16 bytes from 32
+// different rows per load instruction; instead each 128-byte quarter Q of the
+// rows is loaded with 8 lanes per row (instruction p: row 8p + l/8, chunk
+// l%8), stored into the wave's LDS patch and read back in fragment order
+// (lane l: row l%32, chunks 2 ks + l/32 for the four ks of the quarter).
+// `token` is this lane's row id (already clamped to [0, V)); the patch must be
+// free (it is used in turn by the quarters, in order within the wave).
+template <int kKs>
+__device__ __forceinline__ void load_e_frags_lines(bf16x8_t (&e)[WBf16::kMaxKs],
+                                                   const uint16_t* W1, int token, float* patch) {
+  static_assert(kKs % 4 == 0 && kKs <= WBf16::kMaxKs, "whole 128-byte quarters");
+  constexpr int kRank = kKs * WBf16::kKStep;
+  constexpr int kQuarters = kKs / 4;
+  constexpr int kStride = kPatchRowFloats * 4;  // bytes per patch row
+  const int l = threadIdx.x & 63, h = l >> 5;
+  int tq[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) tq[p] = __shfl(token, 8 * p + (l >> 3));
+  u32x4_t raw[kQuarters][4];
+#pragma unroll
+  for (int Q = 0; Q < kQuarters; ++Q)
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      raw[Q][p] = *reinterpret_cast<const u32x4_t*>(W1 + (size_t)tq[p] * kRank +
+                                                    (8 * Q + (l & 7)) * 8);
+  unsigned char* pb = reinterpret_cast<unsigned char*>(patch);
+#pragma unroll
+  for (int Q = 0; Q < kQuarters; ++Q) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      *reinterpret_cast<u32x4_t*>(pb + (8 * p + (l >> 3)) * kStride + (l & 7) * 16) = raw[Q][p];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      e[4 * Q + i] =
+          *reinterpret_cast<const bf16x8_t*>(pb + (l & 31) * kStride + (2 * i + h) * 16);
+  }
+#pragma unroll
+  for (int ks = kKs; ks < WBf16::kMaxKs; ++ks) e[ks] = WBf16::zero();
+}
+
 // Load 16 consecutive fp32 values row[vb .. vb+15] of a full tile; with kVec
 // (rows 16-byte aligned) as four 16-byte non-temporal loads.
 template <bool kVec>
