@@ -45,6 +45,9 @@ namespace dspark {
 namespace {
 
 constexpr int kWaves = 4;
+// Workgroups of a draft step (per request group for R > 96).  More than the
+// 512 the CUs hold at once, so late starters and heavy slabs even out.
+constexpr int kDraftWgs = 512;
 
 // Prefetch distance of the shared stream: 2 for bf16 weights; fp32 weights
 // (E fragments twice as large) keep 1 to stay within the register budget.
@@ -385,23 +388,25 @@ __global__ __launch_bounds__(64 * kMergeWaves) void draft_merge(StepArgs a, int 
   const int spw = (a.n_slabs + kMergeWaves - 1) / kMergeWaves;
   const int s0 = wave * spw, s1 = min(a.n_slabs, s0 + spw);
 
-  float rm[kMergeRounds], rS[kMergeRounds], rkey[kMergeRounds], rt[kMergeRounds];
-  int rid[kMergeRounds];
-#pragma unroll
-  for (int i = 0; i < kMergeRounds; ++i) {
-    const int sl = s0 + 2 * i + h;
-    const bool ok = sl < s1;
-    const float* p = base + (size_t)(ok ? sl : 0) * 5 * a.R;
-    rm[i] = ok ? p[0] : -INFINITY;
-    rS[i] = ok ? p[a.R] : 0.0f;
-    rkey[i] = ok ? p[2 * a.R] : -INFINITY;
-    rt[i] = ok ? p[3 * a.R] : -INFINITY;
-    rid[i] = ok ? __float_as_int(p[4 * a.R]) : -1;
-  }
   MergeAcc acc{-INFINITY, 0.0f, -INFINITY, 0ull};
+  for (int c0 = s0; c0 < s1; c0 += 2 * kMergeRounds) {  // chunks of 2 * kMergeRounds slabs
+    float rm[kMergeRounds], rS[kMergeRounds], rkey[kMergeRounds], rt[kMergeRounds];
+    int rid[kMergeRounds];
 #pragma unroll
-  for (int i = 0; i < kMergeRounds; ++i)
-    acc = macc_merge(acc, MergeAcc{rm[i], rS[i], rt[i], pack_winner(rkey[i], rid[i])});
+    for (int i = 0; i < kMergeRounds; ++i) {
+      const int sl = c0 + 2 * i + h;
+      const bool ok = sl < s1;
+      const float* p = base + (size_t)(ok ? sl : 0) * 5 * a.R;
+      rm[i] = ok ? p[0] : -INFINITY;
+      rS[i] = ok ? p[a.R] : 0.0f;
+      rkey[i] = ok ? p[2 * a.R] : -INFINITY;
+      rt[i] = ok ? p[3 * a.R] : -INFINITY;
+      rid[i] = ok ? __float_as_int(p[4 * a.R]) : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < kMergeRounds; ++i)
+      acc = macc_merge(acc, MergeAcc{rm[i], rS[i], rt[i], pack_winner(rkey[i], rid[i])});
+  }
   MergeAcc o;
   o.m = __shfl_xor(acc.m, 32);
   o.S = __shfl_xor(acc.S, 32);
@@ -478,14 +483,14 @@ StepPlan plan_draft_step(int R, int V, int gamma) {
   if (rt >= 4) {
     p.shared = true;
     p.n_groups = (rt + kWaves - 1) / kWaves;
-    int slabs = kResidentWgs / p.n_groups;
+    int slabs = kDraftWgs / p.n_groups;
     if (p.n_groups > 1) slabs = (slabs / 8) * 8;
     if (slabs < 8) slabs = 8;
     p.n_slabs = slabs;
   } else {
     p.shared = false;
     p.n_groups = rt;
-    int slabs = kResidentWgs / rt;
+    int slabs = kDraftWgs / rt;
     const int max_slabs = (p.n_vtiles + kWaves - 1) / kWaves;
     if (slabs > max_slabs) slabs = max_slabs;
     p.n_slabs = slabs;

@@ -64,7 +64,27 @@ __global__ __launch_bounds__(256) void verify_target_lse(VerifyArgs a, VerifyPla
   const int v1 = min(a.V, v0 + cs);
   float m = -INFINITY, S = 0.0f;
   int idx = -1;
-  for (int v = v0 + 4 * t; v < v1; v += 1024) {
+  int v = v0 + 4 * t;
+  if constexpr (kVec && !kGreedy) {
+    // Four 16-byte loads in flight per thread, folded together.
+    for (; v + 3 * 1024 + 4 <= v1; v += 4096) {
+      f32x4_t q[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        q[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(trow + v + 1024 * j));
+      float xm = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xm = fmaxf(xm, fmaxf(fmaxf(q[j][0], q[j][1]), fmaxf(q[j][2], q[j][3])));
+      const float mn = fmaxf(m, xm * a.kscale);
+      S *= (mn == -INFINITY) ? 1.0f : fast_exp2(m - mn);
+      m = mn;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S += fast_exp2(fmaf(q[j][i], a.kscale, -mn));
+    }
+  }
+  for (; v < v1; v += 1024) {
     float x[4];
     if (kVec && v + 4 <= v1) {
       const f32x4_t q = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(trow + v));
