@@ -25,6 +25,30 @@ synth.custom("edge_v40000_r1_g4", V=40000, rank=256, d=128, gamma=4, R=1, dtype=
              peak="three")
 
 
+# rank-256 bf16 shapes with 16-byte-aligned rows run the production kernels
+# (line-coalesced row and E loads, the skewed MFMA stream) on ragged sizes: a
+# partial last vocabulary tile, a partial last request tile (clamped rows) and
+# both launch shapes.
+synth.custom("edge_v9996_r130_g3", V=9996, rank=256, d=64, gamma=3, R=130, dtype="bf16",
+             peak="three")
+synth.custom("edge_v8196_r33_g2", V=8196, rank=256, d=40, gamma=2, R=33, dtype="bf16",
+             peak="three")
+
+
+@pytest.mark.parametrize("name,T", [
+    ("edge_v9996_r130_g3", 1.0), ("edge_v9996_r130_g3", 0.0), ("edge_v8196_r33_g2", 1.0),
+])
+def test_draft_fast_paths_ragged(name, T):
+    """z is checked at step 1 only (its debug kernel); the other steps run the
+    production kernels and are checked on tokens, p, lse, c and a."""
+    say(f"[draft] {name} T={T}")
+    case = Case(name)
+    _, host, zs = case.run_draft(T, SEED, z_steps=(1,))
+    stats = check_draft(case, host, zs, T, SEED)
+    check_flip_rate(stats)
+    say(f"  {stats}")
+
+
 @pytest.mark.parametrize("name,T", [
     ("tiny_v1024_r4_g4", 1.0), ("tiny_v1024_r4_g4", 0.0),
     ("bruteforce_v8_g3", 1.0), ("bruteforce_v8_g3", 0.7), ("bruteforce_v8_g3", 0.0),

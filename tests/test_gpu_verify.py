@@ -6,7 +6,7 @@ import pytest
 import torch
 
 from oracle import dspark_oracle as O
-from semi_autoregressive_drafting_amd import runner
+from semi_autoregressive_drafting_amd import runner, synth
 from tests.gpu_parity import Case, NEAR_TIE, say
 
 pytestmark = pytest.mark.gpu
@@ -63,3 +63,18 @@ def test_verify_full_round():
         f"c* mean={g['c_star'].mean():.4f}")
     g, res = run_and_check(case, 1.0, 6, ell_override=np.full(128, 7), reqs=np.arange(0, 128, 4))
     say(f"[verify] round ell=7 tau_mean={g['tau_mean'][0]:.4f}")
+
+
+# rank 256 with ragged sizes: 111 rows (a partial last row tile), 37 requests
+# in the sampling pass, a partial last vocabulary tile
+synth.custom("edge_round_v9996_r37_g3", V=9996, rank=256, d=64, gamma=3, R=37, dtype="bf16",
+             peak="three", target=True)
+
+
+@pytest.mark.parametrize("T", [1.0, 0.0])
+def test_verify_ragged_rank256(T):
+    case = Case("edge_round_v9996_r37_g3")
+    g, res = run_and_check(case, T, 31)
+    say(f"[verify] ragged T={T} budget={g['ell'].sum()} tau_mean={g['tau_mean'][0]:.4f}")
+    run_and_check(case, T, 32, ell_override=np.full(37, 3))
+    run_and_check(case, T, 33, ell_override=np.arange(37) % 4)
