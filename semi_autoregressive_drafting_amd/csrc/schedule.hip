@@ -3,8 +3,12 @@
 //
 // One workgroup of 1024 threads:
 //   1. keys (~bits(a) << 32 | flat index) for the N = R*gamma candidates,
-//      padded to a power of two with all-ones keys, sorted ascending in LDS by
-//      a bitonic network: a descending, ties by flat index ascending.
+//      padded to a power of two with all-ones keys, sorted ascending by a
+//      bitonic network: a descending, ties by flat index ascending.  Each
+//      thread keeps kPer consecutive keys in registers: compare-exchanges
+//      inside a thread need nothing, those between threads of one wave go
+//      through cross-lane shuffles, and only partners in different waves
+//      (stride >= 64 * kPer) go through LDS with workgroup barriers.
 //   2. q_i = rint(a_i * 2^32) as int64 (exact scaling, round half to even);
 //      thread t owns a contiguous run of sorted positions, sums its q's, and a
 //      fixed-order scan over the 1024 run totals gives every prefix G_b exactly
@@ -23,45 +27,108 @@ namespace {
 constexpr int kMaxN = 8192;
 constexpr int kThreads = 1024;
 
+__device__ __forceinline__ unsigned long long shfl_xor64(unsigned long long v, int m) {
+  const uint32_t lo = __shfl_xor((uint32_t)v, m), hi = __shfl_xor((uint32_t)(v >> 32), m);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// Bitonic network over n2 = kPer * kThreads * (1 or less) keys; thread t owns
+// positions t * kPer .. t * kPer + kPer - 1 in `k` (n2 / kThreads of them are
+// real when n2 < kPer * kThreads: the rest hold all-ones keys and stay last).
+template <int kPer>
+__device__ void bitonic_sort(unsigned long long (&k)[kPer], unsigned long long* lds, int n2) {
+  const int t = threadIdx.x;
+  const int lane_bits = 6;  // 64 lanes
+  for (int size = 2; size <= n2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      if (stride < kPer) {  // partners inside the thread
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+          const int i = t * kPer + j;
+          if ((i & stride) == 0) {
+            const int jj = j + stride;
+            const bool asc = (i & size) == 0;
+            const unsigned long long x = k[j], y = k[jj];
+            if ((x > y) == asc) {
+              k[j] = y;
+              k[jj] = x;
+            }
+          }
+        }
+      } else if (stride < (kPer << lane_bits)) {  // partners in the same wave
+        const int m = stride / kPer;  // lane distance
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+          const int i = t * kPer + j;
+          const unsigned long long o = shfl_xor64(k[j], m);
+          const bool lower = (i & stride) == 0;
+          const bool asc = (i & size) == 0;
+          // the lower position keeps the smaller key when ascending
+          const bool keep_min = lower == asc;
+          k[j] = keep_min ? (o < k[j] ? o : k[j]) : (o > k[j] ? o : k[j]);
+        }
+      } else {  // partners in other waves: through LDS
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) lds[t * kPer + j] = k[j];
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+          const int i = t * kPer + j;
+          const unsigned long long o = lds[i ^ stride];
+          const bool lower = (i & stride) == 0;
+          const bool asc = (i & size) == 0;
+          const bool keep_min = lower == asc;
+          k[j] = keep_min ? (o < k[j] ? o : k[j]) : (o > k[j] ? o : k[j]);
+        }
+        __syncthreads();
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void schedule_kernel(SchedArgs a) {
   __shared__ unsigned long long key[kMaxN];
-  __shared__ long long tsum[kThreads];
+  __shared__ long long wsum[kThreads / 64];
   __shared__ int ell_s[512];
   __shared__ int stop_s;
   __shared__ double theta_s;
   const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
   const int N = a.R * a.gamma;
-  int n2 = 1;
+  int n2 = kThreads;  // at least one key per thread so every thread runs the network
   while (n2 < N) n2 <<= 1;
 
-  for (int i = t; i < n2; i += kThreads) {
-    unsigned long long k = ~0ull;
-    if (i < N) {
-      const float v = a.a[i];
-      const uint32_t bits = (v > 0.0f) ? __float_as_uint(v) : 0u;  // NaN / <= 0 sort as 0
-      k = ((unsigned long long)(~bits) << 32) | (uint32_t)i;
+  constexpr int kPer = kMaxN / kThreads;
+  const int per2 = n2 / kThreads;  // keys per thread actually in the network
+  unsigned long long k[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = t * per2 + j;
+    unsigned long long v = ~0ull;
+    if (j < per2 && i < N) {
+      const float f = a.a[i];
+      const uint32_t bits = (f > 0.0f) ? __float_as_uint(f) : 0u;  // NaN / <= 0 sort as 0
+      v = ((unsigned long long)(~bits) << 32) | (uint32_t)i;
     }
-    key[i] = k;
+    k[j] = v;
   }
   for (int i = t; i < a.R; i += kThreads) ell_s[i] = 0;
   if (t == 0) stop_s = N;
-  __syncthreads();
-
-  for (int size = 2; size <= n2; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = t; i < (n2 >> 1); i += kThreads) {
-        const int lo = 2 * i - (i & (stride - 1));
-        const int hi = lo + stride;
-        const bool asc = (lo & size) == 0;
-        const unsigned long long x = key[lo], y = key[hi];
-        if ((x > y) == asc) {
-          key[lo] = y;
-          key[hi] = x;
-        }
-      }
-      __syncthreads();
-    }
+  switch (per2) {  // the network over n2 keys, kPer in registers per thread
+    case 1: { unsigned long long k1[1] = {k[0]}; bitonic_sort<1>(k1, key, n2); k[0] = k1[0]; break; }
+    case 2: { unsigned long long k2[2] = {k[0], k[1]}; bitonic_sort<2>(k2, key, n2);
+              k[0] = k2[0]; k[1] = k2[1]; break; }
+    case 4: { unsigned long long k4[4] = {k[0], k[1], k[2], k[3]}; bitonic_sort<4>(k4, key, n2);
+#pragma unroll
+              for (int j = 0; j < 4; ++j) k[j] = k4[j];
+              break; }
+    default: bitonic_sort<kPer>(k, key, n2); break;
   }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if (j < per2) key[t * per2 + j] = k[j];
+  __syncthreads();
 
   const int per = (N + kThreads - 1) / kThreads;
   const int b0 = t * per;
@@ -72,15 +139,21 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(SchedArgs a) {
   };
   long long own = 0;
   for (int i = b0; i < b1; ++i) own += q_at(i);
-  tsum[t] = own;
-  __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
-    const long long add = (t >= off) ? tsum[t - off] : 0;
-    __syncthreads();
-    tsum[t] += add;
-    __syncthreads();
+  // inclusive scan of the per-thread sums: within the wave, then over waves
+  long long incl = own;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t lo = __shfl_up((uint32_t)incl, off), hi = __shfl_up((uint32_t)((unsigned long long)incl >> 32), off);
+    const long long v = (long long)(((unsigned long long)hi << 32) | lo);
+    if (lane >= off) incl += v;
   }
-  const long long base = tsum[t] - own;  // G at position b0
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  long long before = 0;
+  for (int w = 0; w < wave; ++w) before += wsum[w];
+  long long total = 0;
+  for (int w = 0; w < kThreads / 64; ++w) total += wsum[w];
+  const long long base = before + incl - own;  // G at position b0
   const long long tau0 = (long long)a.R << 32;
 
   long long G = base;
@@ -105,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(SchedArgs a) {
       G += q_at(i);
     }
   }
-  if (bstar == N && t == kThreads - 1) theta_s = (double)(tau0 + tsum[kThreads - 1]) * a.sps[a.R + N];
+  if (bstar == N && t == kThreads - 1) theta_s = (double)(tau0 + total) * a.sps[a.R + N];
   __syncthreads();
   for (int i = t; i < a.R; i += kThreads) a.ell[i] = ell_s[i];
   if (t == 0) {
