@@ -76,6 +76,47 @@ def measured_traffic():
     return int(kv["read_bytes"]) + int(kv["write_bytes"])
 
 
+def read_ceiling(nbytes, launches=20):
+    """Pure-read stream over nbytes with the probe kernel (libdspark_probe.so):
+    'rotating' reads a different nbytes window of a pool several times larger
+    than the MALL at each launch (HBM), 'resident' re-reads one window (as the
+    draft step re-reads W2 every step).  GB/s per launch, HIP-event timed."""
+    import ctypes
+    import torch
+    from semi_autoregressive_drafting_amd import build as B
+    lib = ctypes.CDLL(B.PROBE_LIB)
+    lib.dspark_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                      ctypes.c_int, ctypes.c_void_p]
+    lib.dspark_probe_read.restype = ctypes.c_int
+    nbytes = (nbytes + 255) // 256 * 256
+    slots = 12
+    pool = torch.empty(nbytes * slots, dtype=torch.uint8, device="cuda")
+    pool.fill_(1)
+    grid = 2048
+    sink = torch.zeros(grid, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    out = {}
+    for mode in ("rotating", "resident"):
+        def launch(i):
+            off = (i % slots) * nbytes if mode == "rotating" else 0
+            rc = lib.dspark_probe_read(pool.data_ptr() + off, nbytes, sink.data_ptr(), grid, stream)
+            if rc != 0:
+                raise RuntimeError(f"dspark_probe_read failed: {rc}")
+        for i in range(slots):
+            launch(i)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record()
+        for i in range(launches):
+            launch(i)
+        ev1.record()
+        torch.cuda.synchronize()
+        us = ev0.elapsed_time(ev1) * 1e3 / launches
+        out[mode] = {"us_per_launch": round(us, 2), "GBps": round(nbytes / us / 1e3, 1)}
+    del pool
+    return out
+
+
 def cpu_baseline(inp, seed):
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
     32 requests (16 easy, 16 hard) through the whole round (gamma draft steps
@@ -138,41 +179,95 @@ def main():
 
     def one_round(seed, ev=None):
         # runner.draft copies the anchors into x[:, 0] (a tiny copy kernel) and
-        # enqueues the gamma draft steps with one library call
+        # enqueues the gamma draft steps and their merge with one library call
         if ev is not None:
             ev[0].record()
         runner.draft(di, buf, TEMPERATURE, seed)
         if ev is not None:
             ev[1].record()
         runner.schedule(di, buf)
-        if ev is not None:
-            ev[2].record()
         runner.verify(di, buf, TEMPERATURE, seed)
-        if ev is not None:
-            ev[3].record()
 
     for w in range(args.warmup):
         one_round(10_000 + w)
     torch.cuda.synchronize()
 
+    # Timed region: K whole rounds; the two events per round bracket the draft
+    # block (gamma draft-step launches and the merge).
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(K):
         one_round(s, evs[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-
     draft_ms = np.array([evs[s][0].elapsed_time(evs[s][1]) for s in range(K)])
-    step_ms = draft_ms / g   # per draft step, launch gaps included
-    sched_ms = np.array([evs[s][1].elapsed_time(evs[s][2]) for s in range(K)])
-    ver_ms = np.array([evs[s][2].elapsed_time(evs[s][3]) for s in range(K)])
-    gpu_round_ms = np.array([evs[s][0].elapsed_time(evs[s][3]) for s in range(K)])
+    step_ms = draft_ms / g   # per draft step, merge and launch gaps included
     ms_round = wall / K * 1e3
     value = R * g / (wall / K)
 
+    # Phase breakdown from separate rounds (events between the phases).
+    nb = 5
+    ph = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nb)]
+    for s in range(nb):
+        ph[s][0].record()
+        runner.draft(di, buf, TEMPERATURE, 500 + s)
+        ph[s][1].record()
+        runner.schedule(di, buf)
+        ph[s][2].record()
+        runner.verify(di, buf, TEMPERATURE, 500 + s)
+        ph[s][3].record()
+    torch.cuda.synchronize()
+    sched_ms = np.array([ph[s][1].elapsed_time(ph[s][2]) for s in range(nb)])
+    ver_ms = np.array([ph[s][2].elapsed_time(ph[s][3]) for s in range(nb)])
+
+    # Cold draft step: a 512 MB write evicts W2 and U from L2 and the MALL
+    # before each timed step (dspark_draft_step = step kernel + merge).
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    cold, warm = [], []
+    buf.x[:, 0].copy_(di.anchor)
+    for s in range(6):
+        for flush, acc in ((True, cold), (False, warm)):
+            if flush:
+                scratch.fill_(s & 0xFF)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            runner.draft_step(di, buf, 1 + s % g, TEMPERATURE, 700 + s)
+            e1.record()
+            torch.cuda.synchronize()
+            acc.append(e0.elapsed_time(e1) * 1e3)
+    del scratch
+
     sb = draft_step_bytes(R, V, rank, d)
+    ceiling = read_ceiling(sb)
+
+    # The same round replayed from one captured HIP graph (no host launches).
+    graph = None
+    try:
+        gr = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            one_round(900)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(gr):
+            one_round(901)
+        for _ in range(3):
+            gr.replay()
+        torch.cuda.synchronize()
+        tg = time.perf_counter()
+        for _ in range(K):
+            gr.replay()
+        torch.cuda.synchronize()
+        g_round = (time.perf_counter() - tg) / K
+        graph = {"round_us": round(g_round * 1e6, 2),
+                 "draft_tokens_per_s": round(R * g / g_round, 1)}
+        del gr
+    except Exception as exc:  # graph capture unavailable: report it, keep the eager numbers
+        graph = {"error": str(exc)[:200]}
+
     step_s = float(step_ms.mean()) * 1e-3
     achieved = sb / step_s / 1e9
     vb = verify_bytes(R, V, rank, g)
@@ -194,17 +289,21 @@ def main():
                    "R": R, "gamma": g, "V": V, "rank": rank, "d": d,
                    "temperature": TEMPERATURE},
         "roofline": {"kernel": "markov_step_shared (one dspark_draft_step; average over the "
-                               "gamma launches of a draft block, launch gaps included)",
+                               "gamma launches of a draft block, merge and launch gaps included)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(), "bytes_per_launch": sb,
-                     "avg_launch_us": round(step_s * 1e6, 2)},
+                     "avg_launch_us": round(step_s * 1e6, 2),
+                     "frac_of_read_ceiling": round(achieved / ceiling["rotating"]["GBps"], 4)},
+        "read_ceiling": ceiling,
+        "cold_step": {"step_plus_merge_us_cold": round(float(np.median(cold)), 2),
+                      "step_plus_merge_us_warm": round(float(np.median(warm)), 2)},
+        "graph": graph,
         "breakdown_us": {"draft_step_mean": round(float(step_ms.mean()) * 1e3, 2),
                          "draft_step_min": round(float(step_ms.min()) * 1e3, 2),
                          "draft_total": round(float(draft_ms.mean()) * 1e3, 2),
                          "schedule": round(float(sched_ms.mean()) * 1e3, 2),
                          "verify": round(float(ver_ms.mean()) * 1e3, 2),
-                         "round_gpu": round(float(gpu_round_ms.mean()) * 1e3, 2),
                          "round_wall": round(ms_round * 1e3, 2)},
         "verify_roofline": {"bytes": vb, "achieved_GBps": round(vb / (ver_ms.mean() * 1e-3) / 1e9, 1)},
         "draft_only_tokens_per_s": round(R * g / (draft_ms.mean() * 1e-3), 1),

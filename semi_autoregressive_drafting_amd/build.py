@@ -18,6 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdspark.so")
+PROBE_SRC = os.path.join(PKG, "csrc_probe")
+PROBE_LIB = os.path.join(PKG, "libdspark_probe.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -45,6 +47,10 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
+def probe_sources():
+    return sorted(os.path.join(PROBE_SRC, f) for f in os.listdir(PROBE_SRC) if f.endswith(".hip"))
+
+
 def _compile(src, verbose):
     obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
     cmd = [_hipcc(), *HIPCC_FLAGS, "-c", src, "-o", obj]
@@ -58,19 +64,27 @@ def _compile(src, verbose):
     return obj
 
 
-def build(verbose: bool = False, jobs: int | None = None) -> str:
-    """Compile every HIP source for gfx950 and link libdspark.so; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-    jobs = jobs or min(len(srcs), 8)
-    with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, out):
+    tmp = out + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("link failed:\n" + res.stdout + res.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False, jobs: int | None = None) -> str:
+    """Compile every HIP source for gfx950 and link libdspark.so (the drafting
+    path) and libdspark_probe.so (the benchmark's pure-read ceiling); returns
+    the path of libdspark.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sources()
+    probe_srcs = probe_sources()
+    jobs = jobs or min(len(srcs) + len(probe_srcs), 8)
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs + probe_srcs))
+    _link(objs[:len(srcs)], LIB)
+    _link(objs[len(srcs):], PROBE_LIB)
     return LIB
 
 

@@ -8,9 +8,9 @@
 //   V1 verify_target_lse  grid (chunks, rows): per vocabulary chunk of a
 //      target row, online max / sum of 2^(t - m), t = target * log2e / T
 //      (greedy: max and lowest argmax).
-//   V2 verify_accept      one workgroup, one thread per request: merge V1's
-//      chunks -> lse_t per row; run the acceptance chain over the admitted
-//      prefix (u < p_t(x_j) / p_d(x_j)); pick the one row per request that
+//   V2 verify_accept      one workgroup: per row (thread per row) merge V1's
+//      chunks -> lse_t and test u < p_t(x_j) / p_d(x_j); per request the
+//      acceptance chain over the admitted prefix; pick the one row per request that
 //      needs a sample (residual at the first rejection, or bonus at row
 //      ell+1); write n_accept, tau and tau_mean; clear the accumulators of
 //      V3 and V5.  Greedy: also c* and the correction token (V3-V5 skipped).
@@ -139,11 +139,23 @@ __global__ __launch_bounds__(256) void verify_target_lse(VerifyArgs a, VerifyPla
 }
 
 // ---------------------------------------------------------------------------
-// V2: acceptance chain, one thread per request.
+// V2: acceptance, one workgroup of 1024 threads.
+//   Phase 1, one thread per row (r, j) (rows t, t + 1024, ...): merge V1's
+//   chunks -> lse_t (greedy: lowest argmax); the acceptance test of drafted
+//   token x_j, u(stream 2, r, j) < p_t(x_j) / p_d(x_j), kept as one byte in
+//   LDS (tested for every j, used only up to ell[r]).  All rows' loads are
+//   independent, so they are in flight together.
+//   Phase 2, one thread per request: the first rejected position inside the
+//   admitted prefix, the row that needs a sample, n_accept, tau; tau_mean by a
+//   fixed-order tree over the requests.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(512) void verify_accept(VerifyArgs a, VerifyPlan p) {
-  __shared__ int stau[512];
-  const int r = threadIdx.x;
+constexpr int kAcceptThreads = 1024;
+constexpr int kAcceptMaxRows = 512 * 16;  // R * gamma at the largest sizes
+
+__global__ __launch_bounds__(kAcceptThreads) void verify_accept(VerifyArgs a, VerifyPlan p) {
+  __shared__ unsigned char acc_ok[kAcceptMaxRows];
+  __shared__ int stau[kAcceptThreads];
+  const int t = threadIdx.x;
   float* lse_t2 = reinterpret_cast<float*>(a.ws + p.off_lse_t);
   int* targmax = reinterpret_cast<int*>(a.ws + p.off_lse_t);  // greedy reuses the slot
   int* srow = reinterpret_cast<int*>(a.ws + p.off_srow);      // sampled k (1-based) or 0
@@ -151,51 +163,57 @@ __global__ __launch_bounds__(512) void verify_accept(VerifyArgs a, VerifyPlan p)
   unsigned long long* tvsum = reinterpret_cast<unsigned long long*>(a.ws + p.off_tv);
   unsigned long long* best = reinterpret_cast<unsigned long long*>(a.ws + p.off_best);
   const float* lp = reinterpret_cast<const float*>(a.ws + p.off_lsepart);
-  int tau = 0;
-  if (r < a.R) {
-    for (int k = 1; k <= a.gamma; ++k) {
-      const int row = r * a.gamma + (k - 1);
-      const float* q = lp + (size_t)row * p.lse_chunks * 2;
-      if (a.greedy) {
-        float m = -INFINITY;
-        int idx = -1;
-        for (int c = 0; c < p.lse_chunks; ++c) {
-          const float mc = q[2 * c];
-          const int ic = reinterpret_cast<const int*>(q)[2 * c + 1];
-          const bool take = (ic >= 0) && (idx < 0 || mc > m || (mc == m && ic < idx));
-          m = take ? mc : m;
-          idx = take ? ic : idx;
-        }
-        targmax[row] = idx;
-        a.c_star[row] = (a.x[(size_t)r * (a.gamma + 1) + k] == idx) ? 1.0f : 0.0f;
-      } else {
-        float m = -INFINITY, S = 0.0f;
-        for (int c = 0; c < p.lse_chunks; ++c) {
-          const float mc = q[2 * c], sc = q[2 * c + 1];
-          const float M = fmaxf(m, mc);
-          S = (M == -INFINITY) ? 0.0f : S * fast_exp2(m - M) + sc * fast_exp2(mc - M);
-          m = M;
-        }
-        lse_t2[row] = m + log2f(S);
-        tvsum[row] = 0ull;
+  const int n_rows = a.R * a.gamma;
+
+  for (int row = t; row < n_rows; row += kAcceptThreads) {
+    const int r = row / a.gamma, j = row - r * a.gamma + 1;  // drafted position j = k
+    const float* q = lp + (size_t)row * p.lse_chunks * 2;
+    const int xraw = a.x[(size_t)r * (a.gamma + 1) + j];
+    const int xj = clamp_token(xraw, a.V);
+    bool ok;
+    if (a.greedy) {
+      float m = -INFINITY;
+      int idx = -1;
+      for (int c = 0; c < p.lse_chunks; ++c) {
+        const float mc = q[2 * c];
+        const int ic = reinterpret_cast<const int*>(q)[2 * c + 1];
+        const bool take = (ic >= 0) && (idx < 0 || mc > m || (mc == m && ic < idx));
+        m = take ? mc : m;
+        idx = take ? ic : idx;
       }
+      targmax[row] = idx;
+      a.c_star[row] = (xraw == idx) ? 1.0f : 0.0f;
+      ok = xj == idx;  // ratio 1 or 0 against u in [2^-24, 1)
+    } else {
+      const float tx = a.target[(size_t)row * a.V + xj];
+      const float pdx = a.p_d_x[row];
+      float m = -INFINITY, S = 0.0f;
+      for (int c = 0; c < p.lse_chunks; ++c) {
+        const float mc = q[2 * c], sc = q[2 * c + 1];
+        const float M = fmaxf(m, mc);
+        S = (M == -INFINITY) ? 0.0f : S * fast_exp2(m - M) + sc * fast_exp2(mc - M);
+        m = M;
+      }
+      const float l2 = m + log2f(S);
+      lse_t2[row] = l2;
+      tvsum[row] = 0ull;
+      const float pt = exp2f(fmaf(tx, a.kscale, -l2));
+      const float u = bits_to_uniform(pcg(row_key(a.seed, kStreamAccept, (uint32_t)r, (uint32_t)j)));
+      ok = u < pt / pdx;
     }
+    acc_ok[row] = ok ? 1 : 0;
+  }
+  __syncthreads();
+
+  int tau = 0;
+  if (t < a.R) {
+    const int r = t;
     best[r] = 0ull;
-    int n_acc = 0, nxt = -1, kind = 0, ks = 0;
     int ell = a.ell[r];
     ell = ell < 0 ? 0 : (ell > a.gamma ? a.gamma : ell);  // device values are not validated
+    int n_acc = 0, kind = 0, ks = 0, nxt = -1;
     for (int j = 1; j <= ell; ++j) {
-      const int row = r * a.gamma + (j - 1);
-      const int xj = clamp_token(a.x[(size_t)r * (a.gamma + 1) + j], a.V);
-      float ratio;
-      if (a.greedy) {
-        ratio = (xj == targmax[row]) ? 1.0f : 0.0f;
-      } else {
-        const float pt = exp2f(fmaf(a.target[(size_t)row * a.V + xj], a.kscale, -lse_t2[row]));
-        ratio = pt / a.p_d_x[row];
-      }
-      const float u = bits_to_uniform(pcg(row_key(a.seed, kStreamAccept, (uint32_t)r, (uint32_t)j)));
-      if (u < ratio) {
+      if (acc_ok[r * a.gamma + (j - 1)]) {
         ++n_acc;
       } else {
         kind = 1;
@@ -215,13 +233,13 @@ __global__ __launch_bounds__(512) void verify_accept(VerifyArgs a, VerifyPlan p)
     a.next_token[r] = nxt;
     tau = n_acc + 1;
   }
-  stau[r] = tau;
+  stau[t] = tau;
   __syncthreads();
-  for (int s = 256; s > 0; s >>= 1) {
-    if (r < s) stau[r] += stau[r + s];
+  for (int s = kAcceptThreads / 2; s > 0; s >>= 1) {
+    if (t < s) stau[t] += stau[t + s];
     __syncthreads();
   }
-  if (r == 0) *a.tau_mean = (float)stau[0] / (float)a.R;
+  if (t == 0) *a.tau_mean = (float)stau[0] / (float)a.R;
 }
 
 // Map blockIdx to (slab, group); the groups of one slab share an XCD.
@@ -553,7 +571,7 @@ hipError_t launch_verify(const VerifyArgs& a, const VerifyPlan& p, hipStream_t s
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(verify_accept, dim3(1), dim3(512), 0, stream, a, p);
+  hipLaunchKernelGGL(verify_accept, dim3(1), dim3(kAcceptThreads), 0, stream, a, p);
   e = hipGetLastError();
   if (e != hipSuccess || a.greedy) return e;
   if (a.bf16) e = vec ? launch_w<WBf16, true>(a, p, stream) : launch_w<WBf16, false>(a, p, stream);
