@@ -221,6 +221,17 @@ def main():
     torch.cuda.synchronize()
     sched_ms = np.array([ph[s][1].elapsed_time(ph[s][2]) for s in range(nb)])
     ver_ms = np.array([ph[s][2].elapsed_time(ph[s][3]) for s in range(nb)])
+    # the asynchronous scheduler on the same candidates (budget from a copy
+    # standing in for the survival of two steps earlier)
+    a_lag = buf.a.clone()
+    ea = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    async_us = []
+    for s in range(nb):
+        ea[0].record()
+        runner.schedule_async(di, buf, a_lag)
+        ea[1].record()
+        torch.cuda.synchronize()
+        async_us.append(ea[0].elapsed_time(ea[1]) * 1e3)
 
     # Cold draft step: a 512 MB write evicts W2 and U from L2 and the MALL
     # before each timed step (dspark_draft_step = step kernel + merge).
@@ -303,6 +314,7 @@ def main():
                          "draft_step_min": round(float(step_ms.min()) * 1e3, 2),
                          "draft_total": round(float(draft_ms.mean()) * 1e3, 2),
                          "schedule": round(float(sched_ms.mean()) * 1e3, 2),
+                         "schedule_async": round(float(np.median(async_us)), 2),
                          "verify": round(float(ver_ms.mean()) * 1e3, 2),
                          "round_wall": round(ms_round * 1e3, 2)},
         "verify_roofline": {"bytes": vb, "achieved_GBps": round(vb / (ver_ms.mean() * 1e-3) / 1e9, 1)},

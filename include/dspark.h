@@ -158,6 +158,28 @@ dspark_status dspark_schedule(int R, int gamma, const float* a, const double* sp
                               size_t ws_bytes, dspark_stream_t stream);
 
 /*
+ * Asynchronous (production) scheduler [P1 §4.3 生产异步调度; P3
+ * スケジューラの実運用適用]: the budget comes from survival probabilities two
+ * steps old, the selection from the current ones.
+ *   K = the b in 0..N (N = R*gamma) with the largest
+ *       Theta_fix(b) = (double)(R*2^32 + G_b) * sps[R + b], where G_b sums
+ *       q_i = round-half-even(a_lag_i * 2^32) over the first b candidates of
+ *       a_lag in the dspark_schedule key order; every b is examined (no early
+ *       stop) and the smallest b wins a tie.
+ *   Then the first K candidates of a_cur in the same key order (a_cur
+ *   descending, flat index ascending) are admitted.
+ * Outputs (device): ell[R] = admitted positions of request r (a prefix when
+ * the rows of a_cur are non-increasing), *budget = K, *theta =
+ * Theta_fix(K) * 2^-32 (the lagged estimate; may be NULL).
+ * a_lag, a_cur: fp32 [R][gamma], values in [0, 1]; sps as for
+ * dspark_schedule.  One workgroup; R*gamma <= 8192.  ell depends on a_lag
+ * only through K.
+ */
+dspark_status dspark_schedule_async(int R, int gamma, const float* a_lag, const float* a_cur,
+                                    const double* sps, int sps_len, int32_t* ell,
+                                    int32_t* budget, double* theta, dspark_stream_t stream);
+
+/*
  * Verification of drafted blocks against target logits [P1 §3.1 eq. c*;
  * standard rejection sampling: P1 opening and §2.2, P3 問題定義]:
  *   for every (r, k): p_d = softmax((U[r][k-1] + W1[x[r][k-1]] . W2) / T),

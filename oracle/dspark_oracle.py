@@ -28,6 +28,11 @@ What each function follows, and what pins it (tests/test_oracle_pins.py):
   theta_of_ell / schedule      P1 §4.1 eqs. B, tau, Theta and the global sort;
         P1 §4.2 early stop.  Pinned by the P2 cost-model and plan() printouts,
         exhaustive search over ell vectors, prefix contiguity and closed forms.
+  schedule_async               P1 §4.3; P3 スケジューラの実運用適用.  Pinned by
+        brute force over budgets (exact rational Theta), an explicit top-K
+        count, agreement with `schedule` on unimodal curves, a hand-built cliff
+        curve where the early stop and the global maximum differ, and causal
+        isolation (ell changes with a_lag only through K).
   verify                       P1 §3.1 eq. c*, standard rejection sampling (P1
         intro and §2.2; P3 問題定義).  Pinned by the c* = overlap identity,
         special cases, losslessness (output law = p_t) and acceptance-rate = c*.
@@ -280,6 +285,30 @@ def schedule(a, sps):
         b += 1
     ell = np.bincount(order[:b] // g, minlength=R).astype(np.int64)
     return ell, b, float(theta_fix[b]) * 2.0 ** -32, order, theta_fix
+
+
+def schedule_async(a_lag, a_cur, sps):
+    """Production asynchronous scheduling  [P1 §4.3 生产异步调度; P3
+    スケジューラの実運用適用]: the total budget K is chosen from survival
+    probabilities two steps old (a_lag) by the global maximum of Theta over
+    every budget b = 0..N (early stop removed; the smallest b on a tie); the
+    current step then admits the K candidates with the largest current
+    survival a_cur (same order as `schedule`: a descending, index ascending).
+
+    Returns (ell[R], K, Theta_lag(K) in tokens/s, Theta_fixed_lag[0..N])."""
+    a_lag = np.asarray(a_lag, dtype=np.float32)
+    a_cur = np.asarray(a_cur, dtype=np.float32)
+    R, g = a_cur.shape
+    N = R * g
+    order_lag = np.argsort(-a_lag.reshape(-1).astype(np.float64), kind="stable")
+    q = tau_fixed_units(a_lag.reshape(-1)[order_lag])
+    G = np.concatenate([[0], np.cumsum(q)]).astype(np.int64)
+    theta_fix = (np.int64(R) * TAU_ONE + G).astype(np.float64) * \
+        np.asarray(sps, dtype=np.float64)[R + np.arange(N + 1)]
+    K = int(np.argmax(theta_fix))                  # first (smallest) b of the maximum
+    order_cur = np.argsort(-a_cur.reshape(-1).astype(np.float64), kind="stable")
+    ell = np.bincount(order_cur[:K] // g, minlength=R).astype(np.int64)
+    return ell, K, float(theta_fix[K]) * 2.0 ** -32, theta_fix
 
 
 def schedule_exhaustive(a, sps):

@@ -199,6 +199,19 @@ dspark_status dspark_schedule(int R, int gamma, const float* a, const double* sp
   return DSPARK_OK;
 }
 
+dspark_status dspark_schedule_async(int R, int gamma, const float* a_lag, const float* a_cur,
+                                    const double* sps, int sps_len, int32_t* ell,
+                                    int32_t* budget, double* theta, dspark_stream_t stream) {
+  if (!a_lag || !a_cur || !sps || !ell || !budget) return DSPARK_ERR_NULL;
+  if (R < 1 || R > kMaxR || gamma < 1 || gamma > kMaxGamma || R * gamma > kMaxSched)
+    return DSPARK_ERR_SHAPE;
+  if (sps_len < R * (1 + gamma) + 1) return DSPARK_ERR_SHAPE;
+  SchedAsyncArgs args{R, gamma, a_lag, a_cur, sps, ell, budget, theta};
+  if (launch_schedule_async(args, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return DSPARK_ERR_LAUNCH;
+  return DSPARK_OK;
+}
+
 dspark_status dspark_verify(int R, int V, int rank, int gamma, int dt, const void* W1,
                             const void* W2t, const float* U, const float* target,
                             const int32_t* x, const float* lse_d, const float* p_d_x,

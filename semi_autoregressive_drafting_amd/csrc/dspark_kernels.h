@@ -71,6 +71,17 @@ struct SchedArgs {
 };
 hipError_t launch_schedule(const SchedArgs& a, hipStream_t stream);
 
+struct SchedAsyncArgs {
+  int R, gamma;
+  const float* a_lag;  // survival probabilities two steps earlier (budget only)
+  const float* a_cur;  // current survival probabilities (selection)
+  const double* sps;
+  int32_t* ell;
+  int32_t* budget;
+  double* theta;
+};
+hipError_t launch_schedule_async(const SchedAsyncArgs& a, hipStream_t stream);
+
 // Verification (see verify.hip).
 struct VerifyPlan {
   int n_rows;       // R * gamma

@@ -86,18 +86,25 @@ __device__ void bitonic_sort(unsigned long long (&k)[kPer], unsigned long long* 
   }
 }
 
-__global__ __launch_bounds__(kThreads) void schedule_kernel(SchedArgs a) {
-  __shared__ unsigned long long key[kMaxN];
-  __shared__ long long wsum[kThreads / 64];
-  __shared__ int ell_s[512];
-  __shared__ int stop_s;
-  __shared__ double theta_s;
+// Sort the N = R * gamma candidates of `a` into `key` (ascending; see the
+// file comment) and return the per-thread run [b0, b1) of sorted positions with
+// the fixed-point prefix sum G at b0 (`base`) and the total over all N.
+// Called by all kThreads threads; ends with the keys visible in LDS.
+struct Runs {
+  int b0, b1;
+  long long base, total;
+};
+
+__device__ __forceinline__ long long q_of(unsigned long long key) {
+  const float v = __uint_as_float(~(uint32_t)(key >> 32));
+  return (long long)rint((double)v * 4294967296.0);
+}
+
+__device__ Runs sort_and_scan(const float* a, int N, unsigned long long* key, long long* wsum) {
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
-  const int N = a.R * a.gamma;
   int n2 = kThreads;  // at least one key per thread so every thread runs the network
   while (n2 < N) n2 <<= 1;
-
   constexpr int kPer = kMaxN / kThreads;
   const int per2 = n2 / kThreads;  // keys per thread actually in the network
   unsigned long long k[kPer];
@@ -106,14 +113,12 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(SchedArgs a) {
     const int i = t * per2 + j;
     unsigned long long v = ~0ull;
     if (j < per2 && i < N) {
-      const float f = a.a[i];
+      const float f = a[i];
       const uint32_t bits = (f > 0.0f) ? __float_as_uint(f) : 0u;  // NaN / <= 0 sort as 0
       v = ((unsigned long long)(~bits) << 32) | (uint32_t)i;
     }
     k[j] = v;
   }
-  for (int i = t; i < a.R; i += kThreads) ell_s[i] = 0;
-  if (t == 0) stop_s = N;
   switch (per2) {  // the network over n2 keys, kPer in registers per thread
     case 1: { unsigned long long k1[1] = {k[0]}; bitonic_sort<1>(k1, key, n2); k[0] = k1[0]; break; }
     case 2: { unsigned long long k2[2] = {k[0], k[1]}; bitonic_sort<2>(k2, key, n2);
@@ -130,15 +135,12 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(SchedArgs a) {
     if (j < per2) key[t * per2 + j] = k[j];
   __syncthreads();
 
+  Runs u;
   const int per = (N + kThreads - 1) / kThreads;
-  const int b0 = t * per;
-  const int b1 = min(N, b0 + per);
-  auto q_at = [&](int i) -> long long {
-    const float v = __uint_as_float(~(uint32_t)(key[i] >> 32));
-    return (long long)rint((double)v * 4294967296.0);
-  };
+  u.b0 = min(N, t * per);
+  u.b1 = min(N, u.b0 + per);
   long long own = 0;
-  for (int i = b0; i < b1; ++i) own += q_at(i);
+  for (int i = u.b0; i < u.b1; ++i) own += q_of(key[i]);
   // inclusive scan of the per-thread sums: within the wave, then over waves
   long long incl = own;
 #pragma unroll
@@ -151,14 +153,29 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(SchedArgs a) {
   __syncthreads();
   long long before = 0;
   for (int w = 0; w < wave; ++w) before += wsum[w];
-  long long total = 0;
-  for (int w = 0; w < kThreads / 64; ++w) total += wsum[w];
-  const long long base = before + incl - own;  // G at position b0
+  u.total = 0;
+  for (int w = 0; w < kThreads / 64; ++w) u.total += wsum[w];
+  u.base = before + incl - own;  // G at position b0
+  __syncthreads();               // wsum and key may be reused after this
+  return u;
+}
+
+__global__ __launch_bounds__(kThreads) void schedule_kernel(SchedArgs a) {
+  __shared__ unsigned long long key[kMaxN];
+  __shared__ long long wsum[kThreads / 64];
+  __shared__ int ell_s[512];
+  __shared__ int stop_s;
+  __shared__ double theta_s;
+  const int t = threadIdx.x;
+  const int N = a.R * a.gamma;
+  for (int i = t; i < a.R; i += kThreads) ell_s[i] = 0;
+  if (t == 0) stop_s = N;
+  const Runs u = sort_and_scan(a.a, N, key, wsum);
   const long long tau0 = (long long)a.R << 32;
 
-  long long G = base;
-  for (int i = b0; i < b1; ++i) {
-    const long long Gn = G + q_at(i);
+  long long G = u.base;
+  for (int i = u.b0; i < u.b1; ++i) {
+    const long long Gn = G + q_of(key[i]);
     const double th = (double)(tau0 + G) * a.sps[a.R + i];
     const double thn = (double)(tau0 + Gn) * a.sps[a.R + i + 1];
     if (!(thn > th)) {
@@ -170,15 +187,15 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(SchedArgs a) {
   __syncthreads();
   const int bstar = stop_s;
 
-  G = base;
-  for (int i = b0; i < b1; ++i) {
+  G = u.base;
+  for (int i = u.b0; i < u.b1; ++i) {
     if (i == bstar) theta_s = (double)(tau0 + G) * a.sps[a.R + i];
     if (i < bstar) {
       atomicAdd(&ell_s[(int)(key[i] & 0xFFFFFFFFu) / a.gamma], 1);
-      G += q_at(i);
+      G += q_of(key[i]);
     }
   }
-  if (bstar == N && t == kThreads - 1) theta_s = (double)(tau0 + total) * a.sps[a.R + N];
+  if (bstar == N && t == kThreads - 1) theta_s = (double)(tau0 + u.total) * a.sps[a.R + N];
   __syncthreads();
   for (int i = t; i < a.R; i += kThreads) a.ell[i] = ell_s[i];
   if (t == 0) {
@@ -187,10 +204,84 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(SchedArgs a) {
   }
 }
 
+// Asynchronous variant [P1 §4.3; P3 スケジューラの実運用適用]: the budget K is
+// the b in 0..N with the largest Theta_fix(b) computed from the survival
+// probabilities of two steps earlier (a_lag), over all b (no early stop; the
+// smallest such b); then the K candidates with the largest current survival
+// (a_cur, same key order) are admitted.
+__global__ __launch_bounds__(kThreads) void schedule_async_kernel(SchedAsyncArgs a) {
+  __shared__ unsigned long long key[kMaxN];
+  __shared__ long long wsum[kThreads / 64];
+  __shared__ int ell_s[512];
+  __shared__ double red_v[kThreads / 64];
+  __shared__ int red_b[kThreads / 64];
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int N = a.R * a.gamma;
+  for (int i = t; i < a.R; i += kThreads) ell_s[i] = 0;
+  const long long tau0 = (long long)a.R << 32;
+
+  // 1. K from the lagged survival: thread t scores b = i + 1 for i in its run
+  //    (thread 0 also b = 0); the best (Theta, smallest b) wins.
+  const Runs u = sort_and_scan(a.a_lag, N, key, wsum);
+  double bv = -1.0;
+  int bb = 0x7fffffff;
+  if (t == 0) {
+    bv = (double)tau0 * a.sps[a.R];
+    bb = 0;
+  }
+  long long G = u.base;
+  for (int i = u.b0; i < u.b1; ++i) {
+    G += q_of(key[i]);
+    const double th = (double)(tau0 + G) * a.sps[a.R + i + 1];
+    if (th > bv) {  // positions rise within the run: strict '>' keeps the smallest b
+      bv = th;
+      bb = i + 1;
+    }
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    const double ov = __shfl_xor(bv, off);
+    const int ob = __shfl_xor(bb, off);
+    if (ov > bv || (ov == bv && ob < bb)) {
+      bv = ov;
+      bb = ob;
+    }
+  }
+  if (lane == 0) {
+    red_v[wave] = bv;
+    red_b[wave] = bb;
+  }
+  __syncthreads();
+  double kv = red_v[0];
+  int K = red_b[0];
+  for (int w = 1; w < kThreads / 64; ++w)
+    if (red_v[w] > kv || (red_v[w] == kv && red_b[w] < K)) {
+      kv = red_v[w];
+      K = red_b[w];
+    }
+  __syncthreads();  // the key buffer is reused below
+
+  // 2. top-K of the current survival
+  const Runs c = sort_and_scan(a.a_cur, N, key, wsum);
+  for (int i = c.b0; i < c.b1; ++i)
+    if (i < K) atomicAdd(&ell_s[(int)(key[i] & 0xFFFFFFFFu) / a.gamma], 1);
+  __syncthreads();
+  for (int i = t; i < a.R; i += kThreads) a.ell[i] = ell_s[i];
+  if (t == 0) {
+    *a.budget = K;
+    if (a.theta != nullptr) *a.theta = kv * 0x1p-32;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_schedule(const SchedArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_schedule_async(const SchedAsyncArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(schedule_async_kernel, dim3(1), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -20,7 +20,8 @@ DSPARK_F32, DSPARK_BF16 = 0, 1
 DSPARK_OP_DRAFT_STEP, DSPARK_OP_SCHEDULE, DSPARK_OP_VERIFY = 0, 1, 2
 
 EXPORTS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_draft_step",
-           "dspark_draft_block", "dspark_confidence", "dspark_schedule", "dspark_verify")
+           "dspark_draft_block", "dspark_confidence", "dspark_schedule", "dspark_schedule_async",
+           "dspark_verify")
 
 _lib = None
 
@@ -55,6 +56,8 @@ def load():
     L.dspark_confidence.restype = I
     L.dspark_schedule.argtypes = [I, I, P, P, I, P, P, P, P, SZ, P]
     L.dspark_schedule.restype = I
+    L.dspark_schedule_async.argtypes = [I, I, P, P, P, I, P, P, P, P]
+    L.dspark_schedule_async.restype = I
     L.dspark_verify.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, F, U64,
                                 P, P, P, P, P, P, SZ, P]
     L.dspark_verify.restype = I
@@ -125,6 +128,12 @@ def dspark_schedule(R, gamma, a, sps, sps_len, ell, budget, theta, ws=None, ws_b
                     stream=None):
     _call("dspark_schedule", R, gamma, _ptr(a), _ptr(sps), int(sps_len), _ptr(ell),
           _ptr(budget), _ptr(theta), _ptr(ws), int(ws_bytes), _stream(stream))
+
+
+def dspark_schedule_async(R, gamma, a_lag, a_cur, sps, sps_len, ell, budget, theta,
+                          stream=None):
+    _call("dspark_schedule_async", R, gamma, _ptr(a_lag), _ptr(a_cur), _ptr(sps), int(sps_len),
+          _ptr(ell), _ptr(budget), _ptr(theta), _stream(stream))
 
 
 def dspark_verify(R, V, rank, gamma, dt, W1, W2t, U, target, x, lse_d, p_d_x, ell,

@@ -107,6 +107,13 @@ def schedule(di: DeviceInputs, buf: RoundBuffers):
                       buf.theta)
 
 
+def schedule_async(di: DeviceInputs, buf: RoundBuffers, a_lag: torch.Tensor):
+    """Asynchronous scheduling: budget from a_lag (survival two steps old),
+    selection from buf.a."""
+    D.dspark_schedule_async(di.R, di.gamma, a_lag, buf.a, di.sps, di.sps.numel(), buf.ell,
+                            buf.budget, buf.theta)
+
+
 def verify(di: DeviceInputs, buf: RoundBuffers, temperature: float, seed: int):
     D.dspark_verify(di.R, di.V, di.rank, di.gamma, di.dt, di.W1, di.W2t, di.U, di.target,
                     buf.x, buf.lse, buf.p, buf.ell, temperature, seed, buf.c_star,

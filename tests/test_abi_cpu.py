@@ -126,6 +126,16 @@ def test_schedule_validation():
     assert f(600, 4, FAKE, FAKE, 10 ** 6, FAKE, FAKE, FAKE, None, 0, None) == D.DSPARK_ERR_SHAPE
 
 
+def test_schedule_async_validation():
+    f = D.load().dspark_schedule_async
+    assert f(4, 4, None, FAKE, FAKE, 21, FAKE, FAKE, FAKE, None) == D.DSPARK_ERR_NULL
+    assert f(4, 4, FAKE, None, FAKE, 21, FAKE, FAKE, FAKE, None) == D.DSPARK_ERR_NULL
+    assert f(4, 4, FAKE, FAKE, FAKE, 21, FAKE, None, FAKE, None) == D.DSPARK_ERR_NULL
+    assert f(4, 4, FAKE, FAKE, FAKE, 20, FAKE, FAKE, FAKE, None) == D.DSPARK_ERR_SHAPE
+    assert f(0, 4, FAKE, FAKE, FAKE, 10 ** 6, FAKE, FAKE, FAKE, None) == D.DSPARK_ERR_SHAPE
+    assert f(512, 17, FAKE, FAKE, FAKE, 10 ** 6, FAKE, FAKE, FAKE, None) == D.DSPARK_ERR_SHAPE
+
+
 def test_confidence_validation():
     f = D.load().dspark_confidence
     assert f(4, 4, 64, 32, 1024, 0, None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == D.DSPARK_ERR_NULL

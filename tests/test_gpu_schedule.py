@@ -76,3 +76,64 @@ def test_schedule_reproduces_the_plan_demo():
         sps = np.array([1.0 / (0.25e-3 + st(B)) for B in range(N + 1)])
         assert assert_same(a, sps) == row["admitted"]
         assert round(gpu_schedule(a, sps)[2]) == row["adaptive_tok_s"]
+
+
+# ---------------------------------------------------------------------------
+# Asynchronous scheduler: budget from the lagged a, selection from the current a
+# ---------------------------------------------------------------------------
+def gpu_schedule_async(a_lag, a_cur, sps):
+    R, g = a_cur.shape
+    tl = torch.from_numpy(np.ascontiguousarray(a_lag, dtype=np.float32)).cuda()
+    tc = torch.from_numpy(np.ascontiguousarray(a_cur, dtype=np.float32)).cuda()
+    ts = torch.from_numpy(np.ascontiguousarray(sps, dtype=np.float64)).cuda()
+    ell = torch.full((R,), -7, dtype=torch.int32, device="cuda")
+    budget = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    theta = torch.zeros(1, dtype=torch.float64, device="cuda")
+    D.dspark_schedule_async(R, g, tl, tc, ts, ts.numel(), ell, budget, theta)
+    torch.cuda.synchronize()
+    return ell.cpu().numpy(), int(budget.item()), float(theta.item())
+
+
+def assert_same_async(a_lag, a_cur, sps, tag=""):
+    ell_g, K_g, th_g = gpu_schedule_async(a_lag, a_cur, sps)
+    ell_o, K_o, th_o, _ = O.schedule_async(a_lag, a_cur, sps)
+    assert K_g == K_o, (tag, K_g, K_o)
+    np.testing.assert_array_equal(ell_g, ell_o, err_msg=tag)
+    assert th_g == th_o, (tag, th_g, th_o)
+    return K_g
+
+
+@pytest.mark.parametrize("R,g", [(1, 1), (3, 5), (4, 4), (37, 3), (128, 16), (512, 7),
+                                 (512, 16), (300, 9)])
+def test_schedule_async_random(R, g):
+    rng = np.random.default_rng(R * 1000 + g)
+    for trial in range(3):
+        cs = []
+        for _ in range(2):
+            c = rng.uniform(0.0, 1.0, (R, g)).astype(np.float32)
+            c[rng.uniform(size=(R, g)) < 0.1] = 1.0
+            c[rng.uniform(size=(R, g)) < 0.02] = 0.0
+            cs.append(O.survival(c))
+        for name, sps in _tables(rng, R, g):
+            assert_same_async(cs[0], cs[1], sps, f"{R}x{g} {name} #{trial}")
+        # a bumpy table: many local maxima, so the global search matters
+        B = np.arange(R * (1 + g) + 1)
+        sps = 1.0 / (1e-3 + 1e-5 * B + rng.uniform(0, 3e-4, B.size))
+        assert_same_async(cs[0], cs[1], sps, f"{R}x{g} bumpy #{trial}")
+    say(f"[schedule_async] {R}x{g} ok")
+
+
+def test_schedule_async_edges():
+    """K = N (flat table), K = 0 (steeply falling table), the hand-built cliff
+    (K = 4 where the early stop gives 1), a tie between budgets (smallest wins)
+    and all-equal keys (flat-index order)."""
+    rng = np.random.default_rng(3)
+    a = O.survival(rng.uniform(0.2, 1.0, (16, 8)).astype(np.float32))
+    N = 16 * 8
+    assert assert_same_async(a, a, np.ones(16 * 9 + 1)) == N
+    assert assert_same_async(a, a, 1.0 / (1.0 + np.arange(16 * 9 + 1)) ** 3) == 0
+    ones = np.ones((2, 2), dtype=np.float32)
+    assert assert_same_async(ones, ones, np.array([0.0, 0.0, 1.0, 0.9, 0.6, 0.55, 0.5])) == 4
+    assert assert_same_async(ones, ones, np.array([0.0, 0.0, 1.0, 5.0, 2.0, 3.0, 1.0])) == 1
+    half = np.full((16, 8), 0.5, dtype=np.float32)
+    assert_same_async(a, half, synth.sps_table(16, 8, 1e-3, 1e-5))

@@ -425,6 +425,105 @@ def test_schedule_closed_forms_on_the_workload_table():
         assert srt[bb] > (128 + G[bb]) / (128 + bb) - 1e-9
 
 
+def _rank_topk_counts(a, K):
+    """ell from an explicit rank count: candidate i is admitted iff fewer than K
+    candidates precede it (larger a, or equal a and smaller flat index)."""
+    flat = np.asarray(a, dtype=np.float64).reshape(-1)
+    R, g = np.asarray(a).shape
+    ell = np.zeros(R, dtype=np.int64)
+    for i in range(flat.size):
+        rank = int(np.sum(flat > flat[i]) + np.sum(flat[:i] == flat[i]))
+        if rank < K:
+            ell[i // g] += 1
+    return ell
+
+
+def test_schedule_async_brute_force():
+    """K is the budget with the largest (R + sum of the b largest lagged a) *
+    SPS(R + b), found here by exact rational arithmetic over every b; the
+    admitted set is the top K of the current a by an explicit rank count
+    [P1 §4.3; P3 スケジューラの実運用適用]."""
+    from fractions import Fraction
+    rng = np.random.default_rng(11)
+    for trial in range(60):
+        R, g = int(rng.integers(1, 6)), int(rng.integers(1, 6))
+        a_lag = _random_a(rng, R, g)
+        a_cur = _random_a(rng, R, g)
+        B = np.arange(R * (1 + g) + 1)
+        if trial % 2:
+            sps = 1.0 / np.maximum(rng.uniform(1e-3, 3e-3), rng.uniform(1e-5, 1e-3) * B)
+        else:  # bumpy table: several local maxima along the sorted path
+            sps = 1.0 / (1e-3 + 1e-4 * B + rng.uniform(0, 3e-4, B.size))
+        srt = sorted((Fraction(float(v)) for v in a_lag.reshape(-1)), reverse=True)
+        th = [(R + sum(srt[:b], Fraction(0))) * Fraction(float(sps[R + b]))
+              for b in range(R * g + 1)]
+        K_exact = max(range(len(th)), key=lambda b: (th[b], -b))
+        ell, K, theta, theta_fix = O.schedule_async(a_lag, a_cur, sps)
+        assert K == K_exact
+        assert theta == pytest.approx(float(th[K]), rel=1e-9)
+        np.testing.assert_array_equal(ell, _rank_topk_counts(a_cur, K))
+
+
+@pytest.mark.parametrize("R,g", [(4, 4), (3, 3), (2, 5)])
+def test_schedule_async_equals_early_stop_on_unimodal_curves(R, g):
+    """When the lagged and current a coincide and Theta is unimodal along the
+    sorted path, the global maximum is the early-stop point, so both schedulers
+    admit the same prefixes."""
+    rng = np.random.default_rng(12 + R * 10 + g)
+    for trial in range(20):
+        a = _random_a(rng, R, g, 0.2, 1.0)
+        knee = rng.uniform(R + 1, R * (1 + g) - 1)
+        sps = synth.sps_table(R, g, 1e-4 * knee, 1e-4)
+        ell_s, b, th_s, _, _ = O.schedule(a, sps)
+        ell_a, K, th_a, _ = O.schedule_async(a, a, sps)
+        assert K == b and th_a == th_s
+        np.testing.assert_array_equal(ell_a, ell_s)
+
+
+def test_schedule_async_crosses_a_cliff():
+    """Hand-built cost curve with a dip: R = 2, gamma = 2, every a = 1, so
+    tau(b) = 2 + b and Theta(b) = (2 + b) * SPS(2 + b) = 2, 2.7, 2.4, 2.75, 3.0.
+    The early stop halts at the first local maximum (b = 1); the asynchronous
+    scheduler searches every budget and takes b = 4."""
+    a = np.ones((2, 2), dtype=np.float32)
+    sps = np.array([0.0, 0.0, 1.0, 0.9, 0.6, 0.55, 0.5])
+    _, b, th_s, _, _ = O.schedule(a, sps)
+    assert b == 1 and th_s == pytest.approx(2.7, rel=1e-15)
+    ell, K, th, theta_fix = O.schedule_async(a, a, sps)
+    assert K == 4 and th == pytest.approx(3.0, rel=1e-15)
+    np.testing.assert_array_equal(ell, [2, 2])
+    np.testing.assert_allclose(theta_fix * 2.0 ** -32, [2.0, 2.7, 2.4, 2.75, 3.0], rtol=1e-15)
+
+
+def test_schedule_async_ties_take_the_smallest_budget():
+    """Theta(1) = 3 * 5 = 15 = 5 * 3 = Theta(3) is the maximum: K = 1."""
+    a = np.ones((2, 2), dtype=np.float32)
+    sps = np.array([0.0, 0.0, 1.0, 5.0, 2.0, 3.0, 1.0])
+    _, K, th, theta_fix = O.schedule_async(a, a, sps)
+    assert theta_fix[1] == theta_fix[3] == theta_fix.max()
+    assert K == 1 and th == 15.0
+
+
+def test_schedule_async_causal_isolation():
+    """The lagged a decides only how many candidates are admitted, the current a
+    only which: changing a_cur never moves K, and any a_lag with the same K
+    gives the same ell."""
+    rng = np.random.default_rng(13)
+    for trial in range(40):
+        R, g = int(rng.integers(2, 8)), int(rng.integers(2, 8))
+        sps = synth.sps_table(R, g, 1e-4 * rng.uniform(R + 1, R * (1 + g)), 1e-4)
+        a_lag = _random_a(rng, R, g)
+        a_cur = _random_a(rng, R, g)
+        ell, K, _, _ = O.schedule_async(a_lag, a_cur, sps)
+        _, K2, _, _ = O.schedule_async(a_lag, _random_a(rng, R, g), sps)
+        assert K2 == K
+        for _ in range(5):
+            other = _random_a(rng, R, g)
+            ell2, K3, _, _ = O.schedule_async(other, a_cur, sps)
+            if K3 == K:
+                np.testing.assert_array_equal(ell2, ell)
+
+
 # ---------------------------------------------------------------------------
 # Verification
 # ---------------------------------------------------------------------------
