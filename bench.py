@@ -45,16 +45,20 @@ PROFILE_COUNTERS = os.path.join(os.path.dirname(os.path.abspath(__file__)), "pro
                                 "dspark_round_qwen3_8b_r128_g16_hbm_counters.txt")
 
 
+# Sources the draft step kernel is compiled from (the counters go stale when
+# any of them changes).
+DRAFT_KERNEL_SOURCES = ("markov_step.hip", "mfma_stream.h", "dspark_device.h", "dspark_kernels.h")
+
+
 def sources_sha256():
-    """Hash of the kernel sources (every file under csrc/, by name and bytes)."""
-    import glob
+    """Hash of the draft kernel's sources (by name and bytes, in that order)."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)),
                         "semi_autoregressive_drafting_amd", "csrc")
-    for f in sorted(glob.glob(os.path.join(csrc, "*"))):
-        h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
+    for name in DRAFT_KERNEL_SOURCES:
+        h.update(name.encode())
+        with open(os.path.join(csrc, name), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
@@ -148,6 +152,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the read ceiling, cold steps, asynchronous scheduler and graph "
+                         "replay (for counter-collection runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (x4), so that "
                          "FETCH_SIZE / WRITE_SIZE counters can be scaled to bytes")
@@ -167,6 +174,7 @@ def main():
         sys.exit(2)
 
     import torch
+    from semi_autoregressive_drafting_amd import dspark as D
     from semi_autoregressive_drafting_amd import runner, synth
 
     t_gen = time.perf_counter()
@@ -178,13 +186,15 @@ def main():
     R, g, V, rank, d = di.R, di.gamma, di.V, di.rank, di.d
 
     def one_round(seed, ev=None):
-        # runner.draft copies the anchors into x[:, 0] (a tiny copy kernel) and
-        # enqueues the gamma draft steps and their merge with one library call
+        # the anchor copy and the gamma streaming steps, then the record merge;
+        # the events bracket the gamma step launches only
+        buf.x[:, 0].copy_(di.anchor)
         if ev is not None:
             ev[0].record()
-        runner.draft(di, buf, TEMPERATURE, seed)
+        runner.draft_phases(di, buf, TEMPERATURE, seed, D.DSPARK_PHASE_STEPS)
         if ev is not None:
             ev[1].record()
+        runner.draft_phases(di, buf, TEMPERATURE, seed, D.DSPARK_PHASE_MERGE)
         runner.schedule(di, buf)
         runner.verify(di, buf, TEMPERATURE, seed)
 
@@ -192,8 +202,8 @@ def main():
         one_round(10_000 + w)
     torch.cuda.synchronize()
 
-    # Timed region: K whole rounds; the two events per round bracket the draft
-    # block (gamma draft-step launches and the merge).
+    # Timed region: K whole rounds; the two events per round bracket the gamma
+    # back-to-back draft-step launches.
     K = args.steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
     torch.cuda.synchronize()
@@ -203,7 +213,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     draft_ms = np.array([evs[s][0].elapsed_time(evs[s][1]) for s in range(K)])
-    step_ms = draft_ms / g   # per draft step, merge and launch gaps included
+    step_ms = draft_ms / g   # per draft-step launch, gaps between the launches included
     ms_round = wall / K * 1e3
     value = R * g / (wall / K)
 
@@ -219,26 +229,32 @@ def main():
         runner.verify(di, buf, TEMPERATURE, 500 + s)
         ph[s][3].record()
     torch.cuda.synchronize()
+    block_ms = np.array([ph[s][0].elapsed_time(ph[s][1]) for s in range(nb)])
     sched_ms = np.array([ph[s][1].elapsed_time(ph[s][2]) for s in range(nb)])
     ver_ms = np.array([ph[s][2].elapsed_time(ph[s][3]) for s in range(nb)])
+    extras = not args.no_extras
     # the asynchronous scheduler on the same candidates (budget from a copy
     # standing in for the survival of two steps earlier)
-    a_lag = buf.a.clone()
-    ea = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    async_us = []
-    for s in range(nb):
-        ea[0].record()
-        runner.schedule_async(di, buf, a_lag)
-        ea[1].record()
-        torch.cuda.synchronize()
-        async_us.append(ea[0].elapsed_time(ea[1]) * 1e3)
+    async_us = [float("nan")]
+    if extras:
+        a_lag = buf.a.clone()
+        ea = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        async_us = []
+        for s in range(nb):
+            ea[0].record()
+            runner.schedule_async(di, buf, a_lag)
+            ea[1].record()
+            torch.cuda.synchronize()
+            async_us.append(ea[0].elapsed_time(ea[1]) * 1e3)
 
     # Cold draft step: a 512 MB write evicts W2 and U from L2 and the MALL
     # before each timed step (dspark_draft_step = step kernel + merge).
-    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-    cold, warm = [], []
-    buf.x[:, 0].copy_(di.anchor)
-    for s in range(6):
+    cold, warm = [float("nan")], [float("nan")]
+    scratch = torch.empty(512 << 20 if extras else 0, dtype=torch.uint8, device="cuda")
+    if extras:
+        cold, warm = [], []
+        buf.x[:, 0].copy_(di.anchor)
+    for s in range(6 if extras else 0):
         for flush, acc in ((True, cold), (False, warm)):
             if flush:
                 scratch.fill_(s & 0xFF)
@@ -251,11 +267,13 @@ def main():
     del scratch
 
     sb = draft_step_bytes(R, V, rank, d)
-    ceiling = read_ceiling(sb)
+    ceiling = read_ceiling(sb) if extras else None
 
     # The same round replayed from one captured HIP graph (no host launches).
     graph = None
     try:
+        if not extras:
+            raise RuntimeError("skipped (--no-extras)")
         gr = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
@@ -299,26 +317,28 @@ def main():
                                "bf16 W1/W2/h, fp32 logits, T=1, verify target U+N(0,1)",
                    "R": R, "gamma": g, "V": V, "rank": rank, "d": d,
                    "temperature": TEMPERATURE},
-        "roofline": {"kernel": "markov_step_shared (one dspark_draft_step; average over the "
-                               "gamma launches of a draft block, merge and launch gaps included)",
+        "roofline": {"kernel": "markov_step_shared (one draft step; HIP events around the gamma "
+                               "back-to-back launches of a draft block, divided by gamma)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(), "bytes_per_launch": sb,
                      "avg_launch_us": round(step_s * 1e6, 2),
-                     "frac_of_read_ceiling": round(achieved / ceiling["rotating"]["GBps"], 4)},
+                     "frac_of_read_ceiling": (round(achieved / ceiling["rotating"]["GBps"], 4)
+                                              if ceiling else None)},
         "read_ceiling": ceiling,
         "cold_step": {"step_plus_merge_us_cold": round(float(np.median(cold)), 2),
                       "step_plus_merge_us_warm": round(float(np.median(warm)), 2)},
         "graph": graph,
         "breakdown_us": {"draft_step_mean": round(float(step_ms.mean()) * 1e3, 2),
                          "draft_step_min": round(float(step_ms.min()) * 1e3, 2),
-                         "draft_total": round(float(draft_ms.mean()) * 1e3, 2),
+                         "draft_steps_total": round(float(draft_ms.mean()) * 1e3, 2),
+                         "draft_block_with_copy_and_merge": round(float(block_ms.mean()) * 1e3, 2),
                          "schedule": round(float(sched_ms.mean()) * 1e3, 2),
                          "schedule_async": round(float(np.median(async_us)), 2),
                          "verify": round(float(ver_ms.mean()) * 1e3, 2),
                          "round_wall": round(ms_round * 1e3, 2)},
         "verify_roofline": {"bytes": vb, "achieved_GBps": round(vb / (ver_ms.mean() * 1e-3) / 1e9, 1)},
-        "draft_only_tokens_per_s": round(R * g / (draft_ms.mean() * 1e-3), 1),
+        "draft_only_tokens_per_s": round(R * g / (block_ms.mean() * 1e-3), 1),
         "budget_last_round": int(buf.budget.item()),
         "tau_mean_last_round": round(float(buf.tau_mean.item()), 4),
         "cpu_baseline": None,

@@ -128,6 +128,24 @@ dspark_status dspark_draft_block(int R, int V, int rank, int d, int gamma, int d
                                  float* a, void* ws, size_t ws_bytes, dspark_stream_t stream);
 
 /*
+ * dspark_draft_block split into its two phases, so that a caller can place
+ * events between them: DSPARK_PHASE_STEPS enqueues the gamma streaming steps
+ * (winner words and partial records in ws), DSPARK_PHASE_MERGE the record
+ * merge that writes x[:, 1..gamma], p and lse [P1 §2.2 eq. p_k: the exact
+ * draft probability of each sampled token].  Calling STEPS then MERGE on one
+ * stream equals dspark_draft_block (both together: phases = 3); MERGE must
+ * follow the STEPS of the same block with the same arguments and workspace.
+ * phases outside 1..3 -> DSPARK_ERR_VALUE.
+ */
+enum { DSPARK_PHASE_STEPS = 1, DSPARK_PHASE_MERGE = 2 };
+dspark_status dspark_draft_block_phases(int R, int V, int rank, int d, int gamma, int dt,
+                                        const void* W1, const void* W2t, const float* U,
+                                        const void* h, const float* w, float temperature,
+                                        uint64_t seed, int32_t* x, float* p, float* lse,
+                                        float* c, float* a, void* ws, size_t ws_bytes,
+                                        int phases, dspark_stream_t stream);
+
+/*
  * Confidence head and survival for a whole drafted block
  * [P1 §3.1 eq. c_k; P1 §1.1 eq. a_j; §4.1 eq. tau]:
  *   c[r][k-1] = sigma(w[0:d] . h[r][k-1] + w[d:] . W1[x[r][k-1]]),  k = 1..gamma

@@ -146,26 +146,42 @@ dspark_status dspark_draft_step(int R, int V, int rank, int d, int gamma, int k,
   return DSPARK_OK;
 }
 
-dspark_status dspark_draft_block(int R, int V, int rank, int d, int gamma, int dt,
-                                 const void* W1, const void* W2t, const float* U,
-                                 const void* h, const float* w, float temperature,
-                                 uint64_t seed, int32_t* x, float* p, float* lse, float* c,
-                                 float* a, void* ws, size_t ws_bytes, dspark_stream_t stream) {
+dspark_status dspark_draft_block_phases(int R, int V, int rank, int d, int gamma, int dt,
+                                        const void* W1, const void* W2t, const float* U,
+                                        const void* h, const float* w, float temperature,
+                                        uint64_t seed, int32_t* x, float* p, float* lse,
+                                        float* c, float* a, void* ws, size_t ws_bytes,
+                                        int phases, dspark_stream_t stream) {
+  if (phases < 1 || phases > (DSPARK_PHASE_STEPS | DSPARK_PHASE_MERGE)) return DSPARK_ERR_VALUE;
   StepArgs args;
   StepPlan plan;
   const dspark_status s = check_draft(R, V, rank, d, gamma, 0, dt, W1, W2t, U, h, w, temperature,
                                       seed, x, p, lse, c, a, nullptr, ws, ws_bytes, args, plan);
   if (s != DSPARK_OK) return s;
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  for (int k = 1; k <= gamma; ++k) {
-    args.k = k;
-    args.prev_from_best = k > 1;  // x_{k-1} straight from step k-1's winner word
-    if (launch_draft_step(args, plan, st) != hipSuccess) return DSPARK_ERR_LAUNCH;
+  if (phases & DSPARK_PHASE_STEPS) {
+    for (int k = 1; k <= gamma; ++k) {
+      args.k = k;
+      args.prev_from_best = k > 1;  // x_{k-1} straight from step k-1's winner word
+      if (launch_draft_step(args, plan, st) != hipSuccess) return DSPARK_ERR_LAUNCH;
+    }
   }
-  args.k = 1;
-  args.prev_from_best = true;  // x_{k-1} of positions 2..gamma from the winner words
-  if (launch_draft_finalize(args, plan, 1, gamma, st) != hipSuccess) return DSPARK_ERR_LAUNCH;
+  if (phases & DSPARK_PHASE_MERGE) {
+    args.k = 1;
+    args.prev_from_best = true;  // x_{k-1} of positions 2..gamma from the winner words
+    if (launch_draft_finalize(args, plan, 1, gamma, st) != hipSuccess) return DSPARK_ERR_LAUNCH;
+  }
   return DSPARK_OK;
+}
+
+dspark_status dspark_draft_block(int R, int V, int rank, int d, int gamma, int dt,
+                                 const void* W1, const void* W2t, const float* U,
+                                 const void* h, const float* w, float temperature,
+                                 uint64_t seed, int32_t* x, float* p, float* lse, float* c,
+                                 float* a, void* ws, size_t ws_bytes, dspark_stream_t stream) {
+  return dspark_draft_block_phases(R, V, rank, d, gamma, dt, W1, W2t, U, h, w, temperature, seed,
+                                   x, p, lse, c, a, ws, ws_bytes,
+                                   DSPARK_PHASE_STEPS | DSPARK_PHASE_MERGE, stream);
 }
 
 dspark_status dspark_confidence(int R, int gamma, int d, int rank, int V, int dt,

@@ -36,23 +36,24 @@ __device__ __forceinline__ unsigned long long shfl_xor64(unsigned long long v, i
 // positions t * kPer .. t * kPer + kPer - 1 in `k` (n2 / kThreads of them are
 // real when n2 < kPer * kThreads: the rest hold all-ones keys and stay last).
 template <int kPer>
-__device__ void bitonic_sort(unsigned long long (&k)[kPer], unsigned long long* lds, int n2) {
+__device__ __forceinline__ void bitonic_sort(unsigned long long (&k)[kPer], unsigned long long* lds, int n2) {
   const int t = threadIdx.x;
   const int lane_bits = 6;  // 64 lanes
   for (int size = 2; size <= n2; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      if (stride < kPer) {  // partners inside the thread
+      if (stride < kPer) {  // partners inside the thread (constant register indices)
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-          const int i = t * kPer + j;
-          if ((i & stride) == 0) {
-            const int jj = j + stride;
+        for (int cs = kPer / 2; cs > 0; cs >>= 1) {
+          if (cs != stride) continue;
+#pragma unroll
+          for (int j = 0; j < kPer; ++j) {
+            if ((j & cs) != 0) continue;  // i & cs == j & cs since t * kPer is a multiple of kPer
+            const int i = t * kPer + j;
             const bool asc = (i & size) == 0;
-            const unsigned long long x = k[j], y = k[jj];
-            if ((x > y) == asc) {
-              k[j] = y;
-              k[jj] = x;
-            }
+            const unsigned long long x = k[j], y = k[j + cs];
+            const bool sw = (x > y) == asc;
+            k[j] = sw ? y : x;
+            k[j + cs] = sw ? x : y;
           }
         }
       } else if (stride < (kPer << lane_bits)) {  // partners in the same wave
@@ -86,6 +87,18 @@ __device__ void bitonic_sort(unsigned long long (&k)[kPer], unsigned long long* 
   }
 }
 
+// The network on the first P of the kPer register keys.
+template <int P, int kPer>
+__device__ __forceinline__ void sort_prefix(unsigned long long (&k)[kPer], unsigned long long* lds,
+                                            int n2) {
+  unsigned long long kk[P];
+#pragma unroll
+  for (int j = 0; j < P; ++j) kk[j] = k[j];
+  bitonic_sort<P>(kk, lds, n2);
+#pragma unroll
+  for (int j = 0; j < P; ++j) k[j] = kk[j];
+}
+
 // Sort the N = R * gamma candidates of `a` into `key` (ascending; see the
 // file comment) and return the per-thread run [b0, b1) of sorted positions with
 // the fixed-point prefix sum G at b0 (`base`) and the total over all N.
@@ -100,7 +113,7 @@ __device__ __forceinline__ long long q_of(unsigned long long key) {
   return (long long)rint((double)v * 4294967296.0);
 }
 
-__device__ Runs sort_and_scan(const float* a, int N, unsigned long long* key, long long* wsum) {
+__device__ __forceinline__ Runs sort_and_scan(const float* a, int N, unsigned long long* key, long long* wsum) {
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   int n2 = kThreads;  // at least one key per thread so every thread runs the network
@@ -119,14 +132,10 @@ __device__ Runs sort_and_scan(const float* a, int N, unsigned long long* key, lo
     }
     k[j] = v;
   }
-  switch (per2) {  // the network over n2 keys, kPer in registers per thread
-    case 1: { unsigned long long k1[1] = {k[0]}; bitonic_sort<1>(k1, key, n2); k[0] = k1[0]; break; }
-    case 2: { unsigned long long k2[2] = {k[0], k[1]}; bitonic_sort<2>(k2, key, n2);
-              k[0] = k2[0]; k[1] = k2[1]; break; }
-    case 4: { unsigned long long k4[4] = {k[0], k[1], k[2], k[3]}; bitonic_sort<4>(k4, key, n2);
-#pragma unroll
-              for (int j = 0; j < 4; ++j) k[j] = k4[j];
-              break; }
+  switch (per2) {  // the network over n2 keys, per2 in registers per thread
+    case 1: sort_prefix<1>(k, key, n2); break;
+    case 2: sort_prefix<2>(k, key, n2); break;
+    case 4: sort_prefix<4>(k, key, n2); break;
     default: bitonic_sort<kPer>(k, key, n2); break;
   }
   __syncthreads();

@@ -18,9 +18,10 @@ DSPARK_OK, DSPARK_ERR_NULL, DSPARK_ERR_SHAPE, DSPARK_ERR_DTYPE, DSPARK_ERR_VALUE
     DSPARK_ERR_WORKSPACE, DSPARK_ERR_LAUNCH = range(7)
 DSPARK_F32, DSPARK_BF16 = 0, 1
 DSPARK_OP_DRAFT_STEP, DSPARK_OP_SCHEDULE, DSPARK_OP_VERIFY = 0, 1, 2
+DSPARK_PHASE_STEPS, DSPARK_PHASE_MERGE = 1, 2
 
 EXPORTS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_draft_step",
-           "dspark_draft_block", "dspark_confidence", "dspark_schedule", "dspark_schedule_async",
+           "dspark_draft_block", "dspark_draft_block_phases", "dspark_confidence", "dspark_schedule", "dspark_schedule_async",
            "dspark_verify")
 
 _lib = None
@@ -52,6 +53,9 @@ def load():
     L.dspark_draft_block.argtypes = [I, I, I, I, I, I, P, P, P, P, P, F, U64,
                                      P, P, P, P, P, P, SZ, P]
     L.dspark_draft_block.restype = I
+    L.dspark_draft_block_phases.argtypes = [I, I, I, I, I, I, P, P, P, P, P, F, U64,
+                                            P, P, P, P, P, P, SZ, I, P]
+    L.dspark_draft_block_phases.restype = I
     L.dspark_confidence.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P]
     L.dspark_confidence.restype = I
     L.dspark_schedule.argtypes = [I, I, P, P, I, P, P, P, P, SZ, P]
@@ -117,6 +121,15 @@ def dspark_draft_block(R, V, rank, d, gamma, dt, W1, W2t, U, h, w, temperature, 
     _call("dspark_draft_block", R, V, rank, d, gamma, dt, _ptr(W1), _ptr(W2t), _ptr(U),
           _ptr(h), _ptr(w), float(temperature), int(seed), _ptr(x), _ptr(p), _ptr(lse),
           _ptr(c), _ptr(a), _ptr(ws), int(ws_bytes), _stream(stream))
+
+
+def dspark_draft_block_phases(R, V, rank, d, gamma, dt, W1, W2t, U, h, w, temperature, seed,
+                              x, p, lse, c, a, ws, phases, ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _call("dspark_draft_block_phases", R, V, rank, d, gamma, dt, _ptr(W1), _ptr(W2t), _ptr(U),
+          _ptr(h), _ptr(w), float(temperature), int(seed), _ptr(x), _ptr(p), _ptr(lse),
+          _ptr(c), _ptr(a), _ptr(ws), int(ws_bytes), int(phases), _stream(stream))
 
 
 def dspark_confidence(R, gamma, d, rank, V, dt, h, W1, x, w, c, a, stream=None):

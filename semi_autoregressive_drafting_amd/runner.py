@@ -102,6 +102,17 @@ def draft(di: DeviceInputs, buf: RoundBuffers, temperature: float, seed: int):
                          di.w, temperature, seed, buf.x, buf.p, buf.lse, buf.c, buf.a, buf.ws)
 
 
+def draft_phases(di: DeviceInputs, buf: RoundBuffers, temperature: float, seed: int,
+                 phases: int):
+    """One phase (or both) of draft(): D.DSPARK_PHASE_STEPS runs the anchor
+    copy and the gamma streaming steps, D.DSPARK_PHASE_MERGE the record merge."""
+    if phases & D.DSPARK_PHASE_STEPS:
+        buf.x[:, 0].copy_(di.anchor)
+    D.dspark_draft_block_phases(di.R, di.V, di.rank, di.d, di.gamma, di.dt, di.W1, di.W2t, di.U,
+                                di.h, di.w, temperature, seed, buf.x, buf.p, buf.lse, buf.c,
+                                buf.a, buf.ws, phases)
+
+
 def schedule(di: DeviceInputs, buf: RoundBuffers):
     D.dspark_schedule(di.R, di.gamma, buf.a, di.sps, di.sps.numel(), buf.ell, buf.budget,
                       buf.theta)

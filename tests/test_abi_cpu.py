@@ -126,6 +126,17 @@ def test_schedule_validation():
     assert f(600, 4, FAKE, FAKE, 10 ** 6, FAKE, FAKE, FAKE, None, 0, None) == D.DSPARK_ERR_SHAPE
 
 
+def test_draft_block_phases_validation():
+    f = D.load().dspark_draft_block_phases
+    args = [128, 151936, 256, 4096, 16, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 1.0, 0,
+            FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30]
+    assert f(*args, 0, None) == D.DSPARK_ERR_VALUE
+    assert f(*args, 4, None) == D.DSPARK_ERR_VALUE
+    bad = list(args)
+    bad[6] = None
+    assert f(*bad, 3, None) == D.DSPARK_ERR_NULL
+
+
 def test_schedule_async_validation():
     f = D.load().dspark_schedule_async
     assert f(4, 4, None, FAKE, FAKE, 21, FAKE, FAKE, FAKE, None) == D.DSPARK_ERR_NULL

@@ -111,7 +111,8 @@ def test_draft_is_deterministic(name):
 
 
 def test_draft_block_matches_single_steps():
-    """dspark_draft_block gives the same bits as gamma dspark_draft_step calls."""
+    """dspark_draft_block, and its two phases called in turn, give the same bits
+    as gamma dspark_draft_step calls."""
     from semi_autoregressive_drafting_amd import dspark as D
     for name in ("qwen3_4b_r32_g7", "edge_v1000_r100_g2", "tiny_v1024_r4_g4",
                  "edge_v40004_r130_g3"):
@@ -123,6 +124,14 @@ def test_draft_block_matches_single_steps():
         torch.cuda.synchronize()
         for n in ("x", "p", "lse", "c", "a"):
             np.testing.assert_array_equal(getattr(buf, n).cpu().numpy(), h1[n], err_msg=name + n)
+        # the same block as its two phases (steps, then the merge)
+        buf2 = runner.RoundBuffers.allocate(di)
+        runner.draft_phases(di, buf2, 1.0, 11, D.DSPARK_PHASE_STEPS)
+        runner.draft_phases(di, buf2, 1.0, 11, D.DSPARK_PHASE_MERGE)
+        torch.cuda.synchronize()
+        for n in ("x", "p", "lse", "c", "a"):
+            np.testing.assert_array_equal(getattr(buf2, n).cpu().numpy(), h1[n],
+                                          err_msg=name + n + " (phases)")
 
 
 def test_batched_confidence_matches_fused():
