@@ -115,7 +115,8 @@ def test_draft_block_matches_single_steps():
     as gamma dspark_draft_step calls."""
     from semi_autoregressive_drafting_amd import dspark as D
     for name in ("qwen3_4b_r32_g7", "edge_v1000_r100_g2", "tiny_v1024_r4_g4",
-                 "edge_v40004_r130_g3"):
+                 "edge_v40004_r130_g3", "qwen3_8b_r128_g16", "edge_v9996_r130_g3",
+                 "edge_v40001_r128_g2"):
         case = Case(name)
         _, h1, _ = case.run_draft(1.0, 11)
         di = case.di
@@ -132,6 +133,18 @@ def test_draft_block_matches_single_steps():
         for n in ("x", "p", "lse", "c", "a"):
             np.testing.assert_array_equal(getattr(buf2, n).cpu().numpy(), h1[n],
                                           err_msg=name + n + " (phases)")
+
+
+def test_draft_block_greedy_matches_single_steps():
+    """The same at T = 0 on shared rank-256 shapes."""
+    for name in ("qwen3_8b_r128_g16", "edge_v40004_r130_g3"):
+        case = Case(name)
+        _, h1, _ = case.run_draft(0.0, 5)
+        buf = runner.RoundBuffers.allocate(case.di)
+        runner.draft(case.di, buf, 0.0, 5)
+        torch.cuda.synchronize()
+        for n in ("x", "p", "lse", "c", "a"):
+            np.testing.assert_array_equal(getattr(buf, n).cpu().numpy(), h1[n], err_msg=name + n)
 
 
 def test_batched_confidence_matches_fused():
