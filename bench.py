@@ -149,8 +149,8 @@ def cpu_baseline(inp, seed):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the read ceiling, cold steps, asynchronous scheduler and graph "
@@ -198,6 +198,7 @@ def main():
         runner.schedule(di, buf)
         runner.verify(di, buf, TEMPERATURE, seed)
 
+    # warm-up rounds (the first rounds after start-up run at lower clocks)
     for w in range(args.warmup):
         one_round(10_000 + w)
     torch.cuda.synchronize()
