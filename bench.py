@@ -133,17 +133,26 @@ def cpu_baseline(inp, seed):
     W1, W2t = O.as_f64(inp.W1_store), O.as_f64(inp.W2t_store)
     h = O.as_f64(inp.h_store[reqs])
     U = inp.U[reqs].astype(np.float64)
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        rnd = O.draft_round(U, h, inp.w, W1, W2t, inp.anchor[reqs], TEMPERATURE, seed, reqs)
-        ell, b, th, _, _ = O.schedule(rnd["a"], inp.sps[: len(reqs) * (1 + wl.gamma) + 1])
-        O.verify(inp.U[reqs], inp.target[reqs], W1, W2t, rnd["x"], ell, TEMPERATURE, seed, reqs)
-        dt = time.perf_counter() - t0
+    def run(threads):
+        with threadpool_limits(limits=threads):
+            t0 = time.perf_counter()
+            rnd = O.draft_round(U, h, inp.w, W1, W2t, inp.anchor[reqs], TEMPERATURE, seed, reqs)
+            ell, b, th, _, _ = O.schedule(rnd["a"], inp.sps[: len(reqs) * (1 + wl.gamma) + 1])
+            O.verify(inp.U[reqs], inp.target[reqs], W1, W2t, rnd["x"], ell, TEMPERATURE, seed,
+                     reqs)
+            return time.perf_counter() - t0
+
+    host_cores = len(os.sched_getaffinity(0))
+    dt1 = run(1)
+    dtn = run(host_cores)
     tokens = len(reqs) * wl.gamma
-    return {"value": tokens / dt, "unit": "draft tokens/s", "cores": 1, "kind": "oracle",
+    return {"value": tokens / dt1, "unit": "draft tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"{len(reqs)} of {wl.R} requests (16 easy, 16 hard), full round "
                       f"(gamma={wl.gamma} draft steps + schedule + verify), fp64 NumPy, "
-                      f"1 BLAS thread, {dt:.1f} s"}
+                      f"1 BLAS thread, {dt1:.1f} s",
+            "host_cores": host_cores,
+            "all_cores": {"value": tokens / dtn, "blas_threads": host_cores,
+                          "seconds": round(dtn, 2)}}
 
 
 def main():
@@ -292,9 +301,27 @@ def main():
             gr.replay()
         torch.cuda.synchronize()
         g_round = (time.perf_counter() - tg) / K
-        graph = {"round_us": round(g_round * 1e6, 2),
-                 "draft_tokens_per_s": round(R * g / g_round, 1)}
         del gr
+        # the gamma-step loop alone, captured once and replayed back to back
+        gs = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gs):
+            runner.draft_phases(di, buf, TEMPERATURE, 902, D.DSPARK_PHASE_STEPS)
+        for _ in range(3):
+            gs.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(K):
+            gs.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        g_steps_us = e0.elapsed_time(e1) * 1e3 / K
+        runner.draft_phases(di, buf, TEMPERATURE, 902, D.DSPARK_PHASE_MERGE)  # leave ws clean
+        torch.cuda.synchronize()
+        del gs
+        graph = {"round_us": round(g_round * 1e6, 2),
+                 "draft_tokens_per_s": round(R * g / g_round, 1),
+                 "step_loop_us_per_step": round(g_steps_us / g, 2)}
     except Exception as exc:  # graph capture unavailable: report it, keep the eager numbers
         graph = {"error": str(exc)[:200]}
 
@@ -331,6 +358,7 @@ def main():
                       "step_plus_merge_us_warm": round(float(np.median(warm)), 2)},
         "graph": graph,
         "breakdown_us": {"draft_step_mean": round(float(step_ms.mean()) * 1e3, 2),
+                         "draft_step_median": round(float(np.median(step_ms)) * 1e3, 2),
                          "draft_step_min": round(float(step_ms.min()) * 1e3, 2),
                          "draft_steps_total": round(float(draft_ms.mean()) * 1e3, 2),
                          "draft_block_with_copy_and_merge": round(float(block_ms.mean()) * 1e3, 2),
