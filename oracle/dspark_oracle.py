@@ -33,6 +33,9 @@ What each function follows, and what pins it (tests/test_oracle_pins.py):
         count, agreement with `schedule` on unimodal curves, a hand-built cliff
         curve where the early stop and the global maximum differ, and causal
         isolation (ell changes with a_lag only through K).
+  train_losses                 P1 §5 (L_CE, L_TV, L_conf, w_k; P3 defaults).
+        Pinned by the two-token closed form, identical-law special cases,
+        invariance to a constant logit shift, and the default weights.
   verify                       P1 §3.1 eq. c*, standard rejection sampling (P1
         intro and §2.2; P3 問題定義).  Pinned by the c* = overlap identity,
         special cases, losslessness (output law = p_t) and acceptance-rate = c*.
@@ -309,6 +312,58 @@ def schedule_async(a_lag, a_cur, sps):
     order_cur = np.argsort(-a_cur.reshape(-1).astype(np.float64), kind="stable")
     ell = np.bincount(order_cur[:K] // g, minlength=R).astype(np.int64)
     return ell, K, float(theta_fix[K]) * 2.0 ** -32, theta_fix
+
+
+# ----------------------------------------------------------------------------
+# Training objective                                       [P1 §5; P3 アーキテクチャ]
+# ----------------------------------------------------------------------------
+LOSS_ALPHAS = (0.1, 0.9, 1.0)   # alpha_CE, alpha_TV, alpha_conf (P1 §5 and P3 defaults)
+
+
+def position_weights(gamma, lam):
+    """w_k = exp(-(k-1)/lambda), k = 1..gamma  [P1 §5]; P3 writes the same
+    weight with lambda = gamma."""
+    return np.exp(-np.arange(gamma, dtype=np.float64) / float(lam))
+
+
+def train_losses(U, target, W1, W2t, h, w, x_star, T=1.0, lam=None, alphas=LOSS_ALPHAS):
+    """The three training losses of one batch of drafted blocks  [P1 §5]:
+
+        L_CE   = -sum_k w_k log p_k^d(x*_k)
+        L_TV   =  sum_k w_k ||p_k^d - p_k^t||_1
+        L_conf = -sum_k w_k [c*_k log c_k + (1 - c*_k) log(1 - c_k)]
+        L      = a_CE L_CE + a_TV L_TV + a_conf L_conf,
+
+    with c*_k = 1 - 1/2 ||p_k^d - p_k^t||_1 (the acceptance probability, a
+    constant target here) and c_k the confidence head.  The Markov head and the
+    confidence head see the target block x* (teacher forcing): position k uses
+    x*_{k-1}, x*_0 being the anchor.  U, target: [n, gamma, V]; h: [n, gamma, d];
+    x_star: [n, gamma + 1]; lam defaults to gamma.
+
+    Returns a dict of per-position terms [n, gamma] (ce, tv, conf, c, c_star),
+    the weights w [gamma], the per-loss sums over the batch and the total L."""
+    U = np.asarray(U, dtype=np.float64)
+    n, g, V = U.shape
+    lam = g if lam is None else lam
+    wk = position_weights(g, lam)
+    x_star = np.asarray(x_star, dtype=np.int64)
+    ce = np.zeros((n, g)); tv = np.zeros((n, g)); cf = np.zeros((n, g))
+    c = np.zeros((n, g)); cs = np.zeros((n, g))
+    for i in range(n):
+        z_d = draft_logits(U[i], W1, W2t, x_star[i, :g])             # rows k = 1..g
+        logp_d, _ = log_softmax_rows(z_d / T)
+        logp_t, _ = log_softmax_rows(np.asarray(target[i], dtype=np.float64) / T)
+        p_d, p_t = np.exp(logp_d), np.exp(logp_t)
+        ce[i] = -logp_d[np.arange(g), x_star[i, 1:]]
+        tv[i] = np.abs(p_d - p_t).sum(axis=-1)
+        cs[i] = 1.0 - 0.5 * tv[i]
+        c[i] = confidence(as_f64(h[i]), w, W1, x_star[i, :g])
+        cf[i] = -(cs[i] * np.log(c[i]) + (1.0 - cs[i]) * np.log1p(-c[i]))
+    sums = {"ce": float((ce * wk).sum()), "tv": float((tv * wk).sum()),
+            "conf": float((cf * wk).sum())}
+    total = alphas[0] * sums["ce"] + alphas[1] * sums["tv"] + alphas[2] * sums["conf"]
+    return {"ce": ce, "tv": tv, "conf": cf, "c": c, "c_star": cs, "w": wk, "sums": sums,
+            "total": total}
 
 
 def schedule_exhaustive(a, sps):

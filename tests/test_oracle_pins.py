@@ -525,6 +525,75 @@ def test_schedule_async_causal_isolation():
 
 
 # ---------------------------------------------------------------------------
+# Training losses
+# ---------------------------------------------------------------------------
+def _two_token_case(a, b, T, anchor=0, xs=1):
+    """One request, gamma = 1, V = 2, rank 1: W1 = [[0], [0]] so the bias is 0,
+    U = [0, a] and target = [0, b]; h = 0 and w = 0 so c = 1/2."""
+    U = np.array([[[0.0, a]]])
+    target = np.array([[[0.0, b]]])
+    W1 = np.zeros((2, 1))
+    W2t = np.zeros((2, 1))
+    h = np.zeros((1, 1, 3))
+    w = np.zeros(4)
+    x = np.array([[anchor, xs]])
+    return O.train_losses(U, target, W1, W2t, h, w, x, T=T)
+
+
+@pytest.mark.parametrize("a,b,T", [(1.3, -0.4, 1.0), (2.0, 2.0, 0.7), (-3.0, 0.5, 1.5)])
+def test_train_losses_two_token_closed_form(a, b, T):
+    """V = 2: p_d(1) = 1/(1 + e^{-a/T}), p_t(1) = 1/(1 + e^{-b/T});
+    CE = log(1 + e^{-a/T}) for x* = 1, TV = 2 |p_d(1) - p_t(1)|, and with c = 1/2
+    the confidence loss is log 2 whatever c* is  [P1 §5]."""
+    import math
+    r = _two_token_case(a, b, T)
+    pd1 = 1.0 / (1.0 + math.exp(-a / T))
+    pt1 = 1.0 / (1.0 + math.exp(-b / T))
+    assert r["ce"][0, 0] == pytest.approx(math.log1p(math.exp(-a / T)), rel=1e-12)
+    assert r["tv"][0, 0] == pytest.approx(2.0 * abs(pd1 - pt1), rel=1e-12, abs=1e-15)
+    assert r["c_star"][0, 0] == pytest.approx(1.0 - abs(pd1 - pt1), rel=1e-12)
+    assert r["c"][0, 0] == 0.5
+    assert r["conf"][0, 0] == pytest.approx(math.log(2.0), rel=1e-12)
+    alphas = O.LOSS_ALPHAS
+    assert r["total"] == pytest.approx(alphas[0] * r["ce"][0, 0] + alphas[1] * r["tv"][0, 0]
+                                       + alphas[2] * math.log(2.0), rel=1e-12)
+
+
+def test_train_losses_identical_laws_and_shift_invariance():
+    """Target logits equal to the draft logits: TV = 0, c* = 1 and the
+    confidence loss is -log c.  Adding a constant to every logit of a row (draft
+    or target) changes no term."""
+    rng = np.random.default_rng(21)
+    n, g, V, rank, d = 2, 3, 11, 4, 5
+    W1 = rng.normal(0, 0.5, (V, rank)); W2t = rng.normal(0, 0.5, (V, rank))
+    U = rng.normal(0, 1.0, (n, g, V)); h = rng.normal(0, 1.0, (n, g, d))
+    w = rng.normal(0, 0.3, d + rank)
+    x = rng.integers(0, V, (n, g + 1))
+    z = np.stack([O.draft_logits(U[i], W1, W2t, x[i, :g]) for i in range(n)])
+    r = O.train_losses(U, z, W1, W2t, h, w, x, T=0.8)
+    np.testing.assert_allclose(r["tv"], 0.0, atol=1e-13)
+    np.testing.assert_allclose(r["c_star"], 1.0, atol=1e-13)
+    np.testing.assert_allclose(r["conf"], -np.log(r["c"]), rtol=1e-12)
+    target = z + rng.normal(0, 1.0, z.shape)
+    r1 = O.train_losses(U, target, W1, W2t, h, w, x, T=0.8)
+    r2 = O.train_losses(U + rng.normal(0, 5, (n, g, 1)), target + rng.normal(0, 5, (n, g, 1)),
+                        W1, W2t, h, w, x, T=0.8)
+    for key in ("ce", "tv", "conf", "c_star"):
+        np.testing.assert_allclose(r2[key], r1[key], rtol=1e-9, atol=1e-12)
+
+
+def test_train_loss_weights():
+    """w_k = exp(-(k-1)/lambda) with lambda = gamma by default, and the default
+    loss weights 0.1 / 0.9 / 1.0 [P1 §5; P3 アーキテクチャ]."""
+    import math
+    np.testing.assert_allclose(O.position_weights(4, 2.0),
+                               [1.0, math.exp(-0.5), math.exp(-1.0), math.exp(-1.5)], rtol=1e-15)
+    assert O.LOSS_ALPHAS == (0.1, 0.9, 1.0)
+    r = _two_token_case(0.5, 0.1, 1.0)
+    assert r["w"][0] == 1.0
+
+
+# ---------------------------------------------------------------------------
 # Verification
 # ---------------------------------------------------------------------------
 def test_tv_acceptance_identity_and_special_cases():
