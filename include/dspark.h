@@ -73,7 +73,8 @@ typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1 } dspark_dtype;
 typedef enum {
   DSPARK_OP_DRAFT_STEP = 0,
   DSPARK_OP_SCHEDULE = 1,
-  DSPARK_OP_VERIFY = 2
+  DSPARK_OP_VERIFY = 2,
+  DSPARK_OP_TRAIN_LOSS = 3
 } dspark_op;
 
 /* Bytes of device workspace entry point `op` needs for these sizes (0 if the
@@ -220,6 +221,34 @@ dspark_status dspark_verify(int R, int V, int rank, int gamma, int dt, const voi
                             float* c_star, int32_t* n_accept, int32_t* next_token,
                             int32_t* tau, float* tau_mean, void* ws, size_t ws_bytes,
                             dspark_stream_t stream);
+
+/*
+ * Training losses of the sequential and confidence heads [P1 §5 训练目标; P3
+ * アーキテクチャ (default weights)] over R drafted blocks of gamma positions,
+ * with the target block as the Markov input (teacher forcing):
+ *   e_{r,k}  = W1[x*[r][k-1]]  (x*[r][0] is the anchor)
+ *   p_d      = softmax((U[r][k-1] + e . W2) / T),  p_t = softmax(target[r][k-1] / T)
+ *   ce       = -ln p_d(x*[r][k])
+ *   tv       = ||p_d - p_t||_1,  c* = 1 - tv / 2 (a constant target)
+ *   c        = sigma(w . [h[r][k-1]; e])
+ *   conf     = -(c* ln c + (1 - c*) ln(1 - c))
+ *   w_k      = exp(-(k-1) / lambda)  (P3 uses lambda = gamma)
+ * Outputs (device): terms fp32 [R][gamma][4] = (ce, tv, conf, c) per position;
+ * sums fp64 [4] = (sum w_k ce, sum w_k tv, sum w_k conf,
+ * alpha_ce*.. + alpha_tv*.. + alpha_conf*..), summed over the batch in a fixed
+ * order (bit-reproducible).  The P1 defaults are alpha = 0.1, 0.9, 1.0.
+ * Inputs as for dspark_verify (U, target fp32 [R][gamma][V]; W1, W2t, h in dt;
+ * w fp32 [d + rank]); x_star int32 [R][gamma+1].  T > 0 and lambda > 0 (else
+ * DSPARK_ERR_VALUE).  ws: dspark_workspace_bytes(DSPARK_OP_TRAIN_LOSS, ...)
+ * bytes; its contents need no initialisation.  Forward only: the gradients
+ * are not computed here.
+ */
+dspark_status dspark_train_loss(int R, int V, int rank, int d, int gamma, int dt, const void* W1,
+                                const void* W2t, const float* U, const void* h, const float* w,
+                                const float* target, const int32_t* x_star, float temperature,
+                                float lambda, float alpha_ce, float alpha_tv, float alpha_conf,
+                                float* terms, double* sums, void* ws, size_t ws_bytes,
+                                dspark_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -61,6 +61,7 @@ size_t dspark_workspace_bytes(int op, int R, int V, int rank, int gamma) {
     case DSPARK_OP_DRAFT_STEP: return plan_draft_step(R, V, gamma).ws_bytes;
     case DSPARK_OP_SCHEDULE: return 0;
     case DSPARK_OP_VERIFY: return plan_verify(R, V, gamma).ws_bytes;
+    case DSPARK_OP_TRAIN_LOSS: return plan_train(R, V, gamma).ws_bytes;
     default: return 0;
   }
 }
@@ -275,6 +276,56 @@ dspark_status dspark_verify(int R, int V, int rank, int gamma, int dt, const voi
   args.ws = static_cast<unsigned char*>(ws);
   if (launch_verify(args, plan, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return DSPARK_ERR_LAUNCH;
+  return DSPARK_OK;
+}
+
+dspark_status dspark_train_loss(int R, int V, int rank, int d, int gamma, int dt, const void* W1,
+                                const void* W2t, const float* U, const void* h, const float* w,
+                                const float* target, const int32_t* x_star, float temperature,
+                                float lambda, float alpha_ce, float alpha_tv, float alpha_conf,
+                                float* terms, double* sums, void* ws, size_t ws_bytes,
+                                dspark_stream_t stream) {
+  if (dt != DSPARK_F32 && dt != DSPARK_BF16) return DSPARK_ERR_DTYPE;
+  if (!W1 || !W2t || !U || !h || !w || !target || !x_star || !terms || !sums)
+    return DSPARK_ERR_NULL;
+  if (R < 1 || R > kMaxR || V < 2 || V > kMaxV || gamma < 1 || gamma > kMaxGamma || d < 1 ||
+      d > kMaxD)
+    return DSPARK_ERR_SHAPE;
+  dspark_status s = check_rank(dt, rank);
+  if (s != DSPARK_OK) return s;
+  if (!aligned16(W1) || !aligned16(W2t) ||
+      ((V % 4) == 0 && (!aligned16(U) || !aligned16(target))))
+    return DSPARK_ERR_SHAPE;
+  if (!(temperature > 0.0f) || isinf(temperature) || !(lambda > 0.0f) || isinf(lambda) ||
+      !isfinite(alpha_ce) || !isfinite(alpha_tv) || !isfinite(alpha_conf))
+    return DSPARK_ERR_VALUE;
+  const VerifyPlan plan = plan_verify(R, V, gamma);
+  const TrainPlan tplan = plan_train(R, V, gamma);
+  if (!ws || ws_bytes < tplan.ws_bytes || !aligned16(ws)) return DSPARK_ERR_WORKSPACE;
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  unsigned char* wsb = static_cast<unsigned char*>(ws);
+  float* c = reinterpret_cast<float*>(wsb + tplan.off_c);
+  float* surv = reinterpret_cast<float*>(wsb + tplan.off_surv);
+  // c_k = sigma(w . [h_k; W1[x*_{k-1}]]) with the target block as the Markov input
+  ConfArgs cargs{R, gamma, d, rank, V, dt == DSPARK_BF16, h, W1, x_star, w, c, surv};
+  if (launch_confidence(cargs, st) != hipSuccess) return DSPARK_ERR_LAUNCH;
+
+  VerifyArgs args{};
+  args.R = R;
+  args.V = V;
+  args.rank = rank;
+  args.gamma = gamma;
+  args.bf16 = dt == DSPARK_BF16;
+  args.greedy = false;
+  args.W1 = W1;
+  args.W2t = W2t;
+  args.U = U;
+  args.target = target;
+  args.x = x_star;
+  args.kscale = kscale_of(temperature);
+  args.ws = wsb;
+  TrainArgs targs{lambda, alpha_ce, alpha_tv, alpha_conf, c, terms, sums};
+  if (launch_train(args, targs, plan, tplan, st) != hipSuccess) return DSPARK_ERR_LAUNCH;
   return DSPARK_OK;
 }
 

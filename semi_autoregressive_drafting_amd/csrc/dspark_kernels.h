@@ -119,4 +119,25 @@ struct VerifyArgs {
 VerifyPlan plan_verify(int R, int V, int gamma);
 hipError_t launch_verify(const VerifyArgs& a, const VerifyPlan& plan, hipStream_t stream);
 
+// Training losses (verify.hip): the verification workspace followed by these.
+struct TrainPlan {
+  size_t off_dlse;  // draft-normaliser records [n_slabs][3][n_rows]
+  size_t off_lse_d; // draft log-normalisers (natural log) [n_rows]
+  size_t off_ce;    // -log p_d(x*) [n_rows]
+  size_t off_c;     // confidence c_k [n_rows]
+  size_t off_surv;  // survival products of the confidence head (unused) [n_rows]
+  size_t ws_bytes;
+};
+
+struct TrainArgs {
+  float lambda, alpha_ce, alpha_tv, alpha_conf;
+  const float* c;  // confidence c_k [n_rows], computed before the assembly
+  float* terms;    // [n_rows][4]: ce, tv, conf, c
+  double* sums;    // [4]: sum_k w_k ce, sum w_k tv, sum w_k conf, total
+};
+
+TrainPlan plan_train(int R, int V, int gamma);
+hipError_t launch_train(const VerifyArgs& a, const TrainArgs& ta, const VerifyPlan& plan,
+                        const TrainPlan& tp, hipStream_t stream);
+
 }  // namespace dspark

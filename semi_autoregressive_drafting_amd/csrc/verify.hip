@@ -495,6 +495,236 @@ __global__ __launch_bounds__(256) void verify_finalize(VerifyArgs a, VerifyPlan 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Training losses [P1 §5]: T1 the draft normaliser of every row (r, k) with
+// the target block as the Markov input (teacher forcing), and the draft logit
+// of the target token x*_k; then the target normalisers (V1), the c* pass (V3)
+// and the confidence head reused as they are, and T3 the weighted sums.
+// ---------------------------------------------------------------------------
+// U rows only (the draft side), line-coalesced through the wave's LDS patch
+// with kVec.
+template <bool kVec>
+struct URows {
+  const float* urow;
+  float* patch;
+  int V, half;
+  float ubuf[kVec ? 1 : kVerifyDist + 1][16];
+  RowTiles<1, kVec ? kVerifyDist + 1 : 1> rows;
+  static constexpr int kLoads = kVec ? 4 : 16;
+
+  template <int S>
+  __device__ __forceinline__ void prefetch(int vt) {
+    if constexpr (kVec)
+      rows.template load<S>(vt);
+    else
+      load16<false>(ubuf[S], urow, (vt < 0 ? 0 : vt * kVTile) + 16 * half);
+  }
+  template <int S>
+  __device__ __forceinline__ void get(float (&u)[1][16]) {
+    if constexpr (kVec) {
+      rows.template to_lanes<S>(patch, u);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) u[0][i] = ubuf[S][i];
+    }
+  }
+};
+
+// Online max / sum of 2^t (t = z * log2(e) / T) over the lane's entries, and
+// t at the row's target token.
+template <bool kVec>
+struct DraftLseEpi : URows<kVec> {
+  float kscale, m, S, tx;
+  int xs;  // target token of the lane's row
+
+  template <bool kMasked>
+  __device__ __forceinline__ void fold(const float (&u)[16], const f32x16_t& acc, int vt) {
+    const int vb = vt * kVTile + 16 * this->half;
+    float t[16];
+    float tm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      t[i] = (u[i] + acc[i]) * kscale;
+      if (kMasked && vb + i >= this->V) t[i] = -INFINITY;
+      tm = fmaxf(tm, t[i]);
+      tx = (vb + i == xs) ? t[i] : tx;
+    }
+    const float mn = fmaxf(m, tm);
+    if (mn == -INFINITY) return;  // nothing seen yet (a tile past the vocabulary end)
+    S *= fast_exp2(m - mn);
+    m = mn;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) S += fast_exp2(t[i] - mn);
+  }
+  template <int S_>
+  __device__ void consume(const f32x16_t& acc, int vt) {
+    float u[1][16];
+    this->template get<S_>(u);
+    fold<false>(u[0], acc, vt);
+  }
+  __device__ void tail(const f32x16_t& acc, int vt) {
+    float u[16];
+    load16_masked(u, this->urow, vt * kVTile + 16 * this->half, this->V, 0.0f);
+    fold<true>(u, acc, vt);
+  }
+};
+
+// T1: per (row group, slab) records {m, S, t_x} of every row, planes
+// [slab][3][n_rows] in the workspace.
+template <class W, int kKs, bool kVec>
+__global__ __launch_bounds__(kTvThreads) void train_draft_lse(VerifyArgs a, VerifyPlan p,
+                                                              TrainPlan tp) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int half = lane >> 5, col = lane & 31;
+  int slab, grp;
+  slab_group(blockIdx.x, p.n_slabs, p.n_groups, slab, grp);
+  int t_begin, t_end;
+  slab_range(slab, p.n_slabs, p.n_vtiles, t_begin, t_end);
+
+  const int row = (grp * kTvWaves + wave) * kVTile + col;
+  const int rowc = row < p.n_rows ? row : p.n_rows - 1;
+  const int r = rowc / a.gamma, k = rowc % a.gamma + 1;
+  typename W::frag_t e[W::kMaxKs];
+  DraftLseEpi<kVec> epi;
+  epi.urow = a.U + (size_t)rowc * a.V;
+  epi.V = a.V;
+  epi.half = half;
+  epi.patch = reinterpret_cast<float*>(lds + stream_lds_bytes<W>(a.rank, kVerifyDist)) +
+              wave * kPatchFloats;
+  if constexpr (kVec) {
+    const int row0 = (grp * kTvWaves + wave) * kVTile;
+    epi.rows.base[0] = a.U;
+    epi.rows.init([&](int j) {
+      const int rr = row0 + j < p.n_rows ? row0 + j : p.n_rows - 1;
+      return (size_t)rr * a.V;
+    });
+  }
+  epi.kscale = a.kscale;
+  epi.m = -INFINITY;
+  epi.S = 0.0f;
+  epi.tx = -INFINITY;
+  epi.xs = a.x[(size_t)r * (a.gamma + 1) + k];
+  auto gather = [&](typename W::frag_t(&ef)[W::kMaxKs]) {
+    load_e_frags<W, kKs>(ef, a.W1, a.x[(size_t)r * (a.gamma + 1) + (k - 1)], a.rank, a.V, half);
+  };
+  shared_a_stream<W, kKs, kVerifyDist, kTvThreads>(a.W2t, a.V, a.rank, t_begin, t_end, e, gather,
+                                                   lds, epi);
+  // both halves of the tile: merge (half 0 first), lane half 0 stores
+  const float m_o = __shfl_xor(epi.m, 32), s_o = __shfl_xor(epi.S, 32);
+  const float t_o = __shfl_xor(epi.tx, 32);
+  const float M = fmaxf(epi.m, m_o);
+  const float Ssum = (M == -INFINITY) ? 0.0f
+                                      : (half == 0 ? epi.S * fast_exp2(epi.m - M) + s_o * fast_exp2(m_o - M)
+                                                   : s_o * fast_exp2(m_o - M) + epi.S * fast_exp2(epi.m - M));
+  const float tx = fmaxf(epi.tx, t_o);
+  if (half == 0 && row < p.n_rows) {
+    float* rec = reinterpret_cast<float*>(a.ws + tp.off_dlse) + (size_t)slab * 3 * p.n_rows + row;
+    rec[0] = M;
+    rec[p.n_rows] = Ssum;
+    rec[2 * (size_t)p.n_rows] = tx;
+  }
+}
+
+// T2: per row, the draft normaliser and log2 p_d(x*) from the slab records
+// (slab order), the target normaliser from V1's chunks, and a cleared c*
+// accumulator.
+__global__ __launch_bounds__(256) void train_merge(VerifyArgs a, VerifyPlan p, TrainPlan tp) {
+  const int row = blockIdx.x * 256 + threadIdx.x;
+  if (row >= p.n_rows) return;
+  const float* rec = reinterpret_cast<const float*>(a.ws + tp.off_dlse);
+  float m = -INFINITY, S = 0.0f, tx = -INFINITY;
+  for (int sl = 0; sl < p.n_slabs; ++sl) {
+    const float* q = rec + (size_t)sl * 3 * p.n_rows + row;
+    const float ms = q[0], ss = q[p.n_rows];
+    const float M = fmaxf(m, ms);
+    S = (M == -INFINITY) ? 0.0f : S * fast_exp2(m - M) + ss * fast_exp2(ms - M);
+    m = M;
+    tx = fmaxf(tx, q[2 * (size_t)p.n_rows]);
+  }
+  const float l2 = m + log2f(S);
+  reinterpret_cast<float*>(a.ws + tp.off_lse_d)[row] = l2 * kLn2;  // natural log, as V3 expects
+  reinterpret_cast<float*>(a.ws + tp.off_ce)[row] = (l2 - tx) * kLn2;
+  const float* lp = reinterpret_cast<const float*>(a.ws + p.off_lsepart) + (size_t)row * p.lse_chunks * 2;
+  float mt = -INFINITY, St = 0.0f;
+  for (int c = 0; c < p.lse_chunks; ++c) {
+    const float mc = lp[2 * c], sc = lp[2 * c + 1];
+    const float M = fmaxf(mt, mc);
+    St = (M == -INFINITY) ? 0.0f : St * fast_exp2(mt - M) + sc * fast_exp2(mc - M);
+    mt = M;
+  }
+  reinterpret_cast<float*>(a.ws + p.off_lse_t)[row] = mt + log2f(St);
+  reinterpret_cast<unsigned long long*>(a.ws + p.off_tv)[row] = 0ull;
+}
+
+// T3: per-position terms (ce, tv, conf, c) and the weighted sums in a fixed
+// order: thread t folds rows t, t + 1024, ... in order (fp64), then a tree.
+constexpr int kAssembleThreads = 1024;
+
+__global__ __launch_bounds__(kAssembleThreads) void train_assemble(VerifyArgs a, VerifyPlan p,
+                                                                   TrainPlan tp, TrainArgs ta) {
+  __shared__ double red[3][kAssembleThreads];
+  const int t = threadIdx.x;
+  double s_ce = 0.0, s_tv = 0.0, s_cf = 0.0;
+  for (int row = t; row < p.n_rows; row += kAssembleThreads) {
+    const int k = row % a.gamma + 1;
+    const double wk = exp(-(double)(k - 1) / (double)ta.lambda);
+    const float ce = reinterpret_cast<const float*>(a.ws + tp.off_ce)[row];
+    const unsigned long long q = reinterpret_cast<const unsigned long long*>(a.ws + p.off_tv)[row];
+    const double tv = (double)q / kFix;
+    const double cs = 1.0 - 0.5 * tv;
+    const double c = (double)ta.c[row];
+    const double cf = -(cs * log(c) + (1.0 - cs) * log1p(-c));
+    float* out = ta.terms + (size_t)row * 4;
+    out[0] = ce;
+    out[1] = (float)tv;
+    out[2] = (float)cf;
+    out[3] = (float)c;
+    s_ce += wk * (double)ce;
+    s_tv += wk * tv;
+    s_cf += wk * cf;
+  }
+  red[0][t] = s_ce;
+  red[1][t] = s_tv;
+  red[2][t] = s_cf;
+  __syncthreads();
+  for (int s = kAssembleThreads / 2; s > 0; s >>= 1) {
+    if (t < s)
+      for (int j = 0; j < 3; ++j) red[j][t] += red[j][t + s];
+    __syncthreads();
+  }
+  if (t == 0) {
+    ta.sums[0] = red[0][0];
+    ta.sums[1] = red[1][0];
+    ta.sums[2] = red[2][0];
+    ta.sums[3] = (double)ta.alpha_ce * red[0][0] + (double)ta.alpha_tv * red[1][0] +
+                 (double)ta.alpha_conf * red[2][0];
+  }
+}
+
+template <class W, int kKs, bool kVec>
+hipError_t launch_train_passes(const VerifyArgs& a, const VerifyPlan& p, const TrainPlan& tp,
+                               hipStream_t stream) {
+  const size_t lds = stream_lds_bytes<W>(a.rank, kVerifyDist) + kWaves * kPatchFloats * 4;
+  hipLaunchKernelGGL((train_draft_lse<W, kKs, kVec>), dim3(p.n_slabs * p.n_groups),
+                     dim3(kTvThreads), lds, stream, a, p, tp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(train_merge, dim3((p.n_rows + 255) / 256), dim3(256), 0, stream, a, p, tp);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((verify_tv<W, kKs, kVec>), dim3(p.n_slabs * p.n_groups), dim3(kTvThreads),
+                     lds, stream, a, p);
+  return hipGetLastError();
+}
+
+template <class W, bool kVec>
+hipError_t launch_train_w(const VerifyArgs& a, const VerifyPlan& p, const TrainPlan& tp,
+                          hipStream_t stream) {
+  if (W::kKStep * W::kMaxKs == a.rank) return launch_train_passes<W, W::kMaxKs, kVec>(a, p, tp, stream);
+  return launch_train_passes<W, 0, kVec>(a, p, tp, stream);
+}
+
 template <class W, int kKs, bool kVec>
 hipError_t launch_passes(const VerifyArgs& a, const VerifyPlan& p, hipStream_t stream) {
   // W2t slots, then one LDS patch per wave (U and target rows pass in turn).
@@ -557,6 +787,41 @@ VerifyPlan plan_verify(int R, int V, int gamma) {
   off = align256(off + (size_t)p.n_rows * p.lse_chunks * 8);
   p.ws_bytes = off;
   return p;
+}
+
+TrainPlan plan_train(int R, int V, int gamma) {
+  const VerifyPlan p = plan_verify(R, V, gamma);
+  TrainPlan t{};
+  size_t off = p.ws_bytes;
+  t.off_dlse = off;
+  off = align256(off + (size_t)p.n_slabs * 3 * p.n_rows * 4);
+  t.off_lse_d = off;
+  off = align256(off + (size_t)p.n_rows * 4);
+  t.off_ce = off;
+  off = align256(off + (size_t)p.n_rows * 4);
+  t.off_c = off;
+  off = align256(off + (size_t)p.n_rows * 4);
+  t.off_surv = off;
+  off = align256(off + (size_t)p.n_rows * 4);
+  t.ws_bytes = off;
+  return t;
+}
+
+hipError_t launch_train(const VerifyArgs& va, const TrainArgs& ta, const VerifyPlan& p,
+                        const TrainPlan& tp, hipStream_t stream) {
+  VerifyArgs a = va;
+  a.lse_d = reinterpret_cast<const float*>(a.ws + tp.off_lse_d);
+  const bool vec = (a.V % 4) == 0;
+  const dim3 g1(p.lse_chunks, p.n_rows);
+  if (vec) hipLaunchKernelGGL((verify_target_lse<false, true>), g1, dim3(256), 0, stream, a, p);
+  else hipLaunchKernelGGL((verify_target_lse<false, false>), g1, dim3(256), 0, stream, a, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.bf16) e = vec ? launch_train_w<WBf16, true>(a, p, tp, stream) : launch_train_w<WBf16, false>(a, p, tp, stream);
+  else e = vec ? launch_train_w<WF32, true>(a, p, tp, stream) : launch_train_w<WF32, false>(a, p, tp, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(train_assemble, dim3(1), dim3(kAssembleThreads), 0, stream, a, p, tp, ta);
+  return hipGetLastError();
 }
 
 hipError_t launch_verify(const VerifyArgs& a, const VerifyPlan& p, hipStream_t stream) {

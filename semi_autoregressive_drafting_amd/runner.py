@@ -138,3 +138,20 @@ def full_round(di: DeviceInputs, buf: RoundBuffers, temperature: float, seed: in
     schedule(di, buf)
     if di.target is not None:
         verify(di, buf, temperature, seed)
+
+
+def train_loss(di: DeviceInputs, x_star: torch.Tensor, temperature: float = 1.0,
+               lam: float | None = None, alphas=(0.1, 0.9, 1.0), ws: torch.Tensor | None = None):
+    """The training losses of the workload's blocks with x_star [R][gamma+1] as
+    the target block; returns (terms [R][gamma][4], sums [4]) on the device."""
+    R, g = di.R, di.gamma
+    lam = float(g) if lam is None else lam
+    if ws is None:
+        nb = D.dspark_workspace_bytes(D.DSPARK_OP_TRAIN_LOSS, R, di.V, di.rank, g)
+        ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=di.U.device)
+    terms = torch.empty((R, g, 4), dtype=torch.float32, device=di.U.device)
+    sums = torch.empty(4, dtype=torch.float64, device=di.U.device)
+    D.dspark_train_loss(R, di.V, di.rank, di.d, g, di.dt, di.W1, di.W2t, di.U, di.h, di.w,
+                        di.target, x_star, temperature, lam, alphas[0], alphas[1], alphas[2],
+                        terms, sums, ws)
+    return terms, sums

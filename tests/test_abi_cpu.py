@@ -137,6 +137,29 @@ def test_draft_block_phases_validation():
     assert f(*bad, 3, None) == D.DSPARK_ERR_NULL
 
 
+def test_train_loss_validation():
+    f = D.load().dspark_train_loss
+    base = [4, 1024, 32, 64, 4, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1.0, 4.0, 0.1, 0.9,
+            1.0, FAKE, FAKE, FAKE, 1 << 30, None]
+    def call(**kw):
+        a = list(base)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a5=7) == D.DSPARK_ERR_DTYPE
+    assert call(a12=None) == D.DSPARK_ERR_NULL          # x_star
+    assert call(a19=None) == D.DSPARK_ERR_NULL          # sums
+    assert call(a0=0) == D.DSPARK_ERR_SHAPE
+    assert call(a3=0) == D.DSPARK_ERR_SHAPE             # d
+    assert call(a2=30) == D.DSPARK_ERR_SHAPE            # fp32 rank not a multiple of 4
+    assert call(a13=0.0) == D.DSPARK_ERR_VALUE          # T = 0 has no softmax
+    assert call(a14=0.0) == D.DSPARK_ERR_VALUE          # lambda
+    assert call(a15=float("nan")) == D.DSPARK_ERR_VALUE
+    assert call(a21=16) == D.DSPARK_ERR_WORKSPACE
+    assert D.dspark_workspace_bytes(D.DSPARK_OP_TRAIN_LOSS, 4, 1024, 32, 4) > \
+        D.dspark_workspace_bytes(D.DSPARK_OP_VERIFY, 4, 1024, 32, 4)
+
+
 def test_schedule_async_validation():
     f = D.load().dspark_schedule_async
     assert f(4, 4, None, FAKE, FAKE, 21, FAKE, FAKE, FAKE, None) == D.DSPARK_ERR_NULL
