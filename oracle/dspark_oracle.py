@@ -36,6 +36,8 @@ What each function follows, and what pins it (tests/test_oracle_pins.py):
   train_losses                 P1 §5 (L_CE, L_TV, L_conf, w_k; P3 defaults).
         Pinned by the two-token closed form, identical-law special cases,
         invariance to a constant logit shift, and the default weights.
+  train_loss_grads             derivatives of train_losses.  Pinned by central
+        finite differences of train_losses in every input it differentiates.
   verify                       P1 §3.1 eq. c*, standard rejection sampling (P1
         intro and §2.2; P3 問題定義).  Pinned by the c* = overlap identity,
         special cases, losslessness (output law = p_t) and acceptance-rate = c*.
@@ -364,6 +366,54 @@ def train_losses(U, target, W1, W2t, h, w, x_star, T=1.0, lam=None, alphas=LOSS_
     total = alphas[0] * sums["ce"] + alphas[1] * sums["tv"] + alphas[2] * sums["conf"]
     return {"ce": ce, "tv": tv, "conf": cf, "c": c, "c_star": cs, "w": wk, "sums": sums,
             "total": total}
+
+
+def train_loss_grads(U, target, W1, W2t, h, w, x_star, T=1.0, lam=None, alphas=LOSS_ALPHAS):
+    """Gradients of L = a_CE L_CE + a_TV L_TV + a_conf L_conf  [P1 §5] (c* held
+    constant, as a target), written out from the definitions:
+
+      dL/dz_v  = (w_k / T) [a_CE (p_d(v) - 1[v = x*_k]) + a_TV p_d(v) (s_v - mu)],
+                 s_v = sign(p_d(v) - p_t(v)) (0 on equality), mu = sum_u s_u p_d(u);
+                 z = U + e.W2, so dL/dU = dL/dz and dL/dbias = dL/dz;
+      dL/dl    = w_k a_conf (c - c*) for the confidence logit l = w.[h; e];
+      dL/dW2t  = sum_rows dL/dz (outer) e;   dL/de = dL/dz . W2t + dL/dl w[d:];
+      dL/dh    = dL/dl w[:d];                dL/dw = sum_rows dL/dl [h; e].
+
+    Returns dU [n, gamma, V], dW2t [V, rank], dE [n, gamma, rank] (with respect
+    to the gathered rows e = W1[x*_{k-1}]; dW1 is their scatter-add), dh
+    [n, gamma, d], dw [d + rank] and dl [n, gamma]."""
+    U = np.asarray(U, dtype=np.float64)
+    n, g, V = U.shape
+    lam = g if lam is None else lam
+    wk = position_weights(g, lam)
+    x_star = np.asarray(x_star, dtype=np.int64)
+    w = np.asarray(w, dtype=np.float64)
+    d = np.asarray(h).shape[-1]
+    rank = W1.shape[1]
+    dU = np.zeros((n, g, V)); dW2t = np.zeros((V, rank)); dE = np.zeros((n, g, rank))
+    dh = np.zeros((n, g, d)); dw = np.zeros(d + rank); dl = np.zeros((n, g))
+    a_ce, a_tv, a_cf = alphas
+    for i in range(n):
+        e = W1[x_star[i, :g]]                                       # [g, rank]
+        z_d = np.asarray(U[i]) + e @ W2t.T
+        p_d = np.exp(log_softmax_rows(z_d / T)[0])
+        p_t = np.exp(log_softmax_rows(np.asarray(target[i], dtype=np.float64) / T)[0])
+        sgn = np.sign(p_d - p_t)
+        mu = (sgn * p_d).sum(axis=-1, keepdims=True)
+        onehot = np.zeros_like(p_d)
+        onehot[np.arange(g), x_star[i, 1:]] = 1.0
+        gz = (wk[:, None] / T) * (a_ce * (p_d - onehot) + a_tv * p_d * (sgn - mu))
+        dU[i] = gz
+        dW2t += gz.T @ e
+        hi = as_f64(h[i])
+        c = sigmoid(hi @ w[:d] + e @ w[d:])
+        cs = 1.0 - 0.5 * np.abs(p_d - p_t).sum(axis=-1)
+        dl[i] = wk * a_cf * (c - cs)
+        dE[i] = gz @ W2t + dl[i][:, None] * w[d:]
+        dh[i] = dl[i][:, None] * w[:d]
+        dw[:d] += dl[i] @ hi
+        dw[d:] += dl[i] @ e
+    return {"dU": dU, "dW2t": dW2t, "dE": dE, "dh": dh, "dw": dw, "dl": dl}
 
 
 def schedule_exhaustive(a, sps):

@@ -593,6 +593,53 @@ def test_train_loss_weights():
     assert r["w"][0] == 1.0
 
 
+def test_train_loss_grads_match_finite_differences():
+    """Every gradient of train_loss_grads against central differences of the
+    total loss of train_losses (c* held constant: the differences are taken
+    with the TV-derived target frozen, by perturbing only where the oracle
+    treats it as a constant -- U, W2t, the gathered rows, h and w)."""
+    rng = np.random.default_rng(31)
+    n, g, V, rank, d = 2, 3, 7, 3, 4
+    W1 = rng.normal(0, 0.6, (V, rank)); W2t = rng.normal(0, 0.6, (V, rank))
+    U = rng.normal(0, 1.0, (n, g, V)); target = rng.normal(0, 1.0, (n, g, V))
+    h = rng.normal(0, 1.0, (n, g, d)); w = rng.normal(0, 0.4, d + rank)
+    x = rng.integers(0, V, (n, g + 1))
+    x[:, :g] = np.arange(n * g).reshape(n, g) % V    # distinct Markov inputs per row of a request
+    T, lam = 0.9, 2.5
+    G = O.train_loss_grads(U, target, W1, W2t, h, w, x, T=T, lam=lam)
+    c_star = O.train_losses(U, target, W1, W2t, h, w, x, T=T, lam=lam)["c_star"]
+
+    def total(U_, W1_, W2t_, h_, w_):
+        """L with c* frozen at its unperturbed value."""
+        r = O.train_losses(U_, target, W1_, W2t_, h_, w_, x, T=T, lam=lam)
+        wk = r["w"]
+        cf = -(c_star * np.log(r["c"]) + (1 - c_star) * np.log1p(-r["c"]))
+        a = O.LOSS_ALPHAS
+        return (a[0] * (r["ce"] * wk).sum() + a[1] * (r["tv"] * wk).sum() + a[2] * (cf * wk).sum())
+
+    eps = 1e-6
+    def fd(arr, idx, fn):
+        arr[idx] += eps; hi = fn()
+        arr[idx] -= 2 * eps; lo = fn()
+        arr[idx] += eps
+        return (hi - lo) / (2 * eps)
+
+    for idx in [(0, 0, 0), (1, 2, 5), (0, 1, 3)]:
+        assert fd(U, idx, lambda: total(U, W1, W2t, h, w)) == pytest.approx(G["dU"][idx], abs=1e-7)
+    for idx in [(0, 0), (4, 2), (6, 1)]:
+        assert fd(W2t, idx, lambda: total(U, W1, W2t, h, w)) == pytest.approx(G["dW2t"][idx], abs=1e-7)
+    for idx in [(0, 0, 1), (1, 2, 3)]:
+        assert fd(h, idx, lambda: total(U, W1, W2t, h, w)) == pytest.approx(G["dh"][idx], abs=1e-7)
+    for j in [0, 3, 5]:
+        assert fd(w, (j,), lambda: total(U, W1, W2t, h, w)) == pytest.approx(G["dw"][j], abs=1e-7)
+    # the gathered row e of (request 1, position 2) is W1[x[1, 1]], used by that row only
+    r_, k_ = 1, 2
+    tok = x[r_, k_ - 1]
+    for j in range(rank):
+        assert fd(W1, (tok, j), lambda: total(U, W1, W2t, h, w)) == pytest.approx(
+            G["dE"][r_, k_ - 1, j], abs=1e-7)
+
+
 # ---------------------------------------------------------------------------
 # Verification
 # ---------------------------------------------------------------------------
