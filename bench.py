@@ -41,6 +41,25 @@ def verify_bytes(R, V, rank, gamma):
     return 2 * R * gamma * V * 4 + R * gamma * V * 4 + rank * V * 2
 
 
+def train_loss_bytes(R, V, rank, d, gamma):
+    """Algorithmic bytes of the forward training losses: the target logits
+    twice (normaliser pass, then the TV pass), U and W2 twice (draft
+    normaliser pass, then the TV pass) and h once."""
+    n = R * gamma
+    return 2 * n * V * 4 + 2 * n * V * 4 + 2 * rank * V * 2 + n * d * 2
+
+
+def train_grad_bytes(R, V, rank, d, gamma):
+    """Algorithmic bytes of the losses with every gradient: the forward
+    passes; the logit-gradient pass (target, U and W2 read, dU written); the
+    two contractions (dU read by each, W2 transposed once, dW2t written);
+    dW1 cleared and the confidence-head inputs read once more."""
+    n = R * gamma
+    fwd = train_loss_bytes(R, V, rank, d, gamma)
+    return (fwd + (2 * n * V * 4 + rank * V * 2 + n * V * 4) + 2 * n * V * 4
+            + 2 * rank * V * 2 + V * rank * 4 + V * rank * 4 + n * d * 2)
+
+
 PROFILE_COUNTERS = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                                 "dspark_round_qwen3_8b_r128_g16_hbm_counters.txt")
 
@@ -257,6 +276,48 @@ def main():
             torch.cuda.synchronize()
             async_us.append(ea[0].elapsed_time(ea[1]) * 1e3)
 
+    # The forward training losses on the same block, the drafted tokens
+    # standing in for the target block x* (anchor in column 0).
+    train, train_grad = None, None
+    if extras:
+        x_star = buf.x.clone()
+        tws = torch.empty(D.dspark_workspace_bytes(D.DSPARK_OP_TRAIN_LOSS, R, V, rank, g),
+                          dtype=torch.uint8, device="cuda")
+        for _ in range(2):
+            runner.train_loss(di, x_star, ws=tws)
+        et = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        t_us = []
+        for s in range(nb):
+            et[0].record()
+            _, tsums = runner.train_loss(di, x_star, ws=tws)
+            et[1].record()
+            torch.cuda.synchronize()
+            t_us.append(et[0].elapsed_time(et[1]) * 1e3)
+        tb = train_loss_bytes(R, V, rank, d, g)
+        t_med = float(np.median(t_us))
+        train = {"us": round(t_med, 2), "bytes": tb, "achieved_GBps": round(tb / (t_med * 1e-6) / 1e9, 1),
+                 "weighted_sums": [round(float(v), 6) for v in tsums.cpu().tolist()]}
+        del tws
+        # losses and every gradient
+        gws = torch.empty(D.dspark_workspace_bytes(D.DSPARK_OP_TRAIN_GRAD, R, V, rank, g),
+                          dtype=torch.uint8, device="cuda")
+        for _ in range(2):
+            gout = runner.train_loss_grad(di, x_star, ws=gws)
+        del gout
+        g_us = []
+        for s in range(nb):
+            et[0].record()
+            gout = runner.train_loss_grad(di, x_star, ws=gws)
+            et[1].record()
+            torch.cuda.synchronize()
+            g_us.append(et[0].elapsed_time(et[1]) * 1e3)
+            del gout
+        gb = train_grad_bytes(R, V, rank, d, g)
+        g_med = float(np.median(g_us))
+        train_grad = {"us": round(g_med, 2), "bytes": gb,
+                      "achieved_GBps": round(gb / (g_med * 1e-6) / 1e9, 1)}
+        del gws
+
     # Cold draft step: a 512 MB write evicts W2 and U from L2 and the MALL
     # before each timed step (dspark_draft_step = step kernel + merge).
     cold, warm = [float("nan")], [float("nan")]
@@ -366,6 +427,8 @@ def main():
                          "schedule_async": round(float(np.median(async_us)), 2),
                          "verify": round(float(ver_ms.mean()) * 1e3, 2),
                          "round_wall": round(ms_round * 1e3, 2)},
+        "train_loss_forward": train,
+        "train_loss_with_gradients": train_grad,
         "verify_roofline": {"bytes": vb, "achieved_GBps": round(vb / (ver_ms.mean() * 1e-3) / 1e9, 1)},
         "draft_only_tokens_per_s": round(R * g / (block_ms.mean() * 1e-3), 1),
         "budget_last_round": int(buf.budget.item()),

@@ -74,7 +74,8 @@ typedef enum {
   DSPARK_OP_DRAFT_STEP = 0,
   DSPARK_OP_SCHEDULE = 1,
   DSPARK_OP_VERIFY = 2,
-  DSPARK_OP_TRAIN_LOSS = 3
+  DSPARK_OP_TRAIN_LOSS = 3,
+  DSPARK_OP_TRAIN_GRAD = 4  /* rank must be a multiple of 32 (<= 256), else 0 */
 } dspark_op;
 
 /* Bytes of device workspace entry point `op` needs for these sizes (0 if the
@@ -241,7 +242,7 @@ dspark_status dspark_verify(int R, int V, int rank, int gamma, int dt, const voi
  * w fp32 [d + rank]); x_star int32 [R][gamma+1].  T > 0 and lambda > 0 (else
  * DSPARK_ERR_VALUE).  ws: dspark_workspace_bytes(DSPARK_OP_TRAIN_LOSS, ...)
  * bytes; its contents need no initialisation.  Forward only: the gradients
- * are not computed here.
+ * come from dspark_train_loss_grad.
  */
 dspark_status dspark_train_loss(int R, int V, int rank, int d, int gamma, int dt, const void* W1,
                                 const void* W2t, const float* U, const void* h, const float* w,
@@ -249,6 +250,37 @@ dspark_status dspark_train_loss(int R, int V, int rank, int d, int gamma, int dt
                                 float lambda, float alpha_ce, float alpha_tv, float alpha_conf,
                                 float* terms, double* sums, void* ws, size_t ws_bytes,
                                 dspark_stream_t stream);
+
+/*
+ * dspark_train_loss plus the gradients of the weighted total
+ * L = alpha_ce sum w_k ce + alpha_tv sum w_k tv + alpha_conf sum w_k conf
+ * [P1 §5 训练目标], c* held constant (it is a label).  With z = U + e . W2,
+ * s_v = sign(p_d(v) - p_t(v)) (0 where equal) and mu = sum_v s_v p_d(v):
+ *   dU[r][k-1][v] = dL/dz = (w_k / T) (alpha_ce (p_d(v) - [v = x*_k])
+ *                                      + alpha_tv p_d(v) (s_v - mu))
+ *   dl            = w_k alpha_conf (c - c*)       (confidence logit)
+ *   dE            = dU . W2t + dl w[d:]           (gathered rows e)
+ *   dW1[t]        = sum of the dE rows whose Markov input x*[r][k-1] is t
+ *                   (0 for tokens that do not occur)
+ *   dW2t          = dU^T . E                     fp32 [V][rank]
+ *   dh            = dl w[:d]                      fp32 [R][gamma][d]
+ *   dw            = sum over positions of dl [h; e]  fp32 [d + rank]
+ * Outputs (device, fp32, overwritten): dU [R][gamma][V] (16-byte aligned when
+ * V % 4 == 0), dW1 [V][rank], dW2t [V][rank], dh, dw.  The two contractions
+ * round dU to bf16 as an MFMA operand and accumulate in fp32; every other
+ * step is fp32 or fp64.  All sums run in a fixed order (bit-reproducible).
+ * Requires dt = DSPARK_BF16 (else DSPARK_ERR_DTYPE) and rank a multiple of 32
+ * (else DSPARK_ERR_SHAPE).  ws: dspark_workspace_bytes(DSPARK_OP_TRAIN_GRAD,
+ * ...) bytes (it holds a transposed copy of W2t); no initialisation needed.
+ */
+dspark_status dspark_train_loss_grad(int R, int V, int rank, int d, int gamma, int dt,
+                                     const void* W1, const void* W2t, const float* U,
+                                     const void* h, const float* w, const float* target,
+                                     const int32_t* x_star, float temperature, float lambda,
+                                     float alpha_ce, float alpha_tv, float alpha_conf,
+                                     float* terms, double* sums, float* dU, float* dW1,
+                                     float* dW2t, float* dh, float* dw, void* ws,
+                                     size_t ws_bytes, dspark_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -381,7 +381,10 @@ def train_loss_grads(U, target, W1, W2t, h, w, x_star, T=1.0, lam=None, alphas=L
 
     Returns dU [n, gamma, V], dW2t [V, rank], dE [n, gamma, rank] (with respect
     to the gathered rows e = W1[x*_{k-1}]; dW1 is their scatter-add), dh
-    [n, gamma, d], dw [d + rank] and dl [n, gamma]."""
+    [n, gamma, d], dw [d + rank] and dl [n, gamma]; and, for checking a
+    computation that decides the signs s_v in another precision, p_d, p_t
+    [n, gamma, V], mu [n, gamma] and the factors w_k a_CE / T, w_k a_TV / T
+    [gamma] of the two terms of dU."""
     U = np.asarray(U, dtype=np.float64)
     n, g, V = U.shape
     lam = g if lam is None else lam
@@ -392,6 +395,7 @@ def train_loss_grads(U, target, W1, W2t, h, w, x_star, T=1.0, lam=None, alphas=L
     rank = W1.shape[1]
     dU = np.zeros((n, g, V)); dW2t = np.zeros((V, rank)); dE = np.zeros((n, g, rank))
     dh = np.zeros((n, g, d)); dw = np.zeros(d + rank); dl = np.zeros((n, g))
+    P_d = np.zeros((n, g, V)); P_t = np.zeros((n, g, V)); MU = np.zeros((n, g))
     a_ce, a_tv, a_cf = alphas
     for i in range(n):
         e = W1[x_star[i, :g]]                                       # [g, rank]
@@ -400,6 +404,7 @@ def train_loss_grads(U, target, W1, W2t, h, w, x_star, T=1.0, lam=None, alphas=L
         p_t = np.exp(log_softmax_rows(np.asarray(target[i], dtype=np.float64) / T)[0])
         sgn = np.sign(p_d - p_t)
         mu = (sgn * p_d).sum(axis=-1, keepdims=True)
+        P_d[i], P_t[i], MU[i] = p_d, p_t, mu[:, 0]
         onehot = np.zeros_like(p_d)
         onehot[np.arange(g), x_star[i, 1:]] = 1.0
         gz = (wk[:, None] / T) * (a_ce * (p_d - onehot) + a_tv * p_d * (sgn - mu))
@@ -413,7 +418,9 @@ def train_loss_grads(U, target, W1, W2t, h, w, x_star, T=1.0, lam=None, alphas=L
         dh[i] = dl[i][:, None] * w[:d]
         dw[:d] += dl[i] @ hi
         dw[d:] += dl[i] @ e
-    return {"dU": dU, "dW2t": dW2t, "dE": dE, "dh": dh, "dw": dw, "dl": dl}
+    return {"dU": dU, "dW2t": dW2t, "dE": dE, "dh": dh, "dw": dw, "dl": dl,
+            "p_d": P_d, "p_t": P_t, "mu": MU,
+            "f_ce": wk * a_ce / T, "f_tv": wk * a_tv / T}
 
 
 def schedule_exhaustive(a, sps):

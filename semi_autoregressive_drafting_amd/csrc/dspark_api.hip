@@ -55,13 +55,15 @@ const char* dspark_status_string(int status) {
 }
 
 size_t dspark_workspace_bytes(int op, int R, int V, int rank, int gamma) {
-  (void)rank;
   if (R < 1 || R > kMaxR || V < 2 || V > kMaxV || gamma < 1 || gamma > kMaxGamma) return 0;
   switch (op) {
     case DSPARK_OP_DRAFT_STEP: return plan_draft_step(R, V, gamma).ws_bytes;
     case DSPARK_OP_SCHEDULE: return 0;
     case DSPARK_OP_VERIFY: return plan_verify(R, V, gamma).ws_bytes;
-    case DSPARK_OP_TRAIN_LOSS: return plan_train(R, V, gamma).ws_bytes;
+    case DSPARK_OP_TRAIN_LOSS: return plan_train(R, V, rank < 1 ? 1 : rank, gamma).ws_bytes;
+    case DSPARK_OP_TRAIN_GRAD:
+      if (rank < 32 || rank > 256 || rank % 32 != 0) return 0;
+      return plan_train(R, V, rank, gamma).ws_grad_bytes;
     default: return 0;
   }
 }
@@ -279,29 +281,43 @@ dspark_status dspark_verify(int R, int V, int rank, int gamma, int dt, const voi
   return DSPARK_OK;
 }
 
-dspark_status dspark_train_loss(int R, int V, int rank, int d, int gamma, int dt, const void* W1,
-                                const void* W2t, const float* U, const void* h, const float* w,
-                                const float* target, const int32_t* x_star, float temperature,
-                                float lambda, float alpha_ce, float alpha_tv, float alpha_conf,
-                                float* terms, double* sums, void* ws, size_t ws_bytes,
-                                dspark_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Losses, and with g (non-null) every gradient.
+struct GradOut {
+  float *dU, *dW1, *dW2t, *dh, *dw;
+};
+
+dspark_status train_common(int R, int V, int rank, int d, int gamma, int dt, const void* W1,
+                           const void* W2t, const float* U, const void* h, const float* w,
+                           const float* target, const int32_t* x_star, float temperature,
+                           float lambda, float alpha_ce, float alpha_tv, float alpha_conf,
+                           float* terms, double* sums, const GradOut* g, void* ws,
+                           size_t ws_bytes, dspark_stream_t stream) {
   if (dt != DSPARK_F32 && dt != DSPARK_BF16) return DSPARK_ERR_DTYPE;
   if (!W1 || !W2t || !U || !h || !w || !target || !x_star || !terms || !sums)
     return DSPARK_ERR_NULL;
+  if (g && (!g->dU || !g->dW1 || !g->dW2t || !g->dh || !g->dw)) return DSPARK_ERR_NULL;
   if (R < 1 || R > kMaxR || V < 2 || V > kMaxV || gamma < 1 || gamma > kMaxGamma || d < 1 ||
       d > kMaxD)
     return DSPARK_ERR_SHAPE;
   dspark_status s = check_rank(dt, rank);
   if (s != DSPARK_OK) return s;
+  if (g && dt != DSPARK_BF16) return DSPARK_ERR_DTYPE;  // gradients: bf16 weights only
+  if (g && rank % 32 != 0) return DSPARK_ERR_SHAPE;
   if (!aligned16(W1) || !aligned16(W2t) ||
-      ((V % 4) == 0 && (!aligned16(U) || !aligned16(target))))
+      ((V % 4) == 0 && (!aligned16(U) || !aligned16(target))) ||
+      (g && (V % 4) == 0 && !aligned16(g->dU)))
     return DSPARK_ERR_SHAPE;
   if (!(temperature > 0.0f) || isinf(temperature) || !(lambda > 0.0f) || isinf(lambda) ||
       !isfinite(alpha_ce) || !isfinite(alpha_tv) || !isfinite(alpha_conf))
     return DSPARK_ERR_VALUE;
   const VerifyPlan plan = plan_verify(R, V, gamma);
-  const TrainPlan tplan = plan_train(R, V, gamma);
-  if (!ws || ws_bytes < tplan.ws_bytes || !aligned16(ws)) return DSPARK_ERR_WORKSPACE;
+  const TrainPlan tplan = plan_train(R, V, rank, gamma);
+  const size_t need = g ? tplan.ws_grad_bytes : tplan.ws_bytes;
+  if (!ws || ws_bytes < need || !aligned16(ws)) return DSPARK_ERR_WORKSPACE;
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   unsigned char* wsb = static_cast<unsigned char*>(ws);
   float* c = reinterpret_cast<float*>(wsb + tplan.off_c);
@@ -324,9 +340,56 @@ dspark_status dspark_train_loss(int R, int V, int rank, int d, int gamma, int dt
   args.x = x_star;
   args.kscale = kscale_of(temperature);
   args.ws = wsb;
-  TrainArgs targs{lambda, alpha_ce, alpha_tv, alpha_conf, c, terms, sums};
+  TrainArgs targs{};
+  targs.lambda = lambda;
+  targs.alpha_ce = alpha_ce;
+  targs.alpha_tv = alpha_tv;
+  targs.alpha_conf = alpha_conf;
+  targs.inv_t = 1.0f / temperature;
+  targs.c = c;
+  targs.terms = terms;
+  targs.sums = sums;
+  targs.d = d;
+  targs.h = h;
+  targs.w = w;
+  if (g) {
+    targs.dU = g->dU;
+    targs.dW1 = g->dW1;
+    targs.dW2t = g->dW2t;
+    targs.dh = g->dh;
+    targs.dw = g->dw;
+  }
   if (launch_train(args, targs, plan, tplan, st) != hipSuccess) return DSPARK_ERR_LAUNCH;
   return DSPARK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dspark_status dspark_train_loss(int R, int V, int rank, int d, int gamma, int dt, const void* W1,
+                                const void* W2t, const float* U, const void* h, const float* w,
+                                const float* target, const int32_t* x_star, float temperature,
+                                float lambda, float alpha_ce, float alpha_tv, float alpha_conf,
+                                float* terms, double* sums, void* ws, size_t ws_bytes,
+                                dspark_stream_t stream) {
+  return train_common(R, V, rank, d, gamma, dt, W1, W2t, U, h, w, target, x_star, temperature,
+                      lambda, alpha_ce, alpha_tv, alpha_conf, terms, sums, nullptr, ws, ws_bytes,
+                      stream);
+}
+
+dspark_status dspark_train_loss_grad(int R, int V, int rank, int d, int gamma, int dt,
+                                     const void* W1, const void* W2t, const float* U,
+                                     const void* h, const float* w, const float* target,
+                                     const int32_t* x_star, float temperature, float lambda,
+                                     float alpha_ce, float alpha_tv, float alpha_conf,
+                                     float* terms, double* sums, float* dU, float* dW1,
+                                     float* dW2t, float* dh, float* dw, void* ws,
+                                     size_t ws_bytes, dspark_stream_t stream) {
+  const GradOut g{dU, dW1, dW2t, dh, dw};
+  return train_common(R, V, rank, d, gamma, dt, W1, W2t, U, h, w, target, x_star, temperature,
+                      lambda, alpha_ce, alpha_tv, alpha_conf, terms, sums, &g, ws, ws_bytes,
+                      stream);
 }
 
 }  // extern "C"

@@ -126,18 +126,44 @@ struct TrainPlan {
   size_t off_ce;    // -log p_d(x*) [n_rows]
   size_t off_c;     // confidence c_k [n_rows]
   size_t off_surv;  // survival products of the confidence head (unused) [n_rows]
-  size_t ws_bytes;
+  size_t off_mu;    // sum_v sign(p_d - p_t) p_d, signed 2^-40 fixed point [n_rows] (u64)
+  size_t off_dl;    // dL / d(confidence logit) [n_rows]
+  size_t ws_bytes;  // end of the forward workspace
+  // gradients (train_grad.hip), after the forward workspace
+  int n_pad;        // rows rounded up to 128
+  int vp;           // vocabulary rounded up to 64
+  int e_groups;     // 128-row groups of the dE contraction
+  int e_slabs;      // vocabulary slabs of the dE contraction
+  size_t off_w2;    // W2t transposed, bf16 [rank][vp]
+  size_t off_et;    // gathered W1 rows transposed, bf16 [rank][n_pad]
+  size_t off_dep;   // dE slab partials [e_slabs][n_pad][rank]
+  size_t off_de;    // dE [n_rows][rank]
+  size_t ws_grad_bytes;
 };
 
 struct TrainArgs {
   float lambda, alpha_ce, alpha_tv, alpha_conf;
+  float inv_t;     // 1 / T
   const float* c;  // confidence c_k [n_rows], computed before the assembly
   float* terms;    // [n_rows][4]: ce, tv, conf, c
   double* sums;    // [4]: sum_k w_k ce, sum w_k tv, sum w_k conf, total
+  // gradients (all null for the losses alone); bf16 weights and h only
+  int d;
+  const void* h;
+  const float* w;
+  float* dU;       // [n_rows][V]
+  float* dW1;      // [V][rank]
+  float* dW2t;     // [V][rank]
+  float* dh;       // [n_rows][d]
+  float* dw;       // [d + rank]
 };
 
-TrainPlan plan_train(int R, int V, int gamma);
+TrainPlan plan_train(int R, int V, int rank, int gamma);
+// Losses; with ta.dU set also every gradient (then ws holds ws_grad_bytes).
 hipError_t launch_train(const VerifyArgs& a, const TrainArgs& ta, const VerifyPlan& plan,
                         const TrainPlan& tp, hipStream_t stream);
+// The gradients behind the logits, after dU and dl are in place (train_grad.hip).
+hipError_t launch_train_grad_rest(const VerifyArgs& a, const TrainArgs& ta, const VerifyPlan& plan,
+                                  const TrainPlan& tp, hipStream_t stream);
 
 }  // namespace dspark

@@ -297,10 +297,12 @@ struct UTRows {
   }
 };
 
-template <bool kVec>
+// kMu also accumulates sum_v sign(p_d - p_t) p_d, the row constant of the
+// derivative of the TV term (training gradients).
+template <bool kVec, bool kMu>
 struct TvEpi : UTRows<kVec> {
   float kscale, lse2_d, lse2_t;
-  float sabs;
+  float sabs, smu;
 
   template <bool kMasked>
   __device__ __forceinline__ void fold(const float (&ut)[2][16], const f32x16_t& acc, int vt) {
@@ -310,7 +312,9 @@ struct TvEpi : UTRows<kVec> {
       const float pd = fast_exp2(fmaf(ut[0][i] + acc[i], kscale, -lse2_d));
       const float pt = fast_exp2(fmaf(ut[1][i], kscale, -lse2_t));
       const float d = fabsf(pd - pt);
-      sabs += (!kMasked || vb + i < this->V) ? d : 0.0f;
+      const bool in = !kMasked || vb + i < this->V;
+      sabs += in ? d : 0.0f;
+      if constexpr (kMu) smu += (in && pd != pt) ? (pd > pt ? pd : -pd) : 0.0f;
     }
   }
   template <int S>
@@ -326,8 +330,9 @@ struct TvEpi : UTRows<kVec> {
   }
 };
 
-template <class W, int kKs, bool kVec>
-__global__ __launch_bounds__(kTvThreads) void verify_tv(VerifyArgs a, VerifyPlan p) {
+template <class W, int kKs, bool kVec, bool kMu = false>
+__global__ __launch_bounds__(kTvThreads) void verify_tv(VerifyArgs a, VerifyPlan p,
+                                                        unsigned long long* mu_acc = nullptr) {
   extern __shared__ __align__(16) unsigned char lds[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = lane >> 5, col = lane & 31;
@@ -340,7 +345,7 @@ __global__ __launch_bounds__(kTvThreads) void verify_tv(VerifyArgs a, VerifyPlan
   const int rowc = row < p.n_rows ? row : p.n_rows - 1;
   const int r = rowc / a.gamma, k = rowc % a.gamma + 1;
   typename W::frag_t e[W::kMaxKs];
-  TvEpi<kVec> epi;
+  TvEpi<kVec, kMu> epi;
   epi.urow = a.U + (size_t)rowc * a.V;
   epi.trow = a.target + (size_t)rowc * a.V;
   epi.V = a.V;
@@ -360,6 +365,7 @@ __global__ __launch_bounds__(kTvThreads) void verify_tv(VerifyArgs a, VerifyPlan
   epi.lse2_d = a.lse_d[rowc] * kLog2e;
   epi.lse2_t = reinterpret_cast<const float*>(a.ws + p.off_lse_t)[rowc];
   epi.sabs = 0.0f;
+  epi.smu = 0.0f;
   auto gather = [&](typename W::frag_t(&ef)[W::kMaxKs]) {
     load_e_frags<W, kKs>(ef, a.W1, a.x[(size_t)r * (a.gamma + 1) + (k - 1)], a.rank, a.V, half);
   };
@@ -370,6 +376,12 @@ __global__ __launch_bounds__(kTvThreads) void verify_tv(VerifyArgs a, VerifyPlan
   if (half == 0 && row < p.n_rows) {
     const unsigned long long q = (unsigned long long)llrint((double)s * kFix);
     atomicAdd(reinterpret_cast<unsigned long long*>(a.ws + p.off_tv) + row, q);
+  }
+  if constexpr (kMu) {
+    // signed fixed point in two's complement: the wrapping 64-bit sum is exact
+    const float sm = epi.smu + __shfl_xor(epi.smu, 32);
+    if (half == 0 && row < p.n_rows)
+      atomicAdd(mu_acc + row, (unsigned long long)llrint((double)sm * kFix));
   }
 }
 
@@ -655,6 +667,7 @@ __global__ __launch_bounds__(256) void train_merge(VerifyArgs a, VerifyPlan p, T
   }
   reinterpret_cast<float*>(a.ws + p.off_lse_t)[row] = mt + log2f(St);
   reinterpret_cast<unsigned long long*>(a.ws + p.off_tv)[row] = 0ull;
+  reinterpret_cast<unsigned long long*>(a.ws + tp.off_mu)[row] = 0ull;
 }
 
 // T3: per-position terms (ce, tv, conf, c) and the weighted sums in a fixed
@@ -680,6 +693,8 @@ __global__ __launch_bounds__(kAssembleThreads) void train_assemble(VerifyArgs a,
     out[1] = (float)tv;
     out[2] = (float)cf;
     out[3] = (float)c;
+    // derivative of the weighted total with respect to the confidence logit
+    reinterpret_cast<float*>(a.ws + tp.off_dl)[row] = (float)(wk * (double)ta.alpha_conf * (c - cs));
     s_ce += wk * (double)ce;
     s_tv += wk * tv;
     s_cf += wk * cf;
@@ -702,9 +717,109 @@ __global__ __launch_bounds__(kAssembleThreads) void train_assemble(VerifyArgs a,
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// G1: gradient of the weighted total with respect to the logits z = U + e.W2
+// (dL/dU, equal to dL/dz), one pass over W2t, U and the target logits:
+//   dz_v = (w_k / T) [a_CE (p_d(v) - [v = x*_k]) + a_TV p_d(v) (s_v - mu)],
+//   s_v = sign(p_d(v) - p_t(v)), mu = sum_u s_u p_d(u) (from V3 with kMu),
+// with c* held constant [P1 "DSpark" §5; the TV term is differentiated as the
+// L1 norm, whose sign is 0 where p_d = p_t].
+// ---------------------------------------------------------------------------
+template <bool kVec>
+struct GradEpi : UTRows<kVec> {
+  float kscale, lse2_d, lse2_t, mu, sce, stv;
+  int xs;
+  float* drow;  // dU row of the lane; null for a row past the end
+
+  template <bool kMasked>
+  __device__ __forceinline__ void fold(const float (&ut)[2][16], const f32x16_t& acc, int vt) {
+    const int vb = vt * kVTile + 16 * this->half;
+    float g[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float pd = fast_exp2(fmaf(ut[0][i] + acc[i], kscale, -lse2_d));
+      const float pt = fast_exp2(fmaf(ut[1][i], kscale, -lse2_t));
+      const float sg = pd > pt ? 1.0f : (pd < pt ? -1.0f : 0.0f);
+      const float hot = (vb + i == xs) ? 1.0f : 0.0f;
+      g[i] = fmaf(sce, pd - hot, stv * pd * (sg - mu));
+    }
+    if (drow == nullptr) return;
+    if constexpr (kVec && !kMasked) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<f32x4_t*>(drow + vb + 4 * q) = f32x4_t{g[4 * q], g[4 * q + 1], g[4 * q + 2], g[4 * q + 3]};
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (!kMasked || vb + i < this->V) drow[vb + i] = g[i];
+    }
+  }
+  template <int S>
+  __device__ void consume(const f32x16_t& acc, int vt) {
+    float ut[2][16];
+    this->template get<S>(ut);
+    fold<false>(ut, acc, vt);
+  }
+  __device__ void tail(const f32x16_t& acc, int vt) {
+    float ut[2][16];
+    this->get_tail(ut, vt);
+    fold<true>(ut, acc, vt);
+  }
+};
+
+template <class W, int kKs, bool kVec>
+__global__ __launch_bounds__(kTvThreads) void train_grad_logits(VerifyArgs a, VerifyPlan p,
+                                                                TrainPlan tp, TrainArgs ta) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int half = lane >> 5, col = lane & 31;
+  int slab, grp;
+  slab_group(blockIdx.x, p.n_slabs, p.n_groups, slab, grp);
+  int t_begin, t_end;
+  slab_range(slab, p.n_slabs, p.n_vtiles, t_begin, t_end);
+
+  const int row = (grp * kTvWaves + wave) * kVTile + col;
+  const int rowc = row < p.n_rows ? row : p.n_rows - 1;
+  const int r = rowc / a.gamma, k = rowc % a.gamma + 1;
+  typename W::frag_t e[W::kMaxKs];
+  GradEpi<kVec> epi;
+  epi.urow = a.U + (size_t)rowc * a.V;
+  epi.trow = a.target + (size_t)rowc * a.V;
+  epi.V = a.V;
+  epi.half = half;
+  epi.patch = reinterpret_cast<float*>(lds + stream_lds_bytes<W>(a.rank, kVerifyDist)) +
+              wave * kPatchFloats;
+  if constexpr (kVec) {
+    const int row0 = (grp * kTvWaves + wave) * kVTile;
+    epi.rows.base[0] = a.U;
+    epi.rows.base[1] = a.target;
+    epi.rows.init([&](int j) {
+      const int rr = row0 + j < p.n_rows ? row0 + j : p.n_rows - 1;
+      return (size_t)rr * a.V;
+    });
+  }
+  // the same p_d and p_t expressions as V3, so the signs match its mu
+  epi.kscale = a.kscale;
+  epi.lse2_d = a.lse_d[rowc] * kLog2e;
+  epi.lse2_t = reinterpret_cast<const float*>(a.ws + p.off_lse_t)[rowc];
+  const long long mq = (long long)reinterpret_cast<const unsigned long long*>(a.ws + tp.off_mu)[rowc];
+  epi.mu = (float)((double)mq / kFix);
+  const double wk = exp(-(double)(k - 1) / (double)ta.lambda) * (double)ta.inv_t;
+  epi.sce = (float)(wk * (double)ta.alpha_ce);
+  epi.stv = (float)(wk * (double)ta.alpha_tv);
+  epi.xs = a.x[(size_t)r * (a.gamma + 1) + k];
+  epi.drow = row < p.n_rows ? ta.dU + (size_t)row * a.V : nullptr;
+  auto gather = [&](typename W::frag_t(&ef)[W::kMaxKs]) {
+    load_e_frags<W, kKs>(ef, a.W1, a.x[(size_t)r * (a.gamma + 1) + (k - 1)], a.rank, a.V, half);
+  };
+  shared_a_stream<W, kKs, kVerifyDist, kTvThreads>(a.W2t, a.V, a.rank, t_begin, t_end, e, gather,
+                                                   lds, epi);
+}
+
 template <class W, int kKs, bool kVec>
 hipError_t launch_train_passes(const VerifyArgs& a, const VerifyPlan& p, const TrainPlan& tp,
-                               hipStream_t stream) {
+                               bool mu, hipStream_t stream) {
   const size_t lds = stream_lds_bytes<W>(a.rank, kVerifyDist) + kWaves * kPatchFloats * 4;
   hipLaunchKernelGGL((train_draft_lse<W, kKs, kVec>), dim3(p.n_slabs * p.n_groups),
                      dim3(kTvThreads), lds, stream, a, p, tp);
@@ -713,16 +828,38 @@ hipError_t launch_train_passes(const VerifyArgs& a, const VerifyPlan& p, const T
   hipLaunchKernelGGL(train_merge, dim3((p.n_rows + 255) / 256), dim3(256), 0, stream, a, p, tp);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((verify_tv<W, kKs, kVec>), dim3(p.n_slabs * p.n_groups), dim3(kTvThreads),
-                     lds, stream, a, p);
+  if (mu)
+    hipLaunchKernelGGL((verify_tv<W, kKs, kVec, true>), dim3(p.n_slabs * p.n_groups),
+                       dim3(kTvThreads), lds, stream, a, p,
+                       reinterpret_cast<unsigned long long*>(a.ws + tp.off_mu));
+  else
+    hipLaunchKernelGGL((verify_tv<W, kKs, kVec>), dim3(p.n_slabs * p.n_groups), dim3(kTvThreads),
+                       lds, stream, a, p, nullptr);
+  return hipGetLastError();
+}
+
+template <class W, int kKs, bool kVec>
+hipError_t launch_grad_pass(const VerifyArgs& a, const VerifyPlan& p, const TrainPlan& tp,
+                            const TrainArgs& ta, hipStream_t stream) {
+  const size_t lds = stream_lds_bytes<W>(a.rank, kVerifyDist) + kWaves * kPatchFloats * 4;
+  hipLaunchKernelGGL((train_grad_logits<W, kKs, kVec>), dim3(p.n_slabs * p.n_groups),
+                     dim3(kTvThreads), lds, stream, a, p, tp, ta);
   return hipGetLastError();
 }
 
 template <class W, bool kVec>
 hipError_t launch_train_w(const VerifyArgs& a, const VerifyPlan& p, const TrainPlan& tp,
-                          hipStream_t stream) {
-  if (W::kKStep * W::kMaxKs == a.rank) return launch_train_passes<W, W::kMaxKs, kVec>(a, p, tp, stream);
-  return launch_train_passes<W, 0, kVec>(a, p, tp, stream);
+                          bool mu, hipStream_t stream) {
+  if (W::kKStep * W::kMaxKs == a.rank) return launch_train_passes<W, W::kMaxKs, kVec>(a, p, tp, mu, stream);
+  return launch_train_passes<W, 0, kVec>(a, p, tp, mu, stream);
+}
+
+template <bool kVec>
+hipError_t launch_grad_w(const VerifyArgs& a, const VerifyPlan& p, const TrainPlan& tp,
+                         const TrainArgs& ta, hipStream_t stream) {
+  using W = WBf16;
+  if (W::kKStep * W::kMaxKs == a.rank) return launch_grad_pass<W, W::kMaxKs, kVec>(a, p, tp, ta, stream);
+  return launch_grad_pass<W, 0, kVec>(a, p, tp, ta, stream);
 }
 
 template <class W, int kKs, bool kVec>
@@ -730,7 +867,7 @@ hipError_t launch_passes(const VerifyArgs& a, const VerifyPlan& p, hipStream_t s
   // W2t slots, then one LDS patch per wave (U and target rows pass in turn).
   const size_t lds = stream_lds_bytes<W>(a.rank, kVerifyDist) + kWaves * kPatchFloats * 4;
   hipLaunchKernelGGL((verify_tv<W, kKs, kVec>), dim3(p.n_slabs * p.n_groups), dim3(kTvThreads),
-                     lds, stream, a, p);
+                     lds, stream, a, p, nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((verify_sample<W, kKs, kVec>), dim3(p.s_slabs * p.s_groups),
@@ -789,7 +926,7 @@ VerifyPlan plan_verify(int R, int V, int gamma) {
   return p;
 }
 
-TrainPlan plan_train(int R, int V, int gamma) {
+TrainPlan plan_train(int R, int V, int rank, int gamma) {
   const VerifyPlan p = plan_verify(R, V, gamma);
   TrainPlan t{};
   size_t off = p.ws_bytes;
@@ -803,7 +940,29 @@ TrainPlan plan_train(int R, int V, int gamma) {
   off = align256(off + (size_t)p.n_rows * 4);
   t.off_surv = off;
   off = align256(off + (size_t)p.n_rows * 4);
+  t.off_mu = off;
+  off = align256(off + (size_t)p.n_rows * 8);
+  t.off_dl = off;
+  off = align256(off + (size_t)p.n_rows * 4);
   t.ws_bytes = off;
+  // gradients
+  t.n_pad = (p.n_rows + 127) / 128 * 128;
+  t.vp = (V + 63) / 64 * 64;
+  t.e_groups = t.n_pad / 128;
+  const int chunks = t.vp / 64;
+  int slabs = kResidentWgs / t.e_groups;
+  if (slabs < 1) slabs = 1;
+  if (slabs > chunks) slabs = chunks;
+  t.e_slabs = slabs;
+  t.off_w2 = off;
+  off = align256(off + (size_t)rank * t.vp * 2);
+  t.off_et = off;
+  off = align256(off + (size_t)rank * t.n_pad * 2);
+  t.off_dep = off;
+  off = align256(off + (size_t)t.e_slabs * t.n_pad * rank * 4);
+  t.off_de = off;
+  off = align256(off + (size_t)p.n_rows * rank * 4);
+  t.ws_grad_bytes = off;
   return t;
 }
 
@@ -812,16 +971,21 @@ hipError_t launch_train(const VerifyArgs& va, const TrainArgs& ta, const VerifyP
   VerifyArgs a = va;
   a.lse_d = reinterpret_cast<const float*>(a.ws + tp.off_lse_d);
   const bool vec = (a.V % 4) == 0;
+  const bool grad = ta.dU != nullptr;
   const dim3 g1(p.lse_chunks, p.n_rows);
   if (vec) hipLaunchKernelGGL((verify_target_lse<false, true>), g1, dim3(256), 0, stream, a, p);
   else hipLaunchKernelGGL((verify_target_lse<false, false>), g1, dim3(256), 0, stream, a, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.bf16) e = vec ? launch_train_w<WBf16, true>(a, p, tp, stream) : launch_train_w<WBf16, false>(a, p, tp, stream);
-  else e = vec ? launch_train_w<WF32, true>(a, p, tp, stream) : launch_train_w<WF32, false>(a, p, tp, stream);
+  if (a.bf16) e = vec ? launch_train_w<WBf16, true>(a, p, tp, grad, stream) : launch_train_w<WBf16, false>(a, p, tp, grad, stream);
+  else e = vec ? launch_train_w<WF32, true>(a, p, tp, grad, stream) : launch_train_w<WF32, false>(a, p, tp, grad, stream);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(train_assemble, dim3(1), dim3(kAssembleThreads), 0, stream, a, p, tp, ta);
-  return hipGetLastError();
+  if ((e = hipGetLastError()) != hipSuccess || !grad) return e;
+  if (!a.bf16) return hipErrorInvalidValue;
+  e = vec ? launch_grad_w<true>(a, p, tp, ta, stream) : launch_grad_w<false>(a, p, tp, ta, stream);
+  if (e != hipSuccess) return e;
+  return launch_train_grad_rest(a, ta, p, tp, stream);
 }
 
 hipError_t launch_verify(const VerifyArgs& a, const VerifyPlan& p, hipStream_t stream) {

@@ -17,12 +17,13 @@ LIB_PATH = os.path.join(_HERE, "libdspark.so")
 DSPARK_OK, DSPARK_ERR_NULL, DSPARK_ERR_SHAPE, DSPARK_ERR_DTYPE, DSPARK_ERR_VALUE, \
     DSPARK_ERR_WORKSPACE, DSPARK_ERR_LAUNCH = range(7)
 DSPARK_F32, DSPARK_BF16 = 0, 1
-DSPARK_OP_DRAFT_STEP, DSPARK_OP_SCHEDULE, DSPARK_OP_VERIFY, DSPARK_OP_TRAIN_LOSS = 0, 1, 2, 3
+DSPARK_OP_DRAFT_STEP, DSPARK_OP_SCHEDULE, DSPARK_OP_VERIFY, DSPARK_OP_TRAIN_LOSS, \
+    DSPARK_OP_TRAIN_GRAD = 0, 1, 2, 3, 4
 DSPARK_PHASE_STEPS, DSPARK_PHASE_MERGE = 1, 2
 
 EXPORTS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_draft_step",
            "dspark_draft_block", "dspark_draft_block_phases", "dspark_confidence", "dspark_schedule", "dspark_schedule_async",
-           "dspark_verify", "dspark_train_loss")
+           "dspark_verify", "dspark_train_loss", "dspark_train_loss_grad")
 
 _lib = None
 
@@ -68,6 +69,9 @@ def load():
     L.dspark_train_loss.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, F, F, F, F, F,
                                     P, P, P, SZ, P]
     L.dspark_train_loss.restype = I
+    L.dspark_train_loss_grad.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, F, F, F, F, F,
+                                         P, P, P, P, P, P, P, P, SZ, P]
+    L.dspark_train_loss_grad.restype = I
     _lib = L
     return L
 
@@ -172,3 +176,14 @@ def dspark_train_loss(R, V, rank, d, gamma, dt, W1, W2t, U, h, w, target, x_star
           _ptr(w), _ptr(target), _ptr(x_star), float(temperature), float(lam), float(alpha_ce),
           float(alpha_tv), float(alpha_conf), _ptr(terms), _ptr(sums), _ptr(ws), int(ws_bytes),
           _stream(stream))
+
+
+def dspark_train_loss_grad(R, V, rank, d, gamma, dt, W1, W2t, U, h, w, target, x_star,
+                           temperature, lam, alpha_ce, alpha_tv, alpha_conf, terms, sums, dU, dW1,
+                           dW2t, dh, dw, ws, ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _call("dspark_train_loss_grad", R, V, rank, d, gamma, dt, _ptr(W1), _ptr(W2t), _ptr(U),
+          _ptr(h), _ptr(w), _ptr(target), _ptr(x_star), float(temperature), float(lam),
+          float(alpha_ce), float(alpha_tv), float(alpha_conf), _ptr(terms), _ptr(sums), _ptr(dU),
+          _ptr(dW1), _ptr(dW2t), _ptr(dh), _ptr(dw), _ptr(ws), int(ws_bytes), _stream(stream))

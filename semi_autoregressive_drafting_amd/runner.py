@@ -155,3 +155,28 @@ def train_loss(di: DeviceInputs, x_star: torch.Tensor, temperature: float = 1.0,
                         di.target, x_star, temperature, lam, alphas[0], alphas[1], alphas[2],
                         terms, sums, ws)
     return terms, sums
+
+
+def train_loss_grad(di: DeviceInputs, x_star: torch.Tensor, temperature: float = 1.0,
+                    lam: float | None = None, alphas=(0.1, 0.9, 1.0), ws: torch.Tensor | None = None):
+    """The training losses and their gradients; returns a dict of device tensors
+    terms [R][gamma][4], sums [4], dU [R][gamma][V], dW1 [V][rank],
+    dW2t [V][rank], dh [R][gamma][d], dw [d + rank]."""
+    R, g, V, rank, d = di.R, di.gamma, di.V, di.rank, di.d
+    lam = float(g) if lam is None else lam
+    dev = di.U.device
+    if ws is None:
+        nb = D.dspark_workspace_bytes(D.DSPARK_OP_TRAIN_GRAD, R, V, rank, g)
+        ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
+    out = {"terms": torch.empty((R, g, 4), dtype=torch.float32, device=dev),
+           "sums": torch.empty(4, dtype=torch.float64, device=dev),
+           "dU": torch.empty((R, g, V), dtype=torch.float32, device=dev),
+           "dW1": torch.empty((V, rank), dtype=torch.float32, device=dev),
+           "dW2t": torch.empty((V, rank), dtype=torch.float32, device=dev),
+           "dh": torch.empty((R, g, d), dtype=torch.float32, device=dev),
+           "dw": torch.empty(d + rank, dtype=torch.float32, device=dev)}
+    D.dspark_train_loss_grad(R, V, rank, d, g, di.dt, di.W1, di.W2t, di.U, di.h, di.w, di.target,
+                             x_star, temperature, lam, alphas[0], alphas[1], alphas[2],
+                             out["terms"], out["sums"], out["dU"], out["dW1"], out["dW2t"],
+                             out["dh"], out["dw"], ws)
+    return out

@@ -160,6 +160,32 @@ def test_train_loss_validation():
         D.dspark_workspace_bytes(D.DSPARK_OP_VERIFY, 4, 1024, 32, 4)
 
 
+def test_train_loss_grad_validation():
+    f = D.load().dspark_train_loss_grad
+    # bf16, rank 64; outputs terms, sums, dU, dW1, dW2t, dh, dw at 18 .. 24
+    base = [4, 1024, 64, 64, 4, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1.0, 4.0, 0.1, 0.9,
+            1.0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 34, None]
+    def call(**kw):
+        a = list(base)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a5=0) == D.DSPARK_ERR_DTYPE             # gradients need bf16 weights
+    assert call(a5=7) == D.DSPARK_ERR_DTYPE
+    for i in range(20, 25):                             # every gradient output is required
+        assert call(**{f"a{i}": None}) == D.DSPARK_ERR_NULL
+    assert call(a2=48) == D.DSPARK_ERR_SHAPE            # rank not a multiple of 32
+    assert call(a2=288) == D.DSPARK_ERR_SHAPE           # rank above 256
+    assert call(a13=0.0) == D.DSPARK_ERR_VALUE
+    need = D.dspark_workspace_bytes(D.DSPARK_OP_TRAIN_GRAD, 4, 1024, 64, 4)
+    assert need > D.dspark_workspace_bytes(D.DSPARK_OP_TRAIN_LOSS, 4, 1024, 64, 4)
+    assert call(a26=need - 1) == D.DSPARK_ERR_WORKSPACE
+    assert D.dspark_workspace_bytes(D.DSPARK_OP_TRAIN_GRAD, 4, 1024, 48, 4) == 0
+    # the transposed W2t copy dominates at full size: rank x V bf16
+    big = D.dspark_workspace_bytes(D.DSPARK_OP_TRAIN_GRAD, 128, 151936, 256, 16)
+    assert 256 * 151936 * 2 < big < 1 << 30
+
+
 def test_schedule_async_validation():
     f = D.load().dspark_schedule_async
     assert f(4, 4, None, FAKE, FAKE, 21, FAKE, FAKE, FAKE, None) == D.DSPARK_ERR_NULL
