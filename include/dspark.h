@@ -271,7 +271,8 @@ dspark_status dspark_train_loss(int R, int V, int rank, int d, int gamma, int dt
  * step is fp32 or fp64.  All sums run in a fixed order (bit-reproducible).
  * Requires dt = DSPARK_BF16 (else DSPARK_ERR_DTYPE) and rank a multiple of 32
  * (else DSPARK_ERR_SHAPE).  ws: dspark_workspace_bytes(DSPARK_OP_TRAIN_GRAD,
- * ...) bytes (it holds a transposed copy of W2t); no initialisation needed.
+ * ...) bytes (it holds a transposed copy of W2t; sized for any d up to 65536); no
+ * initialisation needed.
  */
 dspark_status dspark_train_loss_grad(int R, int V, int rank, int d, int gamma, int dt,
                                      const void* W1, const void* W2t, const float* U,

@@ -60,10 +60,11 @@ size_t dspark_workspace_bytes(int op, int R, int V, int rank, int gamma) {
     case DSPARK_OP_DRAFT_STEP: return plan_draft_step(R, V, gamma).ws_bytes;
     case DSPARK_OP_SCHEDULE: return 0;
     case DSPARK_OP_VERIFY: return plan_verify(R, V, gamma).ws_bytes;
-    case DSPARK_OP_TRAIN_LOSS: return plan_train(R, V, rank < 1 ? 1 : rank, gamma).ws_bytes;
+    case DSPARK_OP_TRAIN_LOSS: return plan_train(R, V, rank < 1 ? 1 : rank, 1, gamma).ws_bytes;
     case DSPARK_OP_TRAIN_GRAD:
       if (rank < 32 || rank > 256 || rank % 32 != 0) return 0;
-      return plan_train(R, V, rank, gamma).ws_grad_bytes;
+      // sized for the largest d (the dw partials sit at the end of the layout)
+      return plan_train(R, V, rank, kMaxD, gamma).ws_grad_bytes;
     default: return 0;
   }
 }
@@ -315,7 +316,7 @@ dspark_status train_common(int R, int V, int rank, int d, int gamma, int dt, con
       !isfinite(alpha_ce) || !isfinite(alpha_tv) || !isfinite(alpha_conf))
     return DSPARK_ERR_VALUE;
   const VerifyPlan plan = plan_verify(R, V, gamma);
-  const TrainPlan tplan = plan_train(R, V, rank, gamma);
+  const TrainPlan tplan = plan_train(R, V, rank, d, gamma);
   const size_t need = g ? tplan.ws_grad_bytes : tplan.ws_bytes;
   if (!ws || ws_bytes < need || !aligned16(ws)) return DSPARK_ERR_WORKSPACE;
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);

@@ -138,6 +138,7 @@ struct TrainPlan {
   size_t off_et;    // gathered W1 rows transposed, bf16 [rank][n_pad]
   size_t off_dep;   // dE slab partials [e_slabs][n_pad][rank]
   size_t off_de;    // dE [n_rows][rank]
+  size_t off_dwp;   // dw partial sums over row ranges, fp64 [16][d + rank]
   size_t ws_grad_bytes;
 };
 
@@ -158,7 +159,7 @@ struct TrainArgs {
   float* dw;       // [d + rank]
 };
 
-TrainPlan plan_train(int R, int V, int rank, int gamma);
+TrainPlan plan_train(int R, int V, int rank, int d, int gamma);
 // Losses; with ta.dU set also every gradient (then ws holds ws_grad_bytes).
 hipError_t launch_train(const VerifyArgs& a, const TrainArgs& ta, const VerifyPlan& plan,
                         const TrainPlan& tp, hipStream_t stream);

@@ -22,19 +22,19 @@
 //   G4 grad_e_partial   per (128-row group, vocabulary slab) partial dz . W2t
 //   G5 grad_e_reduce    slab partials in slab order + dl w[d:]  -> dE
 //   G6 grad_w2t         per 32-entry vocabulary tile, dz^T . E over all rows
-//   G7 zero_rows / scatter_dw1   dW1 = 0, then per token the sum of its dE
+//   G7 zero_floats / scatter_dw1   dW1 = 0, then per token the sum of its dE
 //      rows in row order (written by the token's first row)
-//   G8 grad_conf        dh, and dw by one thread per column over the rows in
-//      order (fp64)
+//   G8 grad_dh, grad_dw_part / grad_dw_final   dh; dw as fp64 sums over row
+//      ranges, then over the ranges, each in a fixed order
 #include "dspark_kernels.h"
-#include "dspark_device.h"
+#include "mfma_stream.h"
 
 namespace dspark {
 
 namespace {
 
 constexpr int kGThreads = 256;  // 4 waves
-constexpr int kChunk = 64;      // vocabulary entries per K chunk of G4 (4 MFMA K steps)
+constexpr int kChunk = 64;      // K per chunk of the contractions (4 MFMA K steps)
 
 struct GradArgs {
   int V, rank, d, gamma, n_rows, n_pad, vp, e_slabs, e_groups;
@@ -112,15 +112,88 @@ __global__ __launch_bounds__(kGThreads) void gather_et(GradArgs g) {
 }
 
 // ---------------------------------------------------------------------------
-// G4: wave q of workgroup (group, slab) owns rows 32 (4 group + q) .. +31 and
-// all NC 32-wide rank chunks; it walks the slab's vocabulary in chunks of 64
-// (4 K steps of 16).  MFMA operands for K step s (vocabulary v0 = 16 s):
-//   A (rows x K):  lane (m = l%32, half h) holds dz[row m][v0 + 8h .. +7]
-//   B (K x rank):  lane (n = l%32, half h) holds w2[c*32 + n][v0 + 8h .. +7]
-// The dz rows of the next chunk are loaded while the current chunk multiplies.
+// The two contractions share one shape: a workgroup of 4 waves, each wave a
+// 32 x (32 NC) fp32 output block in MFMA accumulators, K walked in chunks of
+// 64.  The B operand of a chunk (rows 0 .. 32 NC - 1 of a bf16 matrix whose
+// rows hold K contiguously) is common to the 4 waves: the workgroup copies it
+// into LDS once (16 bytes per thread and piece, rows padded to 72 elements so
+// that the lanes' 16-byte reads spread over all banks), loading chunk i+1 into
+// registers while chunk i multiplies.  MFMA operands for K step s of a chunk:
+//   A:  lane (m = l%32, half h) holds the 8 values k = 16 s + 8 h .. +7 of row m
+//   B:  lane (n = l%32, half h) holds B-row n at the same 8 k.
 // ---------------------------------------------------------------------------
+constexpr int kLdsRow = kChunk + 8;
+
+template <int NC>
+struct BChunk {
+  static constexpr int kPer = NC;  // 16-byte pieces per thread: NC * 32 rows * 8 pieces / 256
+  u32x4_t reg[kPer];
+  __device__ __forceinline__ void load(const uint16_t* src, int ld, int k0) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int p = threadIdx.x + kGThreads * i, n = p >> 3, q = p & 7;
+      reg[i] = *reinterpret_cast<const u32x4_t*>(src + (size_t)n * ld + k0 + 8 * q);
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* lds) const {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int p = threadIdx.x + kGThreads * i, n = p >> 3, q = p & 7;
+      *reinterpret_cast<u32x4_t*>(lds + n * kLdsRow + 8 * q) = reg[i];
+    }
+  }
+};
+
+template <int NC>
+__device__ __forceinline__ void mma_chunk(f32x16_t (&acc)[NC], const bf16x8_t (&a)[4],
+                                          const uint16_t* lds, int col, int half) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const bf16x8_t af = a[s];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const bf16x8_t bf =
+          *reinterpret_cast<const bf16x8_t*>(lds + (c * 32 + col) * kLdsRow + 16 * s + 8 * half);
+      acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc[c], 0, 0, 0);
+    }
+  }
+}
+
+// Chunk loop over [c_begin, c_end) (at least one chunk).  load_a(a, chunk)
+// fills a wave's A values; B rows come from `bsrc` (row stride ld).
+template <int NC, class LoadA>
+__device__ __forceinline__ void contract(f32x16_t (&acc)[NC], const uint16_t* bsrc, int ld,
+                                         int c_begin, int c_end, uint16_t* lds, LoadA load_a) {
+  const int lane = threadIdx.x & 63;
+  const int half = lane >> 5, col = lane & 31;
+  BChunk<NC> b;
+  float nxt[4][8];
+  bf16x8_t cur[4];  // the current chunk's A operands, rounded to bf16 on arrival
+  b.load(bsrc, ld, c_begin * kChunk);
+  load_a(nxt, c_begin);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) cur[s] = pack_bf16(nxt[s]);
+  b.store(lds);
+  lds_barrier();
+  for (int ch = c_begin; ch < c_end; ++ch) {
+    // the next chunk (the last one again at the end: loads stay unconditional)
+    const int cn = ch + 1 < c_end ? ch + 1 : ch;
+    b.load(bsrc, ld, cn * kChunk);
+    load_a(nxt, cn);
+    mma_chunk<NC>(acc, cur, lds, col, half);
+    lds_barrier();  // every wave is past its reads of this chunk
+    b.store(lds);
+    lds_barrier();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) cur[s] = pack_bf16(nxt[s]);
+  }
+}
+
+// G4: wave q of workgroup (group, slab) owns rows 32 (4 group + q) .. +31;
+// K = the vocabulary of the slab, B = w2.
 template <int NC, bool kVec>
 __global__ __launch_bounds__(kGThreads) void grad_e_partial(GradArgs g) {
+  __shared__ __align__(16) uint16_t lds[NC * 32 * kLdsRow];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = lane >> 5, col = lane & 31;
   const int grp = blockIdx.x % g.e_groups, slab = blockIdx.x / g.e_groups;
@@ -134,9 +207,7 @@ __global__ __launch_bounds__(kGThreads) void grad_e_partial(GradArgs g) {
   f32x16_t acc[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) acc[c] = f32x16_t{};
-
-  // this lane's dz entries of chunk ch: v = 64 ch + 16 s + 8 half + j
-  auto load_chunk = [&](float (&a)[4][8], int ch) {
+  auto load_a = [&](float (&a)[4][8], int ch) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int vb = ch * kChunk + 16 * s + 8 * half;
@@ -154,27 +225,7 @@ __global__ __launch_bounds__(kGThreads) void grad_e_partial(GradArgs g) {
       }
     }
   };
-
-  float cur[4][8], nxt[4][8];
-  if (c_begin < c_end) load_chunk(cur, c_begin);
-  for (int ch = c_begin; ch < c_end; ++ch) {
-    if (ch + 1 < c_end) load_chunk(nxt, ch + 1);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int v0 = ch * kChunk + 16 * s + 8 * half;
-      bf16x8_t b[NC];
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
-        b[c] = *reinterpret_cast<const bf16x8_t*>(g.w2 + (size_t)(c * 32 + col) * g.vp + v0);
-      const bf16x8_t a = pack_bf16(cur[s]);
-#pragma unroll
-      for (int c = 0; c < NC; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[c], acc[c], 0, 0, 0);
-    }
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) cur[s][j] = nxt[s][j];
-  }
+  contract<NC>(acc, g.w2, g.vp, c_begin, c_end, lds, load_a);
   // accumulator i of lane l: row 8 (i/4) + 4 half + i%4 of the tile, rank c*32 + l%32
   float* out = g.dep + (size_t)slab * g.n_pad * g.rank;
 #pragma unroll
@@ -196,19 +247,16 @@ __global__ __launch_bounds__(kGThreads) void grad_e_reduce(GradArgs g) {
   g.de[i] = fmaf(g.dl[row], g.w[g.d + j], s);
 }
 
-// ---------------------------------------------------------------------------
-// G6: wave (workgroup b, wave q) owns vocabulary tile vt = 4 b + q and all NC
-// rank chunks; K runs over the rows in steps of 16:
-//   A (vocab x K):  lane (m = l%32, half h) holds dz[r0 + 8h + j][32 vt + m]
-//   B (K x rank):   lane (n = l%32, half h) holds et[c*32 + n][r0 + 8h .. +7]
-// The dz loads of step r0 + 16 are issued before the MFMAs of step r0.
-// ---------------------------------------------------------------------------
+// G6: wave q of workgroup b owns vocabulary tile vt = 4 b + q (entries past V
+// read as zero and are not written); K = all rows, B = et.  A values are
+// dz[row k][32 vt + m]: 8 rows per lane and step, 128 contiguous bytes per
+// row across the 32 lanes of a half.
 template <int NC>
 __global__ __launch_bounds__(kGThreads) void grad_w2t(GradArgs g) {
+  __shared__ __align__(16) uint16_t lds[NC * 32 * kLdsRow];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = lane >> 5, col = lane & 31;
   const int vt = blockIdx.x * 4 + wave;
-  if (vt * 32 >= g.V) return;  // no barriers below
   const int v = vt * 32 + col;
   const bool vin = v < g.V;
   const float* zcol = g.dz + (vin ? v : 0);
@@ -216,27 +264,16 @@ __global__ __launch_bounds__(kGThreads) void grad_w2t(GradArgs g) {
   f32x16_t acc[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) acc[c] = f32x16_t{};
-  auto load_step = [&](float (&a)[8], int r0) {
+  auto load_a = [&](float (&a)[4][8], int ch) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int rr = r0 + 8 * half + j;
-      a[j] = (vin && rr < g.n_rows) ? zcol[(size_t)rr * g.V] : 0.0f;
-    }
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int rr = ch * kChunk + 16 * s + 8 * half + j;
+        a[s][j] = (vin && rr < g.n_rows) ? zcol[(size_t)rr * g.V] : 0.0f;
+      }
   };
-  float cur[8], nxt[8];
-  load_step(cur, 0);
-  for (int r0 = 0; r0 < g.n_pad; r0 += 16) {
-    if (r0 + 16 < g.n_pad) load_step(nxt, r0 + 16);
-    bf16x8_t b[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
-      b[c] = *reinterpret_cast<const bf16x8_t*>(g.et + (size_t)(c * 32 + col) * g.n_pad + r0 + 8 * half);
-    const bf16x8_t a = pack_bf16(cur);
-#pragma unroll
-    for (int c = 0; c < NC; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[c], acc[c], 0, 0, 0);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) cur[j] = nxt[j];
-  }
+  contract<NC>(acc, g.et, g.n_pad, 0, g.n_pad / kChunk, lds, load_a);
 #pragma unroll
   for (int c = 0; c < NC; ++c)
 #pragma unroll
@@ -253,21 +290,39 @@ __global__ __launch_bounds__(kGThreads) void zero_floats(float* p, size_t n) {
 }
 
 // One workgroup per row; only the first row (in row order) of each token
-// writes, the sum of that token's dE rows taken in row order.
+// writes: the sum of that token's dE rows in row order.  The rows are scanned
+// in windows of 256 (one per thread); a window's matches are compacted into
+// LDS in row order (wave ballots, then wave offsets), and thread j adds their
+// column j.
 __global__ __launch_bounds__(kGThreads) void scatter_dw1(GradArgs g) {
-  const int row = blockIdx.x;
+  __shared__ int list[kGThreads];
+  __shared__ int wcount[4];
+  const int row = blockIdx.x, t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
   const int tok = row_token(g, row);
-  for (int r = 0; r < row; ++r)
-    if (row_token(g, r) == tok) return;  // uniform across the workgroup
-  for (int j = threadIdx.x; j < g.rank; j += kGThreads) {
-    float s = 0.0f;
-    for (int r = row; r < g.n_rows; ++r)
-      if (row_token(g, r) == tok) s += g.de[(size_t)r * g.rank + j];
-    g.dW1[(size_t)tok * g.rank + j] = s;
+  int seen = 0;
+  for (int r = t; r < row; r += kGThreads) seen |= row_token(g, r) == tok;
+  if (__syncthreads_or(seen)) return;  // an earlier row owns this token
+  float s = 0.0f;
+  for (int base = row; base < g.n_rows; base += kGThreads) {
+    const int r = base + t;
+    const bool m = r < g.n_rows && row_token(g, r) == tok;
+    const unsigned long long bal = __ballot(m);
+    if (lane == 0) wcount[wave] = __popcll(bal);
+    __syncthreads();
+    int off = 0;
+    for (int q = 0; q < wave; ++q) off += wcount[q];
+    const int n = wcount[0] + wcount[1] + wcount[2] + wcount[3];
+    if (m) list[off + __popcll(bal & ((1ull << lane) - 1ull))] = r;
+    __syncthreads();
+    if (t < g.rank)
+      for (int i = 0; i < n; ++i) s += g.de[(size_t)list[i] * g.rank + t];
+    __syncthreads();  // list and wcount are rewritten by the next window
   }
+  if (t < g.rank) g.dW1[(size_t)tok * g.rank + t] = s;
 }
 
-// G8: dh = dl w[:d]; dw[j] = sum over rows (in order) of dl [h; e]_j.
+// G8: dh = dl w[:d].
 __global__ __launch_bounds__(kGThreads) void grad_dh(GradArgs g) {
   const size_t i = (size_t)blockIdx.x * kGThreads + threadIdx.x;
   if (i >= (size_t)g.n_rows * g.d) return;
@@ -277,17 +332,39 @@ __global__ __launch_bounds__(kGThreads) void grad_dh(GradArgs g) {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
 
-__global__ __launch_bounds__(kGThreads) void grad_dw(GradArgs g) {
+// dw[j] = sum over rows of dl [h; e]_j in a fixed order: workgroup (b, split)
+// takes columns 64 b .. +63 and rows [split L, (split + 1) L); wave q adds
+// rows q, q + 4, ... of that range in order (fp64), the 4 wave sums are added
+// in wave order into partial[split][j]; grad_dw_final adds the splits in order.
+constexpr int kDwSplits = 16;
+
+__global__ __launch_bounds__(kGThreads) void grad_dw_part(GradArgs g, double* part) {
+  __shared__ double red[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j = blockIdx.x * 64 + lane;
+  const int split = blockIdx.y;
+  const int L = (g.n_rows + kDwSplits - 1) / kDwSplits;
+  const int r0 = split * L, r1 = min(g.n_rows, r0 + L);
+  double s = 0.0;
+  if (j < g.d + g.rank) {
+#pragma unroll 4
+    for (int row = r0 + wave; row < r1; row += 4) {
+      const uint16_t v = j < g.d ? g.h[(size_t)row * g.d + j]
+                                 : g.W1[(size_t)row_token(g, row) * g.rank + (j - g.d)];
+      s += (double)g.dl[row] * (double)bf16_to_f32(v);
+    }
+  }
+  red[wave][lane] = s;
+  __syncthreads();
+  if (wave == 0 && j < g.d + g.rank)
+    part[(size_t)split * (g.d + g.rank) + j] = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+}
+
+__global__ __launch_bounds__(kGThreads) void grad_dw_final(GradArgs g, const double* part) {
   const int j = blockIdx.x * kGThreads + threadIdx.x;
   if (j >= g.d + g.rank) return;
   double s = 0.0;
-  if (j < g.d) {
-    for (int row = 0; row < g.n_rows; ++row)
-      s += (double)g.dl[row] * (double)bf16_to_f32(g.h[(size_t)row * g.d + j]);
-  } else {
-    for (int row = 0; row < g.n_rows; ++row)
-      s += (double)g.dl[row] * (double)bf16_to_f32(g.W1[(size_t)row_token(g, row) * g.rank + (j - g.d)]);
-  }
+  for (int sp = 0; sp < kDwSplits; ++sp) s += part[(size_t)sp * (g.d + g.rank) + j];
   g.dw[j] = (float)s;
 }
 
@@ -366,7 +443,12 @@ hipError_t launch_train_grad_rest(const VerifyArgs& a, const TrainArgs& ta, cons
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(grad_dh, dim3(blocks_for((size_t)g.n_rows * g.d)), dim3(kGThreads), 0, stream, g);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(grad_dw, dim3(blocks_for((size_t)(g.d + g.rank))), dim3(kGThreads), 0, stream, g);
+  double* part = reinterpret_cast<double*>(a.ws + tp.off_dwp);
+  hipLaunchKernelGGL(grad_dw_part, dim3((g.d + g.rank + 63) / 64, kDwSplits), dim3(kGThreads), 0,
+                     stream, g, part);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(grad_dw_final, dim3(blocks_for((size_t)(g.d + g.rank))), dim3(kGThreads), 0,
+                     stream, g, static_cast<const double*>(part));
   return hipGetLastError();
 }
 

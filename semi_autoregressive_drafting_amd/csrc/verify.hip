@@ -926,7 +926,7 @@ VerifyPlan plan_verify(int R, int V, int gamma) {
   return p;
 }
 
-TrainPlan plan_train(int R, int V, int rank, int gamma) {
+TrainPlan plan_train(int R, int V, int rank, int d, int gamma) {
   const VerifyPlan p = plan_verify(R, V, gamma);
   TrainPlan t{};
   size_t off = p.ws_bytes;
@@ -962,6 +962,8 @@ TrainPlan plan_train(int R, int V, int rank, int gamma) {
   off = align256(off + (size_t)t.e_slabs * t.n_pad * rank * 4);
   t.off_de = off;
   off = align256(off + (size_t)p.n_rows * rank * 4);
+  t.off_dwp = off;
+  off = align256(off + (size_t)16 * (d + rank) * 8);
   t.ws_grad_bytes = off;
   return t;
 }
