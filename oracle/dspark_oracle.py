@@ -38,6 +38,12 @@ What each function follows, and what pins it (tests/test_oracle_pins.py):
         invariance to a constant logit shift, and the default weights.
   train_loss_grads             derivatives of train_losses.  Pinned by central
         finite differences of train_losses in every input it differentiates.
+  gru_cell, rnn_draft_round    P1 §2.4 (RNN head; a GRU reading, the pages give
+        no equations).  Pinned by torch.nn.GRUCell (CPU, fp64) on the same
+        weights, by the saturated update gate (z = 1: the state stays 0 and the
+        head reduces to the Markov head with W2 = 0), by the saturated new gate
+        path (z = 0, identity input weights, no recurrence: the Markov head with
+        bias rows bf16(tanh W1[x])), and by the block law summing to 1 at V = 8.
   verify                       P1 §3.1 eq. c*, standard rejection sampling (P1
         intro and §2.2; P3 問題定義).  Pinned by the c* = overlap identity,
         special cases, losslessness (output law = p_t) and acceptance-rate = c*.
@@ -176,16 +182,20 @@ def _top2(keys):
     return x, top1 - top2
 
 
-def draft_step(U_k, W1, W2t, x_prev, T, seed, k, req_ids):
+def draft_step(U_k, W1, W2t, x_prev, T, seed, k, req_ids, E=None):
     """One sequential step k for a set of requests (rows of U_k).
 
     z = U_k + W1[x_{k-1}] W2; for T > 0: s = z/T, lse = log sum_v exp(s_v),
     x_k = lowest v maximising s_v + G_v with G from the DRAFT stream at
     (req, k, v), p_k(x_k) = exp(s_{x_k} - lse).  T = 0: x_k = argmax z, p = 1,
     lse := max z.  Also returns the gap between the top two perturbed scores
-    (natural-log units of s), used to count near ties.
+    (natural-log units of s), used to count near ties.  E, if given, replaces
+    the gathered rows W1[x_{k-1}] (the RNN head's state rows).
     """
-    z = draft_logits(U_k, W1, W2t, x_prev)
+    if E is None:
+        z = draft_logits(U_k, W1, W2t, x_prev)
+    else:
+        z = np.asarray(U_k, dtype=np.float64) + np.asarray(E, dtype=np.float64) @ W2t.T
     n, V = z.shape
     req_ids = np.asarray(req_ids)
     if T > 0:
@@ -517,6 +527,62 @@ def verify(U, Tl, W1, W2t, x, ell, T, seed, req_ids):
 # ----------------------------------------------------------------------------
 # A whole draft round (free running), for the smoke check and the CPU baseline
 # ----------------------------------------------------------------------------
+# ----------------------------------------------------------------------------
+# RNN head  [P1 §2.4; P3 アーキテクチャ]: a block-internal state s_k, updated
+# by a gate from the previous state (the longer prefix), the previous token's
+# embedding and the backbone state h_k.  The pages give no equations; the
+# reading here is a GRU cell in the convention of torch.nn.GRUCell over the
+# input [e_k; h_k], e_k = W1[x_{k-1}], hidden size rank, s_0 = 0, and the
+# state takes the place of e_k in the bias: B_k = bf16(s_k) W2 (the state
+# enters the rank -> vocabulary projection in the weights' precision).
+# ----------------------------------------------------------------------------
+def bf16_round(x):
+    """Round-to-nearest-even to bf16, returned as fp64 (finite inputs)."""
+    f = np.asarray(x, dtype=np.float64).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    return bf16_to_f64(r)
+
+
+def gru_cell(x_in, s, W_ih, W_hh, b_ih, b_hh):
+    """One GRU update, gate order (reset, update, new):
+       r = sigma(W_ir x + b_ir + W_hr s + b_hr)
+       z = sigma(W_iz x + b_iz + W_hz s + b_hz)
+       n = tanh(W_in x + b_in + r * (W_hn s + b_hn))
+       s' = (1 - z) n + z s
+    x_in [n, rank + d], s [n, rank]; W_ih [3 rank, rank + d], W_hh [3 rank, rank]."""
+    H = s.shape[-1]
+    gi = np.asarray(x_in, dtype=np.float64) @ W_ih.T + b_ih
+    gh = np.asarray(s, dtype=np.float64) @ W_hh.T + b_hh
+    r = sigmoid(gi[:, :H] + gh[:, :H])
+    z = sigmoid(gi[:, H:2 * H] + gh[:, H:2 * H])
+    n = np.tanh(gi[:, 2 * H:] + r * gh[:, 2 * H:])
+    return (1.0 - z) * n + z * s
+
+
+def rnn_draft_round(U, h, w, W1, W2t, gru, anchor, T, seed, req_ids):
+    """gamma steps of the RNN head: s_k = gru(s_{k-1}, [W1[x_{k-1}]; h_k]), then the
+    step of draft_step with bf16(s_k) as its rows; confidence and survival as
+    for the Markov head (c_k from h_k and W1[x_{k-1}]).  gru = (W_ih, W_hh,
+    b_ih, b_hh) in fp64.  Also returns the final state s_gamma."""
+    W_ih, W_hh, b_ih, b_hh = gru
+    n, g, V = U.shape
+    rank = W1.shape[1]
+    x = np.empty((n, g + 1), dtype=np.int64)
+    x[:, 0] = anchor
+    p = np.empty((n, g)); lse = np.empty((n, g)); c = np.empty((n, g)); gap = np.empty((n, g))
+    st_ = np.zeros((n, rank))
+    for k in range(1, g + 1):
+        e = W1[x[:, k - 1]]
+        hk = np.asarray(h[:, k - 1], dtype=np.float64)
+        st_ = gru_cell(np.concatenate([e, hk], axis=1), st_, W_ih, W_hh, b_ih, b_hh)
+        step = draft_step(U[:, k - 1], W1, W2t, x[:, k - 1], T, seed, k, req_ids, E=bf16_round(st_))
+        c[:, k - 1] = confidence(hk, w, W1, x[:, k - 1])
+        x[:, k], p[:, k - 1], lse[:, k - 1], gap[:, k - 1] = step["x"], step["p"], step["lse"], step["gap"]
+    return {"x": x, "p": p, "lse": lse, "c": c, "a": survival(c.astype(np.float32)),
+            "state": st_, "gap": gap}
+
+
 def draft_round(U, h, w, W1, W2t, anchor, T, seed, req_ids):
     """gamma sequential steps [P1 §6.2 loop semantics: prev = sampled token],
     confidence and survival for each position.  Inputs in fp64/fp32 arrays:

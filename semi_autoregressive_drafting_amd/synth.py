@@ -45,6 +45,7 @@ import numpy as np
 
 # Array tags for the per-array seed sequences.
 _TAG_U, _TAG_PEAK, _TAG_W1, _TAG_W2, _TAG_H, _TAG_W, _TAG_ANCHOR, _TAG_TARGET = range(1, 9)
+_TAG_GRU = 9
 
 
 @dataclass(frozen=True)
@@ -221,3 +222,20 @@ def generate(name: str, seed: int = 0, requests=None, threads: int | None = None
     return Inputs(wl=wl, seed=seed, req_ids=req_ids, U=U, W1_store=W1, W2t_store=W2t,
                   h_store=h_store, w=w, anchor=anchor_all[req_ids],
                   sps=sps_table(wl.R, wl.gamma, wl.sps_c0, wl.sps_kappa), target=T)
+
+
+def gru_weights(wl: Workload, seed: int = 0):
+    """Weights of the RNN head's gated state update, gate blocks in the order
+    (reset, update, new): W_ih [3 rank][rank + d] and W_hh [3 rank][rank] in the
+    workload's storage (bf16 bits or fp32), N(0, 1/(rank + d)) and
+    N(0, 1/rank) so that gate pre-activations are O(1); b_ih, b_hh [3 rank]
+    fp32 ~ N(0, 0.1^2)."""
+    g = _rng(seed, _TAG_GRU)
+    H, D = wl.rank, wl.rank + wl.d
+    W_ih = g.standard_normal((3 * H, D), dtype=np.float32) * np.float32(1.0 / np.sqrt(D))
+    W_hh = g.standard_normal((3 * H, H), dtype=np.float32) * np.float32(1.0 / np.sqrt(H))
+    b_ih = g.standard_normal(3 * H, dtype=np.float32) * np.float32(0.1)
+    b_hh = g.standard_normal(3 * H, dtype=np.float32) * np.float32(0.1)
+    if wl.dtype == "bf16":
+        W_ih, W_hh = f32_to_bf16_bits(W_ih), f32_to_bf16_bits(W_hh)
+    return W_ih, W_hh, b_ih, b_hh

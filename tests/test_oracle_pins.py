@@ -641,6 +641,115 @@ def test_train_loss_grads_match_finite_differences():
 
 
 # ---------------------------------------------------------------------------
+# RNN head (a GRU reading of P1 §2.4)
+# ---------------------------------------------------------------------------
+def _gru64(wl, seed=0):
+    W_ih, W_hh, b_ih, b_hh = synth.gru_weights(wl, seed)
+    return O.as_f64(W_ih), O.as_f64(W_hh), b_ih.astype(np.float64), b_hh.astype(np.float64)
+
+
+def test_gru_cell_matches_torch_grucell():
+    """The state update equals torch.nn.GRUCell (CPU, float64) on the same weights."""
+    rng = np.random.default_rng(5)
+    H, D, n = 6, 9, 4
+    W_ih, W_hh = rng.normal(0, 0.5, (3 * H, D)), rng.normal(0, 0.5, (3 * H, H))
+    b_ih, b_hh = rng.normal(0, 0.3, 3 * H), rng.normal(0, 0.3, 3 * H)
+    x, s = rng.normal(0, 1, (n, D)), rng.normal(0, 0.7, (n, H))
+    cell = torch.nn.GRUCell(D, H, dtype=torch.float64)
+    with torch.no_grad():
+        cell.weight_ih.copy_(torch.from_numpy(W_ih)); cell.weight_hh.copy_(torch.from_numpy(W_hh))
+        cell.bias_ih.copy_(torch.from_numpy(b_ih)); cell.bias_hh.copy_(torch.from_numpy(b_hh))
+        want = cell(torch.from_numpy(x), torch.from_numpy(s)).numpy()
+    np.testing.assert_allclose(O.gru_cell(x, s, W_ih, W_hh, b_ih, b_hh), want, rtol=1e-14, atol=1e-15)
+
+
+@pytest.mark.parametrize("T", [1.0, 0.0])
+def test_rnn_head_frozen_state_is_markov_without_bias(T):
+    """Update gate saturated at 1: the state stays at s_0 = 0, so the bias is 0 and
+    the RNN head draws exactly what the Markov head draws with W2 = 0."""
+    inp = synth.generate("tiny_v1024_r4_g4", seed=0)
+    wl = inp.wl
+    W1, W2t = O.as_f64(inp.W1_store), O.as_f64(inp.W2t_store)
+    W_ih, W_hh, b_ih, b_hh = _gru64(wl)
+    H = wl.rank
+    b_hh = b_hh.copy(); b_hh[H:2 * H] = 1e3      # sigma(1000) == 1 in fp64
+    h = O.as_f64(inp.h_store)
+    with np.errstate(over="ignore"):  # exp(1000) in the saturated gate's sigmoid
+        rnn = O.rnn_draft_round(inp.U, h, inp.w, W1, W2t, (W_ih, W_hh, b_ih, b_hh), inp.anchor, T,
+                                7, inp.req_ids)
+    assert not rnn["state"].any()
+    mk = O.draft_round(inp.U, h, inp.w, W1, np.zeros_like(W2t), inp.anchor, T, 7, inp.req_ids)
+    np.testing.assert_array_equal(rnn["x"], mk["x"])
+    np.testing.assert_array_equal(rnn["p"], mk["p"])
+    np.testing.assert_array_equal(rnn["c"], mk["c"])
+
+
+def test_rnn_head_memoryless_gate_is_markov_with_tanh_rows():
+    """Update gate saturated at 0, identity weights from e into the new gate and
+    no other input: s_k = tanh(W1[x_{k-1}]), so the RNN head draws what the
+    Markov head draws with bias rows bf16(tanh(W1)) (confidence still from W1)."""
+    inp = synth.generate("tiny_v1024_r4_g4", seed=0)
+    wl = inp.wl
+    W1, W2t = O.as_f64(inp.W1_store), O.as_f64(inp.W2t_store)
+    H, D = wl.rank, wl.rank + wl.d
+    W_ih = np.zeros((3 * H, D)); W_ih[2 * H:, :H] = np.eye(H)
+    W_hh = np.zeros((3 * H, H))
+    b_ih = np.zeros(3 * H); b_hh = np.zeros(3 * H); b_hh[H:2 * H] = -1e3   # sigma(-1000) == 0
+    h = O.as_f64(inp.h_store)
+    T = 1.0
+    with np.errstate(over="ignore"):
+        rnn = O.rnn_draft_round(inp.U, h, inp.w, W1, W2t, (W_ih, W_hh, b_ih, b_hh), inp.anchor, T,
+                                9, inp.req_ids)
+    mk = O.draft_round(inp.U, h, inp.w, O.bf16_round(np.tanh(W1)), W2t, inp.anchor, T, 9, inp.req_ids)
+    np.testing.assert_array_equal(rnn["x"], mk["x"])
+    np.testing.assert_allclose(rnn["p"], mk["p"], rtol=1e-12)
+    for k in range(1, wl.gamma + 1):
+        np.testing.assert_allclose(rnn["c"][:, k - 1],
+                                   O.confidence(h[:, k - 1], inp.w, W1, rnn["x"][:, k - 1]), rtol=1e-12)
+    np.testing.assert_allclose(rnn["state"], np.tanh(W1[rnn["x"][:, -2]]), rtol=1e-12)
+
+
+def test_rnn_block_distribution_sums_to_one():
+    """The RNN head's block law prod_k p_k(x_k | x_0..x_{k-1}) (the state carries
+    the whole prefix) sums to 1 over the 8^3 blocks, depends on more than the
+    previous token, and a sampled block's p_k equal the enumerated conditionals."""
+    inp = synth.generate("bruteforce_v8_g3", seed=0)
+    wl = inp.wl
+    W1, W2t = O.as_f64(inp.W1_store), O.as_f64(inp.W2t_store)
+    gru = _gru64(wl, seed=3)
+    U, h = inp.U[0].astype(np.float64), O.as_f64(inp.h_store)[0]
+    T = 1.0
+    law = {}
+    cond = {}
+
+    def rec(prefix, s, pr):
+        k = len(prefix) - 1
+        if k == wl.gamma:
+            law[tuple(prefix[1:])] = pr
+            return
+        s2 = O.gru_cell(np.concatenate([W1[prefix[-1]], h[k]])[None], s, *gru)
+        z = U[k][None] + O.bf16_round(s2) @ W2t.T
+        p = O.draft_distribution(z, T)[0]
+        cond[tuple(prefix)] = p
+        for v in range(wl.V):
+            rec(prefix + [v], s2, pr * p[v])
+    x0 = int(inp.anchor[0])
+    rec([x0], np.zeros((1, wl.rank)), 1.0)
+    assert abs(sum(law.values()) - 1.0) < 1e-12
+    # x_2's law depends on x_1 beyond its own embedding? compare two prefixes that
+    # end in the same token: (a, t) and (b, t) give different conditionals for x_3
+    d = max(np.abs(cond[(x0, a, 5)] - cond[(x0, b, 5)]).max() for a in range(8) for b in range(8))
+    assert d > 1e-4
+    out = O.rnn_draft_round(inp.U, O.as_f64(inp.h_store), inp.w, W1, W2t, gru, inp.anchor, T, 11,
+                            inp.req_ids)
+    pre = [x0]
+    for k in range(wl.gamma):
+        xk = int(out["x"][0, k + 1])
+        assert out["p"][0, k] == pytest.approx(cond[tuple(pre)][xk], rel=1e-12)
+        pre.append(xk)
+
+
+# ---------------------------------------------------------------------------
 # Verification
 # ---------------------------------------------------------------------------
 def test_tv_acceptance_identity_and_special_cases():
