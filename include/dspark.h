@@ -75,7 +75,8 @@ typedef enum {
   DSPARK_OP_SCHEDULE = 1,
   DSPARK_OP_VERIFY = 2,
   DSPARK_OP_TRAIN_LOSS = 3,
-  DSPARK_OP_TRAIN_GRAD = 4  /* rank must be a multiple of 32 (<= 256), else 0 */
+  DSPARK_OP_TRAIN_GRAD = 4, /* rank must be a multiple of 32 (<= 256), else 0 */
+  DSPARK_OP_DRAFT_RNN = 5   /* rank must be a multiple of 32 (<= 256), else 0 */
 } dspark_op;
 
 /* Bytes of device workspace entry point `op` needs for these sizes (0 if the
@@ -146,6 +147,35 @@ dspark_status dspark_draft_block_phases(int R, int V, int rank, int d, int gamma
                                         uint64_t seed, int32_t* x, float* p, float* lse,
                                         float* c, float* a, void* ws, size_t ws_bytes,
                                         int phases, dspark_stream_t stream);
+
+/*
+ * A draft block with the RNN head [P1 §2.4 RNN Head; P3 アーキテクチャ]: the
+ * pages describe a block-internal state s_k updated by a gate over the
+ * previous state (the longer prefix), the previous token's embedding and the
+ * backbone state h_k, and give no equations.  This entry point reads it as a
+ * GRU cell (gate order reset, update, new; s_0 = 0), with e_k = W1[x[r][k-1]]:
+ *   r   = sigma(W_ih[0:H] [e; h_k] + b_ih[0:H] + W_hh[0:H] s + b_hh[0:H])
+ *   z   = sigma(W_ih[H:2H] [e; h_k] + b_ih[H:2H] + W_hh[H:2H] s + b_hh[H:2H])
+ *   n   = tanh(W_ih[2H:] [e; h_k] + b_ih[2H:] + r * (W_hh[2H:] s + b_hh[2H:]))
+ *   s_k = (1 - z) n + z s_{k-1}                          (H = rank)
+ * and bf16(s_k) replaces W1[x_{k-1}] in the bias of the draft step
+ * (dspark_draft_step's formula otherwise: same sampling, RNG streams,
+ * confidence c_k = sigma(w . [h_k; W1[x_{k-1}]]) and survival a_k).
+ * Inputs as dspark_draft_block (dt must be DSPARK_BF16, else
+ * DSPARK_ERR_DTYPE; h and w required), plus W_ih bf16 [3 rank][rank + d],
+ * W_hh bf16 [3 rank][rank], b_ih, b_hh fp32 [3 rank].  rank must be a
+ * multiple of 32 and d of 16 (DSPARK_ERR_SHAPE).  Outputs as
+ * dspark_draft_block, plus state fp32 [R][rank] = s_gamma (16-byte aligned).
+ * ws: dspark_workspace_bytes(DSPARK_OP_DRAFT_RNN, ...) bytes, zero-filled
+ * once before first use (the draft step's part is left zeroed by each call).
+ */
+dspark_status dspark_draft_block_rnn(int R, int V, int rank, int d, int gamma, int dt,
+                                     const void* W1, const void* W2t, const float* U,
+                                     const void* h, const float* w, const void* W_ih,
+                                     const void* W_hh, const float* b_ih, const float* b_hh,
+                                     float temperature, uint64_t seed, int32_t* x, float* p,
+                                     float* lse, float* c, float* a, float* state, void* ws,
+                                     size_t ws_bytes, dspark_stream_t stream);
 
 /*
  * Confidence head and survival for a whole drafted block

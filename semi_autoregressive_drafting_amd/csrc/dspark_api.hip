@@ -37,6 +37,29 @@ bool bad_temperature(float T) { return !(T >= 0.0f) || isinf(T); }
 
 float kscale_of(float T) { return T > 0.0f ? (float)(1.4426950408889634 / (double)T) : 1.0f; }
 
+// RNN head workspace after the draft step's: input projections, the two state
+// buffers and the bf16 state rows.
+struct RnnPlan {
+  size_t off_P, off_S0, off_S1, off_E, ws_bytes;
+};
+
+size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+RnnPlan plan_rnn(int R, int V, int rank, int gamma) {
+  RnnPlan q{};
+  size_t off = al256(plan_draft_step(R, V, gamma).ws_bytes);
+  q.off_P = off;
+  off = al256(off + (size_t)R * gamma * 3 * rank * 4);
+  q.off_S0 = off;
+  off = al256(off + (size_t)R * rank * 4);
+  q.off_S1 = off;
+  off = al256(off + (size_t)R * rank * 4);
+  q.off_E = off;
+  off = al256(off + (size_t)R * rank * 2);
+  q.ws_bytes = off;
+  return q;
+}
+
 }  // namespace
 
 extern "C" {
@@ -61,6 +84,9 @@ size_t dspark_workspace_bytes(int op, int R, int V, int rank, int gamma) {
     case DSPARK_OP_SCHEDULE: return 0;
     case DSPARK_OP_VERIFY: return plan_verify(R, V, gamma).ws_bytes;
     case DSPARK_OP_TRAIN_LOSS: return plan_train(R, V, rank < 1 ? 1 : rank, 1, gamma).ws_bytes;
+    case DSPARK_OP_DRAFT_RNN:
+      if (rank < 32 || rank > 256 || rank % 32 != 0) return 0;
+      return plan_rnn(R, V, rank, gamma).ws_bytes;
     case DSPARK_OP_TRAIN_GRAD:
       if (rank < 32 || rank > 256 || rank % 32 != 0) return 0;
       // sized for the largest d (the dw partials sit at the end of the layout)
@@ -186,6 +212,60 @@ dspark_status dspark_draft_block(int R, int V, int rank, int d, int gamma, int d
   return dspark_draft_block_phases(R, V, rank, d, gamma, dt, W1, W2t, U, h, w, temperature, seed,
                                    x, p, lse, c, a, ws, ws_bytes,
                                    DSPARK_PHASE_STEPS | DSPARK_PHASE_MERGE, stream);
+}
+
+dspark_status dspark_draft_block_rnn(int R, int V, int rank, int d, int gamma, int dt,
+                                     const void* W1, const void* W2t, const float* U,
+                                     const void* h, const float* w, const void* W_ih,
+                                     const void* W_hh, const float* b_ih, const float* b_hh,
+                                     float temperature, uint64_t seed, int32_t* x, float* p,
+                                     float* lse, float* c, float* a, float* state, void* ws,
+                                     size_t ws_bytes, dspark_stream_t stream) {
+  if (!h || !w || !W_ih || !W_hh || !b_ih || !b_hh || !state) return DSPARK_ERR_NULL;
+  if (dt != DSPARK_BF16) return DSPARK_ERR_DTYPE;  // the state rows are bf16 like W1
+  if (rank % 32 != 0 || d % 16 != 0) return DSPARK_ERR_SHAPE;
+  if (!aligned16(h) || !aligned16(W_ih) || !aligned16(W_hh) || !aligned16(state))
+    return DSPARK_ERR_SHAPE;
+  StepArgs args;
+  StepPlan plan;
+  const dspark_status s = check_draft(R, V, rank, d, gamma, 0, dt, W1, W2t, U, h, w, temperature,
+                                      seed, x, p, lse, c, a, nullptr, ws, ws_bytes, args, plan);
+  if (s != DSPARK_OK) return s;
+  const RnnPlan rp = plan_rnn(R, V, rank, gamma);
+  if (ws_bytes < rp.ws_bytes) return DSPARK_ERR_WORKSPACE;
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  unsigned char* wsb = static_cast<unsigned char*>(ws);
+  RnnArgs ra{};
+  ra.R = R;
+  ra.V = V;
+  ra.rank = rank;
+  ra.d = d;
+  ra.gamma = gamma;
+  ra.W1 = static_cast<const uint16_t*>(W1);
+  ra.W_ih = static_cast<const uint16_t*>(W_ih);
+  ra.W_hh = static_cast<const uint16_t*>(W_hh);
+  ra.b_ih = b_ih;
+  ra.b_hh = b_hh;
+  ra.h = static_cast<const uint16_t*>(h);
+  ra.x = x;
+  ra.best = args.best;
+  ra.P = reinterpret_cast<float*>(wsb + rp.off_P);
+  ra.E = reinterpret_cast<uint16_t*>(wsb + rp.off_E);
+  float* S[2] = {reinterpret_cast<float*>(wsb + rp.off_S0), reinterpret_cast<float*>(wsb + rp.off_S1)};
+  if (launch_rnn_input_proj(ra, st) != hipSuccess) return DSPARK_ERR_LAUNCH;
+  args.E_rows = ra.E;
+  for (int k = 1; k <= gamma; ++k) {
+    float* next = k == gamma ? state : S[k & 1];
+    if (launch_rnn_state_step(ra, k, S[(k - 1) & 1], next, st) != hipSuccess)
+      return DSPARK_ERR_LAUNCH;
+    args.k = k;
+    args.prev_from_best = k > 1;
+    if (launch_draft_step(args, plan, st) != hipSuccess) return DSPARK_ERR_LAUNCH;
+  }
+  args.k = 1;
+  args.prev_from_best = true;
+  if (launch_draft_finalize(args, plan, 1, gamma, st) != hipSuccess) return DSPARK_ERR_LAUNCH;
+  return DSPARK_OK;
 }
 
 dspark_status dspark_confidence(int R, int gamma, int d, int rank, int V, int dt,

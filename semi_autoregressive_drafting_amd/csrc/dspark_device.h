@@ -223,6 +223,13 @@ __device__ __forceinline__ float sigmoid_f32(float x) { return 1.0f / (1.0f + ex
 
 __device__ __forceinline__ int clamp_token(int x, int V) { return x < 0 ? 0 : (x >= V ? V - 1 : x); }
 
+// Vocabulary id in a draft step's 64-bit winner word (-1: no winner).  The
+// word packs an order-preserving key above the complemented id, so a 64-bit
+// atomic max keeps the largest key and, on ties, the lowest id.
+__device__ __forceinline__ int winner_id(unsigned long long w) {
+  return w == 0ull ? -1 : (int)(~(uint32_t)(w & 0xFFFFFFFFull));
+}
+
 // Balanced split of T tiles over n slabs: the first n - T%n slabs get T/n
 // tiles, the rest one more (so low slab ids carry the lighter share).
 __host__ __device__ inline void slab_range(int s, int n, int T, int& b, int& e) {

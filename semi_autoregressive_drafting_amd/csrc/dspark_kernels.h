@@ -29,6 +29,7 @@ struct StepArgs {
   const float* U;
   const void* h;
   const float* w;
+  const void* E_rows;   // RNN head: row r of the bias input per request [R][rank]; null: W1[x_{k-1}]
   float kscale;  // log2(e) / T
   uint64_t seed;
   int32_t* x;
@@ -47,6 +48,24 @@ StepPlan plan_draft_step(int R, int V, int gamma);
 hipError_t launch_draft_step(const StepArgs& a, const StepPlan& plan, hipStream_t stream);
 // Merge records, write x/p/lse and (if h is set) c/a for steps k0 .. k0+nk-1.
 hipError_t launch_draft_finalize(const StepArgs& a, const StepPlan& plan, int k0, int nk,
+                                 hipStream_t stream);
+
+// RNN head (rnn_head.hip); bf16 weights, rank % 32 == 0, d % 16 == 0.
+struct RnnArgs {
+  int R, V, rank, d, gamma;
+  const uint16_t* W1;
+  const uint16_t* W_ih;   // [3 rank][rank + d]
+  const uint16_t* W_hh;   // [3 rank][rank]
+  const float* b_ih;      // [3 rank]
+  const float* b_hh;
+  const uint16_t* h;      // [R][gamma][d]
+  const int32_t* x;       // [R][gamma + 1] (column 0: the anchor)
+  const unsigned long long* best;  // draft steps' winner words [gamma][R]
+  float* P;               // input projections [R * gamma][3 rank]
+  uint16_t* E;            // bf16(s_k) [R][rank], the step's bias rows
+};
+hipError_t launch_rnn_input_proj(const RnnArgs& a, hipStream_t stream);
+hipError_t launch_rnn_state_step(const RnnArgs& a, int k, const float* s_prev, float* s_next,
                                  hipStream_t stream);
 
 struct ConfArgs {

@@ -75,10 +75,6 @@ __device__ __forceinline__ unsigned long long pack_winner(float key, int idx) {
                        (unsigned long long)(~(uint32_t)idx);
 }
 
-__device__ __forceinline__ int winner_id(unsigned long long w) {
-  return w == 0ull ? -1 : (int)(~(uint32_t)(w & 0xFFFFFFFFull));
-}
-
 // Per-lane online state over the lane's vocabulary entries of one request.
 struct LaneState {
   float m;    // running max of t = z * kscale
@@ -294,11 +290,12 @@ __global__ __launch_bounds__(kStreamThreads) void markov_step_shared(StepArgs a)
                  wave * kPatchFloats;
   DraftEpi<kGreedy, kDebug, kVec> epi(a, r, rc, half, r0 + wave * kVTile, patch);
   auto gather = [&](typename W::frag_t(&ef)[W::kMaxKs]) {
+    const void* base = a.E_rows ? a.E_rows : a.W1;
+    const int row = a.E_rows ? rc : clamp_token(prev_token(a, rc), a.V);
     if constexpr (std::is_same<W, WBf16>::value && kKs > 0 && kKs % 4 == 0 && kVec)
-      load_e_frags_lines<kKs>(ef, reinterpret_cast<const uint16_t*>(a.W1),
-                              clamp_token(prev_token(a, rc), a.V), patch);
+      load_e_frags_lines<kKs>(ef, reinterpret_cast<const uint16_t*>(base), row, patch);
     else
-      load_e_frags<W, kKs>(ef, a.W1, prev_token(a, rc), a.rank, a.V, half);
+      load_e_frags<W, kKs>(ef, base, row, a.rank, a.E_rows ? a.R : a.V, half);
   };
   if constexpr (kKs > 0)
     shared_a_stream_skew<W, kKs>(a.W2t, a.V, t_begin, t_end, e, gather, lds, epi);
@@ -331,11 +328,13 @@ __global__ __launch_bounds__(kStreamThreads) void markov_step_private(StepArgs a
   private_a_stream<W, kKs>(
       a.W2t, a.V, a.rank, t_begin + wave, t_end, kWaves, e,
       [&](typename W::frag_t(&ef)[W::kMaxKs]) {
+        const void* base = a.E_rows ? a.E_rows : a.W1;
+        const int row = a.E_rows ? rc : clamp_token(prev_token(a, rc), a.V);
         if constexpr (std::is_same<W, WBf16>::value && kKs > 0 && kKs % 4 == 0 && kVec)
-          load_e_frags_lines<kKs>(ef, reinterpret_cast<const uint16_t*>(a.W1),
-                                  clamp_token(prev_token(a, rc), a.V), patches[kVec ? wave : 0]);
+          load_e_frags_lines<kKs>(ef, reinterpret_cast<const uint16_t*>(base), row,
+                                  patches[kVec ? wave : 0]);
         else
-          load_e_frags<W, kKs>(ef, a.W1, prev_token(a, rc), a.rank, a.V, half);
+          load_e_frags<W, kKs>(ef, base, row, a.rank, a.E_rows ? a.R : a.V, half);
       },
       epi);
 

@@ -18,12 +18,13 @@ DSPARK_OK, DSPARK_ERR_NULL, DSPARK_ERR_SHAPE, DSPARK_ERR_DTYPE, DSPARK_ERR_VALUE
     DSPARK_ERR_WORKSPACE, DSPARK_ERR_LAUNCH = range(7)
 DSPARK_F32, DSPARK_BF16 = 0, 1
 DSPARK_OP_DRAFT_STEP, DSPARK_OP_SCHEDULE, DSPARK_OP_VERIFY, DSPARK_OP_TRAIN_LOSS, \
-    DSPARK_OP_TRAIN_GRAD = 0, 1, 2, 3, 4
+    DSPARK_OP_TRAIN_GRAD, DSPARK_OP_DRAFT_RNN = 0, 1, 2, 3, 4, 5
 DSPARK_PHASE_STEPS, DSPARK_PHASE_MERGE = 1, 2
 
 EXPORTS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_draft_step",
            "dspark_draft_block", "dspark_draft_block_phases", "dspark_confidence", "dspark_schedule", "dspark_schedule_async",
-           "dspark_verify", "dspark_train_loss", "dspark_train_loss_grad")
+           "dspark_verify", "dspark_train_loss", "dspark_train_loss_grad",
+           "dspark_draft_block_rnn")
 
 _lib = None
 
@@ -72,6 +73,9 @@ def load():
     L.dspark_train_loss_grad.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, F, F, F, F, F,
                                          P, P, P, P, P, P, P, P, SZ, P]
     L.dspark_train_loss_grad.restype = I
+    L.dspark_draft_block_rnn.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, F, U64,
+                                         P, P, P, P, P, P, P, SZ, P]
+    L.dspark_draft_block_rnn.restype = I
     _lib = L
     return L
 
@@ -187,3 +191,14 @@ def dspark_train_loss_grad(R, V, rank, d, gamma, dt, W1, W2t, U, h, w, target, x
           _ptr(h), _ptr(w), _ptr(target), _ptr(x_star), float(temperature), float(lam),
           float(alpha_ce), float(alpha_tv), float(alpha_conf), _ptr(terms), _ptr(sums), _ptr(dU),
           _ptr(dW1), _ptr(dW2t), _ptr(dh), _ptr(dw), _ptr(ws), int(ws_bytes), _stream(stream))
+
+
+def dspark_draft_block_rnn(R, V, rank, d, gamma, dt, W1, W2t, U, h, w, W_ih, W_hh, b_ih, b_hh,
+                           temperature, seed, x, p, lse, c, a, state, ws, ws_bytes=None,
+                           stream=None):
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _call("dspark_draft_block_rnn", R, V, rank, d, gamma, dt, _ptr(W1), _ptr(W2t), _ptr(U),
+          _ptr(h), _ptr(w), _ptr(W_ih), _ptr(W_hh), _ptr(b_ih), _ptr(b_hh), float(temperature),
+          int(seed), _ptr(x), _ptr(p), _ptr(lse), _ptr(c), _ptr(a), _ptr(state), _ptr(ws),
+          int(ws_bytes), _stream(stream))

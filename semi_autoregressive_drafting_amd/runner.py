@@ -180,3 +180,31 @@ def train_loss_grad(di: DeviceInputs, x_star: torch.Tensor, temperature: float =
                              out["terms"], out["sums"], out["dU"], out["dW1"], out["dW2t"],
                              out["dh"], out["dw"], ws)
     return out
+
+
+@dataclass
+class RnnWeights:
+    W_ih: torch.Tensor
+    W_hh: torch.Tensor
+    b_ih: torch.Tensor
+    b_hh: torch.Tensor
+
+    @staticmethod
+    def upload(gru, device="cuda") -> "RnnWeights":
+        def dev(a):
+            a = np.ascontiguousarray(a)
+            if a.dtype == np.uint16:
+                a = a.view(np.int16)
+            return torch.from_numpy(a).to(device)
+        return RnnWeights(*(dev(a) for a in gru))
+
+
+def draft_rnn(di: DeviceInputs, buf: RoundBuffers, rw: RnnWeights, temperature: float, seed: int,
+              state: torch.Tensor, ws: torch.Tensor):
+    """gamma steps of the RNN head (state update, then the draft step) and the
+    record merge; s_gamma lands in `state` [R][rank] fp32.  `ws` holds
+    dspark_workspace_bytes(DSPARK_OP_DRAFT_RNN, ...) bytes, zero-filled once."""
+    buf.x[:, 0].copy_(di.anchor)
+    D.dspark_draft_block_rnn(di.R, di.V, di.rank, di.d, di.gamma, di.dt, di.W1, di.W2t, di.U, di.h,
+                             di.w, rw.W_ih, rw.W_hh, rw.b_ih, rw.b_hh, temperature, seed, buf.x,
+                             buf.p, buf.lse, buf.c, buf.a, state, ws)

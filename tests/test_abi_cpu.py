@@ -188,6 +188,28 @@ def test_train_loss_grad_validation():
     assert 256 * 151936 * 2 < big < 1 << 30
 
 
+def test_draft_block_rnn_validation():
+    f = D.load().dspark_draft_block_rnn
+    # bf16, rank 64, d 64; W_ih, W_hh, b_ih, b_hh at 11 .. 14; state 22; ws_bytes 24
+    base = [4, 1024, 64, 64, 4, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1.0, 7,
+            FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None]
+    def call(**kw):
+        a = list(base)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a5=0) == D.DSPARK_ERR_DTYPE             # the state rows are bf16
+    for i in (9, 10, 11, 12, 13, 14, 22):               # h, w, GRU weights and state
+        assert call(**{f"a{i}": None}) == D.DSPARK_ERR_NULL
+    assert call(a2=48) == D.DSPARK_ERR_SHAPE            # rank not a multiple of 32
+    assert call(a3=40) == D.DSPARK_ERR_SHAPE            # d not a multiple of 16
+    assert call(a15=-1.0) == D.DSPARK_ERR_VALUE
+    need = D.dspark_workspace_bytes(D.DSPARK_OP_DRAFT_RNN, 4, 1024, 64, 4)
+    assert need > D.dspark_workspace_bytes(D.DSPARK_OP_DRAFT_STEP, 4, 1024, 64, 4)
+    assert call(a24=need - 1) == D.DSPARK_ERR_WORKSPACE
+    assert D.dspark_workspace_bytes(D.DSPARK_OP_DRAFT_RNN, 4, 1024, 48, 4) == 0
+
+
 def test_schedule_async_validation():
     f = D.load().dspark_schedule_async
     assert f(4, 4, None, FAKE, FAKE, 21, FAKE, FAKE, FAKE, None) == D.DSPARK_ERR_NULL
