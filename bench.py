@@ -212,6 +212,7 @@ def main():
     torch.cuda.synchronize()
     print(f"# inputs ready in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
     R, g, V, rank, d = di.R, di.gamma, di.V, di.rank, di.d
+    di_wl = inp.wl
 
     def one_round(seed, ev=None):
         # the anchor copy and the gamma streaming steps, then the record merge;
@@ -317,6 +318,31 @@ def main():
         train_grad = {"us": round(g_med, 2), "bytes": gb,
                       "achieved_GBps": round(gb / (g_med * 1e-6) / 1e9, 1)}
         del gws
+
+    # The RNN head's draft block on the same inputs (GRU weights from the
+    # generator's RNN stream): input projection, then per step the state
+    # update and the draft step, then the merge.
+    rnn = None
+    if extras:
+        gru = synth.gru_weights(di_wl, 0)
+        rw = runner.RnnWeights.upload(gru)
+        rstate = torch.empty((R, rank), dtype=torch.float32, device="cuda")
+        rws = torch.zeros(D.dspark_workspace_bytes(D.DSPARK_OP_DRAFT_RNN, R, V, rank, g),
+                          dtype=torch.uint8, device="cuda")
+        for s in range(3):
+            runner.draft_rnn(di, buf, rw, TEMPERATURE, 600 + s, rstate, rws)
+        er = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        r_us = []
+        for s in range(nb):
+            er[0].record()
+            runner.draft_rnn(di, buf, rw, TEMPERATURE, 610 + s, rstate, rws)
+            er[1].record()
+            torch.cuda.synchronize()
+            r_us.append(er[0].elapsed_time(er[1]) * 1e3)
+        r_med = float(np.median(r_us))
+        rnn = {"block_us": round(r_med, 2), "us_per_step": round(r_med / g, 2),
+               "draft_tokens_per_s": round(R * g / (r_med * 1e-6), 1)}
+        del rws, rstate
 
     # Cold draft step: a 512 MB write evicts W2 and U from L2 and the MALL
     # before each timed step (dspark_draft_step = step kernel + merge).
@@ -427,6 +453,7 @@ def main():
                          "schedule_async": round(float(np.median(async_us)), 2),
                          "verify": round(float(ver_ms.mean()) * 1e3, 2),
                          "round_wall": round(ms_round * 1e3, 2)},
+        "rnn_head_block": rnn,
         "train_loss_forward": train,
         "train_loss_with_gradients": train_grad,
         "verify_roofline": {"bytes": vb, "achieved_GBps": round(vb / (ver_ms.mean() * 1e-3) / 1e9, 1)},

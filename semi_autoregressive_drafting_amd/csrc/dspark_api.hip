@@ -49,7 +49,7 @@ RnnPlan plan_rnn(int R, int V, int rank, int gamma) {
   RnnPlan q{};
   size_t off = al256(plan_draft_step(R, V, gamma).ws_bytes);
   q.off_P = off;
-  off = al256(off + (size_t)R * gamma * 3 * rank * 4);
+  off = al256(off + (size_t)kProjSplit * R * gamma * 3 * rank * 4);
   q.off_S0 = off;
   off = al256(off + (size_t)R * rank * 4);
   q.off_S1 = off;

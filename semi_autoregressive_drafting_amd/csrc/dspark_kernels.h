@@ -51,6 +51,7 @@ hipError_t launch_draft_finalize(const StepArgs& a, const StepPlan& plan, int k0
                                  hipStream_t stream);
 
 // RNN head (rnn_head.hip); bf16 weights, rank % 32 == 0, d % 16 == 0.
+constexpr int kProjSplit = 4;  // K quarters of the input projection (partial sums in P)
 struct RnnArgs {
   int R, V, rank, d, gamma;
   const uint16_t* W1;
@@ -61,7 +62,7 @@ struct RnnArgs {
   const uint16_t* h;      // [R][gamma][d]
   const int32_t* x;       // [R][gamma + 1] (column 0: the anchor)
   const unsigned long long* best;  // draft steps' winner words [gamma][R]
-  float* P;               // input projections [R * gamma][3 rank]
+  float* P;               // input projections, kProjSplit partials [kProjSplit][R * gamma][3 rank]
   uint16_t* E;            // bf16(s_k) [R][rank], the step's bias rows
 };
 hipError_t launch_rnn_input_proj(const RnnArgs& a, hipStream_t stream);

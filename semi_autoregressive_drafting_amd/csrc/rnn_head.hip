@@ -10,13 +10,14 @@
 // kernel reads it through StepArgs::E_rows).
 //
 //   R1 rnn_input_proj   before the block, for every (request, position):
-//      P = W_ih[:, rank:] h + b_ih  [R*gamma][3 rank] fp32 (bf16 MFMA, K = d);
+//      P = W_ih[:, rank:] h + b_ih  [R*gamma][3 rank] fp32 (bf16 MFMA, K = d),
+//      as kProjSplit partial sums over quarters of K that R2 adds in order;
 //      h does not depend on the drafted tokens.
 //   R2 rnn_state_step   per step k, after step k-1's winner is known:
 //      the e part W_ih[:, :rank] e (bf16 MFMA, exact products) and the
 //      recurrent part W_hh s (s split into two bf16 terms, hi + lo, so the
 //      fp32 state keeps about 16 bits through the product), then the gates;
-//      writes s_k (fp32) and bf16(s_k) for the step.
+//      writes s_k (fp32) and bf16(s_k) for the step.  rank <= 256.
 #include "dspark_kernels.h"
 #include "dspark_device.h"
 
@@ -38,128 +39,228 @@ __device__ __forceinline__ bf16x8_t bf16x8_of(const float (&v)[8]) {
   return r;
 }
 
-// R1: wave (workgroup (bx, by), wave q) computes the 32 x 32 tile of rows
-// 32 bx .. and outputs 32 (4 by + q) ..; A = h rows, B = W_ih rows (columns
-// rank + k), both holding K contiguously.  Lane (l%32, half) supplies the 8
-// k = 16 s + 8 half .. +7 of its row for K step s.
+// R1: wave q of workgroup (bx, by, ks) computes rows 64 bx .. +63 (two
+// 32-row tiles) by outputs 256 by + 64 q .. +63 (two 32-output tiles) over
+// the ks-th quarter of K (partial sums P[ks], added in order by R2); the
+// four waves share the h rows through L1.  A = h rows, B = W_ih rows
+// (columns rank + k), both holding K contiguously; lane (l%32, half)
+// supplies the 8 k = 16 s + 8 half .. +7 of its row for K step s.  The
+// operands of step s + 1 are loaded while step s multiplies.
 __global__ __launch_bounds__(256) void rnn_input_proj(RnnArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = lane >> 5, col = lane & 31;
   const int n_rows = a.R * a.gamma, n_out = 3 * a.rank;
-  const int nt = blockIdx.y * 4 + wave;
-  if (nt * 32 >= n_out) return;  // no barriers in this kernel
-  const int row = blockIdx.x * 32 + col;
-  const int rowc = row < n_rows ? row : n_rows - 1;
-  const uint16_t* hrow = a.h + (size_t)rowc * a.d + 8 * half;
-  const uint16_t* wrow = a.W_ih + (size_t)(nt * 32 + col) * (a.rank + a.d) + a.rank + 8 * half;
-  f32x16_t acc = f32x16_t{};
-#pragma unroll 4
-  for (int k0 = 0; k0 < a.d; k0 += 16) {
-    const bf16x8_t x = *reinterpret_cast<const bf16x8_t*>(hrow + k0);
-    const bf16x8_t wv = *reinterpret_cast<const bf16x8_t*>(wrow + k0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, wv, acc, 0, 0, 0);
-  }
-  // accumulator i: row 8 (i/4) + 4 half + i%4 of the tile, output nt*32 + col
-  const int o = nt * 32 + col;
-  const float b = a.b_ih[o];
+  const int o0 = blockIdx.y * 256 + wave * 64;
+  if (o0 >= n_out) return;  // no barriers in this kernel
+  const int ksteps = a.d / 16, kq = (ksteps + kProjSplit - 1) / kProjSplit;
+  const int s_begin = min(ksteps, (int)blockIdx.z * kq), s_end = min(ksteps, s_begin + kq);
+  const uint16_t* hr[2];
+  const uint16_t* wr[2];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int rr = blockIdx.x * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-    if (rr < n_rows) a.P[(size_t)rr * n_out + o] = acc[i] + b;
+  for (int t = 0; t < 2; ++t) {
+    const int row = min(blockIdx.x * 64 + 32 * t + col, n_rows - 1);
+    const int o = min(o0 + 32 * t + col, n_out - 1);
+    hr[t] = a.h + (size_t)row * a.d + 8 * half;
+    wr[t] = a.W_ih + (size_t)o * (a.rank + a.d) + a.rank + 8 * half;
+  }
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) acc[t][u] = f32x16_t{};
+  bf16x8_t x[2], wv[2], xn[2], wn[2];
+  const int s_first = s_begin < s_end ? s_begin : 0;  // an empty quarter still loads a valid step
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    x[t] = *reinterpret_cast<const bf16x8_t*>(hr[t] + 16 * s_first);
+    wv[t] = *reinterpret_cast<const bf16x8_t*>(wr[t] + 16 * s_first);
+  }
+  for (int st = s_begin; st < s_end; ++st) {
+    const int sn = st + 1 < s_end ? st + 1 : st;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      xn[t] = *reinterpret_cast<const bf16x8_t*>(hr[t] + 16 * sn);
+      wn[t] = *reinterpret_cast<const bf16x8_t*>(wr[t] + 16 * sn);
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        acc[t][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x[t], wv[u], acc[t][u], 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      x[t] = xn[t];
+      wv[t] = wn[t];
+    }
+  }
+  // accumulator i of tile (t, u): row 64 bx + 32 t + 8 (i/4) + 4 half + i%4,
+  // output o0 + 32 u + col; the input bias goes into the first quarter
+  float* P = a.P + (size_t)blockIdx.z * n_rows * n_out;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int o = o0 + 32 * u + col;
+    if (o >= n_out) continue;
+    const float b = blockIdx.z == 0 ? a.b_ih[o] : 0.0f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int rr = blockIdx.x * 64 + 32 * t + 8 * (i >> 2) + 4 * half + (i & 3);
+        if (rr < n_rows) P[(size_t)rr * n_out + o] = acc[t][u][i] + b;
+      }
   }
 }
 
-// R2: wave (workgroup (jb, rt)) owns requests 32 rt .. +31 and state entries
-// 32 jb .. +31.  MFMA M = requests, N = state entries, K = rank:
+// R2: workgroup (jb, rt) owns requests 32 rt .. +31 and state entries
+// 32 jb .. +31, with 12 waves: wave w computes gate g = w / 4 (reset, update,
+// new) over the K quarter q = w % 4.  MFMA M = requests, N = state entries:
 //   A  e:  W1[x_{k-1}[m]][k ..]       s:  hi / lo bf16 terms of s_{k-1}[m][k ..]
 //   B  W_ih[g rank + n][k ..] (the e columns), W_hh[g rank + n][k ..]
-__global__ __launch_bounds__(64) void rnn_state_step(RnnArgs a, int k, const float* s_prev,
-                                                     float* s_next) {
-  const int lane = threadIdx.x;
+// The kernel is bound by dependent memory round trips (a few microseconds
+// each here), so every wave issues all of its loads at the start and only the
+// e rows wait for the token.  The quarters meet in LDS in a fixed order, the
+// first one bringing the input projection and the recurrent bias; wave 0
+// then forms s_k.
+constexpr int kStateQ = 4;       // K quarters
+constexpr int kStateMaxSteps = 4;  // K steps per quarter at rank 256
+
+template <bool kRec>
+__device__ __forceinline__ void state_step_body(const RnnArgs& a, int k, const float* s_prev,
+                                                float* s_next, float (*red)[2][16][64]) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = w / kStateQ, q = w % kStateQ;
   const int half = lane >> 5, col = lane & 31;
   const int jb = blockIdx.x, rt = blockIdx.y;
-  const int H = a.rank;
-  const int m = rt * 32 + col;
-  const int mc = m < a.R ? m : a.R - 1;
-  int tok;
-  if (k > 1)
-    tok = winner_id(a.best[(size_t)(k - 2) * a.R + mc]);
-  else
-    tok = a.x[(size_t)mc * (a.gamma + 1)];
+  const int H = a.rank, KS = H / 16;
+  const int kq = (KS + kStateQ - 1) / kStateQ;
+  const int s_begin = min(KS, q * kq), s_end = min(KS, s_begin + kq);
+  const int mc = min(rt * 32 + col, a.R - 1);
+  const int n = jb * 32 + col;
+  const uint16_t* wi = a.W_ih + (size_t)(g * H + n) * (H + a.d) + 8 * half;
+  const uint16_t* wh = a.W_hh + (size_t)(g * H + n) * H + 8 * half;
+  const float* srow = s_prev + (size_t)mc * H + 8 * half;
+
+  // loads that do not depend on the token
+  bf16x8_t wiv[kStateMaxSteps], whv[kStateMaxSteps], ev[kStateMaxSteps];
+  f32x4_t sv[kStateMaxSteps][2];
+#pragma unroll
+  for (int j = 0; j < kStateMaxSteps; ++j) {
+    const int k0 = 16 * min(s_begin + j, KS - 1);
+    wiv[j] = *reinterpret_cast<const bf16x8_t*>(wi + k0);
+    if constexpr (kRec) {
+      whv[j] = *reinterpret_cast<const bf16x8_t*>(wh + k0);
+      sv[j][0] = *reinterpret_cast<const f32x4_t*>(srow + k0);
+      sv[j][1] = *reinterpret_cast<const f32x4_t*>(srow + k0 + 4);
+    }
+  }
+  // wave 0 keeps s_{k-1} of its outputs for the final blend
+  float sp[16];
+  if (kRec && w == 0) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = min(rt * 32 + 8 * (i >> 2) + 4 * half + (i & 3), a.R - 1);
+      sp[i] = s_prev[(size_t)r * H + n];
+    }
+  }
+  // the first quarter also brings the input projection (its partials in order)
+  float pre[16];
+  if (q == 0) {
+    const size_t qstride = (size_t)a.R * a.gamma * 3 * H;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = min(rt * 32 + 8 * (i >> 2) + 4 * half + (i & 3), a.R - 1);
+      const float* pq = a.P + ((size_t)r * a.gamma + (k - 1)) * (3 * H) + g * H + n;
+      float v = pq[0];
+#pragma unroll
+      for (int p = 1; p < kProjSplit; ++p) v += pq[p * qstride];
+      pre[i] = v;
+    }
+  }
+  int tok = k > 1 ? winner_id(a.best[(size_t)(k - 2) * a.R + mc]) : a.x[(size_t)mc * (a.gamma + 1)];
   tok = clamp_token(tok, a.V);
   const uint16_t* erow = a.W1 + (size_t)tok * H + 8 * half;
-  const float* srow = s_prev + (size_t)mc * H + 8 * half;
-  const int n = jb * 32 + col;
+#pragma unroll
+  for (int j = 0; j < kStateMaxSteps; ++j)
+    ev[j] = *reinterpret_cast<const bf16x8_t*>(erow + 16 * min(s_begin + j, KS - 1));
 
-  f32x16_t gi[3], gh[3];
+  f32x16_t gi = f32x16_t{}, gh = f32x16_t{};
 #pragma unroll
-  for (int g = 0; g < 3; ++g) {
-    gi[g] = f32x16_t{};
-    gh[g] = f32x16_t{};
-  }
-  for (int k0 = 0; k0 < H; k0 += 16) {
-    const bf16x8_t e = *reinterpret_cast<const bf16x8_t*>(erow + k0);
-#pragma unroll
-    for (int g = 0; g < 3; ++g) {
-      const bf16x8_t wv = *reinterpret_cast<const bf16x8_t*>(
-          a.W_ih + (size_t)(g * H + n) * (H + a.d) + k0 + 8 * half);
-      gi[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(e, wv, gi[g], 0, 0, 0);
-    }
-    if (k > 1) {  // s_0 = 0: the recurrent products vanish at the first step
+  for (int j = 0; j < kStateMaxSteps; ++j) {
+    if (s_begin + j >= s_end) break;
+    gi = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ev[j], wiv[j], gi, 0, 0, 0);
+    if constexpr (kRec) {
       float hi[8], lo[8];
-      const f32x4_t s0 = *reinterpret_cast<const f32x4_t*>(srow + k0);
-      const f32x4_t s1 = *reinterpret_cast<const f32x4_t*>(srow + k0 + 4);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        hi[j] = s0[j];
-        hi[4 + j] = s1[j];
+      for (int t = 0; t < 4; ++t) {
+        hi[t] = sv[j][0][t];
+        hi[4 + t] = sv[j][1][t];
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float v = hi[j];
-        hi[j] = bf16_value(bf16_bits_rne(v));
-        lo[j] = v - hi[j];
+      for (int t = 0; t < 8; ++t) {
+        const float v = hi[t];
+        hi[t] = bf16_value(bf16_bits_rne(v));
+        lo[t] = v - hi[t];
       }
-      const bf16x8_t shi = bf16x8_of(hi), slo = bf16x8_of(lo);
-#pragma unroll
-      for (int g = 0; g < 3; ++g) {
-        const bf16x8_t wv = *reinterpret_cast<const bf16x8_t*>(a.W_hh + (size_t)(g * H + n) * H + k0 +
-                                                               8 * half);
-        gh[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(shi, wv, gh[g], 0, 0, 0);
-        gh[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(slo, wv, gh[g], 0, 0, 0);
-      }
+      gh = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf16x8_of(hi), whv[j], gh, 0, 0, 0);
+      gh = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf16x8_of(lo), whv[j], gh, 0, 0, 0);
     }
   }
+  // quarters in order: ((q0 + input projection) + q1) + q2 + q3, and likewise
+  // ((q0 + recurrent bias) + q1) + ... for the recurrent part
+  const float bh = a.b_hh[g * H + n];
+  for (int qq = 0; qq < kStateQ; ++qq) {
+    if (q == qq) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (qq == 0) {
+          red[g][0][i][lane] = gi[i] + pre[i];
+          red[g][1][i][lane] = gh[i] + bh;
+        } else {
+          red[g][0][i][lane] += gi[i];
+          red[g][1][i][lane] += gh[i];
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (w != 0) return;
   // accumulator i: request 32 rt + 8 (i/4) + 4 half + i%4, state entry n
-  const float bhr = a.b_hh[n], bhz = a.b_hh[H + n], bhn = a.b_hh[2 * H + n];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int r = rt * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
     if (r >= a.R) continue;
-    const float* pre = a.P + ((size_t)r * a.gamma + (k - 1)) * (3 * H);
-    const float sp = k > 1 ? s_prev[(size_t)r * H + n] : 0.0f;
-    const float rg = 1.0f / (1.0f + expf(-(gi[0][i] + pre[n] + gh[0][i] + bhr)));
-    const float zg = 1.0f / (1.0f + expf(-(gi[1][i] + pre[H + n] + gh[1][i] + bhz)));
-    const float ng = tanhf(gi[2][i] + pre[2 * H + n] + rg * (gh[2][i] + bhn));
-    const float s = (1.0f - zg) * ng + zg * sp;
+    const float rg = 1.0f / (1.0f + expf(-(red[0][0][i][lane] + red[0][1][i][lane])));
+    const float zg = 1.0f / (1.0f + expf(-(red[1][0][i][lane] + red[1][1][i][lane])));
+    const float ng = tanhf(red[2][0][i][lane] + rg * red[2][1][i][lane]);
+    const float s = (1.0f - zg) * ng + zg * (kRec ? sp[i] : 0.0f);
     s_next[(size_t)r * H + n] = s;
     a.E[(size_t)r * H + n] = bf16_bits_rne(s);
   }
 }
 
+__global__ __launch_bounds__(64 * 3 * kStateQ) void rnn_state_step(RnnArgs a, int k,
+                                                                   const float* s_prev,
+                                                                   float* s_next) {
+  __shared__ float red[3][2][16][64];  // per gate: input part, recurrent part
+  if (k > 1)
+    state_step_body<true>(a, k, s_prev, s_next, red);
+  else
+    state_step_body<false>(a, k, s_prev, s_next, red);  // s_0 = 0
+}
+
 }  // namespace
 
 hipError_t launch_rnn_input_proj(const RnnArgs& a, hipStream_t stream) {
-  const int n_rows = a.R * a.gamma, n_tiles = 3 * a.rank / 32;
-  hipLaunchKernelGGL(rnn_input_proj, dim3((n_rows + 31) / 32, (n_tiles + 3) / 4), dim3(256), 0,
-                     stream, a);
+  const int n_rows = a.R * a.gamma, n_out = 3 * a.rank;
+  hipLaunchKernelGGL(rnn_input_proj, dim3((n_rows + 63) / 64, (n_out + 255) / 256, kProjSplit),
+                     dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_rnn_state_step(const RnnArgs& a, int k, const float* s_prev, float* s_next,
                                  hipStream_t stream) {
-  hipLaunchKernelGGL(rnn_state_step, dim3(a.rank / 32, (a.R + 31) / 32), dim3(64), 0, stream, a,
-                     k, s_prev, s_next);
+  hipLaunchKernelGGL(rnn_state_step, dim3(a.rank / 32, (a.R + 31) / 32), dim3(64 * 3 * kStateQ), 0,
+                     stream, a, k, s_prev, s_next);
   return hipGetLastError();
 }
 
