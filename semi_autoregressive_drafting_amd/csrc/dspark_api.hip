@@ -37,10 +37,10 @@ bool bad_temperature(float T) { return !(T >= 0.0f) || isinf(T); }
 
 float kscale_of(float T) { return T > 0.0f ? (float)(1.4426950408889634 / (double)T) : 1.0f; }
 
-// RNN head workspace after the draft step's: input projections, the two state
-// buffers and the bf16 state rows.
+// RNN head workspace after the draft step's: input-projection partials and
+// their step-major sums, the two state buffers and the bf16 state rows.
 struct RnnPlan {
-  size_t off_P, off_S0, off_S1, off_E, ws_bytes;
+  size_t off_P, off_Pk, off_S0, off_S1, off_E, ws_bytes;
 };
 
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -50,6 +50,8 @@ RnnPlan plan_rnn(int R, int V, int rank, int gamma) {
   size_t off = al256(plan_draft_step(R, V, gamma).ws_bytes);
   q.off_P = off;
   off = al256(off + (size_t)kProjSplit * R * gamma * 3 * rank * 4);
+  q.off_Pk = off;
+  off = al256(off + (size_t)R * gamma * 3 * rank * 4);
   q.off_S0 = off;
   off = al256(off + (size_t)R * rank * 4);
   q.off_S1 = off;
@@ -250,6 +252,7 @@ dspark_status dspark_draft_block_rnn(int R, int V, int rank, int d, int gamma, i
   ra.x = x;
   ra.best = args.best;
   ra.P = reinterpret_cast<float*>(wsb + rp.off_P);
+  ra.Pk = reinterpret_cast<float*>(wsb + rp.off_Pk);
   ra.E = reinterpret_cast<uint16_t*>(wsb + rp.off_E);
   float* S[2] = {reinterpret_cast<float*>(wsb + rp.off_S0), reinterpret_cast<float*>(wsb + rp.off_S1)};
   if (launch_rnn_input_proj(ra, st) != hipSuccess) return DSPARK_ERR_LAUNCH;

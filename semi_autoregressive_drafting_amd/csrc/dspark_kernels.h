@@ -63,6 +63,7 @@ struct RnnArgs {
   const int32_t* x;       // [R][gamma + 1] (column 0: the anchor)
   const unsigned long long* best;  // draft steps' winner words [gamma][R]
   float* P;               // input projections, kProjSplit partials [kProjSplit][R * gamma][3 rank]
+  float* Pk;              // their sums, step-major [gamma][R][3 rank]
   uint16_t* E;            // bf16(s_k) [R][rank], the step's bias rows
 };
 hipError_t launch_rnn_input_proj(const RnnArgs& a, hipStream_t stream);

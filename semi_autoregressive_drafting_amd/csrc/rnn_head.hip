@@ -11,8 +11,9 @@
 //
 //   R1 rnn_input_proj   before the block, for every (request, position):
 //      P = W_ih[:, rank:] h + b_ih  [R*gamma][3 rank] fp32 (bf16 MFMA, K = d),
-//      as kProjSplit partial sums over quarters of K that R2 adds in order;
-//      h does not depend on the drafted tokens.
+//      as kProjSplit partial sums over quarters of K; rnn_proj_reduce adds
+//      them in order into the step-major Pk [gamma][R][3 rank].  h does not
+//      depend on the drafted tokens.
 //   R2 rnn_state_step   per step k, after step k-1's winner is known:
 //      the e part W_ih[:, :rank] e (bf16 MFMA, exact products) and the
 //      recurrent part W_hh s (s split into two bf16 terms, hi + lo, so the
@@ -111,6 +112,24 @@ __global__ __launch_bounds__(256) void rnn_input_proj(RnnArgs a) {
   }
 }
 
+// R1b: Pk[k-1][r][o] = sum of the K quarters of P[.][r gamma + k - 1][o] in
+// quarter order: one pass that also makes each step's projections one
+// contiguous block (a step reads R * 3 rank values at once).
+__global__ __launch_bounds__(256) void rnn_proj_reduce(RnnArgs a) {
+  const int n_out = 3 * a.rank;
+  const size_t total = (size_t)a.R * a.gamma * n_out;
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int o = (int)(i % n_out);
+  const size_t kr = i / n_out;  // (k - 1) * R + r
+  const int r = (int)(kr % a.R), km1 = (int)(kr / a.R);
+  const size_t src = ((size_t)r * a.gamma + km1) * n_out + o;
+  float v = a.P[src];
+#pragma unroll
+  for (int q = 1; q < kProjSplit; ++q) v += a.P[(size_t)q * total + src];
+  a.Pk[i] = v;
+}
+
 // R2: workgroup (jb, rt) owns requests 32 rt .. +31 and state entries
 // 32 jb .. +31, with 12 waves: wave w computes gate g = w / 4 (reset, update,
 // new) over the K quarter q = w % 4.  MFMA M = requests, N = state entries:
@@ -162,18 +181,13 @@ __device__ __forceinline__ void state_step_body(const RnnArgs& a, int k, const f
       sp[i] = s_prev[(size_t)r * H + n];
     }
   }
-  // the first quarter also brings the input projection (its partials in order)
+  // the first quarter also brings the input projection of step k
   float pre[16];
   if (q == 0) {
-    const size_t qstride = (size_t)a.R * a.gamma * 3 * H;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int r = min(rt * 32 + 8 * (i >> 2) + 4 * half + (i & 3), a.R - 1);
-      const float* pq = a.P + ((size_t)r * a.gamma + (k - 1)) * (3 * H) + g * H + n;
-      float v = pq[0];
-#pragma unroll
-      for (int p = 1; p < kProjSplit; ++p) v += pq[p * qstride];
-      pre[i] = v;
+      pre[i] = a.Pk[((size_t)(k - 1) * a.R + r) * (3 * H) + g * H + n];
     }
   }
   int tok = k > 1 ? winner_id(a.best[(size_t)(k - 2) * a.R + mc]) : a.x[(size_t)mc * (a.gamma + 1)];
@@ -254,6 +268,10 @@ hipError_t launch_rnn_input_proj(const RnnArgs& a, hipStream_t stream) {
   const int n_rows = a.R * a.gamma, n_out = 3 * a.rank;
   hipLaunchKernelGGL(rnn_input_proj, dim3((n_rows + 63) / 64, (n_out + 255) / 256, kProjSplit),
                      dim3(256), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t total = (size_t)n_rows * n_out;
+  hipLaunchKernelGGL(rnn_proj_reduce, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
