@@ -174,6 +174,44 @@ def cpu_baseline(inp, seed):
                           "seconds": round(dtn, 2)}}
 
 
+def cpu_oracle_next_rows(inp, x_star_row, seed):
+    """The oracle, as it stands, on small samples of the rows beyond the round
+    (one BLAS thread): the RNN head's block, the training losses and their
+    gradients.  Rates are per request-position of the sample."""
+    from threadpoolctl import threadpool_limits
+    from oracle import dspark_oracle as O
+    from semi_autoregressive_drafting_amd import synth
+
+    wl = inp.wl
+    W1, W2t = O.as_f64(inp.W1_store), O.as_f64(inp.W2t_store)
+    gru = synth.gru_weights(wl, 0)
+    g64 = (O.as_f64(gru[0]), O.as_f64(gru[1]), gru[2].astype(np.float64), gru[3].astype(np.float64))
+    out = {}
+    with threadpool_limits(limits=1):
+        reqs = np.arange(4)
+        t0 = time.perf_counter()
+        O.rnn_draft_round(inp.U[reqs], O.as_f64(inp.h_store[reqs]), inp.w, W1, W2t, g64,
+                          inp.anchor[reqs], TEMPERATURE, seed, reqs)
+        dt = time.perf_counter() - t0
+        out["rnn_head_block"] = {"value": len(reqs) * wl.gamma / dt, "unit": "draft tokens/s",
+                                 "sample": f"{len(reqs)} requests, gamma={wl.gamma}", "seconds": round(dt, 2)}
+        reqs = np.arange(2)
+        xs = np.repeat(x_star_row[None], len(reqs), axis=0)
+        t0 = time.perf_counter()
+        O.train_losses(inp.U[reqs], inp.target[reqs], W1, W2t, inp.h_store[reqs], inp.w, xs)
+        dt = time.perf_counter() - t0
+        out["train_loss_forward"] = {"value": len(reqs) * wl.gamma / dt, "unit": "positions/s",
+                                     "sample": f"{len(reqs)} requests", "seconds": round(dt, 2)}
+        reqs = np.arange(1)
+        t0 = time.perf_counter()
+        O.train_loss_grads(inp.U[reqs], inp.target[reqs], W1, W2t, inp.h_store[reqs], inp.w, xs[:1])
+        dt = time.perf_counter() - t0
+        out["train_loss_with_gradients"] = {"value": len(reqs) * wl.gamma / dt, "unit": "positions/s",
+                                            "sample": f"{len(reqs)} request", "seconds": round(dt, 2)}
+    out["cores"] = 1
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -280,8 +318,10 @@ def main():
     # The forward training losses on the same block, the drafted tokens
     # standing in for the target block x* (anchor in column 0).
     train, train_grad = None, None
+    x_star_host = None
     if extras:
         x_star = buf.x.clone()
+        x_star_host = x_star[0].cpu().numpy().astype(np.int64)
         tws = torch.empty(D.dspark_workspace_bytes(D.DSPARK_OP_TRAIN_LOSS, R, V, rank, g),
                           dtype=torch.uint8, device="cuda")
         for _ in range(2):
@@ -297,6 +337,8 @@ def main():
         tb = train_loss_bytes(R, V, rank, d, g)
         t_med = float(np.median(t_us))
         train = {"us": round(t_med, 2), "bytes": tb, "achieved_GBps": round(tb / (t_med * 1e-6) / 1e9, 1),
+                 "frac_of_hbm_peak": round(tb / (t_med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                 "positions_per_s": round(R * g / (t_med * 1e-6), 1),
                  "weighted_sums": [round(float(v), 6) for v in tsums.cpu().tolist()]}
         del tws
         # losses and every gradient
@@ -316,7 +358,9 @@ def main():
         gb = train_grad_bytes(R, V, rank, d, g)
         g_med = float(np.median(g_us))
         train_grad = {"us": round(g_med, 2), "bytes": gb,
-                      "achieved_GBps": round(gb / (g_med * 1e-6) / 1e9, 1)}
+                      "achieved_GBps": round(gb / (g_med * 1e-6) / 1e9, 1),
+                      "frac_of_hbm_peak": round(gb / (g_med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                      "positions_per_s": round(R * g / (g_med * 1e-6), 1)}
         del gws
 
     # The RNN head's draft block on the same inputs (GRU weights from the
@@ -465,6 +509,8 @@ def main():
     if not args.no_cpu_baseline and os.environ.get("RANK", "0") == "0":
         print("# timing the CPU oracle on a bounded sample ...", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(inp, 0)
+        if extras:
+            out["cpu_oracle_next_rows"] = cpu_oracle_next_rows(inp, x_star_host, 0)
     print(json.dumps(out), flush=True)
 
 
