@@ -188,26 +188,26 @@ def cpu_oracle_next_rows(inp, x_star_row, seed):
     g64 = (O.as_f64(gru[0]), O.as_f64(gru[1]), gru[2].astype(np.float64), gru[3].astype(np.float64))
     out = {}
     with threadpool_limits(limits=1):
-        reqs = np.arange(4)
+        reqs = np.arange(16)
         t0 = time.perf_counter()
         O.rnn_draft_round(inp.U[reqs], O.as_f64(inp.h_store[reqs]), inp.w, W1, W2t, g64,
                           inp.anchor[reqs], TEMPERATURE, seed, reqs)
         dt = time.perf_counter() - t0
         out["rnn_head_block"] = {"value": len(reqs) * wl.gamma / dt, "unit": "draft tokens/s",
                                  "sample": f"{len(reqs)} requests, gamma={wl.gamma}", "seconds": round(dt, 2)}
-        reqs = np.arange(2)
+        reqs = np.arange(8)
         xs = np.repeat(x_star_row[None], len(reqs), axis=0)
         t0 = time.perf_counter()
         O.train_losses(inp.U[reqs], inp.target[reqs], W1, W2t, inp.h_store[reqs], inp.w, xs)
         dt = time.perf_counter() - t0
         out["train_loss_forward"] = {"value": len(reqs) * wl.gamma / dt, "unit": "positions/s",
                                      "sample": f"{len(reqs)} requests", "seconds": round(dt, 2)}
-        reqs = np.arange(1)
+        reqs = np.arange(4)
         t0 = time.perf_counter()
-        O.train_loss_grads(inp.U[reqs], inp.target[reqs], W1, W2t, inp.h_store[reqs], inp.w, xs[:1])
+        O.train_loss_grads(inp.U[reqs], inp.target[reqs], W1, W2t, inp.h_store[reqs], inp.w, xs[:4])
         dt = time.perf_counter() - t0
         out["train_loss_with_gradients"] = {"value": len(reqs) * wl.gamma / dt, "unit": "positions/s",
-                                            "sample": f"{len(reqs)} request", "seconds": round(dt, 2)}
+                                            "sample": f"{len(reqs)} requests", "seconds": round(dt, 2)}
     out["cores"] = 1
     return out
 
