@@ -17,8 +17,10 @@
 // a vocabulary-major copy of W2t and a row-major copy of E^T in the
 // workspace.  Every sum runs in a fixed order: results are bit-reproducible.
 //
-//   G2 transpose_w2     W2t [V][rank] -> w2 [rank][vp] (zero past V)
-//   G3 gather_et        E^T [rank][n_pad] from W1 and x* (zero past n_rows)
+//   G2 transpose_w2     W2t [V][rank] -> w2, zero past V
+//   G3 gather_et        E^T from W1 and x*, zero past n_rows
+//      Both copies are chunk-major, [K / 64][rank][64]: the B operand of one
+//      64-wide K chunk of a contraction is one contiguous 32 KB block.
 //   G4 grad_e_partial   per (128-row group, vocabulary slab) partial dz . W2t
 //   G5 grad_e_reduce    slab partials in slab order + dl w[d:]  -> dE
 //   G6 grad_w2t         per 32-entry vocabulary tile, dz^T . E over all rows
@@ -45,8 +47,8 @@ struct GradArgs {
   const int32_t* x;  // x* [R][gamma + 1]
   const float* dz;   // [n_rows][V]
   const float* dl;   // [n_rows]
-  uint16_t* w2;      // [rank][vp]
-  uint16_t* et;      // [rank][n_pad]
+  uint16_t* w2;      // W2t transposed, chunk-major [vp / 64][rank][64]
+  uint16_t* et;      // E^T, chunk-major [n_pad / 64][rank][64]
   float* dep;        // [e_slabs][n_pad][rank]
   float* de;         // [n_rows][rank]
   float* dW1;
@@ -74,8 +76,8 @@ __device__ __forceinline__ bf16x8_t pack_bf16(const float (&v)[8]) {
 }
 
 // ---------------------------------------------------------------------------
-// G2 / G3: 64 x 64 tiles through LDS.  src(row, col) is read along col and
-// written transposed along row: dst[col][row], dst row stride ld.
+// G2 / G3: 64 x 64 tiles through LDS, read along rank and written along K
+// into the chunk-major copy: element (n, k) at ((k / 64) rank + n) 64 + k % 64.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kGThreads) void transpose_w2(GradArgs g) {
   __shared__ uint16_t tile[64][66];
@@ -89,7 +91,7 @@ __global__ __launch_bounds__(kGThreads) void transpose_w2(GradArgs g) {
   for (int i = threadIdx.x; i < 64 * 64; i += kGThreads) {
     const int nn = i >> 6, vv = i & 63;
     const int v = v0 + vv, n = n0 + nn;
-    if (n < g.rank && v < g.vp) g.w2[(size_t)n * g.vp + v] = tile[vv][nn];
+    if (n < g.rank && v < g.vp) g.w2[((size_t)(v >> 6) * g.rank + n) * 64 + (v & 63)] = tile[vv][nn];
   }
 }
 
@@ -107,16 +109,17 @@ __global__ __launch_bounds__(kGThreads) void gather_et(GradArgs g) {
   for (int i = threadIdx.x; i < 64 * 64; i += kGThreads) {
     const int nn = i >> 6, rr = i & 63;
     const int row = r0 + rr, n = n0 + nn;
-    if (n < g.rank && row < g.n_pad) g.et[(size_t)n * g.n_pad + row] = tile[rr][nn];
+    if (n < g.rank && row < g.n_pad)
+      g.et[((size_t)(row >> 6) * g.rank + n) * 64 + (row & 63)] = tile[rr][nn];
   }
 }
 
 // ---------------------------------------------------------------------------
 // The two contractions share one shape: a workgroup of 4 waves, each wave a
 // 32 x (32 NC) fp32 output block in MFMA accumulators, K walked in chunks of
-// 64.  The B operand of a chunk (rows 0 .. 32 NC - 1 of a bf16 matrix whose
-// rows hold K contiguously) is common to the 4 waves: the workgroup copies it
-// into LDS once (16 bytes per thread and piece, rows padded to 72 elements so
+// 64.  The B operand of a chunk (32 NC rows of 64 K values, one contiguous
+// block of the chunk-major copy) is common to the 4 waves: the workgroup
+// copies it into LDS once (16 bytes per thread and piece, rows padded to 72 elements so
 // that the lanes' 16-byte reads spread over all banks), loading chunk i+1 into
 // registers while chunk i multiplies.  MFMA operands for K step s of a chunk:
 //   A:  lane (m = l%32, half h) holds the 8 values k = 16 s + 8 h .. +7 of row m
@@ -128,11 +131,12 @@ template <int NC>
 struct BChunk {
   static constexpr int kPer = NC;  // 16-byte pieces per thread: NC * 32 rows * 8 pieces / 256
   u32x4_t reg[kPer];
-  __device__ __forceinline__ void load(const uint16_t* src, int ld, int k0) {
+  // chunk: the block of one K chunk, rows of 64 values
+  __device__ __forceinline__ void load(const uint16_t* chunk) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      const int p = threadIdx.x + kGThreads * i, n = p >> 3, q = p & 7;
-      reg[i] = *reinterpret_cast<const u32x4_t*>(src + (size_t)n * ld + k0 + 8 * q);
+      const int p = threadIdx.x + kGThreads * i;
+      reg[i] = *reinterpret_cast<const u32x4_t*>(chunk + 8 * p);
     }
   }
   __device__ __forceinline__ void store(uint16_t* lds) const {
@@ -160,16 +164,17 @@ __device__ __forceinline__ void mma_chunk(f32x16_t (&acc)[NC], const bf16x8_t (&
 }
 
 // Chunk loop over [c_begin, c_end) (at least one chunk).  load_a(a, chunk)
-// fills a wave's A values; B rows come from `bsrc` (row stride ld).
+// fills a wave's A values; B comes from the chunk-major copy `bsrc`.
 template <int NC, class LoadA>
-__device__ __forceinline__ void contract(f32x16_t (&acc)[NC], const uint16_t* bsrc, int ld,
-                                         int c_begin, int c_end, uint16_t* lds, LoadA load_a) {
+__device__ __forceinline__ void contract(f32x16_t (&acc)[NC], const uint16_t* bsrc, int c_begin,
+                                         int c_end, uint16_t* lds, LoadA load_a) {
+  constexpr size_t kChunkElems = (size_t)NC * 32 * kChunk;
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5, col = lane & 31;
   BChunk<NC> b;
   float nxt[4][8];
   bf16x8_t cur[4];  // the current chunk's A operands, rounded to bf16 on arrival
-  b.load(bsrc, ld, c_begin * kChunk);
+  b.load(bsrc + c_begin * kChunkElems);
   load_a(nxt, c_begin);
 #pragma unroll
   for (int s = 0; s < 4; ++s) cur[s] = pack_bf16(nxt[s]);
@@ -178,7 +183,7 @@ __device__ __forceinline__ void contract(f32x16_t (&acc)[NC], const uint16_t* bs
   for (int ch = c_begin; ch < c_end; ++ch) {
     // the next chunk (the last one again at the end: loads stay unconditional)
     const int cn = ch + 1 < c_end ? ch + 1 : ch;
-    b.load(bsrc, ld, cn * kChunk);
+    b.load(bsrc + cn * kChunkElems);
     load_a(nxt, cn);
     mma_chunk<NC>(acc, cur, lds, col, half);
     lds_barrier();  // every wave is past its reads of this chunk
@@ -196,7 +201,18 @@ __global__ __launch_bounds__(kGThreads) void grad_e_partial(GradArgs g) {
   __shared__ __align__(16) uint16_t lds[NC * 32 * kLdsRow];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = lane >> 5, col = lane & 31;
-  const int grp = blockIdx.x % g.e_groups, slab = blockIdx.x / g.e_groups;
+  // blockIdx -> (group, slab): workgroups are dealt to the 8 XCDs in turn, so
+  // when the slabs divide evenly among them every group of a slab runs on one
+  // XCD and the slab's w2 chunks are fetched into one L2 only.
+  int grp, slab;
+  if (g.e_slabs % 8 == 0) {
+    const int xcd = blockIdx.x % 8, j = blockIdx.x / 8;
+    slab = xcd * (g.e_slabs / 8) + j / g.e_groups;
+    grp = j % g.e_groups;
+  } else {
+    grp = blockIdx.x % g.e_groups;
+    slab = blockIdx.x / g.e_groups;
+  }
   const int rt = grp * 4 + wave;
   const int row = rt * 32 + col;
   const int rowc = row < g.n_rows ? row : g.n_rows - 1;
@@ -225,7 +241,7 @@ __global__ __launch_bounds__(kGThreads) void grad_e_partial(GradArgs g) {
       }
     }
   };
-  contract<NC>(acc, g.w2, g.vp, c_begin, c_end, lds, load_a);
+  contract<NC>(acc, g.w2, c_begin, c_end, lds, load_a);
   // accumulator i of lane l: row 8 (i/4) + 4 half + i%4 of the tile, rank c*32 + l%32
   float* out = g.dep + (size_t)slab * g.n_pad * g.rank;
 #pragma unroll
@@ -273,7 +289,7 @@ __global__ __launch_bounds__(kGThreads) void grad_w2t(GradArgs g) {
         a[s][j] = (vin && rr < g.n_rows) ? zcol[(size_t)rr * g.V] : 0.0f;
       }
   };
-  contract<NC>(acc, g.et, g.n_pad, 0, g.n_pad / kChunk, lds, load_a);
+  contract<NC>(acc, g.et, 0, g.n_pad / kChunk, lds, load_a);
 #pragma unroll
   for (int c = 0; c < NC; ++c)
 #pragma unroll
