@@ -453,7 +453,7 @@ def tv_acceptance(p_d, p_t):
     return 1.0 - 0.5 * np.abs(np.asarray(p_d) - np.asarray(p_t)).sum(axis=-1)
 
 
-def verify(U, Tl, W1, W2t, x, ell, T, seed, req_ids):
+def verify(U, Tl, W1, W2t, x, ell, T, seed, req_ids, E=None):
     """Per-position c* for all gamma positions, then standard rejection sampling
     over each request's admitted prefix (positions 1..ell_r).
 
@@ -461,6 +461,8 @@ def verify(U, Tl, W1, W2t, x, ell, T, seed, req_ids):
     token block (x[:,0] = anchor); ell: [n].  Returns a dict with c_star
     [n,gamma], overlap [n,gamma] (= sum min(p_d, p_t)), n_accept [n],
     next_token [n], tau [n] and per-request diagnostics for near-tie counting.
+    E [n, gamma, rank], if given, holds the bias rows of each position in place
+    of W1[x_{k-1}] (blocks drafted by the RNN head).
     """
     U = np.asarray(U)
     n, g, V = U.shape
@@ -471,7 +473,10 @@ def verify(U, Tl, W1, W2t, x, ell, T, seed, req_ids):
                            "accept_margin", "sample_gap", "p_d_x", "p_t_x")}
     for i in range(n):
         req = int(req_ids[i])
-        z_d = draft_logits(U[i], W1, W2t, x[i, :g])              # rows k = 1..gamma
+        if E is None:
+            z_d = draft_logits(U[i], W1, W2t, x[i, :g])          # rows k = 1..gamma
+        else:
+            z_d = np.asarray(U[i], dtype=np.float64) + np.asarray(E[i], dtype=np.float64) @ W2t.T
         z_t = np.asarray(Tl[i], dtype=np.float64)
         # greedy drafting's law at position k is the point mass on its drafted token
         p_d = draft_distribution(z_d, T) if T > 0 else np.eye(V)[x[i, 1:]]
@@ -525,9 +530,6 @@ def verify(U, Tl, W1, W2t, x, ell, T, seed, req_ids):
 
 
 # ----------------------------------------------------------------------------
-# A whole draft round (free running), for the smoke check and the CPU baseline
-# ----------------------------------------------------------------------------
-# ----------------------------------------------------------------------------
 # RNN head  [P1 §2.4; P3 アーキテクチャ]: a block-internal state s_k, updated
 # by a gate from the previous state (the longer prefix), the previous token's
 # embedding and the backbone state h_k.  The pages give no equations; the
@@ -564,25 +566,31 @@ def rnn_draft_round(U, h, w, W1, W2t, gru, anchor, T, seed, req_ids):
     """gamma steps of the RNN head: s_k = gru(s_{k-1}, [W1[x_{k-1}]; h_k]), then the
     step of draft_step with bf16(s_k) as its rows; confidence and survival as
     for the Markov head (c_k from h_k and W1[x_{k-1}]).  gru = (W_ih, W_hh,
-    b_ih, b_hh) in fp64.  Also returns the final state s_gamma."""
+    b_ih, b_hh) in fp64.  Also returns the final state s_gamma and the bias rows
+    bf16(s_k) of every position (what verification needs in place of W1[x])."""
     W_ih, W_hh, b_ih, b_hh = gru
     n, g, V = U.shape
     rank = W1.shape[1]
     x = np.empty((n, g + 1), dtype=np.int64)
     x[:, 0] = anchor
     p = np.empty((n, g)); lse = np.empty((n, g)); c = np.empty((n, g)); gap = np.empty((n, g))
+    rows = np.empty((n, g, rank))
     st_ = np.zeros((n, rank))
     for k in range(1, g + 1):
         e = W1[x[:, k - 1]]
         hk = np.asarray(h[:, k - 1], dtype=np.float64)
         st_ = gru_cell(np.concatenate([e, hk], axis=1), st_, W_ih, W_hh, b_ih, b_hh)
-        step = draft_step(U[:, k - 1], W1, W2t, x[:, k - 1], T, seed, k, req_ids, E=bf16_round(st_))
+        rows[:, k - 1] = bf16_round(st_)
+        step = draft_step(U[:, k - 1], W1, W2t, x[:, k - 1], T, seed, k, req_ids, E=rows[:, k - 1])
         c[:, k - 1] = confidence(hk, w, W1, x[:, k - 1])
         x[:, k], p[:, k - 1], lse[:, k - 1], gap[:, k - 1] = step["x"], step["p"], step["lse"], step["gap"]
     return {"x": x, "p": p, "lse": lse, "c": c, "a": survival(c.astype(np.float32)),
-            "state": st_, "gap": gap}
+            "state": st_, "gap": gap, "rows": rows}
 
 
+# ----------------------------------------------------------------------------
+# A whole draft round (free running), for the smoke check and the CPU baseline
+# ----------------------------------------------------------------------------
 def draft_round(U, h, w, W1, W2t, anchor, T, seed, req_ids):
     """gamma sequential steps [P1 §6.2 loop semantics: prev = sampled token],
     confidence and survival for each position.  Inputs in fp64/fp32 arrays:

@@ -709,6 +709,32 @@ def test_rnn_head_memoryless_gate_is_markov_with_tanh_rows():
     np.testing.assert_allclose(rnn["state"], np.tanh(W1[rnn["x"][:, -2]]), rtol=1e-12)
 
 
+def test_verify_with_markov_rows_equals_verify():
+    """Verification with explicit bias rows W1[x_{k-1}] is verification itself."""
+    inp = synth.generate("tiny_v1024_r4_g4", seed=0, target=True)
+    W1, W2t = O.as_f64(inp.W1_store), O.as_f64(inp.W2t_store)
+    rnd = O.draft_round(inp.U, O.as_f64(inp.h_store), inp.w, W1, W2t, inp.anchor, 1.0, 3, inp.req_ids)
+    ell = np.array([4, 2, 0, 3])
+    a = O.verify(inp.U, inp.target, W1, W2t, rnd["x"], ell, 1.0, 3, inp.req_ids)
+    b = O.verify(inp.U, inp.target, W1, W2t, rnd["x"], ell, 1.0, 3, inp.req_ids,
+                 E=W1[rnd["x"][:, :inp.wl.gamma]])
+    for key in ("c_star", "n_accept", "next_token", "tau"):
+        np.testing.assert_array_equal(a[key], b[key])
+
+
+def test_rnn_rows_reproduce_the_drafted_probabilities():
+    """The rows an RNN block returns give back, through verification's own
+    logits, the kept draft probabilities of the drafted tokens."""
+    inp = synth.generate("tiny_v1024_r4_g4", seed=0, target=True)
+    wl = inp.wl
+    W1, W2t = O.as_f64(inp.W1_store), O.as_f64(inp.W2t_store)
+    rnd = O.rnn_draft_round(inp.U, O.as_f64(inp.h_store), inp.w, W1, W2t, _gru64(wl), inp.anchor,
+                            1.0, 5, inp.req_ids)
+    v = O.verify(inp.U, inp.target, W1, W2t, rnd["x"], np.full(wl.R, wl.gamma), 1.0, 5,
+                 inp.req_ids, E=rnd["rows"])
+    np.testing.assert_allclose(v["p_d_x"], rnd["p"], rtol=1e-12)
+
+
 def test_rnn_block_distribution_sums_to_one():
     """The RNN head's block law prod_k p_k(x_k | x_0..x_{k-1}) (the state carries
     the whole prefix) sums to 1 over the 8^3 blocks, depends on more than the
