@@ -165,7 +165,9 @@ dspark_status dspark_draft_block_phases(int R, int V, int rank, int d, int gamma
  * DSPARK_ERR_DTYPE; h and w required), plus W_ih bf16 [3 rank][rank + d],
  * W_hh bf16 [3 rank][rank], b_ih, b_hh fp32 [3 rank].  rank must be a
  * multiple of 32 and d of 16 (DSPARK_ERR_SHAPE).  Outputs as
- * dspark_draft_block, plus state fp32 [R][rank] = s_gamma (16-byte aligned).
+ * dspark_draft_block, plus state fp32 [R][rank] = s_gamma (16-byte aligned)
+ * and, unless rows is NULL, rows bf16 [R][gamma][rank] = bf16(s_k) of every
+ * position: the bias rows that dspark_verify_rnn needs.
  * ws: dspark_workspace_bytes(DSPARK_OP_DRAFT_RNN, ...) bytes, zero-filled
  * once before first use (the draft step's part is left zeroed by each call).
  */
@@ -174,8 +176,8 @@ dspark_status dspark_draft_block_rnn(int R, int V, int rank, int d, int gamma, i
                                      const void* h, const float* w, const void* W_ih,
                                      const void* W_hh, const float* b_ih, const float* b_hh,
                                      float temperature, uint64_t seed, int32_t* x, float* p,
-                                     float* lse, float* c, float* a, float* state, void* ws,
-                                     size_t ws_bytes, dspark_stream_t stream);
+                                     float* lse, float* c, float* a, float* state, void* rows,
+                                     void* ws, size_t ws_bytes, dspark_stream_t stream);
 
 /*
  * Confidence head and survival for a whole drafted block
@@ -252,6 +254,21 @@ dspark_status dspark_verify(int R, int V, int rank, int gamma, int dt, const voi
                             float* c_star, int32_t* n_accept, int32_t* next_token,
                             int32_t* tau, float* tau_mean, void* ws, size_t ws_bytes,
                             dspark_stream_t stream);
+
+/*
+ * dspark_verify for blocks drafted by the RNN head [P1 §2.4]: p_d at
+ * position k is recomputed from rows[r][k-1] (bf16 [R][gamma][rank], 16-byte
+ * aligned, as written by dspark_draft_block_rnn) in place of W1[x[r][k-1]];
+ * everything else, arguments, outputs, workspace and errors included, is
+ * dspark_verify's.  rows NULL -> DSPARK_ERR_NULL.
+ */
+dspark_status dspark_verify_rnn(int R, int V, int rank, int gamma, int dt, const void* W1,
+                                const void* W2t, const float* U, const float* target,
+                                const int32_t* x, const void* rows, const float* lse_d,
+                                const float* p_d_x, const int32_t* ell, float temperature,
+                                uint64_t seed, float* c_star, int32_t* n_accept,
+                                int32_t* next_token, int32_t* tau, float* tau_mean, void* ws,
+                                size_t ws_bytes, dspark_stream_t stream);
 
 /*
  * Training losses of the sequential and confidence heads [P1 §5 训练目标; P3

@@ -155,6 +155,57 @@ dspark_status check_draft(int R, int V, int rank, int d, int gamma, int k, int d
   return DSPARK_OK;
 }
 
+dspark_status verify_common(int R, int V, int rank, int gamma, int dt, const void* W1,
+                                   const void* W2t, const float* U, const float* target,
+                                   const int32_t* x, const void* rows, const float* lse_d,
+                                   const float* p_d_x, const int32_t* ell, float temperature,
+                                   uint64_t seed, float* c_star, int32_t* n_accept,
+                                   int32_t* next_token, int32_t* tau, float* tau_mean, void* ws,
+                                   size_t ws_bytes, dspark_stream_t stream) {
+  if (dt != DSPARK_F32 && dt != DSPARK_BF16) return DSPARK_ERR_DTYPE;
+  if (!W1 || !W2t || !U || !target || !x || !lse_d || !p_d_x || !ell || !c_star || !n_accept ||
+      !next_token || !tau || !tau_mean)
+    return DSPARK_ERR_NULL;
+  if (R < 1 || R > kMaxR || V < 2 || V > kMaxV || gamma < 1 || gamma > kMaxGamma)
+    return DSPARK_ERR_SHAPE;
+  dspark_status s = check_rank(dt, rank);
+  if (s != DSPARK_OK) return s;
+  if (!aligned16(W1) || !aligned16(W2t) || (rows && !aligned16(rows)) ||
+      ((V % 4) == 0 && (!aligned16(U) || !aligned16(target))))
+    return DSPARK_ERR_SHAPE;
+  if (bad_temperature(temperature)) return DSPARK_ERR_VALUE;
+  const VerifyPlan plan = plan_verify(R, V, gamma);
+  if (!ws || ws_bytes < plan.ws_bytes || !aligned16(ws)) return DSPARK_ERR_WORKSPACE;
+
+  VerifyArgs args{};
+  args.R = R;
+  args.V = V;
+  args.rank = rank;
+  args.gamma = gamma;
+  args.bf16 = dt == DSPARK_BF16;
+  args.greedy = temperature == 0.0f;
+  args.W1 = W1;
+  args.W2t = W2t;
+  args.U = U;
+  args.target = target;
+  args.x = x;
+  args.E_rows = rows;
+  args.lse_d = lse_d;
+  args.p_d_x = p_d_x;
+  args.ell = ell;
+  args.kscale = kscale_of(temperature);
+  args.seed = seed;
+  args.c_star = c_star;
+  args.n_accept = n_accept;
+  args.next_token = next_token;
+  args.tau = tau;
+  args.tau_mean = tau_mean;
+  args.ws = static_cast<unsigned char*>(ws);
+  if (launch_verify(args, plan, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return DSPARK_ERR_LAUNCH;
+  return DSPARK_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -221,8 +272,8 @@ dspark_status dspark_draft_block_rnn(int R, int V, int rank, int d, int gamma, i
                                      const void* h, const float* w, const void* W_ih,
                                      const void* W_hh, const float* b_ih, const float* b_hh,
                                      float temperature, uint64_t seed, int32_t* x, float* p,
-                                     float* lse, float* c, float* a, float* state, void* ws,
-                                     size_t ws_bytes, dspark_stream_t stream) {
+                                     float* lse, float* c, float* a, float* state, void* rows,
+                                     void* ws, size_t ws_bytes, dspark_stream_t stream) {
   if (!h || !w || !W_ih || !W_hh || !b_ih || !b_hh || !state) return DSPARK_ERR_NULL;
   if (dt != DSPARK_BF16) return DSPARK_ERR_DTYPE;  // the state rows are bf16 like W1
   if (rank % 32 != 0 || d % 16 != 0) return DSPARK_ERR_SHAPE;
@@ -254,6 +305,7 @@ dspark_status dspark_draft_block_rnn(int R, int V, int rank, int d, int gamma, i
   ra.P = reinterpret_cast<float*>(wsb + rp.off_P);
   ra.Pk = reinterpret_cast<float*>(wsb + rp.off_Pk);
   ra.E = reinterpret_cast<uint16_t*>(wsb + rp.off_E);
+  ra.rows_out = static_cast<uint16_t*>(rows);
   float* S[2] = {reinterpret_cast<float*>(wsb + rp.off_S0), reinterpret_cast<float*>(wsb + rp.off_S1)};
   if (launch_rnn_input_proj(ra, st) != hipSuccess) return DSPARK_ERR_LAUNCH;
   args.E_rows = ra.E;
@@ -322,47 +374,22 @@ dspark_status dspark_verify(int R, int V, int rank, int gamma, int dt, const voi
                             float* c_star, int32_t* n_accept, int32_t* next_token,
                             int32_t* tau, float* tau_mean, void* ws, size_t ws_bytes,
                             dspark_stream_t stream) {
-  if (dt != DSPARK_F32 && dt != DSPARK_BF16) return DSPARK_ERR_DTYPE;
-  if (!W1 || !W2t || !U || !target || !x || !lse_d || !p_d_x || !ell || !c_star || !n_accept ||
-      !next_token || !tau || !tau_mean)
-    return DSPARK_ERR_NULL;
-  if (R < 1 || R > kMaxR || V < 2 || V > kMaxV || gamma < 1 || gamma > kMaxGamma)
-    return DSPARK_ERR_SHAPE;
-  dspark_status s = check_rank(dt, rank);
-  if (s != DSPARK_OK) return s;
-  if (!aligned16(W1) || !aligned16(W2t) ||
-      ((V % 4) == 0 && (!aligned16(U) || !aligned16(target))))
-    return DSPARK_ERR_SHAPE;
-  if (bad_temperature(temperature)) return DSPARK_ERR_VALUE;
-  const VerifyPlan plan = plan_verify(R, V, gamma);
-  if (!ws || ws_bytes < plan.ws_bytes || !aligned16(ws)) return DSPARK_ERR_WORKSPACE;
+  return verify_common(R, V, rank, gamma, dt, W1, W2t, U, target, x, nullptr, lse_d, p_d_x, ell,
+                       temperature, seed, c_star, n_accept, next_token, tau, tau_mean, ws,
+                       ws_bytes, stream);
+}
 
-  VerifyArgs args{};
-  args.R = R;
-  args.V = V;
-  args.rank = rank;
-  args.gamma = gamma;
-  args.bf16 = dt == DSPARK_BF16;
-  args.greedy = temperature == 0.0f;
-  args.W1 = W1;
-  args.W2t = W2t;
-  args.U = U;
-  args.target = target;
-  args.x = x;
-  args.lse_d = lse_d;
-  args.p_d_x = p_d_x;
-  args.ell = ell;
-  args.kscale = kscale_of(temperature);
-  args.seed = seed;
-  args.c_star = c_star;
-  args.n_accept = n_accept;
-  args.next_token = next_token;
-  args.tau = tau;
-  args.tau_mean = tau_mean;
-  args.ws = static_cast<unsigned char*>(ws);
-  if (launch_verify(args, plan, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
-    return DSPARK_ERR_LAUNCH;
-  return DSPARK_OK;
+dspark_status dspark_verify_rnn(int R, int V, int rank, int gamma, int dt, const void* W1,
+                                const void* W2t, const float* U, const float* target,
+                                const int32_t* x, const void* rows, const float* lse_d,
+                                const float* p_d_x, const int32_t* ell, float temperature,
+                                uint64_t seed, float* c_star, int32_t* n_accept,
+                                int32_t* next_token, int32_t* tau, float* tau_mean, void* ws,
+                                size_t ws_bytes, dspark_stream_t stream) {
+  if (!rows) return DSPARK_ERR_NULL;
+  return verify_common(R, V, rank, gamma, dt, W1, W2t, U, target, x, rows, lse_d, p_d_x, ell,
+                       temperature, seed, c_star, n_accept, next_token, tau, tau_mean, ws,
+                       ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -64,6 +64,7 @@ struct RnnArgs {
   const unsigned long long* best;  // draft steps' winner words [gamma][R]
   float* P;               // input projections, kProjSplit partials [kProjSplit][R * gamma][3 rank]
   float* Pk;              // their sums, step-major [gamma][R][3 rank]
+  uint16_t* rows_out;     // optional: bf16(s_k) of every position [R][gamma][rank]
   uint16_t* E;            // bf16(s_k) [R][rank], the step's bias rows
 };
 hipError_t launch_rnn_input_proj(const RnnArgs& a, hipStream_t stream);
@@ -124,6 +125,7 @@ struct VerifyArgs {
   const float* U;
   const float* target;
   const int32_t* x;
+  const void* E_rows;      // RNN head: bias rows per (request, position) [R][gamma][rank]; null: W1[x]
   const float* lse_d;
   const float* p_d_x;
   const int32_t* ell;
@@ -155,8 +157,8 @@ struct TrainPlan {
   int vp;           // vocabulary rounded up to 64
   int e_groups;     // 128-row groups of the dE contraction
   int e_slabs;      // vocabulary slabs of the dE contraction
-  size_t off_w2;    // W2t transposed, bf16 [rank][vp]
-  size_t off_et;    // gathered W1 rows transposed, bf16 [rank][n_pad]
+  size_t off_w2;    // W2t transposed, bf16, chunk-major [vp / 64][rank][64]
+  size_t off_et;    // gathered W1 rows transposed, bf16, chunk-major [n_pad / 64][rank][64]
   size_t off_dep;   // dE slab partials [e_slabs][n_pad][rank]
   size_t off_de;    // dE [n_rows][rank]
   size_t off_dwp;   // dw partial sums over row ranges, fp64 [16][d + rank]

@@ -249,6 +249,7 @@ __device__ __forceinline__ void state_step_body(const RnnArgs& a, int k, const f
     const float s = (1.0f - zg) * ng + zg * (kRec ? sp[i] : 0.0f);
     s_next[(size_t)r * H + n] = s;
     a.E[(size_t)r * H + n] = bf16_bits_rne(s);
+    if (a.rows_out) a.rows_out[((size_t)r * a.gamma + (k - 1)) * H + n] = bf16_bits_rne(s);
   }
 }
 

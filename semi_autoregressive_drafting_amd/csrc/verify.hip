@@ -242,6 +242,17 @@ __global__ __launch_bounds__(kAcceptThreads) void verify_accept(VerifyArgs a, Ve
   if (t == 0) *a.tau_mean = (float)stau[0] / (float)a.R;
 }
 
+// E fragments of request r at position k: the caller's bias rows (RNN head)
+// or the Markov rows W1[x_{k-1}].
+template <class W, int kKs>
+__device__ __forceinline__ void verify_gather(typename W::frag_t (&ef)[W::kMaxKs],
+                                              const VerifyArgs& a, int r, int k, int half) {
+  if (a.E_rows)
+    load_e_frags<W, kKs>(ef, a.E_rows, r * a.gamma + (k - 1), a.rank, a.R * a.gamma, half);
+  else
+    load_e_frags<W, kKs>(ef, a.W1, a.x[(size_t)r * (a.gamma + 1) + (k - 1)], a.rank, a.V, half);
+}
+
 // Map blockIdx to (slab, group); the groups of one slab share an XCD.
 __device__ __forceinline__ void slab_group(int b, int n_slabs, int n_groups, int& slab, int& grp) {
   if (n_groups == 1 || n_slabs % 8 != 0) {
@@ -366,9 +377,7 @@ __global__ __launch_bounds__(kTvThreads) void verify_tv(VerifyArgs a, VerifyPlan
   epi.lse2_t = reinterpret_cast<const float*>(a.ws + p.off_lse_t)[rowc];
   epi.sabs = 0.0f;
   epi.smu = 0.0f;
-  auto gather = [&](typename W::frag_t(&ef)[W::kMaxKs]) {
-    load_e_frags<W, kKs>(ef, a.W1, a.x[(size_t)r * (a.gamma + 1) + (k - 1)], a.rank, a.V, half);
-  };
+  auto gather = [&](typename W::frag_t(&ef)[W::kMaxKs]) { verify_gather<W, kKs>(ef, a, r, k, half); };
   shared_a_stream<W, kKs, kVerifyDist, kTvThreads>(a.W2t, a.V, a.rank, t_begin, t_end, e, gather,
                                                    lds, epi);
 
@@ -471,9 +480,7 @@ __global__ __launch_bounds__(kStreamThreads) void verify_sample(VerifyArgs a, Ve
   epi.bE = 0.0f;
   epi.bLn = -1.0f;
   epi.bV = -1;
-  auto gather = [&](typename W::frag_t(&ef)[W::kMaxKs]) {
-    load_e_frags<W, kKs>(ef, a.W1, a.x[(size_t)rc * (a.gamma + 1) + (k - 1)], a.rank, a.V, half);
-  };
+  auto gather = [&](typename W::frag_t(&ef)[W::kMaxKs]) { verify_gather<W, kKs>(ef, a, rc, k, half); };
   shared_a_stream<W, kKs, kVerifyDist>(a.W2t, a.V, a.rank, t_begin, t_end, e, gather, lds, epi);
 
   float key = (epi.bV >= 0 && epi.bE > 0.0f) ? fast_log2(epi.bE) - fast_log2(-epi.bLn) : -INFINITY;

@@ -24,7 +24,7 @@ DSPARK_PHASE_STEPS, DSPARK_PHASE_MERGE = 1, 2
 EXPORTS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_draft_step",
            "dspark_draft_block", "dspark_draft_block_phases", "dspark_confidence", "dspark_schedule", "dspark_schedule_async",
            "dspark_verify", "dspark_train_loss", "dspark_train_loss_grad",
-           "dspark_draft_block_rnn")
+           "dspark_draft_block_rnn", "dspark_verify_rnn")
 
 _lib = None
 
@@ -74,7 +74,10 @@ def load():
                                          P, P, P, P, P, P, P, P, SZ, P]
     L.dspark_train_loss_grad.restype = I
     L.dspark_draft_block_rnn.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P, F, U64,
-                                         P, P, P, P, P, P, P, SZ, P]
+                                         P, P, P, P, P, P, P, P, SZ, P]
+    L.dspark_verify_rnn.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, P, F, U64,
+                                    P, P, P, P, P, P, SZ, P]
+    L.dspark_verify_rnn.restype = I
     L.dspark_draft_block_rnn.restype = I
     _lib = L
     return L
@@ -194,11 +197,22 @@ def dspark_train_loss_grad(R, V, rank, d, gamma, dt, W1, W2t, U, h, w, target, x
 
 
 def dspark_draft_block_rnn(R, V, rank, d, gamma, dt, W1, W2t, U, h, w, W_ih, W_hh, b_ih, b_hh,
-                           temperature, seed, x, p, lse, c, a, state, ws, ws_bytes=None,
+                           temperature, seed, x, p, lse, c, a, state, rows, ws, ws_bytes=None,
                            stream=None):
     if ws_bytes is None:
         ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
     _call("dspark_draft_block_rnn", R, V, rank, d, gamma, dt, _ptr(W1), _ptr(W2t), _ptr(U),
           _ptr(h), _ptr(w), _ptr(W_ih), _ptr(W_hh), _ptr(b_ih), _ptr(b_hh), float(temperature),
-          int(seed), _ptr(x), _ptr(p), _ptr(lse), _ptr(c), _ptr(a), _ptr(state), _ptr(ws),
+          int(seed), _ptr(x), _ptr(p), _ptr(lse), _ptr(c), _ptr(a), _ptr(state), _ptr(rows),
+          _ptr(ws), int(ws_bytes), _stream(stream))
+
+
+def dspark_verify_rnn(R, V, rank, gamma, dt, W1, W2t, U, target, x, rows, lse_d, p_d_x, ell,
+                      temperature, seed, c_star, n_accept, next_token, tau, tau_mean, ws,
+                      ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _call("dspark_verify_rnn", R, V, rank, gamma, dt, _ptr(W1), _ptr(W2t), _ptr(U), _ptr(target),
+          _ptr(x), _ptr(rows), _ptr(lse_d), _ptr(p_d_x), _ptr(ell), float(temperature), int(seed),
+          _ptr(c_star), _ptr(n_accept), _ptr(next_token), _ptr(tau), _ptr(tau_mean), _ptr(ws),
           int(ws_bytes), _stream(stream))

@@ -200,11 +200,21 @@ class RnnWeights:
 
 
 def draft_rnn(di: DeviceInputs, buf: RoundBuffers, rw: RnnWeights, temperature: float, seed: int,
-              state: torch.Tensor, ws: torch.Tensor):
+              state: torch.Tensor, ws: torch.Tensor, rows: torch.Tensor | None = None):
     """gamma steps of the RNN head (state update, then the draft step) and the
-    record merge; s_gamma lands in `state` [R][rank] fp32.  `ws` holds
-    dspark_workspace_bytes(DSPARK_OP_DRAFT_RNN, ...) bytes, zero-filled once."""
+    record merge; s_gamma lands in `state` [R][rank] fp32 and, if given, the
+    bias rows bf16(s_k) of every position in `rows` [R][gamma][rank] (int16
+    storage).  `ws` holds dspark_workspace_bytes(DSPARK_OP_DRAFT_RNN, ...)
+    bytes, zero-filled once."""
     buf.x[:, 0].copy_(di.anchor)
     D.dspark_draft_block_rnn(di.R, di.V, di.rank, di.d, di.gamma, di.dt, di.W1, di.W2t, di.U, di.h,
                              di.w, rw.W_ih, rw.W_hh, rw.b_ih, rw.b_hh, temperature, seed, buf.x,
-                             buf.p, buf.lse, buf.c, buf.a, state, ws)
+                             buf.p, buf.lse, buf.c, buf.a, state, rows, ws)
+
+
+def verify_rnn(di: DeviceInputs, buf: RoundBuffers, rows: torch.Tensor, temperature: float,
+               seed: int):
+    """Verification of an RNN-head block, its bias rows from draft_rnn."""
+    D.dspark_verify_rnn(di.R, di.V, di.rank, di.gamma, di.dt, di.W1, di.W2t, di.U, di.target,
+                        buf.x, rows, buf.lse, buf.p, buf.ell, temperature, seed, buf.c_star,
+                        buf.n_accept, buf.next_token, buf.tau, buf.tau_mean, buf.vws)

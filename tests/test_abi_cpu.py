@@ -190,9 +190,10 @@ def test_train_loss_grad_validation():
 
 def test_draft_block_rnn_validation():
     f = D.load().dspark_draft_block_rnn
-    # bf16, rank 64, d 64; W_ih, W_hh, b_ih, b_hh at 11 .. 14; state 22; ws_bytes 24
+    # bf16, rank 64, d 64; W_ih, W_hh, b_ih, b_hh at 11 .. 14; state 22; rows 23
+    # (optional); ws_bytes 25
     base = [4, 1024, 64, 64, 4, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1.0, 7,
-            FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None]
+            FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None]
     def call(**kw):
         a = list(base)
         for i, v in kw.items():
@@ -206,8 +207,25 @@ def test_draft_block_rnn_validation():
     assert call(a15=-1.0) == D.DSPARK_ERR_VALUE
     need = D.dspark_workspace_bytes(D.DSPARK_OP_DRAFT_RNN, 4, 1024, 64, 4)
     assert need > D.dspark_workspace_bytes(D.DSPARK_OP_DRAFT_STEP, 4, 1024, 64, 4)
-    assert call(a24=need - 1) == D.DSPARK_ERR_WORKSPACE
+    assert call(a25=need - 1) == D.DSPARK_ERR_WORKSPACE
     assert D.dspark_workspace_bytes(D.DSPARK_OP_DRAFT_RNN, 4, 1024, 48, 4) == 0
+
+
+def test_verify_rnn_validation():
+    f = D.load().dspark_verify_rnn
+    # rows at 10; ws_bytes at 22
+    base = [4, 1024, 32, 4, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1.0, 7,
+            FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None]
+    def call(**kw):
+        a = list(base)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a10=None) == D.DSPARK_ERR_NULL          # the bias rows are required
+    assert call(a10=FAKE + 8) == D.DSPARK_ERR_SHAPE     # and 16-byte aligned
+    assert call(a9=None) == D.DSPARK_ERR_NULL
+    assert call(a14=-1.0) == D.DSPARK_ERR_VALUE
+    assert call(a22=16) == D.DSPARK_ERR_WORKSPACE
 
 
 def test_schedule_async_validation():

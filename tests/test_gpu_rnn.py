@@ -25,6 +25,8 @@ pytestmark = pytest.mark.gpu
 # the private (R <= 32) / shared (R > 32) launch shapes
 synth.custom("rnn_v997_r37_g3", V=997, rank=32, d=48, gamma=3, R=37, dtype="bf16", peak="three")
 synth.custom("rnn_v4099_r20_g5", V=4099, rank=64, d=80, gamma=5, R=20, dtype="bf16", peak="three")
+# one request, a vocabulary below one MFMA tile pair, the smallest d
+synth.custom("rnn_v50_r1_g2", V=50, rank=32, d=16, gamma=2, R=1, dtype="bf16", peak="three")
 
 STATE_ATOL = 1e-4
 
@@ -86,6 +88,7 @@ def _check(inp, gru, host, T, seed, reqs=None):
 
 @pytest.mark.parametrize("name,T", [
     ("rnn_v997_r37_g3", 1.0), ("rnn_v997_r37_g3", 0.0), ("rnn_v4099_r20_g5", 0.7),
+    ("rnn_v50_r1_g2", 1.0),
 ])
 def test_rnn_draft_block_small(name, T):
     say(f"[rnn] {name} T={T}")
@@ -107,3 +110,54 @@ def test_rnn_draft_block_full_size_and_repeatable():
     np.testing.assert_array_equal(buf.x.cpu().numpy(), host["x"])
     np.testing.assert_array_equal(buf.p.cpu().numpy(), host["p"])
     np.testing.assert_array_equal(state.cpu().numpy(), host["state"])
+
+
+def test_rnn_round_verifies_against_its_own_rows():
+    """Draft with the RNN head (bias rows written out), schedule, verify with
+    those rows.  The oracle rebuilds the rows from the GPU's tokens through its
+    own GRU and verifies with them: c* within 1e-3, accept decisions and
+    next tokens exact away from near ties; the GPU's rows equal the oracle's up
+    to one bf16 step."""
+    from tests.test_gpu_verify import ACCEPT_NEAR_TIE, CSTAR_ATOL, CSTAR_RTOL
+    name = "rnn_round_v4099_r40_g4"
+    synth.custom(name, V=4099, rank=64, d=48, gamma=4, R=40, dtype="bf16", peak="three", target=True)
+    inp = synth.generate(name, seed=0, target=True)
+    wl = inp.wl
+    di = runner.DeviceInputs.upload(inp)
+    buf = runner.RoundBuffers.allocate(di)
+    gru = synth.gru_weights(wl, 0)
+    rw = runner.RnnWeights.upload(gru)
+    state = torch.empty((wl.R, wl.rank), dtype=torch.float32, device="cuda")
+    rows = torch.empty((wl.R, wl.gamma, wl.rank), dtype=torch.int16, device="cuda")
+    nb = D.dspark_workspace_bytes(D.DSPARK_OP_DRAFT_RNN, wl.R, wl.V, wl.rank, wl.gamma)
+    ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    T, seed = 1.0, 41
+    runner.draft_rnn(di, buf, rw, T, seed, state, ws, rows)
+    runner.schedule(di, buf)
+    runner.verify_rnn(di, buf, rows, T, seed)
+    torch.cuda.synchronize()
+    g = {n: getattr(buf, n).cpu().numpy() for n in ("x", "ell", "c_star", "n_accept", "next_token",
+                                                    "tau")}
+    rows_g = O.bf16_to_f64(rows.cpu().numpy().view(np.uint16))
+    # oracle rows from the GPU's tokens
+    W1, W2t = O.as_f64(inp.W1_store), O.as_f64(inp.W2t_store)
+    g64 = (O.as_f64(gru[0]), O.as_f64(gru[1]), gru[2].astype(np.float64), gru[3].astype(np.float64))
+    h = O.as_f64(inp.h_store)
+    x = g["x"].astype(np.int64)
+    s = np.zeros((wl.R, wl.rank))
+    rows_o = np.empty((wl.R, wl.gamma, wl.rank))
+    for k in range(1, wl.gamma + 1):
+        s = O.gru_cell(np.concatenate([W1[x[:, k - 1]], h[:, k - 1]], axis=1), s, *g64)
+        rows_o[:, k - 1] = O.bf16_round(s)
+    assert (np.abs(rows_g - rows_o) <= 2.0 ** -7 * np.abs(rows_o) + 1e-30).all()
+    res = O.verify(inp.U, inp.target, W1, W2t, x, g["ell"], T, seed, np.arange(wl.R), E=rows_o)
+    cs_o = res["c_star"]
+    assert np.all(np.abs(g["c_star"] - cs_o) <= np.maximum(CSTAR_ATOL, CSTAR_RTOL * np.abs(cs_o)))
+    near = (res["accept_margin"] < ACCEPT_NEAR_TIE) | (res["sample_gap"] < NEAR_TIE)
+    ok = ((g["n_accept"] == res["n_accept"]) & (g["next_token"] == res["next_token"])
+          & (g["tau"] == res["tau"]))
+    assert np.all(ok | near), np.nonzero(~ok & ~near)
+    # with the Markov rows the verdict would be different: the rows matter
+    res_m = O.verify(inp.U, inp.target, W1, W2t, x, g["ell"], T, seed, np.arange(wl.R))
+    assert np.abs(res_m["c_star"] - cs_o).max() > 1e-3
+    say(f"  ok: budget {g['ell'].sum()}, tau mean {g['tau'].mean():.3f}")
