@@ -384,9 +384,25 @@ def main():
             torch.cuda.synchronize()
             r_us.append(er[0].elapsed_time(er[1]) * 1e3)
         r_med = float(np.median(r_us))
+        # the RNN head's whole round: its block (bias rows written out),
+        # schedule, and verification with those rows
+        rrows = torch.empty((R, g, rank), dtype=torch.int16, device="cuda")
+        rr_us = []
+        for s in range(nb + 2):
+            er[0].record()
+            runner.draft_rnn(di, buf, rw, TEMPERATURE, 620 + s, rstate, rws, rrows)
+            runner.schedule(di, buf)
+            runner.verify_rnn(di, buf, rrows, TEMPERATURE, 620 + s)
+            er[1].record()
+            torch.cuda.synchronize()
+            if s >= 2:
+                rr_us.append(er[0].elapsed_time(er[1]) * 1e3)
+        rr_med = float(np.median(rr_us))
         rnn = {"block_us": round(r_med, 2), "us_per_step": round(r_med / g, 2),
-               "draft_tokens_per_s": round(R * g / (r_med * 1e-6), 1)}
-        del rws, rstate
+               "draft_tokens_per_s": round(R * g / (r_med * 1e-6), 1),
+               "round_us": round(rr_med, 2),
+               "round_draft_tokens_per_s": round(R * g / (rr_med * 1e-6), 1)}
+        del rws, rstate, rrows
 
     # Cold draft step: a 512 MB write evicts W2 and U from L2 and the MALL
     # before each timed step (dspark_draft_step = step kernel + merge).
