@@ -257,8 +257,8 @@ dspark_status dspark_verify(int R, int V, int rank, int gamma, int dt, const voi
 
 /*
  * dspark_verify for blocks drafted by the RNN head [P1 §2.4]: p_d at
- * position k is recomputed from rows[r][k-1] (bf16 [R][gamma][rank], 16-byte
- * aligned, as written by dspark_draft_block_rnn) in place of W1[x[r][k-1]];
+ * position k is recomputed from rows[r][k-1] ([R][gamma][rank] in dt, 16-byte
+ * aligned; dspark_draft_block_rnn writes them in bf16) in place of W1[x[r][k-1]];
  * everything else, arguments, outputs, workspace and errors included, is
  * dspark_verify's.  rows NULL -> DSPARK_ERR_NULL.
  */
