@@ -138,14 +138,14 @@ __global__ __launch_bounds__(256) void rnn_proj_reduce(RnnArgs a) {
 // The kernel is bound by dependent memory round trips (a few microseconds
 // each here), so every wave issues all of its loads at the start and only the
 // e rows wait for the token.  The quarters meet in LDS in a fixed order, the
-// first one bringing the input projection and the recurrent bias; wave 0
-// then forms s_k.
+// first one bringing the input projection and the recurrent bias; waves 0 .. 3
+// then form s_k, four of each lane's 16 entries each.
 constexpr int kStateQ = 4;       // K quarters
 constexpr int kStateMaxSteps = 4;  // K steps per quarter at rank 256
 
 template <bool kRec>
 __device__ __forceinline__ void state_step_body(const RnnArgs& a, int k, const float* s_prev,
-                                                float* s_next, float (*red)[2][16][64]) {
+                                                float* s_next, float (*red)[3][2][16][64]) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = w / kStateQ, q = w % kStateQ;
   const int half = lane >> 5, col = lane & 31;
@@ -172,13 +172,15 @@ __device__ __forceinline__ void state_step_body(const RnnArgs& a, int k, const f
       sv[j][1] = *reinterpret_cast<const f32x4_t*>(srow + k0 + 4);
     }
   }
-  // wave 0 keeps s_{k-1} of its outputs for the final blend
-  float sp[16];
-  if (kRec && w == 0) {
+  // waves 0 .. 3 each blend 4 of the 16 accumulator entries at the end, and
+  // keep s_{k-1} of those entries
+  float sp[4];
+  if (kRec && w < 4) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int ii = 0; ii < 4; ++ii) {
+      const int i = 4 * w + ii;
       const int r = min(rt * 32 + 8 * (i >> 2) + 4 * half + (i & 3), a.R - 1);
-      sp[i] = s_prev[(size_t)r * H + n];
+      sp[ii] = s_prev[(size_t)r * H + n];
     }
   }
   // the first quarter also brings the input projection of step k
@@ -219,34 +221,41 @@ __device__ __forceinline__ void state_step_body(const RnnArgs& a, int k, const f
       gh = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf16x8_of(lo), whv[j], gh, 0, 0, 0);
     }
   }
-  // quarters in order: ((q0 + input projection) + q1) + q2 + q3, and likewise
-  // ((q0 + recurrent bias) + q1) + ... for the recurrent part
+  // quarters in a fixed order over two LDS slots: slot 0 = (q0 + input
+  // projection) + q2, slot 1 = q1 + q3 (the recurrent part likewise, with its
+  // bias in q0), and the gate input is slot 0 + slot 1
   const float bh = a.b_hh[g * H + n];
-  for (int qq = 0; qq < kStateQ; ++qq) {
-    if (q == qq) {
+  if (q < 2) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (qq == 0) {
-          red[g][0][i][lane] = gi[i] + pre[i];
-          red[g][1][i][lane] = gh[i] + bh;
-        } else {
-          red[g][0][i][lane] += gi[i];
-          red[g][1][i][lane] += gh[i];
-        }
-      }
+    for (int i = 0; i < 16; ++i) {
+      red[q][g][0][i][lane] = q == 0 ? gi[i] + pre[i] : gi[i];
+      red[q][g][1][i][lane] = q == 0 ? gh[i] + bh : gh[i];
     }
-    __syncthreads();
   }
-  if (w != 0) return;
-  // accumulator i: request 32 rt + 8 (i/4) + 4 half + i%4, state entry n
+  __syncthreads();
+  if (q >= 2) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 16; ++i) {
+      red[q - 2][g][0][i][lane] += gi[i];
+      red[q - 2][g][1][i][lane] += gh[i];
+    }
+  }
+  __syncthreads();
+  if (w >= 4) return;
+  // accumulator i: request 32 rt + 8 (i/4) + 4 half + i%4, state entry n;
+  // wave w blends i = 4 w .. 4 w + 3
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii) {
+    const int i = 4 * w + ii;
     const int r = rt * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
     if (r >= a.R) continue;
-    const float rg = 1.0f / (1.0f + expf(-(red[0][0][i][lane] + red[0][1][i][lane])));
-    const float zg = 1.0f / (1.0f + expf(-(red[1][0][i][lane] + red[1][1][i][lane])));
-    const float ng = tanhf(red[2][0][i][lane] + rg * red[2][1][i][lane]);
-    const float s = (1.0f - zg) * ng + zg * (kRec ? sp[i] : 0.0f);
+    auto part = [&](int gate, int which) {
+      return red[0][gate][which][i][lane] + red[1][gate][which][i][lane];
+    };
+    const float rg = 1.0f / (1.0f + expf(-(part(0, 0) + part(0, 1))));
+    const float zg = 1.0f / (1.0f + expf(-(part(1, 0) + part(1, 1))));
+    const float ng = tanhf(part(2, 0) + rg * part(2, 1));
+    const float s = (1.0f - zg) * ng + zg * (kRec ? sp[ii] : 0.0f);
     s_next[(size_t)r * H + n] = s;
     a.E[(size_t)r * H + n] = bf16_bits_rne(s);
     if (a.rows_out) a.rows_out[((size_t)r * a.gamma + (k - 1)) * H + n] = bf16_bits_rne(s);
@@ -256,7 +265,7 @@ __device__ __forceinline__ void state_step_body(const RnnArgs& a, int k, const f
 __global__ __launch_bounds__(64 * 3 * kStateQ) void rnn_state_step(RnnArgs a, int k,
                                                                    const float* s_prev,
                                                                    float* s_next) {
-  __shared__ float red[3][2][16][64];  // per gate: input part, recurrent part
+  __shared__ float red[2][3][2][16][64];  // slot, gate, input / recurrent part
   if (k > 1)
     state_step_body<true>(a, k, s_prev, s_next, red);
   else
