@@ -40,73 +40,102 @@ __device__ __forceinline__ bf16x8_t bf16x8_of(const float (&v)[8]) {
   return r;
 }
 
-// R1: wave q of workgroup (bx, by, ks) computes rows 64 bx .. +63 (two
-// 32-row tiles) by outputs 256 by + 64 q .. +63 (two 32-output tiles) over
-// the ks-th quarter of K (partial sums P[ks], added in order by R2); the
-// four waves share the h rows through L1.  A = h rows, B = W_ih rows
-// (columns rank + k), both holding K contiguously; lane (l%32, half)
-// supplies the 8 k = 16 s + 8 half .. +7 of its row for K step s.  The
-// operands of step s + 1 are loaded while step s multiplies.
+// R1: workgroup (bx, by, z) computes the 128 x 128 block of rows 128 bx ..
+// and outputs 128 by .. over the z-th of kProjSplit K ranges (partial sums
+// P[z], the input bias in the first); wave q owns rows 64 (q / 2) .. +63 by
+// outputs 64 (q % 2) .. +63 (2 x 2 MFMA tiles).  A = h rows, B = W_ih rows
+// (columns rank + k); each 64-wide K chunk of both is copied into LDS once
+// (16 bytes per thread and piece, rows padded to 72 elements), the next
+// chunk's pieces loaded into registers while the current one multiplies.
+// Lane (l%32, half) reads the 8 k = 16 s + 8 half .. +7 of its row for K
+// step s.  K past d (a partial last chunk) reads as zero.
+constexpr int kProjTile = 128;
+constexpr int kProjRow = 72;  // LDS row stride (elements)
+
 __global__ __launch_bounds__(256) void rnn_input_proj(RnnArgs a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ __align__(16) uint16_t lA[kProjTile * kProjRow];
+  __shared__ __align__(16) uint16_t lB[kProjTile * kProjRow];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
   const int n_rows = a.R * a.gamma, n_out = 3 * a.rank;
-  const int o0 = blockIdx.y * 256 + wave * 64;
-  if (o0 >= n_out) return;  // no barriers in this kernel
-  const int ksteps = a.d / 16, kq = (ksteps + kProjSplit - 1) / kProjSplit;
-  const int s_begin = min(ksteps, (int)blockIdx.z * kq), s_end = min(ksteps, s_begin + kq);
-  const uint16_t* hr[2];
-  const uint16_t* wr[2];
+  const int row0 = blockIdx.x * kProjTile, out0 = blockIdx.y * kProjTile;
+  const int chunks = (a.d + 63) / 64, cq = (chunks + kProjSplit - 1) / kProjSplit;
+  const int c_begin = min(chunks, (int)blockIdx.z * cq), c_end = min(chunks, c_begin + cq);
+
+  // this thread's 4 pieces of each chunk: tile row p / 8, 8 K values at 8 (p % 8)
+  const uint16_t* asrc[4];
+  const uint16_t* bsrc[4];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int row = min(blockIdx.x * 64 + 32 * t + col, n_rows - 1);
-    const int o = min(o0 + 32 * t + col, n_out - 1);
-    hr[t] = a.h + (size_t)row * a.d + 8 * half;
-    wr[t] = a.W_ih + (size_t)o * (a.rank + a.d) + a.rank + 8 * half;
+  for (int i = 0; i < 4; ++i) {
+    const int pc = tid + 256 * i, r = pc >> 3;
+    asrc[i] = a.h + (size_t)min(row0 + r, n_rows - 1) * a.d + 8 * (pc & 7);
+    bsrc[i] = a.W_ih + (size_t)min(out0 + r, n_out - 1) * (a.rank + a.d) + a.rank + 8 * (pc & 7);
   }
+  u32x4_t ra[4], rb[4];
+  auto load = [&](int ch) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int k0 = ch * 64 + 8 * ((tid + 256 * i) & 7);
+      const bool in = k0 < a.d;  // d % 16 == 0: a piece is wholly inside or outside
+      ra[i] = in ? *reinterpret_cast<const u32x4_t*>(asrc[i] + ch * 64) : u32x4_t{};
+      rb[i] = in ? *reinterpret_cast<const u32x4_t*>(bsrc[i] + ch * 64) : u32x4_t{};
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int pc = tid + 256 * i, r = pc >> 3, q = pc & 7;
+      *reinterpret_cast<u32x4_t*>(lA + r * kProjRow + 8 * q) = ra[i];
+      *reinterpret_cast<u32x4_t*>(lB + r * kProjRow + 8 * q) = rb[i];
+    }
+  };
+
   f32x16_t acc[2][2];
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int u = 0; u < 2; ++u) acc[t][u] = f32x16_t{};
-  bf16x8_t x[2], wv[2], xn[2], wn[2];
-  const int s_first = s_begin < s_end ? s_begin : 0;  // an empty quarter still loads a valid step
+  const int mr = 64 * (wave >> 1), nr = 64 * (wave & 1);
+  if (c_begin < c_end) {
+    load(c_begin);
+    store();
+    __syncthreads();
+    for (int ch = c_begin; ch < c_end; ++ch) {
+      if (ch + 1 < c_end) load(ch + 1);
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    x[t] = *reinterpret_cast<const bf16x8_t*>(hr[t] + 16 * s_first);
-    wv[t] = *reinterpret_cast<const bf16x8_t*>(wr[t] + 16 * s_first);
-  }
-  for (int st = s_begin; st < s_end; ++st) {
-    const int sn = st + 1 < s_end ? st + 1 : st;
+      for (int s = 0; s < 4; ++s) {
+        bf16x8_t x[2], wv[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      xn[t] = *reinterpret_cast<const bf16x8_t*>(hr[t] + 16 * sn);
-      wn[t] = *reinterpret_cast<const bf16x8_t*>(wr[t] + 16 * sn);
+        for (int t = 0; t < 2; ++t) {
+          x[t] = *reinterpret_cast<const bf16x8_t*>(lA + (mr + 32 * t + col) * kProjRow + 16 * s + 8 * half);
+          wv[t] = *reinterpret_cast<const bf16x8_t*>(lB + (nr + 32 * t + col) * kProjRow + 16 * s + 8 * half);
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+            acc[t][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x[t], wv[u], acc[t][u], 0, 0, 0);
+      }
+      __syncthreads();  // every wave is past its reads of this chunk
+      if (ch + 1 < c_end) {
+        store();
+        __syncthreads();
+      }
     }
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-        acc[t][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x[t], wv[u], acc[t][u], 0, 0, 0);
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      x[t] = xn[t];
-      wv[t] = wn[t];
-    }
   }
-  // accumulator i of tile (t, u): row 64 bx + 32 t + 8 (i/4) + 4 half + i%4,
-  // output o0 + 32 u + col; the input bias goes into the first quarter
+  // accumulator i of tile (t, u): row row0 + mr + 32 t + 8 (i/4) + 4 half + i%4,
+  // output out0 + nr + 32 u + col
   float* P = a.P + (size_t)blockIdx.z * n_rows * n_out;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int o = o0 + 32 * u + col;
+    const int o = out0 + nr + 32 * u + col;
     if (o >= n_out) continue;
     const float b = blockIdx.z == 0 ? a.b_ih[o] : 0.0f;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int rr = blockIdx.x * 64 + 32 * t + 8 * (i >> 2) + 4 * half + (i & 3);
+        const int rr = row0 + mr + 32 * t + 8 * (i >> 2) + 4 * half + (i & 3);
         if (rr < n_rows) P[(size_t)rr * n_out + o] = acc[t][u][i] + b;
       }
   }
@@ -276,7 +305,9 @@ __global__ __launch_bounds__(64 * 3 * kStateQ) void rnn_state_step(RnnArgs a, in
 
 hipError_t launch_rnn_input_proj(const RnnArgs& a, hipStream_t stream) {
   const int n_rows = a.R * a.gamma, n_out = 3 * a.rank;
-  hipLaunchKernelGGL(rnn_input_proj, dim3((n_rows + 63) / 64, (n_out + 255) / 256, kProjSplit),
+  hipLaunchKernelGGL(rnn_input_proj,
+                     dim3((n_rows + kProjTile - 1) / kProjTile, (n_out + kProjTile - 1) / kProjTile,
+                          kProjSplit),
                      dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
