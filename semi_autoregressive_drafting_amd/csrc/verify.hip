@@ -738,6 +738,8 @@ struct GradEpi : UTRows<kVec> {
   float kscale, lse2_d, lse2_t, mu, sce, stv;
   int xs;
   float* drow;  // dU row of the lane; null for a row past the end
+  float* dU;    // with kVec: full tiles leave through the wave's LDS patch as whole row lines
+  bool line_ok[4];  // the row of this lane's line store q exists
 
   template <bool kMasked>
   __device__ __forceinline__ void fold(const float (&ut)[2][16], const f32x16_t& acc, int vt) {
@@ -751,12 +753,24 @@ struct GradEpi : UTRows<kVec> {
       const float hot = (vb + i == xs) ? 1.0f : 0.0f;
       g[i] = fmaf(sce, pd - hot, stv * pd * (sg - mu));
     }
-    if (drow == nullptr) return;
     if constexpr (kVec && !kMasked) {
+      // the inverse of the row loads' patch pass: lane layout in, row lines
+      // out (the patch is free once this tile's inputs were read from it)
+      const int l = threadIdx.x & 63;
+      float* wr = this->patch + (l & 31) * kPatchRowFloats + 16 * (l >> 5);
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<f32x4_t*>(drow + vb + 4 * q) = f32x4_t{g[4 * q], g[4 * q + 1], g[4 * q + 2], g[4 * q + 3]};
-    } else {
+      for (int c = 0; c < 4; ++c)
+        *reinterpret_cast<f32x4_t*>(wr + 4 * c) = f32x4_t{g[4 * c], g[4 * c + 1], g[4 * c + 2], g[4 * c + 3]};
+      const float* rd = this->patch + (l >> 3) * kPatchRowFloats + 4 * (l & 7);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(rd + 8 * q * kPatchRowFloats);
+        if (line_ok[q]) *reinterpret_cast<f32x4_t*>(dU + this->rows.off[q] + vt * kVTile) = v;
+      }
+      return;
+    }
+    if (drow == nullptr) return;
+    {
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         if (!kMasked || vb + i < this->V) drow[vb + i] = g[i];
@@ -817,6 +831,10 @@ __global__ __launch_bounds__(kTvThreads) void train_grad_logits(VerifyArgs a, Ve
   epi.stv = (float)(wk * (double)ta.alpha_tv);
   epi.xs = a.x[(size_t)r * (a.gamma + 1) + k];
   epi.drow = row < p.n_rows ? ta.dU + (size_t)row * a.V : nullptr;
+  epi.dU = ta.dU;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    epi.line_ok[q] = (grp * kTvWaves + wave) * kVTile + 8 * q + (lane >> 3) < p.n_rows;
   auto gather = [&](typename W::frag_t(&ef)[W::kMaxKs]) {
     load_e_frags<W, kKs>(ef, a.W1, a.x[(size_t)r * (a.gamma + 1) + (k - 1)], a.rank, a.V, half);
   };
