@@ -274,3 +274,15 @@ def test_python_binding_rejects_host_tensors():
     import torch
     with pytest.raises(ValueError):
         D._ptr(torch.zeros(4))
+
+
+def test_bench_refuses_several_gpus():
+    """bench.py measures one GPU: --gpus 2 exits at once with a message."""
+    import subprocess
+    import sys
+    import os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=60)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
