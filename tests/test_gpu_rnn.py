@@ -96,6 +96,15 @@ def test_rnn_draft_block_small(name, T):
     _check(inp, gru, host, T, 21)
 
 
+def test_rnn_draft_block_full_size_greedy():
+    """Greedy drafting with the RNN head at R = 32, gamma = 7 (the private launch
+    shape), full vocabulary, rank 256."""
+    name = "qwen3_4b_r32_g7"
+    say(f"[rnn] {name} T=0")
+    inp, gru, host, _ = _run(name, 0.0, 3)
+    _check(inp, gru, host, 0.0, 3, np.linspace(0, inp.wl.R - 1, 6).round().astype(int))
+
+
 def test_rnn_draft_block_full_size_and_repeatable():
     """The headline shape (R = 128, gamma = 16, V = 151936, rank 256, d 4096):
     a spread sample of 6 requests against the oracle; a second call on the

@@ -44,9 +44,9 @@ def _x_star(inp, seed, repeat=False):
     return x
 
 
-def _run(inp, xs, T, lam):
+def _run(inp, xs, T, lam, alphas=O.LOSS_ALPHAS):
     di = runner.DeviceInputs.upload(inp)
-    out = runner.train_loss_grad(di, torch.from_numpy(xs).cuda(), T, lam)
+    out = runner.train_loss_grad(di, torch.from_numpy(xs).cuda(), T, lam, alphas)
     torch.cuda.synchronize()
     return {k: v.cpu().numpy().astype(np.float64) for k, v in out.items()}
 
@@ -55,11 +55,12 @@ def _check_dU(got_dU, G, xs, reqs):
     """dU of requests `reqs` against the oracle (G computed on those requests)."""
     pd, pt, mu = G["p_d"], G["p_t"], G["mu"][..., None]
     fce, ftv = G["f_ce"][None, :, None], G["f_tv"][None, :, None]
+    afce, aftv = np.abs(fce), np.abs(ftv)  # term magnitudes (a weight may be negative)
     n, g, V = pd.shape
     hot = np.zeros_like(pd)
     for i in range(n):
         hot[i, np.arange(g), xs[reqs[i], 1:]] = 1.0
-    scale = fce * (pd + hot) + 2.0 * ftv * pd
+    scale = afce * (pd + hot) + 2.0 * aftv * pd
     tol = 1e-3 * scale + 1e-12
     err = np.abs(got_dU - G["dU"])
     bad = err > tol
@@ -82,18 +83,21 @@ def _dl_scale(got_terms, wk, a_conf):
     """w_k a_conf (|c| + |c*|) per position from the GPU's (checked) terms."""
     c = got_terms[..., 3]
     cs = 1.0 - 0.5 * got_terms[..., 1]
-    return wk[None, :] * a_conf * (np.abs(c) + np.abs(cs))
+    return wk[None, :] * abs(a_conf) * (np.abs(c) + np.abs(cs))
 
 
-def _check_all(name, T, lam, seed=5, repeat=False):
-    say(f"[grad] {name} T={T} lambda={lam} repeat={repeat}")
+def _check_all(name, T, lam, seed=5, repeat=False, alphas=O.LOSS_ALPHAS):
+    say(f"[grad] {name} T={T} lambda={lam} repeat={repeat} alphas={alphas}")
     inp = synth.generate(name, seed=0, target=True)
     wl = inp.wl
     xs = _x_star(inp, seed, repeat)
-    got = _run(inp, xs, T, lam)
+    got = _run(inp, xs, T, lam, alphas)
     W1, W2t = O.as_f64(inp.W1_store), O.as_f64(inp.W2t_store)
     h = O.as_f64(inp.h_store)
-    G = O.train_loss_grads(inp.U, inp.target, W1, W2t, inp.h_store, inp.w, xs, T=T, lam=lam)
+    # the library takes the weights in fp32
+    alphas = tuple(float(np.float32(x)) for x in alphas)
+    G = O.train_loss_grads(inp.U, inp.target, W1, W2t, inp.h_store, inp.w, xs, T=T, lam=lam,
+                           alphas=alphas)
     reqs = np.arange(wl.R)
     _check_dU(got["dU"], G, xs, reqs)
 
@@ -103,7 +107,7 @@ def _check_all(name, T, lam, seed=5, repeat=False):
     wd = np.asarray(inp.w, dtype=np.float64)
     lam_ = wl.gamma if lam is None else lam
     wk = O.position_weights(wl.gamma, lam_)
-    dls = _dl_scale(got["terms"], wk, O.LOSS_ALPHAS[2])
+    dls = _dl_scale(got["terms"], wk, alphas[2])
     tol_dE = 2.0 ** -7 * (aU @ np.abs(W2t)) + 1e-3 * dls[..., None] * np.abs(wd[wl.d:]) + 1e-7
     dW1_ref = np.zeros_like(W1)
     dW1_tol = np.zeros_like(W1)
@@ -127,7 +131,8 @@ def _check_all(name, T, lam, seed=5, repeat=False):
     assert (np.abs(got["dw"] - G["dw"]) <= tol_dw).all(), "dw"
 
     # the losses themselves match the forward entry point's
-    o = O.train_losses(inp.U, inp.target, W1, W2t, inp.h_store, inp.w, xs, T=T, lam=lam)
+    o = O.train_losses(inp.U, inp.target, W1, W2t, inp.h_store, inp.w, xs, T=T, lam=lam,
+                       alphas=alphas)
     np.testing.assert_allclose(got["terms"][..., 1], o["tv"], rtol=1e-3, atol=1e-5)
     assert got["sums"][3] == pytest.approx(o["total"], rel=1e-3)
     say("  ok")
@@ -143,6 +148,11 @@ def _check_all(name, T, lam, seed=5, repeat=False):
 ])
 def test_train_grads_small(name, T, lam, repeat):
     _check_all(name, T, lam, repeat=repeat)
+
+
+def test_train_grads_other_weights_and_temperature():
+    """Non-default loss weights (a negative one included) and a low temperature."""
+    _check_all("grad_v1000_r100_g2", 0.5, 1.5, alphas=(0.3, -0.25, 2.0))
 
 
 def test_train_grads_deterministic():
