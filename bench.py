@@ -236,7 +236,7 @@ def main():
         print(json.dumps({"copy_bytes_per_launch": src.numel() * 4, "launches": 4}))
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
 

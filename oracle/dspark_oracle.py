@@ -54,7 +54,7 @@ the GPU) is the PCG hash of Jarzynski & Olano, "Hash Functions for GPU
 Rendering", JCGT 9(3), 2020, keyed as described at `stream_key`.  Only its
 statistical behaviour is pinned (uniformity of u and the sampler tests above).
 
-Readings taken where the pages are silent (each also listed in the design doc):
+Readings taken where the pages are silent:
   * sampling is Gumbel-argmax with the counter generator; ties -> lowest id;
   * s = (U_k + bias) / T; p_d and p_t use the same T; T = 0 means argmax
     (point mass, p = 1, lse reported as max z);
