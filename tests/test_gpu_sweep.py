@@ -45,6 +45,15 @@ def test_sweep_round(name):
 
 
 @pytest.mark.parametrize("name", SHAPES)
+def test_sweep_round_greedy(name):
+    say(f"[sweep] greedy round {name}")
+    case = Case(name)
+    buf, host, zs = case.run_draft(0.0, 80, z_steps=(1,))
+    check_flip_rate(check_draft(case, host, zs, 0.0, 80))
+    run_and_check(case, 0.0, 81)
+
+
+@pytest.mark.parametrize("name", SHAPES)
 def test_sweep_train_grads(name):
     GRAD._check_all(name, 1.0, None)
 
