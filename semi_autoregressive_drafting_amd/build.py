@@ -31,6 +31,8 @@ HIPCC_FLAGS = [
     "-Wno-unused-function",
     # packed fp32 VALU forms are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results land in VGPRs, so epilogues read them without v_accvgpr_read
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     f"-I{os.path.join(ROOT, 'include')}",
     f"-I{CSRC}",
 ]

@@ -59,8 +59,12 @@ __device__ __forceinline__ uint32_t row_state(uint32_t key, uint32_t v) {
   return (key + v) * kLcgMul + kLcgInc;
 }
 
+// ((bits >> 9) + 0.5) * 2^-23, built as the float 1 + (bits >> 9) * 2^-23
+// (exponent 127 funnel-shifted onto the top 23 bits) minus (1 - 2^-24).  Both
+// operands lie within a factor of two of each other, so the difference is exact
+// (Sterbenz) and equals the value above bit for bit.
 __device__ __forceinline__ float bits_to_uniform(uint32_t bits) {
-  return fmaf((float)(bits >> 9), 0x1p-23f, 0x1p-24f);
+  return __uint_as_float(__builtin_amdgcn_alignbit(0x7Fu, bits, 9u)) - (1.0f - 0x1p-24f);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

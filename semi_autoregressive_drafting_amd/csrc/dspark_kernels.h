@@ -114,6 +114,7 @@ struct VerifyPlan {
   int s_slabs;      // sampling pass: vocabulary slabs per group
   int n_vtiles;
   int lse_chunks;   // vocabulary chunks per row in the target normaliser pass
+  int fuse_sample;  // 1: the c* pass also runs the sampling race (no row tile meets > 2 requests)
   size_t off_lse_t, off_tv, off_best, off_srow, off_skind, off_lsepart, ws_bytes;
 };
 

@@ -22,7 +22,10 @@
 //      (at most one per request): Gumbel race over max(p_t - p_d, 0)
 //      (residual) or p_t (bonus), merged across workgroups with a 64-bit
 //      atomic max of (order-preserving key, ~id), which is order-independent
-//      and keeps the lowest id on ties.
+//      and keeps the lowest id on ties.  When no 32-row tile meets more than
+//      two requests (within gamma <= 16 that is gamma = 16), V3 runs this
+//      race itself from the p_d and p_t it already holds and V5 is not
+//      launched.
 //   V4 verify_finalize    (T > 0) c* = 1 - sum/2 per row; winner -> next_token.
 #include "dspark_kernels.h"
 #include "mfma_stream.h"
@@ -308,25 +311,73 @@ struct UTRows {
   }
 };
 
+// Gumbel race of the rows that need a sample, run inside the c* pass when a
+// row tile holds the sampled rows of at most two requests (slot 0: the tile's
+// first request, slot 1: the next one).  The lanes holding such a row publish
+// the tile's p_d and p_t of that row through a per-wave LDS slot; then lane l
+// races entry l % 32 of slot l / 32, so the race costs one entry per lane and
+// tile instead of sixteen.  Per entry it is the same race as the sampling pass
+// (same weights, same generator draws), merged across lanes and workgroups by
+// the same order-independent (key, ~id) maximum.
+struct SampleRace {
+  float* slot;     // per wave: [2 slots][p_d 32 | p_t 32] floats
+  int pub;         // this lane's row is the sampled row of slot pub (or -1)
+  bool active;     // the slot this lane races has a sampled row
+  int kind;        // 1 residual max(p_t - p_d, 0), 2 bonus p_t
+  uint32_t state;  // generator state of the sampled row
+  float bE, bLn;
+  int bV;
+
+  template <bool kMasked>
+  __device__ __forceinline__ void step(const float (&pd)[16], const float (&pt)[16], int vt,
+                                       int half, int lane, int V) {
+    if (pub >= 0) {
+      float* dst = slot + pub * 64 + 16 * half;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        *reinterpret_cast<f32x4_t*>(dst + 4 * j) = f32x4_t{pd[4 * j], pd[4 * j + 1], pd[4 * j + 2], pd[4 * j + 3]};
+        *reinterpret_cast<f32x4_t*>(dst + 32 + 4 * j) = f32x4_t{pt[4 * j], pt[4 * j + 1], pt[4 * j + 2], pt[4 * j + 3]};
+      }
+    }
+    // A wave's LDS operations complete in issue order, so the reads below see
+    // the stores above (and the next tile's stores come after these reads).
+    const float* src = slot + (lane >> 5) * 64 + (lane & 31);
+    const float d = src[0], t = src[32];
+    const int v = vt * kVTile + (lane & 31);
+    float e = (kind == 1) ? fmaxf(t - d, 0.0f) : t;
+    if (!active || (kMasked && v >= V)) e = 0.0f;
+    const float ln = fast_log2(bits_to_uniform(rxs_m_xs(state + (uint32_t)v * kLcgMul)));
+    const bool win = e * bLn < bE * ln;  // e / L > bE / bL with L = -ln
+    bE = win ? e : bE;
+    bLn = win ? ln : bLn;
+    bV = win ? v : bV;
+  }
+};
+
 // kMu also accumulates sum_v sign(p_d - p_t) p_d, the row constant of the
-// derivative of the TV term (training gradients).
-template <bool kVec, bool kMu>
+// derivative of the TV term (training gradients).  kSample also runs the
+// sampling race (SampleRace).
+template <bool kVec, bool kMu, bool kSample = false>
 struct TvEpi : UTRows<kVec> {
   float kscale, lse2_d, lse2_t;
   float sabs, smu;
+  SampleRace race;
 
   template <bool kMasked>
   __device__ __forceinline__ void fold(const float (&ut)[2][16], const f32x16_t& acc, int vt) {
     const int vb = vt * kVTile + 16 * this->half;
+    float pd[16], pt[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float pd = fast_exp2(fmaf(ut[0][i] + acc[i], kscale, -lse2_d));
-      const float pt = fast_exp2(fmaf(ut[1][i], kscale, -lse2_t));
-      const float d = fabsf(pd - pt);
+      pd[i] = fast_exp2(fmaf(ut[0][i] + acc[i], kscale, -lse2_d));
+      pt[i] = fast_exp2(fmaf(ut[1][i], kscale, -lse2_t));
+      const float d = fabsf(pd[i] - pt[i]);
       const bool in = !kMasked || vb + i < this->V;
       sabs += in ? d : 0.0f;
-      if constexpr (kMu) smu += (in && pd != pt) ? (pd > pt ? pd : -pd) : 0.0f;
+      if constexpr (kMu) smu += (in && pd[i] != pt[i]) ? (pd[i] > pt[i] ? pd[i] : -pd[i]) : 0.0f;
     }
+    if constexpr (kSample)
+      race.template step<kMasked>(pd, pt, vt, this->half, threadIdx.x & 63, this->V);
   }
   template <int S>
   __device__ void consume(const f32x16_t& acc, int vt) {
@@ -341,7 +392,7 @@ struct TvEpi : UTRows<kVec> {
   }
 };
 
-template <class W, int kKs, bool kVec, bool kMu = false>
+template <class W, int kKs, bool kVec, bool kMu = false, bool kSample = false>
 __global__ __launch_bounds__(kTvThreads) void verify_tv(VerifyArgs a, VerifyPlan p,
                                                         unsigned long long* mu_acc = nullptr) {
   extern __shared__ __align__(16) unsigned char lds[];
@@ -356,7 +407,7 @@ __global__ __launch_bounds__(kTvThreads) void verify_tv(VerifyArgs a, VerifyPlan
   const int rowc = row < p.n_rows ? row : p.n_rows - 1;
   const int r = rowc / a.gamma, k = rowc % a.gamma + 1;
   typename W::frag_t e[W::kMaxKs];
-  TvEpi<kVec, kMu> epi;
+  TvEpi<kVec, kMu, kSample> epi;
   epi.urow = a.U + (size_t)rowc * a.V;
   epi.trow = a.target + (size_t)rowc * a.V;
   epi.V = a.V;
@@ -377,9 +428,59 @@ __global__ __launch_bounds__(kTvThreads) void verify_tv(VerifyArgs a, VerifyPlan
   epi.lse2_t = reinterpret_cast<const float*>(a.ws + p.off_lse_t)[rowc];
   epi.sabs = 0.0f;
   epi.smu = 0.0f;
+  int race_r = 0;
+  if constexpr (kSample) {
+    // The sampled rows of the (at most two) requests that meet this row tile.
+    const int row0 = (grp * kTvWaves + wave) * kVTile;
+    const int rlast = min(row0 + kVTile - 1, p.n_rows - 1);
+    const int* srow = reinterpret_cast<const int*>(a.ws + p.off_srow);
+    const int* skind = reinterpret_cast<const int*>(a.ws + p.off_skind);
+    int scol[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int rq = row0 / a.gamma + q;
+      const int ks = rq < a.R ? srow[rq] : 0;
+      const int sr = rq * a.gamma + ks - 1;
+      scol[q] = (ks > 0 && sr >= row0 && sr <= rlast) ? sr - row0 : -1;
+    }
+    SampleRace& rc = epi.race;
+    rc.slot = reinterpret_cast<float*>(lds + stream_lds_bytes<W>(a.rank, kVerifyDist)) +
+              kTvWaves * kPatchFloats + wave * 128;
+    rc.pub = col == scol[0] ? 0 : (col == scol[1] ? 1 : -1);
+    const int q = lane >> 5;
+    race_r = row0 / a.gamma + q;
+    rc.active = scol[q] >= 0;
+    const int rr = rc.active ? race_r : 0;
+    rc.kind = rc.active ? skind[rr] : 2;
+    const uint32_t stream = rc.kind == 1 ? kStreamResid : kStreamBonus;
+    rc.state = row_key(a.seed, stream, (uint32_t)rr, (uint32_t)(rc.active ? srow[rr] : 1)) *
+                   kLcgMul + kLcgInc;
+    rc.bE = 0.0f;
+    rc.bLn = -1.0f;
+    rc.bV = -1;
+  }
   auto gather = [&](typename W::frag_t(&ef)[W::kMaxKs]) { verify_gather<W, kKs>(ef, a, r, k, half); };
   shared_a_stream<W, kKs, kVerifyDist, kTvThreads>(a.W2t, a.V, a.rank, t_begin, t_end, e, gather,
                                                    lds, epi);
+  if constexpr (kSample) {
+    const SampleRace& rc = epi.race;
+    float key = (rc.bV >= 0 && rc.bE > 0.0f) ? fast_log2(rc.bE) - fast_log2(-rc.bLn) : -INFINITY;
+    int idx = (rc.bV >= 0 && rc.bE > 0.0f) ? rc.bV : -1;
+#pragma unroll
+    for (int m = 1; m < 32; m <<= 1) {
+      const float ko = __shfl_xor(key, m);
+      const int io = __shfl_xor(idx, m);
+      if (rec_beats(ko, io, key, idx)) {
+        key = ko;
+        idx = io;
+      }
+    }
+    if (col == 0 && rc.active && idx >= 0) {
+      const unsigned long long packed =
+          ((unsigned long long)ordered(key) << 32) | (unsigned long long)(~(uint32_t)idx);
+      atomicMax(reinterpret_cast<unsigned long long*>(a.ws + p.off_best) + race_r, packed);
+    }
+  }
 
   const float s = epi.sabs + __shfl_xor(epi.sabs, 32);
   if (half == 0 && row < p.n_rows) {
@@ -891,6 +992,12 @@ template <class W, int kKs, bool kVec>
 hipError_t launch_passes(const VerifyArgs& a, const VerifyPlan& p, hipStream_t stream) {
   // W2t slots, then one LDS patch per wave (U and target rows pass in turn).
   const size_t lds = stream_lds_bytes<W>(a.rank, kVerifyDist) + kWaves * kPatchFloats * 4;
+  if (p.fuse_sample) {
+    // the sampling race rides on the c* pass: one race slot pair per wave
+    hipLaunchKernelGGL((verify_tv<W, kKs, kVec, false, true>), dim3(p.n_slabs * p.n_groups),
+                       dim3(kTvThreads), lds + kTvWaves * 128 * 4, stream, a, p, nullptr);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((verify_tv<W, kKs, kVec>), dim3(p.n_slabs * p.n_groups), dim3(kTvThreads),
                      lds, stream, a, p, nullptr);
   hipError_t e = hipGetLastError();
@@ -928,6 +1035,12 @@ VerifyPlan plan_verify(int R, int V, int gamma) {
   p.n_slabs = plan_slabs(p.n_groups, p.n_vtiles, kTvResidentWgs);
   p.s_groups = ((R + kVTile - 1) / kVTile + kWaves - 1) / kWaves;
   p.s_slabs = plan_slabs(p.s_groups, p.n_vtiles, kResidentWgs);
+  // The race rides on the c* pass when no row tile meets more than two requests.
+  p.fuse_sample = 1;
+  for (int t = 0; t < p.n_rtiles && p.fuse_sample; ++t) {
+    const int last = t * kVTile + kVTile - 1 < p.n_rows - 1 ? t * kVTile + kVTile - 1 : p.n_rows - 1;
+    if (last / gamma - (t * kVTile) / gamma > 1) p.fuse_sample = 0;
+  }
   int chunks = (2048 + p.n_rows - 1) / p.n_rows;
   const int max_chunks = (V + 1023) / 1024;
   if (chunks > max_chunks) chunks = max_chunks;

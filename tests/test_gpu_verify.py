@@ -1,6 +1,8 @@
 """GPU parity of verification (per-position c*, acceptance chain, residual /
 bonus resampling, realised tau) against the oracle, fed the GPU's own drafted
 block and admitted lengths."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -78,3 +80,40 @@ def test_verify_ragged_rank256(T):
     say(f"[verify] ragged T={T} budget={g['ell'].sum()} tau_mean={g['tau_mean'][0]:.4f}")
     run_and_check(case, T, 32, ell_override=np.full(37, 3))
     run_and_check(case, T, 33, ell_override=np.arange(37) % 4)
+
+
+# gamma = 16: no 32-row tile meets more than two requests, so the c* pass runs
+# the sampling race itself.  A partial last row tile with a vocabulary that is
+# not a multiple of 4 (row-by-row loads), and a single request (one half-filled
+# row tile) with rank 128 and a partial last vocabulary tile.
+synth.custom("fuse_round_v5003_r9_g16", V=5003, rank=256, d=64, gamma=16, R=9, dtype="bf16",
+             peak="three", target=True)
+synth.custom("fuse_round_v6000_r1_g16", V=6000, rank=128, d=64, gamma=16, R=1, dtype="bf16",
+             peak="three", target=True)
+
+
+@pytest.mark.parametrize("name", ["fuse_round_v5003_r9_g16", "fuse_round_v6000_r1_g16"])
+def test_verify_race_in_cstar_pass(name):
+    case = Case(name)
+    R, g = case.wl.R, case.wl.gamma
+    g1, _ = run_and_check(case, 1.0, 41)
+    say(f"[verify] {name} budget={g1['ell'].sum()} tau_mean={g1['tau_mean'][0]:.4f}")
+    # every position admitted: bonus rows only where ell < gamma
+    run_and_check(case, 1.0, 42, ell_override=np.full(R, g))
+    # a spread of admitted lengths, including none (a bonus at position 1)
+    run_and_check(case, 1.0, 43, ell_override=(np.arange(R) * 5) % (g + 1))
+    run_and_check(case, 0.7, 44, ell_override=np.full(R, g - 1))
+
+
+synth.WORKLOADS["qwen3_8b_r128_g16_target"] = dataclasses.replace(
+    synth.WORKLOADS["qwen3_8b_r128_g16"], name="qwen3_8b_r128_g16_target", target=True)
+
+
+def test_verify_full_size_sampled():
+    """Verification at R = 128, gamma = 16, V = 151936 in the benchmark's launch
+    configuration, checked against the oracle on every eighth request."""
+    case = Case("qwen3_8b_r128_g16_target")
+    reqs = np.arange(0, 128, 8)
+    g, _ = run_and_check(case, 1.0, 51, reqs=reqs)
+    say(f"[verify] full size budget={g['ell'].sum()} tau_mean={g['tau_mean'][0]:.4f}")
+    run_and_check(case, 1.0, 52, ell_override=np.arange(128) % 17, reqs=reqs + 3)
