@@ -259,7 +259,7 @@ def main():
         buf.x[:, 0].copy_(di.anchor)
         if ev is not None:
             ev[0].record()
-        runner.draft_phases(di, buf, TEMPERATURE, seed, D.DSPARK_PHASE_STEPS)
+        runner.draft_phases(di, buf, TEMPERATURE, seed, D.DSPARK_PHASE_STEPS, copy_anchor=False)
         if ev is not None:
             ev[1].record()
         runner.draft_phases(di, buf, TEMPERATURE, seed, D.DSPARK_PHASE_MERGE)

@@ -103,10 +103,11 @@ def draft(di: DeviceInputs, buf: RoundBuffers, temperature: float, seed: int):
 
 
 def draft_phases(di: DeviceInputs, buf: RoundBuffers, temperature: float, seed: int,
-                 phases: int):
+                 phases: int, copy_anchor: bool = True):
     """One phase (or both) of draft(): D.DSPARK_PHASE_STEPS runs the anchor
-    copy and the gamma streaming steps, D.DSPARK_PHASE_MERGE the record merge."""
-    if phases & D.DSPARK_PHASE_STEPS:
+    copy (unless the caller has placed the anchor itself) and the gamma
+    streaming steps, D.DSPARK_PHASE_MERGE the record merge."""
+    if phases & D.DSPARK_PHASE_STEPS and copy_anchor:
         buf.x[:, 0].copy_(di.anchor)
     D.dspark_draft_block_phases(di.R, di.V, di.rank, di.d, di.gamma, di.dt, di.W1, di.W2t, di.U,
                                 di.h, di.w, temperature, seed, buf.x, buf.p, buf.lse, buf.c,
