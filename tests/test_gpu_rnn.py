@@ -121,15 +121,20 @@ def test_rnn_draft_block_full_size_and_repeatable():
     np.testing.assert_array_equal(state.cpu().numpy(), host["state"])
 
 
-def test_rnn_round_verifies_against_its_own_rows():
+@pytest.mark.parametrize("name,V,R,gamma", [
+    ("rnn_round_v4099_r40_g4", 4099, 40, 4),
+    # gamma = 16: the c* pass also runs the sampling race, here with bias rows
+    ("rnn_round_v3001_r6_g16", 3001, 6, 16),
+])
+def test_rnn_round_verifies_against_its_own_rows(name, V, R, gamma):
     """Draft with the RNN head (bias rows written out), schedule, verify with
     those rows.  The oracle rebuilds the rows from the GPU's tokens through its
     own GRU and verifies with them: c* within 1e-3, accept decisions and
     next tokens exact away from near ties; the GPU's rows equal the oracle's up
     to one bf16 step plus the state tolerance."""
     from tests.test_gpu_verify import ACCEPT_NEAR_TIE, CSTAR_ATOL, CSTAR_RTOL
-    name = "rnn_round_v4099_r40_g4"
-    synth.custom(name, V=4099, rank=64, d=48, gamma=4, R=40, dtype="bf16", peak="three", target=True)
+    synth.custom(name, V=V, rank=64, d=48, gamma=gamma, R=R, dtype="bf16", peak="three",
+                 target=True)
     inp = synth.generate(name, seed=0, target=True)
     wl = inp.wl
     di = runner.DeviceInputs.upload(inp)
