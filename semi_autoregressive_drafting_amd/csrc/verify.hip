@@ -335,8 +335,9 @@ struct SampleRace {
       float* dst = slot + pub * 64 + 16 * half;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        *reinterpret_cast<f32x4_t*>(dst + 4 * j) = f32x4_t{pd[4 * j], pd[4 * j + 1], pd[4 * j + 2], pd[4 * j + 3]};
-        *reinterpret_cast<f32x4_t*>(dst + 32 + 4 * j) = f32x4_t{pt[4 * j], pt[4 * j + 1], pt[4 * j + 2], pt[4 * j + 3]};
+        const int i = 4 * j;
+        *reinterpret_cast<f32x4_t*>(dst + i) = f32x4_t{pd[i], pd[i + 1], pd[i + 2], pd[i + 3]};
+        *reinterpret_cast<f32x4_t*>(dst + 32 + i) = f32x4_t{pt[i], pt[i + 1], pt[i + 2], pt[i + 3]};
       }
     }
     // A wave's LDS operations complete in issue order, so the reads below see
