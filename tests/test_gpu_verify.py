@@ -117,3 +117,19 @@ def test_verify_full_size_sampled():
     g, _ = run_and_check(case, 1.0, 51, reqs=reqs)
     say(f"[verify] full size budget={g['ell'].sum()} tau_mean={g['tau_mean'][0]:.4f}")
     run_and_check(case, 1.0, 52, ell_override=np.arange(128) % 17, reqs=reqs + 3)
+
+
+# The largest row count the entry points take: R = 512 requests of gamma = 16
+# (8192 rows: the acceptance kernel's and the scheduler's maximum), with a
+# vocabulary that is not a multiple of 4.
+synth.custom("maxrows_v4099_r512_g16", V=4099, rank=256, d=64, gamma=16, R=512, dtype="bf16",
+             peak="three", target=True)
+
+
+@pytest.mark.parametrize("T", [1.0, 0.0])
+def test_verify_max_rows(T):
+    case = Case("maxrows_v4099_r512_g16")
+    reqs = np.arange(0, 512, 16)
+    g, _ = run_and_check(case, T, 61, reqs=reqs)
+    say(f"[verify] max rows T={T} budget={g['ell'].sum()} tau_mean={g['tau_mean'][0]:.4f}")
+    run_and_check(case, T, 62, ell_override=np.arange(512) % 17, reqs=reqs + 5)
