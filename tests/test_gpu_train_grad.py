@@ -35,6 +35,9 @@ synth.custom("grad_v4099_r8_g5", V=4099, rank=64, d=72, gamma=5, R=8, dtype="bf1
 synth.custom("grad_v64_r1_g1", V=64, rank=32, d=16, gamma=1, R=1, dtype="bf16", peak="three")
 # V % 8 == 4: the last vector load of a row holds 4 entries
 synth.custom("grad_v1004_r20_g3", V=1004, rank=64, d=32, gamma=3, R=20, dtype="bf16", peak="three")
+# the largest row count (R = 512, gamma = 16: 8192 rows, 64 row groups of the contractions)
+synth.custom("grad_v1031_r512_g16", V=1031, rank=64, d=24, gamma=16, R=512, dtype="bf16",
+             peak="three")
 
 
 def _x_star(inp, seed, repeat=False):
@@ -148,6 +151,7 @@ def _check_all(name, T, lam, seed=5, repeat=False, alphas=O.LOSS_ALPHAS):
     ("grad_v4099_r8_g5", 1.0, None, True),
     ("grad_v64_r1_g1", 1.0, None, False),
     ("grad_v1004_r20_g3", 1.0, None, True),
+    ("grad_v1031_r512_g16", 1.0, None, True),
 ])
 def test_train_grads_small(name, T, lam, repeat):
     _check_all(name, T, lam, repeat=repeat)
