@@ -27,6 +27,9 @@ synth.custom("rnn_v997_r37_g3", V=997, rank=32, d=48, gamma=3, R=37, dtype="bf16
 synth.custom("rnn_v4099_r20_g5", V=4099, rank=64, d=80, gamma=5, R=20, dtype="bf16", peak="three")
 # one request, a vocabulary below one MFMA tile pair, the smallest d
 synth.custom("rnn_v50_r1_g2", V=50, rank=32, d=16, gamma=2, R=1, dtype="bf16", peak="three")
+# the largest batch and block (R = 512, gamma = 16) at the largest rank
+synth.custom("rnn_v1031_r512_g16", V=1031, rank=256, d=32, gamma=16, R=512, dtype="bf16",
+             peak="three")
 
 STATE_ATOL = 1e-4
 
@@ -88,7 +91,7 @@ def _check(inp, gru, host, T, seed, reqs=None):
 
 @pytest.mark.parametrize("name,T", [
     ("rnn_v997_r37_g3", 1.0), ("rnn_v997_r37_g3", 0.0), ("rnn_v4099_r20_g5", 0.7),
-    ("rnn_v50_r1_g2", 1.0),
+    ("rnn_v50_r1_g2", 1.0), ("rnn_v1031_r512_g16", 1.0),
 ])
 def test_rnn_draft_block_small(name, T):
     say(f"[rnn] {name} T={T}")
