@@ -41,11 +41,15 @@ synth.custom("edge_v40004_r130_g3", V=40004, rank=256, d=64, gamma=3, R=130, dty
              peak="three")
 synth.custom("edge_v40001_r128_g2", V=40001, rank=256, d=48, gamma=2, R=128, dtype="bf16",
              peak="three")
+# the largest batch and block: R = 512 (four request groups), gamma = 16
+synth.custom("edge_v4099_r512_g16", V=4099, rank=256, d=48, gamma=16, R=512, dtype="bf16",
+             peak="three")
 
 
 @pytest.mark.parametrize("name,T", [
     ("edge_v9996_r130_g3", 1.0), ("edge_v9996_r130_g3", 0.0), ("edge_v8196_r33_g2", 1.0),
     ("edge_v40004_r130_g3", 1.0), ("edge_v40004_r130_g3", 0.0), ("edge_v40001_r128_g2", 1.0),
+    ("edge_v4099_r512_g16", 1.0), ("edge_v4099_r512_g16", 0.0),
 ])
 def test_draft_fast_paths_ragged(name, T):
     """z is checked at step 1 only (its debug kernel); the other steps run the
