@@ -479,7 +479,11 @@ def verify(U, Tl, W1, W2t, x, ell, T, seed, req_ids, E=None):
             z_d = np.asarray(U[i], dtype=np.float64) + np.asarray(E[i], dtype=np.float64) @ W2t.T
         z_t = np.asarray(Tl[i], dtype=np.float64)
         # greedy drafting's law at position k is the point mass on its drafted token
-        p_d = draft_distribution(z_d, T) if T > 0 else np.eye(V)[x[i, 1:]]
+        if T > 0:
+            p_d = draft_distribution(z_d, T)
+        else:
+            p_d = np.zeros((g, V))
+            p_d[np.arange(g), x[i, 1:]] = 1.0
         p_t = draft_distribution(z_t, T)
         out["c_star"].append(tv_acceptance(p_d, p_t))
         out["overlap"].append(np.minimum(p_d, p_t).sum(axis=-1))

@@ -133,3 +133,40 @@ def test_verify_max_rows(T):
     g, _ = run_and_check(case, T, 61, reqs=reqs)
     say(f"[verify] max rows T={T} budget={g['ell'].sum()} tau_mean={g['tau_mean'][0]:.4f}")
     run_and_check(case, T, 62, ell_override=np.arange(512) % 17, reqs=reqs + 5)
+
+
+def test_max_vocabulary_round():
+    """One request, one position at the largest vocabulary the entry points
+    take (V = 2^24): draft step (z, token, p, lse, c, a), schedule and
+    verification against the oracle.  The weights are a random 4096-row block
+    tiled down the vocabulary (drawing 2 x 2^29 fresh values would take minutes
+    on the host); U and the target noise are fresh per entry."""
+    V = 1 << 24
+    small = synth.custom("vmax_block_v4096_r1_g1", V=4096, rank=32, d=16, gamma=1, R=1,
+                         dtype="bf16", peak="three", target=True)
+    wl = synth.custom("vmax_v16777216_r1_g1", V=V, rank=32, d=16, gamma=1, R=1, dtype="bf16",
+                      peak="three", target=True)
+    base = synth.generate(small.name, seed=0)
+    rng = np.random.default_rng(2024)
+    U = (rng.standard_normal((1, 1, V), dtype=np.float32) * np.float32(2.0))
+    U[0, 0, rng.choice(V, 3, replace=False)] += np.float32(6.0)
+    target = U + rng.standard_normal((1, 1, V), dtype=np.float32)
+    inp = dataclasses.replace(base, wl=wl, U=U, target=target,
+                              W1_store=np.tile(base.W1_store, (V // 4096, 1)),
+                              W2t_store=np.tile(base.W2t_store, (V // 4096, 1)),
+                              anchor=np.array([V - 1], dtype=np.int32))
+    case = Case.__new__(Case)
+    case.inp, case.wl = inp, wl
+    case.di = runner.DeviceInputs.upload(inp)
+    # the oracle's fp64 weights: the same tiling of the block's exact values
+    case.W1 = np.tile(O.as_f64(base.W1_store), (V // 4096, 1))
+    case.W2t = np.tile(O.as_f64(base.W2t_store), (V // 4096, 1))
+    from tests.gpu_parity import check_draft
+    for T in (1.0, 0.0):
+        _, host, zs = case.run_draft(T, 71, z_steps=(1,))
+        check_draft(case, host, zs, T, 71)
+        g, _ = run_and_check(case, T, 72)
+        say(f"[verify] V=2^24 T={T} x={host['x'][0]} next={g['next_token']} c*={g['c_star']}")
+        # nothing admitted: the bonus token is drawn over the whole vocabulary
+        g, _ = run_and_check(case, T, 73, ell_override=[0])
+        assert 0 <= g["next_token"][0] < V
