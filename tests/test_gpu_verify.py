@@ -117,6 +117,8 @@ def test_verify_full_size_sampled():
     g, _ = run_and_check(case, 1.0, 51, reqs=reqs)
     say(f"[verify] full size budget={g['ell'].sum()} tau_mean={g['tau_mean'][0]:.4f}")
     run_and_check(case, 1.0, 52, ell_override=np.arange(128) % 17, reqs=reqs + 3)
+    g, _ = run_and_check(case, 0.0, 53, reqs=reqs + 5)
+    say(f"[verify] full size greedy budget={g['ell'].sum()} tau_mean={g['tau_mean'][0]:.4f}")
 
 
 # The largest row count the entry points take: R = 512 requests of gamma = 16
