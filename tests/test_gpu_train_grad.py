@@ -91,13 +91,15 @@ def _dl_scale(got_terms, wk, a_conf):
     return wk[None, :] * abs(a_conf) * (np.abs(c) + np.abs(cs))
 
 
-def _check_all(name, T, lam, seed=5, repeat=False, alphas=O.LOSS_ALPHAS):
+def _check_all(name, T, lam, seed=5, repeat=False, alphas=O.LOSS_ALPHAS, inp=None, w64=None):
+    """inp / w64: prebuilt inputs and their exact fp64 (W1, W2t), else the
+    workload's generated ones."""
     say(f"[grad] {name} T={T} lambda={lam} repeat={repeat} alphas={alphas}")
-    inp = synth.generate(name, seed=0, target=True)
+    inp = synth.generate(name, seed=0, target=True) if inp is None else inp
     wl = inp.wl
     xs = _x_star(inp, seed, repeat)
     got = _run(inp, xs, T, lam, alphas)
-    W1, W2t = O.as_f64(inp.W1_store), O.as_f64(inp.W2t_store)
+    W1, W2t = (O.as_f64(inp.W1_store), O.as_f64(inp.W2t_store)) if w64 is None else w64
     h = O.as_f64(inp.h_store)
     # the library takes the weights in fp32
     alphas = tuple(float(np.float32(x)) for x in alphas)
@@ -220,3 +222,25 @@ def test_train_grad_rejects_fp32_weights():
     xs = _x_star(inp, 1)
     with pytest.raises(D.DsparkError):
         _run(inp, xs, 1.0, None)
+
+
+def test_train_grads_max_vocabulary():
+    """Two rows (one request, gamma = 2) at the largest vocabulary, V = 2^24;
+    the weights are a random 4096-row block tiled down the vocabulary."""
+    import dataclasses
+    V = 1 << 24
+    small = synth.custom("grad_block_v4096_r1_g2", V=4096, rank=32, d=16, gamma=2, R=1,
+                         dtype="bf16", peak="three", target=True)
+    wl = synth.custom("grad_v16777216_r1_g2", V=V, rank=32, d=16, gamma=2, R=1, dtype="bf16",
+                      peak="three", target=True)
+    base = synth.generate(small.name, seed=0)
+    rng = np.random.default_rng(2025)
+    U = rng.standard_normal((1, 2, V), dtype=np.float32) * np.float32(2.0)
+    target = U + rng.standard_normal((1, 2, V), dtype=np.float32)
+    inp = dataclasses.replace(base, wl=wl, U=U, target=target,
+                              W1_store=np.tile(base.W1_store, (V // 4096, 1)),
+                              W2t_store=np.tile(base.W2t_store, (V // 4096, 1)),
+                              anchor=np.array([V - 1], dtype=np.int32))
+    w64 = (np.tile(O.as_f64(base.W1_store), (V // 4096, 1)),
+           np.tile(O.as_f64(base.W2t_store), (V // 4096, 1)))
+    _check_all(wl.name, 1.0, None, inp=inp, w64=w64)
