@@ -20,8 +20,12 @@ What each function follows, and what pins it (tests/test_oracle_pins.py):
         toy printout (0.62 / 0.81) and a two-token closed form.
   draft_distribution           P1 §2.2 eq. p_k and eq. P(X|x0).  Pinned by
         brute-force enumeration (sum over all blocks = 1) and closed forms.
-  draft_step (Gumbel-argmax)   sampling of p_k.  Pinned by a chi-square test of
-        sampled blocks against the enumerated P(X|x0), and T=0 -> argmax.
+  draft_step (two-level Gumbel-argmax)   sampling of p_k.  Pinned by a
+        chi-square test of sampled blocks against the enumerated P(X|x0) (V = 8:
+        one vocabulary block), chi-square tests of single steps at V = 40 and
+        V = 100 (several blocks, a ragged last block) against softmax, the
+        reduction to the textbook Gumbel-max for V <= 16 and for one-hot blocks,
+        and T=0 -> argmax.
   confidence                   P1 §3.1 eq. c_k.  Pinned by closed forms.
   survival / expected_tau      P1 §1.1 eq. a_j and eq. tau.  Pinned by the P2
         Markov toy printout and closed forms.
@@ -55,7 +59,13 @@ Rendering", JCGT 9(3), 2020, keyed as described at `stream_key`.  Only its
 statistical behaviour is pinned (uniformity of u and the sampler tests above).
 
 Readings taken where the pages are silent:
-  * sampling is Gumbel-argmax with the counter generator; ties -> lowest id;
+  * draft sampling is the Gumbel-max trick applied at two levels: the
+    vocabulary is cut into aligned blocks of 16 ids; a block is drawn by
+    Gumbel-argmax of the block log-masses (noise from the DRAFT stream at
+    counter = block index), then an id inside it by Gumbel-argmax of the logits
+    (noise from the DRAFT_ENTRY stream at counter = id).  The law of the result
+    is exactly softmax(s); ties -> lowest block, then lowest id.  Verification's
+    residual and bonus draws are one-level Gumbel-argmax over the vocabulary;
   * s = (U_k + bias) / T; p_d and p_t use the same T; T = 0 means argmax
     (point mass, p = 1, lse reported as max z);
   * the confidence head has no bias term; w = [w_h (d); w_e (rank)]; c_1 uses
@@ -81,7 +91,7 @@ import numpy as np
 # ----------------------------------------------------------------------------
 # Counter-based random numbers (written from the JCGT 2020 definition).
 # ----------------------------------------------------------------------------
-STREAM_DRAFT, STREAM_ACCEPT, STREAM_RESID, STREAM_BONUS = 1, 2, 3, 4
+STREAM_DRAFT, STREAM_ACCEPT, STREAM_RESID, STREAM_BONUS, STREAM_DRAFT_ENTRY = 1, 2, 3, 4, 5
 
 _U32 = np.uint32
 
@@ -173,7 +183,8 @@ def draft_distribution(z, T):
 
 
 def _top2(keys):
-    """(argmax with lowest index on ties, top1 - top2 gap) per row."""
+    """(argmax with lowest index on ties, top1 - top2 gap) per row of a 2-D
+    array.  With a single column, or a single finite entry, the gap is +inf."""
     x = np.argmax(keys, axis=-1)
     top1 = np.take_along_axis(keys, x[:, None], axis=-1)[:, 0]
     rest = keys.copy()
@@ -182,15 +193,55 @@ def _top2(keys):
     return x, top1 - top2
 
 
+DRAFT_BLOCK = 16   # vocabulary ids per block of the two-level draft sampler
+
+
+def block_log_mass(s):
+    """log sum_{v in b} exp(s_v) for the aligned blocks b = [16j, 16j + 16) of the
+    vocabulary (the last one ragged when V % 16 != 0); s [n, V] -> [n, nb]."""
+    s = np.asarray(s, dtype=np.float64)
+    n, V = s.shape
+    nb = -(-V // DRAFT_BLOCK)
+    pad = np.full((n, nb * DRAFT_BLOCK), -np.inf)
+    pad[:, :V] = s
+    blk = pad.reshape(n, nb, DRAFT_BLOCK)
+    mb = blk.max(axis=2)
+    return mb + np.log(np.exp(blk - mb[..., None]).sum(axis=2))
+
+
+def draft_block_keys(s, seed, k, req_ids):
+    """Perturbed block scores: block log-mass + G, G from the DRAFT stream at
+    counter = block index."""
+    lb = block_log_mass(s)
+    nb = lb.shape[1]
+    u = uniforms(np.asarray(seed)[..., None] if np.ndim(seed) else seed, STREAM_DRAFT,
+                 np.asarray(req_ids)[:, None], k, np.arange(nb, dtype=np.uint32)[None, :])
+    return lb + gumbel(u)
+
+
+def draft_entry_keys(s_row, block, seed, k, req):
+    """Perturbed scores s_v + G_v of the ids of one block of one row, G from the
+    DRAFT_ENTRY stream at counter = v.  Returns (ids, keys)."""
+    V = len(s_row)
+    ids = np.arange(block * DRAFT_BLOCK, min(V, (block + 1) * DRAFT_BLOCK))
+    u = uniforms(seed, STREAM_DRAFT_ENTRY, req, k, ids.astype(np.uint32))
+    return ids, np.asarray(s_row, dtype=np.float64)[ids] + gumbel(u)
+
+
 def draft_step(U_k, W1, W2t, x_prev, T, seed, k, req_ids, E=None):
     """One sequential step k for a set of requests (rows of U_k).
 
     z = U_k + W1[x_{k-1}] W2; for T > 0: s = z/T, lse = log sum_v exp(s_v),
-    x_k = lowest v maximising s_v + G_v with G from the DRAFT stream at
-    (req, k, v), p_k(x_k) = exp(s_{x_k} - lse).  T = 0: x_k = argmax z, p = 1,
-    lse := max z.  Also returns the gap between the top two perturbed scores
-    (natural-log units of s), used to count near ties.  E, if given, replaces
-    the gathered rows W1[x_{k-1}] (the RNN head's state rows).
+    p_k(v) = exp(s_v - lse), and x_k is drawn from p_k by the two-level
+    Gumbel-max trick: the block b* maximising block_log_mass(s)_b + G_b (lowest
+    b on ties), then the id maximising s_v + G'_v inside b* (lowest id on
+    ties).  P(b*) = sum_{v in b*} p_k(v) and P(v | b*) = p_k(v) / P(b*), so
+    x_k ~ p_k exactly.  T = 0: x_k = argmax z, p = 1, lse := max z.
+
+    Returned near-tie diagnostics (natural-log units of s): block_keys [n, nb]
+    and gap = min(top-two gap of the block keys, top-two gap of the entry keys
+    inside b*); at T = 0 the top-two gap of z.  E, if given, replaces the
+    gathered rows W1[x_{k-1}] (the RNN head's state rows).
     """
     if E is None:
         z = draft_logits(U_k, W1, W2t, x_prev)
@@ -202,17 +253,36 @@ def draft_step(U_k, W1, W2t, x_prev, T, seed, k, req_ids, E=None):
         s = z / T
         m = s.max(axis=1)
         lse = m + np.log(np.exp(s - m[:, None]).sum(axis=1))
-        v = np.arange(V, dtype=np.uint32)[None, :]
-        u = uniforms(np.asarray(seed)[..., None] if np.ndim(seed) else seed,
-                     STREAM_DRAFT, req_ids[:, None], k, v)
-        keys = s + gumbel(u)
-        x, gap = _top2(keys)
+        bkeys = draft_block_keys(s, seed, k, req_ids)
+        bstar, gap_b = _top2(bkeys)
+        # the ids of each row's drawn block, their noise and perturbed scores
+        ids = bstar[:, None] * DRAFT_BLOCK + np.arange(DRAFT_BLOCK)[None, :]
+        valid = ids < V
+        idc = np.minimum(ids, V - 1)
+        u = uniforms(np.asarray(seed)[..., None] if np.ndim(seed) else seed, STREAM_DRAFT_ENTRY,
+                     req_ids[:, None], k, idc.astype(np.uint32))
+        ekeys = np.where(valid, np.take_along_axis(s, idc, axis=1) + gumbel(u), -np.inf)
+        xi, gap_e = _top2(ekeys)
+        x = ids[np.arange(n), xi].astype(np.int64)
+        gap = np.minimum(gap_b, gap_e)
         p = np.exp(s[np.arange(n), x] - lse)
-    else:
-        x, gap = _top2(z)
-        p = np.ones(n)
-        lse = z.max(axis=1)
-    return {"z": z, "x": x.astype(np.int64), "p": p, "lse": lse, "gap": gap}
+        return {"z": z, "x": x, "p": p, "lse": lse, "gap": gap, "block_keys": bkeys}
+    x, gap = _top2(z)
+    return {"z": z, "x": x.astype(np.int64), "p": np.ones(n), "lse": z.max(axis=1), "gap": gap}
+
+
+def draft_token_deficit(st, i, x_other, T, seed, k, req):
+    """How far another token x_other of row i of a draft_step result falls short
+    of being the sampler's choice, in natural-log units of s: T > 0 -> the larger
+    of (max block key - key of x_other's block) and (max entry key inside that
+    block - entry key of x_other); T = 0 -> max z - z[x_other].  0 for the
+    sampler's own token; a differing token is a near-tie flip iff this is small."""
+    if T == 0:
+        return float(st["z"][i].max() - st["z"][i, x_other])
+    bk = st["block_keys"][i]
+    b = int(x_other) // DRAFT_BLOCK
+    ids, ekeys = draft_entry_keys(st["z"][i] / T, b, seed, k, req)
+    return float(max(bk.max() - bk[b], ekeys.max() - ekeys[ids == x_other][0]))
 
 
 # ----------------------------------------------------------------------------

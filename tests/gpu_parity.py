@@ -1,11 +1,13 @@
 """Helpers of the GPU parity tests: run a round through the C ABI and check it,
 step by step, against the CPU oracle fed the same inputs.
 
-Tolerances (bias/logits 2e-3 absolute; p_k and c_k 1e-3 relative; sampled
-tokens may differ only where the oracle's top two perturbed scores are within
-1e-3, and such flips must stay under 0.1% of the samples; token ids, survival
-products, schedules and admitted sets bit-exact) are written where they are
-checked.
+Tolerances (bias/logits 2e-3 absolute; p_k and c_k 1e-3 relative; a sampled
+token may differ from the oracle's only where the GPU's token is itself within
+1e-3 of the oracle's top perturbed score at every level of the two-level
+sampler (its block's key against the best block key, its id's key against the
+best key inside that block), and such flips must stay under 0.1% of the
+samples; token ids, survival products, schedules and admitted sets bit-exact)
+are written where they are checked.
 """
 from __future__ import annotations
 
@@ -69,10 +71,12 @@ def check_draft(case: Case, host, zs, T, seed, reqs=None, stats=None):
         xg = x[reqs, k]
         assert np.all((xg >= 0) & (xg < wl.V)), f"step {k}: token id out of range"
         flip = xg != st["x"]
-        if np.any(flip):
-            gaps = st["gap"][flip]
-            assert np.all(gaps < NEAR_TIE), (
-                f"step {k}: token mismatch away from a near tie, gaps {gaps[gaps >= NEAR_TIE]}")
+        for i in np.nonzero(flip)[0]:
+            # the GPU's own token must be a near-tie alternative of the oracle's:
+            # its block and, inside the block, its id within NEAR_TIE of the top
+            dfc = O.draft_token_deficit(st, i, int(xg[i]), T, seed, k, int(reqs[i]))
+            assert dfc < NEAR_TIE, (f"step {k} req {reqs[i]}: token {xg[i]} vs oracle "
+                                    f"{st['x'][i]} away from a near tie (deficit {dfc})")
         stats["samples"] += len(reqs)
         stats["flips"] += int(flip.sum())
         # probabilities at the GPU's token, from the oracle's distribution

@@ -174,18 +174,24 @@ def test_batched_confidence_matches_fused():
 
 
 def test_counter_uniforms_bit_exact():
-    """With U = 0, W = 0 and T = 1 every entry has the same logit, so the draft
-    token is the argmax of the Gumbel noise alone: the GPU's token must equal
-    the oracle's argmax of its own uniforms (independent implementations of the
-    same counter generator)."""
+    """With U = 0, W = 0 and T = 1 every id has the same logit, so every block
+    has the same mass and the draft token is decided by the noise alone: the
+    block is the argmax of the block uniforms (DRAFT stream, counter = block),
+    the id the argmax of the id uniforms inside it (DRAFT_ENTRY stream,
+    counter = id).  The GPU's token must equal the one the oracle's own
+    uniforms give (independent implementations of the same counter
+    generator)."""
     from oracle import dspark_oracle as O
     synth.custom("flat_v4096_r64_g2", V=4096, rank=16, d=8, gamma=2, R=64, dtype="bf16",
                  peak="none", weight_std=0.0)
     case = Case("flat_v4096_r64_g2")
     case.di.U.zero_()
     _, host, _ = case.run_draft(1.0, 99)
-    v = np.arange(4096, dtype=np.uint32)
+    nb = 4096 // O.DRAFT_BLOCK
     for k in (1, 2):
         for r in range(64):
-            u = O.uniforms(99, O.STREAM_DRAFT, r, k, v)
-            assert host["x"][r, k] == int(np.argmax(u)), (r, k)
+            ub = O.uniforms(99, O.STREAM_DRAFT, r, k, np.arange(nb, dtype=np.uint32))
+            b = int(np.argmax(ub))
+            ids = np.arange(b * O.DRAFT_BLOCK, (b + 1) * O.DRAFT_BLOCK, dtype=np.uint32)
+            ue = O.uniforms(99, O.STREAM_DRAFT_ENTRY, r, k, ids)
+            assert host["x"][r, k] == int(ids[np.argmax(ue)]), (r, k)

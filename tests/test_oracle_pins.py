@@ -26,23 +26,27 @@ def _golden(name):
 
 
 # ---------------------------------------------------------------------------
-# Page printouts (P2)
+# Page printouts (P2).  Only figures that follow from the page's equations are
+# checked against the printouts; the printed figures that depend on the
+# listings' own random draws are not reproduced (the inputs here are drawn
+# independently, and those cases are checked against exact search instead).
 # ---------------------------------------------------------------------------
-def _h100_step_time(model):
-    """Step time of the P2 cost model: the larger of the weight-read time and
-    the compute time of all tokens in the forward."""
-    def st(tokens):
-        return max(model["weight_bytes"] / model["bandwidth"],
-                   tokens * model["flop_per_token"] / model["flops"])
-    return st
+def _forward_time(model):
+    """Time of one target forward over B tokens in the P2 cost model: reading
+    the weights once, or computing B tokens, whichever takes longer (a
+    roofline bound; P2 "负载越高，K 越要小")."""
+    t_read = model["weight_bytes"] / model["bandwidth"]
+    per_token = model["flop_per_token"] / model["flops"]
+    return lambda B: max(t_read, B * per_token)
 
 
 def test_p2_cost_model_printout():
     """Theta of uniform verify lengths with constant confidence alpha reproduces
-    the P2 cost-model printout: tokens/s, best K and speed-up ratios."""
+    the P2 cost-model printout: tokens/s, best K and speed-up ratios (these
+    follow from the cost equations alone; no random input is involved)."""
     g = _golden("p2_cost_model_printout.json")
     m = g["model"]
-    st = _h100_step_time(m)
+    fwd = _forward_time(m)
     for row in g["rows"]:
         batch = row["batch"]
 
@@ -52,7 +56,7 @@ def test_p2_cost_model_printout():
             draft = 0.0 if k == 0 else (m["t_draft"] if parallel else k * m["t_draft"])
             B = batch * (1 + k)
             sps = np.zeros(B + 1)
-            sps[B] = 1.0 / (draft + st(B))
+            sps[B] = 1.0 / (draft + fwd(B))
             return O.theta_of_ell(a, [k] * batch, sps)
 
         base = thr(0, False)
@@ -64,87 +68,104 @@ def test_p2_cost_model_printout():
             assert f"{thr(best, par) / base:.2f}" == f"{row[rr]:.2f}"
 
 
-def _plan_confidences(batch, gamma):
-    """The plan() demo's confidences: half the rows 0.9, half 0.55, times
-    U(0.9, 1.1) from torch's CPU generator, clamped at 0.99 (fp32)."""
-    base = torch.cat([torch.full((batch // 2, gamma), 0.9),
-                      torch.full((batch - batch // 2, gamma), 0.55)])
-    noise = torch.rand(batch, gamma).mul(0.2).add(0.9)
-    return (base * noise).clamp(max=0.99).numpy()
+def _theta_exact(a, ell, sps_B):
+    """Theta(ell) = tau(ell) * SPS(B) from the definitions [P1 §4.1], with tau in
+    exact rationals (fractions) from the fp32 survival values."""
+    from fractions import Fraction
+    tau = Fraction(len(a))
+    for r, l in enumerate(ell):
+        for j in range(l):
+            tau += Fraction(float(a[r, j]))
+    return tau * Fraction(sps_B)
 
 
-def test_p2_plan_printout():
-    """The early-stop scheduler reproduces the P2 adaptive-verification demo:
-    admitted positions, per-class mean lengths and all three throughputs."""
+def test_p2_plan_budgets():
+    """The adaptive-verification setting of P2 "按负载决定验证多少" (two request
+    classes, 7 positions, cost 1/(draft time + forward time)) with confidences
+    drawn here, independently of the page's listing.  Checked: the no-spec
+    rates the page prints (they follow from the cost model alone), that at
+    batch 16 every candidate is admitted as printed (112: the whole table lies
+    before the knee of the cost curve, whatever the confidences), and at every
+    batch the early stop's budget against the best prefix of the sorted order
+    found by exact rational arithmetic over all budgets."""
     g = _golden("p2_plan_printout.json")
-    st = _h100_step_time(_golden("p2_cost_model_printout.json")["model"])
+    fwd = _forward_time(_golden("p2_cost_model_printout.json")["model"])
     gamma = g["gamma"]
-    torch.manual_seed(0)
+    rng = np.random.default_rng(2024)
     for row in g["rows"]:
         batch = row["batch"]
-        a = O.survival(_plan_confidences(batch, gamma))
+        base = np.where(np.arange(batch) < batch // 2, 0.9, 0.55)[:, None]
+        c = np.minimum(base * rng.uniform(0.9, 1.1, (batch, gamma)), 0.99).astype(np.float32)
+        a = O.survival(c)
         N = batch * (1 + gamma)
-        sps = np.array([1.0 / (0.25e-3 + st(B)) for B in range(N + 1)])
+        sps = np.array([1.0 / (0.25e-3 + fwd(B)) for B in range(N + 1)])
         ell, b, theta, order, theta_fix = O.schedule(a, sps)
-        assert b == row["admitted"]
-        assert round(theta) == row["adaptive_tok_s"]
-        assert f"{ell[:batch // 2].mean():.1f}" == f"{row['easy_mean_len']:.1f}"
-        assert f"{ell[batch // 2:].mean():.1f}" == f"{row['hard_mean_len']:.1f}"
-        assert round(O.theta_of_ell(a, [gamma] * batch, sps)) == row["verify_all_tok_s"]
-        sps_none = np.array([1.0 / st(max(B, 1)) for B in range(N + 1)])
+        sps_none = np.array([1.0 / fwd(max(B, 1)) for B in range(N + 1)])
         assert round(O.theta_of_ell(a, [0] * batch, sps_none)) == row["no_spec_tok_s"]
-        # the demo takes the global maximum; Theta is unimodal here so early stop agrees
-        assert int(np.argmax(theta_fix)) == b
+        if batch == 16:
+            assert b == row["admitted"] == batch * gamma
+        # exact Theta of every prefix of the sorted candidate order
+        best_b, best = 0, None
+        ell_b = np.zeros(batch, dtype=np.int64)
+        for bb in range(batch * gamma + 1):
+            if bb > 0:
+                ell_b[order[bb - 1] // gamma] += 1
+            th = _theta_exact(a, ell_b, sps[batch + bb])
+            if best is None or th > best:
+                best, best_b = th, bb
+        assert b == best_b, (batch, b, best_b)
+        assert int(ell.sum()) == b
 
 
-def _toy_chain():
-    torch.manual_seed(0)
-    V = 64
-    P = torch.full((V, V), 0.1 / (V - 2))
-    for a in range(V):
-        b, c = torch.randperm(V)[:2]
-        P[a, b] = 0.45
-        P[a, c] = 0.45
-    return P
-
-
-def test_p2_markov_toy_printout():
-    """Greedy drafting through the oracle's Markov step, with the toy chain's
-    log-transition matrix as the low-rank head (W1 = I, W2 = log P) and zero base
-    logits, and with marginal-argmax base logits and no head, reproduces the
-    printed expected accepted lengths 0.81 and 0.62 via a_j = prod c_i."""
+def test_p2_markov_toy_closed_form():
+    """P2 "一次前向给出一整块草稿": a chain over V = 64 tokens in which each token
+    has two successors of probability 0.45 and spreads 0.1 over the rest
+    (drawn here with numpy, not the page's generator).  Greedy drafting through
+    the oracle's Markov step with W1 = I and W2 = log P picks a 0.45 successor
+    at every position, so the expected accepted length over K = 6 positions is
+    sum_j 0.45^j = 0.8090..., which the page prints as 0.81.  Drafting from the
+    marginals alone (no transition head) is checked against the same quantity
+    computed from the chain by exact enumeration of the drafted path."""
     g = _golden("p2_markov_toy_printout.json")
-    P = _toy_chain()
     V, K = g["V"], g["K"]
-    Pn = P.numpy().astype(np.float64)
-    W1 = np.eye(V)
-    W2t = np.log(Pn).T.copy()          # W2 = log P (rank = V), stored transposed
-    zero_head = np.zeros((V, V))
+    rng = np.random.default_rng(64)
+    P = np.full((V, V), 0.1 / (V - 2))
+    for t in range(V):
+        b, c = rng.choice(V, 2, replace=False)
+        P[t, b] = P[t, c] = 0.45
+    W1, W2t = np.eye(V), np.log(P).T.copy()
 
-    def expected_accepted(draft, last):
-        prev = [last] + list(draft[:-1])
-        c = np.array([[Pn[p, x] for p, x in zip(prev, draft)]], dtype=np.float32)
+    def expected_accepted(path, start):
+        prev = [start] + list(path[:-1])
+        c = np.array([[P[p, x] for p, x in zip(prev, path)]], dtype=np.float32)
         return O.expected_tau(O.survival(c))[0] - 1.0
 
-    with_tr, indep = 0.0, 0.0
+    closed = sum(0.45 ** j for j in range(1, K + 1))
+    assert f"{closed:.2f}" == f"{g['expected_accepted_with_transition']:.2f}"
     for t in range(V):
         xs = [t]
         for k in range(1, K + 1):
             st = O.draft_step(np.zeros((1, V)), W1, W2t, np.array([xs[-1]]), 0.0, 0, k, np.array([0]))
             xs.append(int(st["x"][0]))
-        with_tr += expected_accepted(xs[1:], t)
-        dist = torch.zeros(V)
-        dist[t] = 1
+            assert P[xs[-2], xs[-1]] == 0.45
+        assert abs(expected_accepted(xs[1:], t) - closed) < 1e-6
+        # marginal drafter: x_k = argmax of the k-step marginal from t
+        dist = np.zeros(V)
+        dist[t] = 1.0
         xp = []
         for k in range(1, K + 1):
             dist = dist @ P
             with np.errstate(divide="ignore"):
-                U = np.log(dist.numpy().astype(np.float64))[None]
-            st = O.draft_step(U, W1, zero_head, np.array([0]), 0.0, 0, k, np.array([0]))
+                st = O.draft_step(np.log(dist)[None], W1, np.zeros((V, V)), np.array([0]), 0.0, 0,
+                                  k, np.array([0]))
             xp.append(int(st["x"][0]))
-        indep += expected_accepted(xp, t)
-    assert f"{with_tr / V:.2f}" == f"{g['expected_accepted_with_transition']:.2f}"
-    assert f"{indep / V:.2f}" == f"{g['expected_accepted_independent']:.2f}"
+            assert dist[xp[-1]] >= dist.max() * (1 - 1e-12)
+        want, run, prev = 0.0, 1.0, t
+        for x in xp:
+            run *= P[prev, x]
+            want += run
+            prev = x
+        assert abs(expected_accepted(xp, t) - want) < 1e-6
 
 
 # ---------------------------------------------------------------------------
@@ -273,6 +294,118 @@ def test_sampler_probability_and_greedy():
     st0 = O.draft_step(z - O.markov_bias(W1, W2t, xp), W1, W2t, xp, 0.0, 7, 2, np.arange(6))
     assert st0["x"][0] == 10 and np.all(st0["p"] == 1.0)
     np.testing.assert_array_equal(st0["x"][1:], np.argmax(z[1:], axis=1))
+
+
+def _sample_many(z_row, T, N, seed=77, k=3):
+    """N independent draws from one logit row: N requests with the same row (the
+    request index keys the noise streams)."""
+    U = np.repeat(np.asarray(z_row, dtype=np.float64)[None], N, axis=0)
+    V = U.shape[1]
+    st = O.draft_step(U, np.zeros((V, 1)), np.zeros((V, 1)), np.zeros(N, dtype=np.int64), T,
+                      seed, k, np.arange(N))
+    return st["x"]
+
+
+@pytest.mark.parametrize("V,T", [(40, 1.0), (100, 0.6), (13, 1.0)])
+def test_two_level_sampler_follows_softmax(V, T):
+    """The two-level Gumbel-argmax draws x with P(x = v) = softmax(z/T)_v: the
+    chi-square of 200k draws against softmax, on vocabularies of several blocks
+    with a ragged last block (40 = 16+16+8, 100 = 6*16+4) and of one block (13),
+    with a few dominant ids spread over different blocks."""
+    rng = np.random.default_rng(V)
+    z = rng.normal(0.0, 1.0, V)
+    z[rng.choice(V, 3, replace=False)] += np.array([3.0, 2.5, 2.0])
+    N = 200_000
+    x = _sample_many(z, T, N)
+    counts = np.bincount(x, minlength=V)
+    p = np.exp(z / T - (z / T).max())
+    p /= p.sum()
+    expected = p * N
+    big = expected >= 5
+    obs, exp = counts[big], expected[big]
+    if not big.all():
+        obs, exp = np.append(obs, counts[~big].sum()), np.append(exp, expected[~big].sum())
+    chi2 = ((obs - exp) ** 2 / exp).sum()
+    assert chi2 < stats.chi2.ppf(1 - 1e-6, len(obs) - 1), chi2
+    # the block level alone: P(block) = the block's probability mass
+    nb = -(-V // O.DRAFT_BLOCK)
+    cb = np.bincount(x // O.DRAFT_BLOCK, minlength=nb)
+    pb = np.array([p[j * 16:(j + 1) * 16].sum() for j in range(nb)]) * N
+    chi2b = ((cb - pb) ** 2 / pb).sum()
+    assert nb == 1 or chi2b < stats.chi2.ppf(1 - 1e-6, nb - 1), chi2b
+
+
+def test_two_level_sampler_block_masses():
+    """Block log-masses equal log(sum of exp) over aligned 16-id ranges, with
+    the last block ragged; a block holding one dominant id and far smaller
+    others has log-mass equal to that id's logit."""
+    z = np.arange(37, dtype=np.float64)[None] * 0.1
+    lb = O.block_log_mass(z)
+    assert lb.shape == (1, 3)
+    for j, (a, b) in enumerate(((0, 16), (16, 32), (32, 37))):
+        assert abs(lb[0, j] - math.log(sum(math.exp(0.1 * v) for v in range(a, b)))) < 1e-12
+    z2 = np.full((1, 32), -1000.0)
+    z2[0, 5], z2[0, 20] = 3.0, -2.0
+    np.testing.assert_allclose(O.block_log_mass(z2)[0], [3.0, -2.0], atol=1e-12)
+
+
+def test_draft_token_deficit_bounds_every_other_token():
+    """The near-tie measure of another token is 0 for the sampler's own token
+    and at least the step's top-two gap for every other token (a differing
+    token is a flip only when some level of the sampler is near a tie)."""
+    rng = np.random.default_rng(9)
+    V, n, T = 70, 6, 0.9
+    U = rng.normal(0, 2, (n, V))
+    st = O.draft_step(U, np.zeros((V, 1)), np.zeros((V, 1)), np.zeros(n, dtype=np.int64), T, 5,
+                      2, np.arange(n))
+    for i in range(n):
+        assert O.draft_token_deficit(st, i, st["x"][i], T, 5, 2, i) == 0.0
+        others = [O.draft_token_deficit(st, i, v, T, 5, 2, i) for v in range(V) if v != st["x"][i]]
+        assert min(others) >= st["gap"][i] > 0
+    st0 = O.draft_step(U, np.zeros((V, 1)), np.zeros((V, 1)), np.zeros(n, dtype=np.int64), 0.0, 5,
+                       2, np.arange(n))
+    for i in range(n):
+        assert O.draft_token_deficit(st0, i, st0["x"][i], 0.0, 5, 2, i) == 0.0
+        d = [O.draft_token_deficit(st0, i, v, 0.0, 5, 2, i) for v in range(V) if v != st0["x"][i]]
+        assert abs(min(d) - st0["gap"][i]) < 1e-12
+
+
+def test_top2_hand_built_rows():
+    """_top2 on hand-made rows: the lowest index wins exact ties with gap 0;
+    -inf entries never win and a lone finite entry has an infinite gap; V = 2."""
+    keys = np.array([[1.0, 3.0, 3.0, 2.0],
+                     [-np.inf, 0.5, -np.inf, -np.inf],
+                     [2.0, -1.0, 0.25, 1.5],
+                     [-np.inf, -np.inf, 7.0, 6.75]])
+    x, gap = O._top2(keys)
+    np.testing.assert_array_equal(x, [1, 1, 0, 2])
+    assert gap[0] == 0.0 and gap[1] == np.inf and gap[2] == 0.5 and gap[3] == 0.25
+    x2, g2 = O._top2(np.array([[0.0, 1e-9], [4.0, 4.0]]))
+    np.testing.assert_array_equal(x2, [1, 0])
+    assert g2[0] == 1e-9 and g2[1] == 0.0
+
+
+def test_bf16_round_matches_torch_conversion():
+    """bf16_round agrees with torch's float32 -> bfloat16 conversion (round to
+    nearest, ties to even) on random values over many binades, on exact
+    halfway cases between bf16 neighbours (both parities) and on signed zeros
+    and the largest finite values; an fp64 input is first rounded to the
+    nearest fp32 (the state the kernels hold), then to bf16."""
+    rng = np.random.default_rng(16)
+    vals = (rng.standard_normal(100_000) * np.exp2(rng.integers(-30, 30, 100_000))).astype(np.float32)
+    lo = rng.integers(0, 1 << 16, 4096).astype(np.uint32) << 16
+    halfway = (lo | 0x8000).view(np.float32)                          # exactly between neighbours
+    near = np.concatenate([(lo | 0x7FFF).view(np.float32), (lo | 0x8001).view(np.float32)])
+    special = np.array([0.0, -0.0, 3.3895314e38, -3.3895314e38, 1e-40, -1e-40], dtype=np.float32)
+    allv = np.concatenate([vals, halfway, near, special])
+    allv = allv[np.isfinite(allv)]
+    want = torch.from_numpy(allv).to(torch.bfloat16).to(torch.float64).numpy()
+    got = O.bf16_round(allv.astype(np.float64))
+    np.testing.assert_array_equal(got, want)
+    # double rounding is the reading: fp64 -> fp32 (nearest) -> bf16 (nearest)
+    x64 = np.float64(1.0) + 2.0 ** -8 + 2.0 ** -30     # above the bf16 halfway point 1 + 2^-8
+    assert np.float32(x64) == np.float32(1.0 + 2.0 ** -8)  # ... but fp32 lands exactly on it
+    assert O.bf16_round(np.array([x64]))[0] == 1.0         # then ties-to-even goes down
 
 
 def test_uniforms_are_uniform_and_exact():
