@@ -104,11 +104,12 @@ const char* dspark_status_string(int status);
  * Reads x[:, k-1]; writes x[:, k], p, lse (and c, a) at column k-1.
  * ws: dspark_workspace_bytes(DSPARK_OP_DRAFT_STEP, ...) bytes of device memory
  * (per-workgroup partial records for gamma steps, then gamma x R 64-bit winner
- * words), ZERO-FILLED before its first use: the winner words are atomic-max
- * targets that every call leaves at zero again.  Calls that may run
- * concurrently need separate workspaces.
- * Enqueues two kernels: the streaming step and the finalisation (record merge,
- * confidence head, survival product).
+ * words, each alone in a 128-byte line), ZERO-FILLED before its first use: the
+ * winner words are atomic-max targets that every call leaves at zero again.
+ * Calls that may run concurrently need separate workspaces.
+ * Enqueues two kernels: the streaming step, which also computes c and a of
+ * step k (they are valid once it has run), and the finalisation (the record
+ * merge, which writes x[:, k], p and lse).
  */
 dspark_status dspark_draft_step(int R, int V, int rank, int d, int gamma, int k, int dt,
                                 const void* W1, const void* W2t, const float* U,

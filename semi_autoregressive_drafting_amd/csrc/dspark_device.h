@@ -31,7 +31,10 @@ constexpr uint32_t kLcgMul = 747796405u;
 constexpr uint32_t kLcgInc = 2891336453u;
 constexpr uint32_t kRxsMul = 277803737u;
 
-constexpr uint32_t kStreamDraft = 1, kStreamAccept = 2, kStreamResid = 3, kStreamBonus = 4;
+constexpr uint32_t kStreamDraft = 1, kStreamAccept = 2, kStreamResid = 3, kStreamBonus = 4,
+                   kStreamDraftEntry = 5;
+// Ids per block of the two-level draft sampler (aligned vocabulary blocks).
+constexpr int kDraftBlock = 16;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -226,6 +229,16 @@ __device__ __forceinline__ float conf_dot_wg(const typename W::store_t* hrow,
 __device__ __forceinline__ float sigmoid_f32(float x) { return 1.0f / (1.0f + expf(-x)); }
 
 __device__ __forceinline__ int clamp_token(int x, int V) { return x < 0 ? 0 : (x >= V ? V - 1 : x); }
+
+// Winner words of the draft steps: one 64-bit word per (step, request), each
+// alone in its 128-byte line.  Every workgroup of a step publishes into the
+// words of all its requests with a device-scope atomic max, and atomics on one
+// line are serialised; with 16 requests per line the step's atomics queued
+// behind each other for several microseconds.
+constexpr int kWinnerStride = 16;  // 64-bit words from one winner word to the next
+__host__ __device__ inline size_t winner_index(int k_idx, int R, int r) {
+  return ((size_t)k_idx * R + r) * kWinnerStride;
+}
 
 // Vocabulary id in a draft step's 64-bit winner word (-1: no winner).  The
 // word packs an order-preserving key above the complemented id, so a 64-bit

@@ -16,7 +16,7 @@ struct StepPlan {
   int n_groups;       // request groups (128 requests shared, 32 private)
   int n_vtiles;       // 32-wide vocabulary tiles
   size_t rec_step;    // workspace: per-step record planes [gamma][n_slabs][5][R]
-  size_t off_best;    //   then the winner words [gamma][R] (u64)
+  size_t off_best;    //   then the winner words [gamma][R] (u64, kWinnerStride apart)
   size_t ws_bytes;
 };
 
@@ -40,13 +40,14 @@ struct StepArgs {
   float* z_debug;
   float* rec;                // records of step 1; step k at rec + (k-1) * rec_step_f
   size_t rec_step_f;         // floats per step plane
-  unsigned long long* best;  // winner words [gamma][R]
+  unsigned long long* best;  // winner words [gamma][R], kWinnerStride apart
   int n_vtiles, n_slabs, n_groups;
 };
 
 StepPlan plan_draft_step(int R, int V, int gamma);
 hipError_t launch_draft_step(const StepArgs& a, const StepPlan& plan, hipStream_t stream);
-// Merge records, write x/p/lse and (if h is set) c/a for steps k0 .. k0+nk-1.
+// Merge the records of steps k0 .. k0+nk-1 and write x, p and lse (c and a are
+// written by the step kernels themselves).
 hipError_t launch_draft_finalize(const StepArgs& a, const StepPlan& plan, int k0, int nk,
                                  hipStream_t stream);
 

@@ -8,14 +8,20 @@
 //     E = W1[x_{k-1}] into VGPRs, forms each 32 x 32 bias tile E . W2 with bf16
 //     (or fp32) MFMA, adds the base logits U_k and folds the tile into an
 //     online max / sum-exp and a Gumbel race, so the R x V bias never reaches
-//     HBM.  The race is argmax_v s_v + G_v in its exponential-race form: the
-//     winner maximises e_v / L_v with e_v = 2^(t_v - m) (already needed for
-//     the sum) and L_v = -log2 u_v, one logarithm per entry.  At the end the
-//     workgroup stores one partial record per request (m, S, key, t_best, id)
-//     with plain stores and publishes its winner with one 64-bit atomic max of
-//     (order-preserving key, ~id): the maximum is independent of the order in
-//     which workgroups arrive and keeps the lowest id on equal keys.  The next
-//     step reads x_k from that word, so nothing waits for a merge.
+//     HBM.  Sampling is the Gumbel-max trick at two levels over aligned blocks
+//     of 16 ids (each lane's 16 entries of a tile are exactly one block): the
+//     stream races blocks, maximising M_b / L_b with M_b = sum_{v in b}
+//     2^(t_v - m) (the block's share of the softmax sum) and L_b = -log2 u_b
+//     (one uniform and one logarithm per block), and keeps the 16 logits of
+//     the lane's leading block in registers.  After the stream each lane draws
+//     an id inside its leading block by the same race over the block's ids
+//     (e_v / L_v, a second noise stream).  The workgroup then stores one
+//     partial record per request (m, S, block key, t of the drawn id, id) with
+//     plain stores and publishes its winner with one 64-bit atomic max of
+//     (order-preserving block key, ~id): the maximum is independent of the
+//     order in which workgroups arrive and keeps the lowest block (hence the
+//     lowest id) on equal keys.  The next step reads x_k from that word, so
+//     nothing waits for a merge.
 //
 //     The first slabs (the ones with the lighter share of tiles) also run the
 //     confidence head for one request each after their stream:
@@ -45,8 +51,9 @@ namespace dspark {
 namespace {
 
 constexpr int kWaves = 4;
-// Workgroups of a draft step (per request group for R > 96).  More than the
-// 512 the CUs hold at once, so late starters and heavy slabs even out.
+// Workgroups of a draft step (in total over the request groups): two per CU.
+// Two independent 4-wave pipelines per CU hide memory latency better than one
+// 8-wave workgroup whose waves meet at every barrier.
 constexpr int kDraftWgs = 512;
 
 // Prefetch distance of the shared stream: 2 for bf16 weights; fp32 weights
@@ -79,9 +86,9 @@ __device__ __forceinline__ unsigned long long pack_winner(float key, int idx) {
 struct LaneState {
   float m;    // running max of t = z * kscale
   float S;    // sum of 2^(t - m)
-  float bE;   // race winner's 2^(t - m) (rescaled with m); greedy: best z
-  float bLn;  // race winner's log2(u) < 0
-  int bV;     // winner id, -1 if none
+  float bE;   // leading block's mass sum 2^(t - m) (rescaled with m); greedy: best z
+  float bLn;  // leading block's log2(u) < 0
+  int bV;     // leading block's first id (greedy: best id), -1 if none
 };
 
 // U rows of the wave's 32 requests: with kVec (16-byte aligned rows) read as
@@ -94,7 +101,9 @@ struct DraftEpi {
   float* patch;  // this wave's LDS patch (kVec)
   int V, R, r, half;
   float kscale;
-  uint32_t state_row;  // LCG state of vocabulary entry 0 of this row
+  uint32_t state_row;  // LCG state of block 0 of this row (block stream)
+  uint32_t state_ent;  // LCG state of id 0 of this row (id stream)
+  float zb[kGreedy ? 1 : 16];                    // logits of the leading block
   float ubuf[kVec ? 1 : kMaxDist + 1][16];       // own-row U (scalar path)
   RowTiles<1, kVec ? kMaxDist + 1 : 1> rows;     // line-coalesced U (kVec)
   LaneState st;
@@ -111,6 +120,11 @@ struct DraftEpi {
       rows.init([&](int j) { return (size_t)(r0w + (j < jmax ? j : jmax)) * rstride; });
     }
     state_row = row_key(a.seed, kStreamDraft, (uint32_t)rc, (uint32_t)a.k) * kLcgMul + kLcgInc;
+    state_ent = kGreedy ? 0u
+                        : row_key(a.seed, kStreamDraftEntry, (uint32_t)rc, (uint32_t)a.k) * kLcgMul +
+                              kLcgInc;
+#pragma unroll
+    for (int i = 0; i < (kGreedy ? 1 : 16); ++i) zb[i] = 0.0f;
     st.m = -INFINITY;
     st.S = 0.0f;
     st.bE = kGreedy ? -INFINITY : 0.0f;
@@ -144,19 +158,24 @@ struct DraftEpi {
       st.bE *= f;
       st.m = mnew;
       const float negm = -mnew;
-      const uint32_t s0 = state_row + (uint32_t)vb * kLcgMul;
+      // the block's mass (vb is a multiple of 16: the lane's entries are one block)
+      float sb = 0.0f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float e = fast_exp2(fmaf(z[i], kscale, negm));
         if constexpr (kMasked) e = (vb + i < V) ? e : 0.0f;
-        st.S += e;
-        const float ln = fast_log2(bits_to_uniform(rxs_m_xs(s0 + (uint32_t)i * kLcgMul)));
-        // e / L > bE / bL  <=>  e * bLn < bE * ln     (L = -ln > 0)
-        const bool win = e * st.bLn < st.bE * ln;
-        st.bE = win ? e : st.bE;
-        st.bLn = win ? ln : st.bLn;
-        st.bV = win ? vb + i : st.bV;
+        sb += e;
       }
+      st.S += sb;
+      const float ln = fast_log2(
+          bits_to_uniform(rxs_m_xs(state_row + (uint32_t)(vb / kDraftBlock) * kLcgMul)));
+      // sb / L > bE / bL  <=>  sb * bLn < bE * ln     (L = -ln > 0)
+      const bool win = sb * st.bLn < st.bE * ln;
+      st.bE = win ? sb : st.bE;
+      st.bLn = win ? ln : st.bLn;
+      st.bV = win ? vb : st.bV;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) zb[i] = win ? z[i] : zb[i];
     }
   }
 
@@ -192,28 +211,79 @@ struct DraftEpi {
     fold_tile<true>(u, acc, vt);
   }
 
-  __device__ Rec record() const {
+  // The record of the lane's request over both halves of the wave (lanes l and
+  // l ^ 32 hold the same request, different ids): the softmax statistics merged,
+  // the leading block of the two (larger block key; the lower block on equal
+  // keys), and the id drawn inside that block by the race e_v / L_v with
+  // e_v = 2^(t_v - t_max) and L_v = -log2 u_v from the id stream, the two lanes
+  // taking 8 ids each.  Both lanes return the same record.
+  __device__ Rec row_record() const {
     Rec q;
-    if (kGreedy) {
+    if constexpr (kGreedy) {
       q.m = st.bE;
       q.S = 0.0f;
       q.key = st.bE;
       q.tbest = st.bE;
       q.idx = st.bV;
+      return rec_merge(q, rec_shfl_xor(q, 32));
     } else {
-      q.m = st.m;
-      q.S = st.S;
-      if (st.bV >= 0 && st.bE > 0.0f) {
-        q.tbest = st.m + fast_log2(st.bE);
-        q.key = q.tbest - fast_log2(-st.bLn);
-        q.idx = st.bV;
-      } else {
-        q.tbest = -INFINITY;
-        q.key = -INFINITY;
-        q.idx = -1;
+      const bool has = st.bV >= 0 && st.bE > 0.0f;
+      const float key = has ? st.m + fast_log2(st.bE) - fast_log2(-st.bLn) : -INFINITY;
+      const int vb = has ? st.bV : -1;
+      const float okey = __shfl_xor(key, 32);
+      const int ovb = __shfl_xor(vb, 32);
+      const bool take_o = rec_beats(okey, ovb, key, vb);
+      const int wvb = take_o ? ovb : vb;
+      q.key = take_o ? okey : key;
+      // softmax statistics (the same bits in both lanes: IEEE addition commutes)
+      const float om = __shfl_xor(st.m, 32), oS = __shfl_xor(st.S, 32);
+      q.m = fmaxf(st.m, om);
+      q.S = (q.m == -INFINITY) ? 0.0f
+                               : st.S * fast_exp2(st.m - q.m) + oS * fast_exp2(om - q.m);
+      // the leading block's logits in both lanes
+      float zw[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float oz = __shfl_xor(zb[i], 32);
+        zw[i] = take_o ? oz : zb[i];
       }
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tmax = (wvb + i < V) ? fmaxf(tmax, zw[i] * kscale) : tmax;
+      // this lane's 8 ids: wvb + 8 half + j
+      const int i0 = wvb + 8 * half;
+      const uint32_t s0 = state_ent + (uint32_t)i0 * kLcgMul;
+      float eE = 0.0f, eLn = -1.0f, tsel = -INFINITY;
+      int isel = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float t = (half ? zw[8 + j] : zw[j]) * kscale;
+        float e = fast_exp2(t - tmax);
+        e = (i0 + j < V) ? e : 0.0f;
+        const float ln = fast_log2(bits_to_uniform(rxs_m_xs(s0 + (uint32_t)j * kLcgMul)));
+        const bool win = e * eLn < eE * ln;
+        eE = win ? e : eE;
+        eLn = win ? ln : eLn;
+        tsel = win ? t : tsel;
+        isel = win ? j : isel;
+      }
+      // the two halves' winners: the upper ids (half 1) win only on a strictly
+      // larger ratio
+      const float oE = __shfl_xor(eE, 32), oLn = __shfl_xor(eLn, 32), ot = __shfl_xor(tsel, 32);
+      const int oi = __shfl_xor(isel, 32);
+      const float aE = half ? oE : eE, aLn = half ? oLn : eLn, bE2 = half ? eE : oE,
+                  bLn2 = half ? eLn : oLn;
+      const bool hi = bE2 * aLn < aE * bLn2;
+      const float t_lo = half ? ot : tsel, t_hi = half ? tsel : ot;
+      const int i_lo = half ? oi : isel, i_hi = half ? isel : oi;
+      q.tbest = hi ? t_hi : t_lo;
+      q.idx = wvb < 0 ? -1 : wvb + (hi ? 8 + i_hi : i_lo);
+      if (wvb < 0) {
+        q.key = -INFINITY;
+        q.tbest = -INFINITY;
+      }
+      return q;
     }
-    return q;
   }
 };
 
@@ -222,9 +292,46 @@ struct DraftEpi {
 // winner word.
 __device__ __forceinline__ int prev_token(const StepArgs& a, int rc) {
   if (a.k > 1 && a.prev_from_best)
-    return winner_id(a.best[(size_t)(a.k - 2) * a.R + rc]);
+    return winner_id(a.best[winner_index(a.k - 2, a.R, rc)]);
   return a.x[(size_t)rc * (a.gamma + 1) + (a.k - 1)];
 }
+
+// Tokens x_{k-1} of a wave's 32 requests r0w .. r0w + 31 (past R - 1: request
+// R - 1).  The words are read through the scalar cache with wave-uniform
+// addresses: scalar loads are counted apart from the vector loads, so the
+// tokens arrive without waiting behind the first tiles' vector loads (vector
+// loads retire in issue order); only the row gather queues behind those.
+// issue() starts the 32 loads, token() waits for them and gives lane l the
+// token of request r0w + l % 32.
+struct WaveTokens {
+  typedef const __attribute__((address_space(4))) uint32_t* cptr;
+  uint32_t t[32];
+  bool from_best;
+  __device__ __forceinline__ void issue(const StepArgs& a, int r0w) {
+    r0w = __builtin_amdgcn_readfirstlane(r0w);
+    // word j of the wave sits at base + j * stride (32-bit words)
+    from_best = a.k > 1 && a.prev_from_best;
+    cptr base;
+    size_t stride;
+    if (from_best) {  // the low word of each winner word holds ~id
+      base = (cptr)(uintptr_t)a.best + 2 * winner_index(a.k - 2, a.R, r0w);
+      stride = 2 * kWinnerStride;
+    } else {
+      base = (cptr)(uintptr_t)a.x + (size_t)r0w * (a.gamma + 1) + (a.k - 1);
+      stride = (size_t)(a.gamma + 1);
+    }
+    const int last = __builtin_amdgcn_readfirstlane(min(31, a.R - 1 - r0w));
+#pragma unroll
+    for (int j = 0; j < 32; ++j) t[j] = base[(size_t)(j < last ? j : last) * stride];
+  }
+  __device__ __forceinline__ int token() const {
+    const int col = threadIdx.x & 31;
+    int tok = 0;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) tok = (col == j) ? (int)t[j] : tok;
+    return from_best ? ~tok : tok;
+  }
+};
 
 // Records of step k live in slab-major planes: rec[(slab * 5 + field) * R + r].
 __device__ __forceinline__ void put_rec(float* base, int R, int slab, int r, const Rec& q) {
@@ -239,7 +346,7 @@ __device__ __forceinline__ void put_rec(float* base, int R, int slab, int r, con
 __device__ __forceinline__ void publish(const StepArgs& a, int slab, int r, const Rec& q) {
   put_rec(a.rec + (size_t)(a.k - 1) * a.rec_step_f, a.R, slab, r, q);
   if (q.idx >= 0)
-    atomicMax(a.best + (size_t)(a.k - 1) * a.R + r, pack_winner(q.key, q.idx));
+    atomicMax(a.best + winner_index(a.k - 1, a.R, r), pack_winner(q.key, q.idx));
 }
 
 // Confidence head and survival product of step k for requests r0 + slab,
@@ -289,9 +396,11 @@ __global__ __launch_bounds__(kStreamThreads) void markov_step_shared(StepArgs a)
   float* patch = reinterpret_cast<float*>(lds + draft_stream_lds<W, kKs>(a.rank)) +
                  wave * kPatchFloats;
   DraftEpi<kGreedy, kDebug, kVec> epi(a, r, rc, half, r0 + wave * kVTile, patch);
+  WaveTokens toks;
+  if (!a.E_rows) toks.issue(a, r0 + wave * kVTile);
   auto gather = [&](typename W::frag_t(&ef)[W::kMaxKs]) {
     const void* base = a.E_rows ? a.E_rows : a.W1;
-    const int row = a.E_rows ? rc : clamp_token(prev_token(a, rc), a.V);
+    const int row = a.E_rows ? rc : clamp_token(toks.token(), a.V);
     if constexpr (std::is_same<W, WBf16>::value && kKs > 0 && kKs % 4 == 0 && kVec)
       load_e_frags_lines<kKs>(ef, reinterpret_cast<const uint16_t*>(base), row, patch);
     else
@@ -303,8 +412,7 @@ __global__ __launch_bounds__(kStreamThreads) void markov_step_shared(StepArgs a)
     shared_a_stream<W, kKs, draft_dist<W>()>(a.W2t, a.V, a.rank, t_begin, t_end, e, gather, lds,
                                              epi);
 
-  Rec q = epi.record();
-  q = rec_merge(q, rec_shfl_xor(q, 32));
+  const Rec q = epi.row_record();
   if (half == 0 && r < a.R) publish(a, slab, r, q);
   if (a.h != nullptr) step_confidence<W>(a, slab, r0, min(kWaves * kVTile, a.R - r0));
 }
@@ -325,11 +433,13 @@ __global__ __launch_bounds__(kStreamThreads) void markov_step_private(StepArgs a
   __shared__ __align__(16) float patches[kVec ? kWaves : 1][kPatchFloats];
   typename W::frag_t e[W::kMaxKs];
   DraftEpi<kGreedy, kDebug, kVec> epi(a, r, rc, half, r0, patches[kVec ? wave : 0]);
+  WaveTokens toks;
+  if (!a.E_rows) toks.issue(a, r0);
   private_a_stream<W, kKs>(
       a.W2t, a.V, a.rank, t_begin + wave, t_end, kWaves, e,
       [&](typename W::frag_t(&ef)[W::kMaxKs]) {
         const void* base = a.E_rows ? a.E_rows : a.W1;
-        const int row = a.E_rows ? rc : clamp_token(prev_token(a, rc), a.V);
+        const int row = a.E_rows ? rc : clamp_token(toks.token(), a.V);
         if constexpr (std::is_same<W, WBf16>::value && kKs > 0 && kKs % 4 == 0 && kVec)
           load_e_frags_lines<kKs>(ef, reinterpret_cast<const uint16_t*>(base), row,
                                   patches[kVec ? wave : 0]);
@@ -338,8 +448,7 @@ __global__ __launch_bounds__(kStreamThreads) void markov_step_private(StepArgs a
       },
       epi);
 
-  Rec q = epi.record();
-  q = rec_merge(q, rec_shfl_xor(q, 32));
+  const Rec q = epi.row_record();
   if (half == 0) srec[wave][col] = q;
   __syncthreads();
   if (wave == 0 && half == 0 && r < a.R) {
@@ -427,7 +536,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void draft_merge(StepArgs a, int 
       a.p[oi] = exp2f(f.tb - lse2);
       a.lse[oi] = lse2 * kLn2;
     }
-    a.best[(size_t)(k - 1) * a.R + r] = 0ull;  // leave the workspace zeroed for the next call
+    a.best[winner_index(k - 1, a.R, r)] = 0ull;  // leave the workspace zeroed for the next call
   }
 }
 
@@ -498,7 +607,7 @@ StepPlan plan_draft_step(int R, int V, int gamma) {
   p.grid_y = 1;
   p.rec_step = align256((size_t)p.n_slabs * 5 * R * 4);
   p.off_best = p.rec_step * gamma;
-  p.ws_bytes = p.off_best + align256((size_t)gamma * R * 8);
+  p.ws_bytes = p.off_best + align256((size_t)gamma * R * 8 * kWinnerStride);
   return p;
 }
 

@@ -221,7 +221,7 @@ __device__ __forceinline__ void state_step_body(const RnnArgs& a, int k, const f
       pre[i] = a.Pk[((size_t)(k - 1) * a.R + r) * (3 * H) + g * H + n];
     }
   }
-  int tok = k > 1 ? winner_id(a.best[(size_t)(k - 2) * a.R + mc]) : a.x[(size_t)mc * (a.gamma + 1)];
+  int tok = k > 1 ? winner_id(a.best[winner_index(k - 2, a.R, mc)]) : a.x[(size_t)mc * (a.gamma + 1)];
   tok = clamp_token(tok, a.V);
   const uint16_t* erow = a.W1 + (size_t)tok * H + 8 * half;
 #pragma unroll
