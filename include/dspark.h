@@ -132,6 +132,30 @@ dspark_status dspark_draft_block(int R, int V, int rank, int d, int gamma, int d
                                  float* a, void* ws, size_t ws_bytes, dspark_stream_t stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * dspark_draft_block without the workspace arguments.  Same arguments
+ * otherwise, same kernels, and the same results bit for bit as
+ * dspark_draft_block with a zero-filled workspace.
+ *
+ * The workspace is a static device array inside the library, 22 MiB per GPU,
+ * held from the library's first use on that GPU until the process ends.  It
+ * fits the draft workspace of every shape this ABI accepts; a shape whose
+ * workspace did not fit would return DSPARK_ERR_WORKSPACE before any HIP
+ * call.  Nothing is allocated or freed: the call only enqueues kernels
+ * (a small fill kernel clears the winner words, then the gamma steps and
+ * the merge).  Every call on a GPU shares that GPU's array, so calls that
+ * overlap in time on one GPU (other streams, other threads) race and give
+ * wrong results; serialise them.  Errors: as dspark_draft_block, plus
+ * DSPARK_ERR_LAUNCH if the array's device address cannot be obtained.
+ */
+dspark_status dspark_draft_block_noalloc(int R, int V, int rank, int d, int gamma, int dt,
+                                         const void* W1, const void* W2t, const float* U,
+                                         const void* h, const float* w, float temperature,
+                                         uint64_t seed, int32_t* x, float* p, float* lse,
+                                         float* c, float* a, dspark_stream_t stream);
+
+/*
  * dspark_draft_block split into its two phases, so that a caller can place
  * events between them: DSPARK_PHASE_STEPS enqueues the gamma streaming steps
  * (winner words and partial records in ws), DSPARK_PHASE_MERGE the record

@@ -7,10 +7,21 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "dspark.h"
 #include "dspark_kernels.h"
 
 using namespace dspark;
+
+// The workspace of dspark_draft_block_noalloc: one copy per GPU in the code
+// object, held until the process ends.  22 MiB holds the draft workspace of
+// every shape the ABI accepts (the largest, R = 512 and gamma = 16, needs
+// 22,020,096 bytes).  In host code the name stands for a host-side symbol, not
+// a device address: the device address comes from hipGetSymbolAddress, once
+// per device (scratch_address below), and only that address is passed on.
+constexpr size_t kNoAllocScratchBytes = (size_t)22 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
 namespace {
 
@@ -60,6 +71,26 @@ RnnPlan plan_rnn(int R, int V, int rank, int gamma) {
   off = al256(off + (size_t)R * rank * 2);
   q.ws_bytes = off;
   return q;
+}
+
+// Device address of `scratch` on the current device, looked up on the first
+// call made with that device current and kept per device afterwards.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+dspark_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DSPARK_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_addr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return DSPARK_ERR_LAUNCH;
+    g_scratch_addr[dev] = ptr;
+  }
+  *out = g_scratch_addr[dev];
+  return DSPARK_OK;
 }
 
 }  // namespace
@@ -254,6 +285,40 @@ dspark_status dspark_draft_block_phases(int R, int V, int rank, int d, int gamma
     args.prev_from_best = true;  // x_{k-1} of positions 2..gamma from the winner words
     if (launch_draft_finalize(args, plan, 1, gamma, st) != hipSuccess) return DSPARK_ERR_LAUNCH;
   }
+  return DSPARK_OK;
+}
+
+dspark_status dspark_draft_block_noalloc(int R, int V, int rank, int d, int gamma, int dt,
+                                         const void* W1, const void* W2t, const float* U,
+                                         const void* h, const float* w, float temperature,
+                                         uint64_t seed, int32_t* x, float* p, float* lse,
+                                         float* c, float* a, dspark_stream_t stream) {
+  // validate first (no HIP call yet): the workspace stand-in is only checked
+  // for its size, which must fit the static scratch
+  StepArgs args;
+  StepPlan plan;
+  void* const stand_in = reinterpret_cast<void*>((uintptr_t)256);
+  const dspark_status s = check_draft(R, V, rank, d, gamma, 0, dt, W1, W2t, U, h, w, temperature,
+                                      seed, x, p, lse, c, a, nullptr, stand_in,
+                                      kNoAllocScratchBytes, args, plan);
+  if (s != DSPARK_OK) return s;
+  void* ws = nullptr;
+  const dspark_status t = scratch_address(&ws);
+  if (t != DSPARK_OK) return t;
+  args.rec = static_cast<float*>(ws);
+  args.best =
+      reinterpret_cast<unsigned long long*>(static_cast<unsigned char*>(ws) + plan.off_best);
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  // the scratch keeps whatever the previous call on this GPU left there
+  if (launch_clear_winners(args, plan, st) != hipSuccess) return DSPARK_ERR_LAUNCH;
+  for (int k = 1; k <= gamma; ++k) {
+    args.k = k;
+    args.prev_from_best = k > 1;
+    if (launch_draft_step(args, plan, st) != hipSuccess) return DSPARK_ERR_LAUNCH;
+  }
+  args.k = 1;
+  args.prev_from_best = true;
+  if (launch_draft_finalize(args, plan, 1, gamma, st) != hipSuccess) return DSPARK_ERR_LAUNCH;
   return DSPARK_OK;
 }
 

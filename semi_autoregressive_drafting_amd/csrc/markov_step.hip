@@ -615,6 +615,20 @@ hipError_t launch_draft_step(const StepArgs& a, const StepPlan& plan, hipStream_
   return a.bf16 ? launch_w<WBf16>(a, plan, stream) : launch_w<WF32>(a, plan, stream);
 }
 
+// Zero the winner words of a block (a workspace whose earlier contents are
+// unknown): n 64-bit words from `best`, plain vector stores.
+__global__ __launch_bounds__(256) void clear_words(unsigned long long* best, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+    best[i] = 0ull;
+}
+
+hipError_t launch_clear_winners(const StepArgs& a, const StepPlan& plan, hipStream_t stream) {
+  const size_t n = (plan.ws_bytes - plan.off_best) / sizeof(unsigned long long);
+  const int blocks = (int)min((size_t)1024, (n + 255) / 256);
+  hipLaunchKernelGGL(clear_words, dim3(blocks), dim3(256), 0, stream, a.best, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_draft_finalize(const StepArgs& a, const StepPlan& plan, int k0, int nk,
                                  hipStream_t stream) {
   (void)plan;

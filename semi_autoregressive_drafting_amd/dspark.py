@@ -24,7 +24,7 @@ DSPARK_PHASE_STEPS, DSPARK_PHASE_MERGE = 1, 2
 EXPORTS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_draft_step",
            "dspark_draft_block", "dspark_draft_block_phases", "dspark_confidence", "dspark_schedule", "dspark_schedule_async",
            "dspark_verify", "dspark_train_loss", "dspark_train_loss_grad",
-           "dspark_draft_block_rnn", "dspark_verify_rnn")
+           "dspark_draft_block_rnn", "dspark_verify_rnn", "dspark_draft_block_noalloc")
 
 _lib = None
 
@@ -58,6 +58,9 @@ def load():
     L.dspark_draft_block_phases.argtypes = [I, I, I, I, I, I, P, P, P, P, P, F, U64,
                                             P, P, P, P, P, P, SZ, I, P]
     L.dspark_draft_block_phases.restype = I
+    L.dspark_draft_block_noalloc.argtypes = [I, I, I, I, I, I, P, P, P, P, P, F, U64,
+                                             P, P, P, P, P, P]
+    L.dspark_draft_block_noalloc.restype = I
     L.dspark_confidence.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P]
     L.dspark_confidence.restype = I
     L.dspark_schedule.argtypes = [I, I, P, P, I, P, P, P, P, SZ, P]
@@ -135,6 +138,13 @@ def dspark_draft_block(R, V, rank, d, gamma, dt, W1, W2t, U, h, w, temperature, 
     _call("dspark_draft_block", R, V, rank, d, gamma, dt, _ptr(W1), _ptr(W2t), _ptr(U),
           _ptr(h), _ptr(w), float(temperature), int(seed), _ptr(x), _ptr(p), _ptr(lse),
           _ptr(c), _ptr(a), _ptr(ws), int(ws_bytes), _stream(stream))
+
+
+def dspark_draft_block_noalloc(R, V, rank, d, gamma, dt, W1, W2t, U, h, w, temperature, seed,
+                               x, p, lse, c, a, stream=None):
+    _call("dspark_draft_block_noalloc", R, V, rank, d, gamma, dt, _ptr(W1), _ptr(W2t), _ptr(U),
+          _ptr(h), _ptr(w), float(temperature), int(seed), _ptr(x), _ptr(p), _ptr(lse),
+          _ptr(c), _ptr(a), _stream(stream))
 
 
 def dspark_draft_block_phases(R, V, rank, d, gamma, dt, W1, W2t, U, h, w, temperature, seed,

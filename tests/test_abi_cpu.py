@@ -116,6 +116,40 @@ def test_draft_block_validation():
     assert f(*bad) == D.DSPARK_ERR_WORKSPACE
 
 
+def test_draft_block_noalloc_validation():
+    """The no-allocation block validates like dspark_draft_block before any HIP
+    call (there is no workspace argument to get wrong)."""
+    f = D.load().dspark_draft_block_noalloc
+    args = [4, 1024, 32, 64, 4, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 1.0, 0, FAKE, FAKE, FAKE,
+            FAKE, FAKE, None]
+    bad = list(args); bad[6] = None
+    assert f(*bad) == D.DSPARK_ERR_NULL
+    bad = list(args); bad[13] = None
+    assert f(*bad) == D.DSPARK_ERR_NULL
+    bad = list(args); bad[4] = 0
+    assert f(*bad) == D.DSPARK_ERR_SHAPE
+    bad = list(args); bad[0] = 513
+    assert f(*bad) == D.DSPARK_ERR_SHAPE
+    bad = list(args); bad[5] = 7
+    assert f(*bad) == D.DSPARK_ERR_DTYPE
+    bad = list(args); bad[11] = float("nan")
+    assert f(*bad) == D.DSPARK_ERR_VALUE
+    bad = list(args); bad[9] = None   # h without w
+    assert f(*bad) == D.DSPARK_ERR_NULL
+
+
+def test_noalloc_scratch_fits_every_accepted_shape():
+    """The static workspace of dspark_draft_block_noalloc (22 MiB) holds the
+    draft workspace of the largest shape the ABI accepts (R = 512, gamma = 16),
+    at any vocabulary size."""
+    f = D.dspark_workspace_bytes
+    biggest = max(f(D.DSPARK_OP_DRAFT_STEP, R, V, 256, g)
+                  for R in (1, 96, 97, 128, 129, 384, 511, 512) for g in (1, 7, 16)
+                  for V in (2, 1024, 151936, 1 << 24))
+    assert biggest == f(D.DSPARK_OP_DRAFT_STEP, 512, 151936, 256, 16)
+    assert biggest <= 22 << 20
+
+
 def test_schedule_validation():
     lib = D.load()
     f = lib.dspark_schedule
