@@ -274,11 +274,7 @@ dspark_status dspark_draft_block_phases(int R, int V, int rank, int d, int gamma
   if (s != DSPARK_OK) return s;
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (phases & DSPARK_PHASE_STEPS) {
-    for (int k = 1; k <= gamma; ++k) {
-      args.k = k;
-      args.prev_from_best = k > 1;  // x_{k-1} straight from step k-1's winner word
-      if (launch_draft_step(args, plan, st) != hipSuccess) return DSPARK_ERR_LAUNCH;
-    }
+    if (launch_draft_steps(args, plan, st) != hipSuccess) return DSPARK_ERR_LAUNCH;
   }
   if (phases & DSPARK_PHASE_MERGE) {
     args.k = 1;
@@ -311,11 +307,7 @@ dspark_status dspark_draft_block_noalloc(int R, int V, int rank, int d, int gamm
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   // the scratch keeps whatever the previous call on this GPU left there
   if (launch_clear_winners(args, plan, st) != hipSuccess) return DSPARK_ERR_LAUNCH;
-  for (int k = 1; k <= gamma; ++k) {
-    args.k = k;
-    args.prev_from_best = k > 1;
-    if (launch_draft_step(args, plan, st) != hipSuccess) return DSPARK_ERR_LAUNCH;
-  }
+  if (launch_draft_steps(args, plan, st) != hipSuccess) return DSPARK_ERR_LAUNCH;
   args.k = 1;
   args.prev_from_best = true;
   if (launch_draft_finalize(args, plan, 1, gamma, st) != hipSuccess) return DSPARK_ERR_LAUNCH;

@@ -226,6 +226,49 @@ __device__ __forceinline__ float conf_dot_wg(const typename W::store_t* hrow,
   return dot;
 }
 
+// conf_dot_part for bf16 rows in 16-byte chunks, split in two so that the loads
+// can be issued long before the arithmetic: load() issues this lane's chunks
+// (at most kConfChunks, i.e. d + rank up to 4 * 64 * 8 * kConfChunks), dot()
+// then performs conf_dot_part's fused multiply-adds in its order and the same
+// butterfly, so the result is bit-identical.
+constexpr int kConfChunks = 3;
+struct ConfPreload {
+  u32x4_t v[kConfChunks];
+  f32x4_t w0[kConfChunks], w1[kConfChunks];
+  int n;  // chunks of this lane
+  __device__ __forceinline__ void load(const uint16_t* hrow, const uint16_t* erow, const float* w,
+                                       int d, int j0, int j1, int lane) {
+    n = 0;
+#pragma unroll
+    for (int c = 0; c < kConfChunks; ++c) {
+      const int j = j0 + lane * 8 + c * 64 * 8;
+      const bool ok = j < j1;
+      const int jj = ok ? j : 0;  // a valid address whose values are not used
+      const uint16_t* src = jj < d ? hrow + jj : erow + (jj - d);
+      v[c] = *reinterpret_cast<const u32x4_t*>(src);
+      w0[c] = *reinterpret_cast<const f32x4_t*>(w + jj);
+      w1[c] = *reinterpret_cast<const f32x4_t*>(w + jj + 4);
+      n += ok ? 1 : 0;
+    }
+  }
+  __device__ __forceinline__ float dot() const {
+    float dot = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kConfChunks; ++c) {
+      if (c < n) {
+        const uint16_t* vs = reinterpret_cast<const uint16_t*>(&v[c]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dot = fmaf(w0[c][q], WBf16::to_f32(vs[q]), dot);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dot = fmaf(w1[c][q], WBf16::to_f32(vs[4 + q]), dot);
+      }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) dot += __shfl_xor(dot, m);
+    return dot;
+  }
+};
+
 __device__ __forceinline__ float sigmoid_f32(float x) { return 1.0f / (1.0f + expf(-x)); }
 
 __device__ __forceinline__ int clamp_token(int x, int V) { return x < 0 ? 0 : (x >= V ? V - 1 : x); }

@@ -46,6 +46,8 @@ struct StepArgs {
 
 StepPlan plan_draft_step(int R, int V, int gamma);
 hipError_t launch_draft_step(const StepArgs& a, const StepPlan& plan, hipStream_t stream);
+// The gamma steps of a block, in order (a.k and a.prev_from_best are set here).
+hipError_t launch_draft_steps(StepArgs a, const StepPlan& plan, hipStream_t stream);
 // Zero the winner words of the workspace (its region from plan.off_best on).
 hipError_t launch_clear_winners(const StepArgs& a, const StepPlan& plan, hipStream_t stream);
 // Merge the records of steps k0 .. k0+nk-1 and write x, p and lse (c and a are

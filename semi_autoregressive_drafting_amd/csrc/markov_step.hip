@@ -110,18 +110,22 @@ struct DraftEpi {
   static constexpr int kLoads = kVec ? 4 : 16;
 
   // r0w: first request of the wave's 32-row tile.
-  __device__ DraftEpi(const StepArgs& a, int r_, int rc, int half_, int r0w, float* patch_)
+  __device__ DraftEpi(const StepArgs& a, int k, int r_, int rc, int half_, int r0w, float* patch_)
       : zdbg(a.z_debug), patch(patch_), V(a.V), R(a.R), r(r_), half(half_), kscale(a.kscale) {
-    urow = a.U + ((size_t)rc * a.gamma + (a.k - 1)) * a.V;
     if constexpr (kVec) {
-      rows.base[0] = a.U + (size_t)(a.k - 1) * a.V;
       const int jmax = a.R - 1 - r0w;
       const size_t rstride = (size_t)a.gamma * a.V;
       rows.init([&](int j) { return (size_t)(r0w + (j < jmax ? j : jmax)) * rstride; });
     }
-    state_row = row_key(a.seed, kStreamDraft, (uint32_t)rc, (uint32_t)a.k) * kLcgMul + kLcgInc;
+    next_step(a, k, rc);
+  }
+  // Point at step k (logit rows, noise streams) and reset the lane state.
+  __device__ __forceinline__ void next_step(const StepArgs& a, int k, int rc) {
+    urow = a.U + ((size_t)rc * a.gamma + (k - 1)) * a.V;
+    if constexpr (kVec) rows.base[0] = a.U + (size_t)(k - 1) * a.V;
+    state_row = row_key(a.seed, kStreamDraft, (uint32_t)rc, (uint32_t)k) * kLcgMul + kLcgInc;
     state_ent = kGreedy ? 0u
-                        : row_key(a.seed, kStreamDraftEntry, (uint32_t)rc, (uint32_t)a.k) * kLcgMul +
+                        : row_key(a.seed, kStreamDraftEntry, (uint32_t)rc, (uint32_t)k) * kLcgMul +
                               kLcgInc;
 #pragma unroll
     for (int i = 0; i < (kGreedy ? 1 : 16); ++i) zb[i] = 0.0f;
@@ -290,10 +294,9 @@ struct DraftEpi {
 // Token x_{k-1} of request rc: the anchor column, the column written by the
 // previous call's finalisation, or (inside a block) the previous step's
 // winner word.
-__device__ __forceinline__ int prev_token(const StepArgs& a, int rc) {
-  if (a.k > 1 && a.prev_from_best)
-    return winner_id(a.best[winner_index(a.k - 2, a.R, rc)]);
-  return a.x[(size_t)rc * (a.gamma + 1) + (a.k - 1)];
+__device__ __forceinline__ int prev_token(const StepArgs& a, int k, bool pfb, int rc) {
+  if (k > 1 && pfb) return winner_id(a.best[winner_index(k - 2, a.R, rc)]);
+  return a.x[(size_t)rc * (a.gamma + 1) + (k - 1)];
 }
 
 // Tokens x_{k-1} of a wave's 32 requests r0w .. r0w + 31 (past R - 1: request
@@ -307,17 +310,17 @@ struct WaveTokens {
   typedef const __attribute__((address_space(4))) uint32_t* cptr;
   uint32_t t[32];
   bool from_best;
-  __device__ __forceinline__ void issue(const StepArgs& a, int r0w) {
+  __device__ __forceinline__ void issue(const StepArgs& a, int k, bool pfb, int r0w) {
     r0w = __builtin_amdgcn_readfirstlane(r0w);
     // word j of the wave sits at base + j * stride (32-bit words)
-    from_best = a.k > 1 && a.prev_from_best;
+    from_best = k > 1 && pfb;
     cptr base;
     size_t stride;
     if (from_best) {  // the low word of each winner word holds ~id
-      base = (cptr)(uintptr_t)a.best + 2 * winner_index(a.k - 2, a.R, r0w);
+      base = (cptr)(uintptr_t)a.best + 2 * winner_index(k - 2, a.R, r0w);
       stride = 2 * kWinnerStride;
     } else {
-      base = (cptr)(uintptr_t)a.x + (size_t)r0w * (a.gamma + 1) + (a.k - 1);
+      base = (cptr)(uintptr_t)a.x + (size_t)r0w * (a.gamma + 1) + (k - 1);
       stride = (size_t)(a.gamma + 1);
     }
     const int last = __builtin_amdgcn_readfirstlane(min(31, a.R - 1 - r0w));
@@ -343,31 +346,78 @@ __device__ __forceinline__ void put_rec(float* base, int R, int slab, int r, con
   p[4 * R] = __int_as_float(q.idx);
 }
 
-__device__ __forceinline__ void publish(const StepArgs& a, int slab, int r, const Rec& q) {
-  put_rec(a.rec + (size_t)(a.k - 1) * a.rec_step_f, a.R, slab, r, q);
-  if (q.idx >= 0)
-    atomicMax(a.best + winner_index(a.k - 1, a.R, r), pack_winner(q.key, q.idx));
+__device__ __forceinline__ void publish(const StepArgs& a, int k, int slab, int r, const Rec& q) {
+  put_rec(a.rec + (size_t)(k - 1) * a.rec_step_f, a.R, slab, r, q);
+  if (q.idx >= 0) atomicMax(a.best + winner_index(k - 1, a.R, r), pack_winner(q.key, q.idx));
 }
 
 // Confidence head and survival product of step k for requests r0 + slab,
 // r0 + slab + n_slabs, ... < r0 + nr.  Called by the whole workgroup.
 template <class W>
-__device__ __forceinline__ void step_confidence(const StepArgs& a, int slab, int r0, int nr) {
+__device__ __forceinline__ void step_confidence(const StepArgs& a, int k, bool pfb, int slab,
+                                                int r0, int nr) {
   using store_t = typename W::store_t;
   __shared__ float red[4];
   for (int q = slab; q < nr; q += a.n_slabs) {
     const int r = r0 + q;
-    const size_t o = (size_t)r * a.gamma + (a.k - 1);
-    const int xp = clamp_token(prev_token(a, r), a.V);
+    const size_t o = (size_t)r * a.gamma + (k - 1);
+    const int xp = clamp_token(prev_token(a, k, pfb, r), a.V);
     const store_t* hrow = reinterpret_cast<const store_t*>(a.h) + o * a.d;
     const store_t* erow = reinterpret_cast<const store_t*>(a.W1) + (size_t)xp * a.rank;
     const float c = sigmoid_f32(conf_dot_wg<W>(hrow, erow, a.w, a.d, a.rank, red));
     if (threadIdx.x == 0) {
-      const float prev = (a.k == 1) ? 1.0f : a.a[o - 1];
+      const float prev = (k == 1) ? 1.0f : a.a[o - 1];
       a.c[o] = c;
       a.a[o] = __fmul_rn(prev, c);
     }
   }
+}
+
+// The end of a draft step in the shared launch: the confidence head's row loads
+// (preloaded form), the request's record and winner word, then the confidence
+// head and survival product of request r0 + slab.  conf_tok holds its token.
+template <class W, class Epi>
+__device__ __forceinline__ void finish_step(const StepArgs& a, int k, bool pfb, Epi& epi, int slab,
+                                            int r0, int nr, int r, bool conf_pre,
+                                            const int& conf_tok, float* conf_red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5;
+  const int conf_n = a.d + a.rank;
+  ConfPreload cp;
+  float a_prev = 1.0f;
+  size_t co = 0;
+  if (conf_pre) {
+    lds_barrier();  // conf_tok, written during the gather
+    co = (size_t)(r0 + slab) * a.gamma + (k - 1);
+    const int n4 = ((conf_n + 3) / 4 + 7) / 8 * 8;
+    const int j0 = min(conf_n, wave * n4), j1 = min(conf_n, j0 + n4);
+    cp.load(reinterpret_cast<const uint16_t*>(a.h) + co * a.d,
+            reinterpret_cast<const uint16_t*>(a.W1) + (size_t)conf_tok * a.rank, a.w, a.d, j0,
+            j1, lane);
+    if (k > 1) a_prev = a.a[co - 1];
+  }
+  const Rec q = epi.row_record();
+  if (half == 0 && r < a.R) publish(a, k, slab, r, q);
+  if (conf_pre) {
+    const float part = cp.dot();
+    if (lane == 0) conf_red[wave] = part;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const float c = sigmoid_f32(((conf_red[0] + conf_red[1]) + conf_red[2]) + conf_red[3]);
+      a.c[co] = c;
+      a.a[co] = __fmul_rn(a_prev, c);
+    }
+  } else if (a.h != nullptr) {
+    step_confidence<W>(a, k, pfb, slab, r0, nr);
+  }
+}
+
+// Whether the preloaded confidence head applies to request r0 + slab.
+template <class W>
+__device__ __forceinline__ bool conf_preloadable(const StepArgs& a, int slab, int nr) {
+  return std::is_same<W, WBf16>::value && a.h != nullptr && !a.E_rows && slab < nr &&
+         a.d % 8 == 0 && a.d + a.rank <= 4 * 64 * 8 * kConfChunks &&
+         ((reinterpret_cast<uintptr_t>(a.h) | reinterpret_cast<uintptr_t>(a.W1) |
+           reinterpret_cast<uintptr_t>(a.w)) & 15u) == 0;
 }
 
 template <class W, int kKs, bool kGreedy, bool kDebug, bool kVec>
@@ -395,12 +445,21 @@ __global__ __launch_bounds__(kStreamThreads) void markov_step_shared(StepArgs a)
   typename W::frag_t e[W::kMaxKs];
   float* patch = reinterpret_cast<float*>(lds + draft_stream_lds<W, kKs>(a.rank)) +
                  wave * kPatchFloats;
-  DraftEpi<kGreedy, kDebug, kVec> epi(a, r, rc, half, r0 + wave * kVTile, patch);
+  DraftEpi<kGreedy, kDebug, kVec> epi(a, a.k, r, rc, half, r0 + wave * kVTile, patch);
   WaveTokens toks;
-  if (!a.E_rows) toks.issue(a, r0 + wave * kVTile);
+  if (!a.E_rows) toks.issue(a, a.k, a.prev_from_best, r0 + wave * kVTile);
+  // The confidence head of request r0 + slab (one per workgroup at most: there
+  // are never fewer slabs than requests in a group).  With bf16 rows that fit
+  // the preloaded form, its token is kept in LDS from the gather and its row
+  // loads are issued right after the stream, under the id draw and the publish.
+  const int nr = min(kWaves * kVTile, a.R - r0);
+  __shared__ int conf_tok;
+  __shared__ float conf_red[4];
+  const bool conf_pre = conf_preloadable<W>(a, slab, nr);
   auto gather = [&](typename W::frag_t(&ef)[W::kMaxKs]) {
     const void* base = a.E_rows ? a.E_rows : a.W1;
     const int row = a.E_rows ? rc : clamp_token(toks.token(), a.V);
+    if (conf_pre && wave == (slab >> 5) && lane == (slab & 31)) conf_tok = row;
     if constexpr (std::is_same<W, WBf16>::value && kKs > 0 && kKs % 4 == 0 && kVec)
       load_e_frags_lines<kKs>(ef, reinterpret_cast<const uint16_t*>(base), row, patch);
     else
@@ -412,9 +471,7 @@ __global__ __launch_bounds__(kStreamThreads) void markov_step_shared(StepArgs a)
     shared_a_stream<W, kKs, draft_dist<W>()>(a.W2t, a.V, a.rank, t_begin, t_end, e, gather, lds,
                                              epi);
 
-  const Rec q = epi.row_record();
-  if (half == 0 && r < a.R) publish(a, slab, r, q);
-  if (a.h != nullptr) step_confidence<W>(a, slab, r0, min(kWaves * kVTile, a.R - r0));
+  finish_step<W>(a, a.k, a.prev_from_best, epi, slab, r0, nr, r, conf_pre, conf_tok, conf_red);
 }
 
 template <class W, int kKs, bool kGreedy, bool kDebug, bool kVec>
@@ -432,9 +489,9 @@ __global__ __launch_bounds__(kStreamThreads) void markov_step_private(StepArgs a
   const int rc = r < a.R ? r : a.R - 1;
   __shared__ __align__(16) float patches[kVec ? kWaves : 1][kPatchFloats];
   typename W::frag_t e[W::kMaxKs];
-  DraftEpi<kGreedy, kDebug, kVec> epi(a, r, rc, half, r0, patches[kVec ? wave : 0]);
+  DraftEpi<kGreedy, kDebug, kVec> epi(a, a.k, r, rc, half, r0, patches[kVec ? wave : 0]);
   WaveTokens toks;
-  if (!a.E_rows) toks.issue(a, r0);
+  if (!a.E_rows) toks.issue(a, a.k, a.prev_from_best, r0);
   private_a_stream<W, kKs>(
       a.W2t, a.V, a.rank, t_begin + wave, t_end, kWaves, e,
       [&](typename W::frag_t(&ef)[W::kMaxKs]) {
@@ -454,9 +511,9 @@ __global__ __launch_bounds__(kStreamThreads) void markov_step_private(StepArgs a
   if (wave == 0 && half == 0 && r < a.R) {
     Rec m = srec[0][col];
     for (int w = 1; w < kWaves; ++w) m = rec_merge(m, srec[w][col]);
-    publish(a, slab, r, m);
+    publish(a, a.k, slab, r, m);
   }
-  if (a.h != nullptr) step_confidence<W>(a, slab, r0, min(kVTile, a.R - r0));
+  if (a.h != nullptr) step_confidence<W>(a, a.k, a.prev_from_best, slab, r0, min(kVTile, a.R - r0));
 }
 
 // ---------------------------------------------------------------------------
@@ -609,6 +666,16 @@ StepPlan plan_draft_step(int R, int V, int gamma) {
   p.off_best = p.rec_step * gamma;
   p.ws_bytes = p.off_best + align256((size_t)gamma * R * 8 * kWinnerStride);
   return p;
+}
+
+hipError_t launch_draft_steps(StepArgs a, const StepPlan& plan, hipStream_t stream) {
+  for (int k = 1; k <= a.gamma; ++k) {
+    a.k = k;
+    a.prev_from_best = k > 1;  // x_{k-1} straight from step k-1's winner word
+    const hipError_t err = launch_draft_step(a, plan, stream);
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_draft_step(const StepArgs& a, const StepPlan& plan, hipStream_t stream) {

@@ -255,50 +255,54 @@ __device__ __forceinline__ void shared_a_stream(const void* W2t, int V, int rank
 //   e. epilogue of tile i with acc_cur                 } scheduler groups below
 //   f. issue the epilogue's loads of tile i+2 into slot S (tile i is folded).
 // A partial last tile of the vocabulary is handled after the loop.
-template <class W, int kKs, int kThreads = kStreamThreads, class LoadE, class Epi>
-__device__ __forceinline__ void shared_a_stream_skew(const void* W2t, int V, int t_begin,
-                                                     int t_end,
-                                                     typename W::frag_t (&e)[W::kMaxKs],
-                                                     LoadE&& load_e, unsigned char* lds,
-                                                     Epi& epi) {
+//
+// SkewStream holds the stream's per-thread offsets and W2t register buffers;
+// shared_a_stream_skew is its plain use.
+template <class W, int kKs, int kThreads = kStreamThreads>
+struct SkewStream {
   static_assert(kKs > 0, "compile-time rank");
   using store_t = typename W::store_t;
-  constexpr int kRowBytes = kKs * W::kKStep * (int)sizeof(store_t);
-  constexpr int kRs = kRowBytes + 16;
-  constexpr int kCpr = kRowBytes / 16;
-  constexpr int kChunks = kVTile * kCpr;          // 16-byte chunks per tile
-  constexpr int kPer = kChunks / kThreads;
+  static constexpr int kRowBytes = kKs * W::kKStep * (int)sizeof(store_t);
+  static constexpr int kRs = kRowBytes + 16;
+  static constexpr int kCpr = kRowBytes / 16;
+  static constexpr int kChunks = kVTile * kCpr;  // 16-byte chunks per tile
+  static constexpr int kPer = kChunks / kThreads;
   static_assert(kChunks % kThreads == 0, "whole chunks per thread");
-  constexpr int kTileLds = kVTile * kRs;
-  const int lane = threadIdx.x & 63;
-  const int half = lane >> 5;
-  const unsigned char* wbase = reinterpret_cast<const unsigned char*>(W2t);
-  const int t_full = min(t_end, V / kVTile);
+  static constexpr int kTileLds = kVTile * kRs;
 
+  const unsigned char* wbase;
+  int V, t_full;
   int coff[kPer], loff[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int c = threadIdx.x + j * kThreads;
-    coff[j] = c * 16;
-    const int row = c / kCpr;
-    loff[j] = row * kRs + (c - row * kCpr) * 16;
-  }
   u32x4_t wreg[2][kPer];
-  auto fetch_w = [&](auto slot, int vt) {
-    constexpr int S = decltype(slot)::value;
+
+  __device__ __forceinline__ SkewStream(const void* W2t, int V_, int t_end)
+      : wbase(reinterpret_cast<const unsigned char*>(W2t)), V(V_), t_full(min(t_end, V_ / kVTile)) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int c = threadIdx.x + j * kThreads;
+      coff[j] = c * 16;
+      const int row = c / kCpr;
+      loff[j] = row * kRs + (c - row * kCpr) * 16;
+    }
+  }
+  template <int S>
+  __device__ __forceinline__ void fetch_w(int vt) {
     const unsigned char* tile = wbase + (vt < t_full ? (size_t)vt * kChunks * 16 : 0);
 #pragma unroll
     for (int j = 0; j < kPer; ++j) wreg[S][j] = *reinterpret_cast<const u32x4_t*>(tile + coff[j]);
-  };
-  auto stash = [&](auto slot, unsigned char* dst) {
-    constexpr int S = decltype(slot)::value;
+  }
+  template <int S>
+  __device__ __forceinline__ void stash(unsigned char* dst) {
 #pragma unroll
     for (int j = 0; j < kPer; ++j) *reinterpret_cast<u32x4_t*>(dst + loff[j]) = wreg[S][j];
-  };
-  const int arow_off = tile_perm(lane & 31) * kRs;
+  }
   // 16 A-fragment reads and MFMAs; reads run up to kAhead fragments ahead.
-  auto mma = [&](const unsigned char* slot_base) {
-    const store_t* arow = reinterpret_cast<const store_t*>(slot_base + arow_off);
+  __device__ __forceinline__ f32x16_t mma(const unsigned char* slot_base,
+                                          const typename W::frag_t (&e)[W::kMaxKs]) const {
+    const int lane = threadIdx.x & 63;
+    const int half = lane >> 5;
+    const store_t* arow =
+        reinterpret_cast<const store_t*>(slot_base + tile_perm(lane & 31) * kRs);
     typename W::frag_t af[kKs];
 #pragma unroll
     for (int ks = 0; ks < kKs; ++ks) af[ks] = W::load(arow, ks, half);
@@ -306,72 +310,88 @@ __device__ __forceinline__ void shared_a_stream_skew(const void* W2t, int V, int
 #pragma unroll
     for (int ks = 0; ks < kKs; ++ks) acc = W::mma(af[ks], e[ks], acc);
     return acc;
-  };
-  // Scheduler groups for one iteration body: the first kAhead A reads, then
-  // per MFMA one more read and a share of the epilogue's VALU work.
-  constexpr int kAhead = 4;
-  constexpr int kValuPerMfma = 24;
-  auto pin = [&]() {
-    __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 1);
+  }
+  // The stream over tiles [t_begin, t_end).  load_e(e) fills the E fragments;
+  // it runs after the first tile's loads are issued, so the row gather (which
+  // depends on a token id read from memory) overlaps them.
+  template <class LoadE, class Epi>
+  __device__ __forceinline__ void run(int t_begin, int t_end, typename W::frag_t (&e)[W::kMaxKs],
+                                      LoadE&& load_e, unsigned char* lds, Epi& epi) {
+    // Scheduler groups for one iteration body: the first kAhead A reads, then
+    // per MFMA one more read and a share of the epilogue's VALU work.
+    constexpr int kAhead = 4;
+    constexpr int kValuPerMfma = 24;
+    auto pin = [&]() {
+      __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 1);
 #pragma unroll
-    for (int ks = 0; ks < kKs; ++ks) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-      if (ks + kAhead < kKs) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-      __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 1);
-    }
-  };
+      for (int ks = 0; ks < kKs; ++ks) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        if (ks + kAhead < kKs) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 1);
+      }
+    };
+    f32x16_t acc_cur = {};
+    auto body = [&](auto slot, int vt) {
+      constexpr int S = decltype(slot)::value;
+      // Everything but the epilogue loads of tile i+1 has arrived: the W2t of
+      // tile i+1 (stored next) and the epilogue rows of tile i.
+      wait_loads_le<Epi::kLoads>();
+      stash<S ^ 1>(lds + (S ^ 1) * kTileLds);
+      lds_barrier();
+      fetch_w<S>(vt + 2);
+      const f32x16_t acc_next = mma(lds + (S ^ 1) * kTileLds, e);
+      epi.template consume<S>(acc_cur, vt);
+      epi.template prefetch<S>(vt + 2 < t_full ? vt + 2 : -1);
+      pin();
+      acc_cur = acc_next;
+    };
 
-  f32x16_t acc_cur = {};
-  auto body = [&](auto slot, int vt) {
-    constexpr int S = decltype(slot)::value;
-    // Everything but the epilogue loads of tile i+1 has arrived: the W2t of
-    // tile i+1 (stored next) and the epilogue rows of tile i.
-    wait_loads_le<Epi::kLoads>();
-    stash(slot_t<S ^ 1>{}, lds + (S ^ 1) * kTileLds);
-    lds_barrier();
-    fetch_w(slot_t<S>{}, vt + 2);
-    const f32x16_t acc_next = mma(lds + (S ^ 1) * kTileLds);
-    epi.template consume<S>(acc_cur, vt);
-    epi.template prefetch<S>(vt + 2 < t_full ? vt + 2 : -1);
-    pin();
-    acc_cur = acc_next;
-  };
-
-  if (t_begin < t_full) {
-    fetch_w(slot_t<0>{}, t_begin);
-    epi.template prefetch<0>(t_begin);
-  }
-  load_e(e);
-  wait_all_loads();  // the E fragments never stay pending into the loop
-  if (t_begin < t_full) {
-    stash(slot_t<0>{}, lds);
-    fetch_w(slot_t<1>{}, t_begin + 1);
-    epi.template prefetch<1>(t_begin + 1 < t_full ? t_begin + 1 : -1);
-    lds_barrier();
-    acc_cur = mma(lds);
-    int vt = t_begin;
-    for (;;) {
-      body(slot_t<0>{}, vt);
-      if (++vt >= t_full) break;
-      body(slot_t<1>{}, vt);
-      if (++vt >= t_full) break;
+    if (t_begin < t_full) {
+      fetch_w<0>(t_begin);
+      epi.template prefetch<0>(t_begin);
     }
-  }
-  if (t_end > t_full) {  // the partial last tile (rows >= V read as zero)
-    const int vt = t_full;
-    const int valid = (V - vt * kVTile) * kCpr;
-    lds_barrier();  // every wave is past its last LDS read
+    load_e(e);
+    wait_all_loads();  // the E fragments never stay pending into the loop
+    if (t_begin < t_full) {
+      stash<0>(lds);
+      fetch_w<1>(t_begin + 1);
+      epi.template prefetch<1>(t_begin + 1 < t_full ? t_begin + 1 : -1);
+      lds_barrier();
+      acc_cur = mma(lds, e);
+      int vt = t_begin;
+      for (;;) {
+        body(slot_t<0>{}, vt);
+        if (++vt >= t_full) break;
+        body(slot_t<1>{}, vt);
+        if (++vt >= t_full) break;
+      }
+    }
+    if (t_end > t_full) {  // the partial last tile (rows >= V read as zero)
+      const int vt = t_full;
+      const int valid = (V - vt * kVTile) * kCpr;
+      lds_barrier();  // every wave is past its last LDS read
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int c = threadIdx.x + j * kThreads;
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (c < valid) v = *reinterpret_cast<const u32x4_t*>(wbase + (size_t)vt * kChunks * 16 + c * 16);
-      *reinterpret_cast<u32x4_t*>(lds + loff[j]) = v;
+      for (int j = 0; j < kPer; ++j) {
+        const int c = threadIdx.x + j * kThreads;
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (c < valid) v = *reinterpret_cast<const u32x4_t*>(wbase + (size_t)vt * kChunks * 16 + c * 16);
+        *reinterpret_cast<u32x4_t*>(lds + loff[j]) = v;
+      }
+      lds_barrier();
+      const f32x16_t acc = mma(lds, e);
+      epi.tail(acc, vt);
     }
-    lds_barrier();
-    const f32x16_t acc = mma(lds);
-    epi.tail(acc, vt);
   }
+};
+
+template <class W, int kKs, int kThreads = kStreamThreads, class LoadE, class Epi>
+__device__ __forceinline__ void shared_a_stream_skew(const void* W2t, int V, int t_begin,
+                                                     int t_end,
+                                                     typename W::frag_t (&e)[W::kMaxKs],
+                                                     LoadE&& load_e, unsigned char* lds,
+                                                     Epi& epi) {
+  SkewStream<W, kKs, kThreads> ss(W2t, V, t_end);
+  ss.run(t_begin, t_end, e, load_e, lds, epi);
 }
 
 // A single wave streams tiles t_begin, t_begin + t_stride, ... < t_end; the
