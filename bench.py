@@ -99,32 +99,54 @@ def measured_traffic():
     return int(kv["read_bytes"]) + int(kv["write_bytes"])
 
 
+COLD_PROFILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                            "dspark_markov_step_qwen3_8b_r128_g16_cold_kernel_stats.txt")
+
+
+def profiled_cold_us():
+    """Average kernel duration of the cold single draft steps from the
+    committed rocprofv3 kernel-trace summary of `bench.py --cold-only`, or
+    None when the kernel sources have changed since it was taken."""
+    try:
+        with open(COLD_PROFILE) as fh:
+            lines = [l for l in fh if l.startswith("cold markov_step_shared ")]
+    except OSError:
+        return None
+    if not lines:
+        return None
+    kv = dict(t.split("=", 1) for t in lines[-1].split()[2:])
+    if kv.get("source_sha256") != sources_sha256():
+        return None
+    return float(kv["avg_us"])
+
+
 def read_ceiling(nbytes, launches=20):
-    """Pure-read stream over nbytes with the probe kernel (libdspark_probe.so):
+    """Pure-read streams over nbytes with the probe kernels (libdspark_probe.so).
+
     'rotating' reads a different nbytes window of a pool several times larger
-    than the MALL at each launch (HBM), 'resident' re-reads one window (as the
-    draft step re-reads W2 every step).  GB/s per launch, HIP-event timed."""
-    import ctypes
+    than the MALL at each launch (so every byte comes from HBM), 'resident'
+    re-reads one window (as the draft step re-reads W2 every step).  The
+    probe's variants are swept (16-byte loads in flight per lane, nontemporal
+    or cached loads, interleaved or one slice per workgroup, grid size); the
+    fastest rotating variant is the read ceiling.  GB/s per launch, timed with
+    HIP events on the stream the probe runs on."""
     import torch
-    from semi_autoregressive_drafting_amd import build as B
-    lib = ctypes.CDLL(B.PROBE_LIB)
-    lib.dspark_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
-                                      ctypes.c_int, ctypes.c_void_p]
-    lib.dspark_probe_read.restype = ctypes.c_int
+    lib = _probe_lib()
     nbytes = (nbytes + 255) // 256 * 256
     slots = 12
     pool = torch.empty(nbytes * slots, dtype=torch.uint8, device="cuda")
     pool.fill_(1)
-    grid = 2048
-    sink = torch.zeros(grid, dtype=torch.int32, device="cuda")
+    grids = (512, 1024, 2048, 4096)
+    sink = torch.zeros(max(grids), dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
-    out = {}
-    for mode in ("rotating", "resident"):
+
+    def timed(mode, unroll, nt, blocked, grid):
         def launch(i):
             off = (i % slots) * nbytes if mode == "rotating" else 0
-            rc = lib.dspark_probe_read(pool.data_ptr() + off, nbytes, sink.data_ptr(), grid, stream)
+            rc = lib.dspark_probe_read_ex(pool.data_ptr() + off, nbytes, sink.data_ptr(), grid,
+                                          unroll, nt, blocked, stream)
             if rc != 0:
-                raise RuntimeError(f"dspark_probe_read failed: {rc}")
+                raise RuntimeError(f"dspark_probe_read_ex failed: {rc}")
         for i in range(slots):
             launch(i)
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -135,9 +157,157 @@ def read_ceiling(nbytes, launches=20):
         ev1.record()
         torch.cuda.synchronize()
         us = ev0.elapsed_time(ev1) * 1e3 / launches
-        out[mode] = {"us_per_launch": round(us, 2), "GBps": round(nbytes / us / 1e3, 1)}
+        return {"us_per_launch": round(us, 2), "GBps": round(nbytes / us / 1e3, 1),
+                "loads_in_flight": unroll, "nontemporal": bool(nt), "blocked": bool(blocked),
+                "grid": grid}
+
+    sweep = [timed("rotating", u, nt, bl, g) for u in (4, 8, 16) for nt in (0, 1)
+             for bl in (0, 1) for g in grids]
+    best = max(sweep, key=lambda e: e["GBps"])
+    plain = next(e for e in sweep if (e["loads_in_flight"], e["nontemporal"], e["blocked"],
+                                      e["grid"]) == (4, False, False, 2048))
+    resident = timed("resident", best["loads_in_flight"], int(best["nontemporal"]),
+                     int(best["blocked"]), best["grid"])
     del pool
+    return {"bytes": nbytes, "rotating": best, "plain_4_in_flight": plain, "resident": resident,
+            "variants_swept": len(sweep),
+            "top5": [[e["loads_in_flight"], int(e["nontemporal"]), int(e["blocked"]), e["grid"],
+                      e["GBps"]] for e in sorted(sweep, key=lambda e: -e["GBps"])[:5]]}
+
+
+def one_step_block(di, k):
+    """Inputs and buffers of a one-step draft block on position k's U and h
+    rows: its STEPS phase is exactly one launch of the draft-step kernel."""
+    import dataclasses
+    from semi_autoregressive_drafting_amd import runner
+    di1 = dataclasses.replace(di, gamma=1, U=di.U[:, k - 1:k].contiguous(),
+                              h=di.h[:, k - 1:k].contiguous(), target=None)
+    return di1, runner.RoundBuffers.allocate(di1)
+
+
+def _probe_lib():
+    import ctypes
+    from semi_autoregressive_drafting_amd import build as B
+    lib = ctypes.CDLL(B.PROBE_LIB)
+    lib.dspark_probe_read_ex.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_void_p]
+    lib.dspark_probe_read_ex.restype = ctypes.c_int
+    return lib
+
+
+def cold_single_steps(di, n, flush_bytes=1 << 30, modes=("cold", "hot")):
+    """One draft-step launch at a time (a one-step block, events around its
+    STEPS phase only).  'cold': right after a cached read over flush_bytes
+    (four times the MALL), which leaves neither W2, U nor W1 in L2 or the
+    MALL (a read leaves no dirty lines behind to be written back during the
+    step).  'hot': the same launch right after an identical untimed one, so
+    that everything it reads is cached.  Nothing synchronises the host between
+    the flush (or the untimed launch) and the timed launch, so the GPU is busy
+    up to it.  Microseconds per launch."""
+    import torch
+    from semi_autoregressive_drafting_amd import dspark as D
+    from semi_autoregressive_drafting_amd import runner
+    di1, b1 = one_step_block(di, 1)
+    lib = _probe_lib()
+    scratch = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda")
+    scratch.fill_(3)
+    sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def launch(seed):
+        b1.x[:, 0].copy_(di1.anchor)
+        runner.draft_phases(di1, b1, TEMPERATURE, seed, D.DSPARK_PHASE_STEPS, copy_anchor=False)
+
+    out = {m: [] for m in modes}
+    for s in range(n + 2):
+        for mode in modes:
+            if mode == "cold":
+                if lib.dspark_probe_read_ex(scratch.data_ptr(), flush_bytes, sink.data_ptr(),
+                                            4096, 16, 0, 0, stream) != 0:
+                    raise RuntimeError("flush read failed")
+            else:
+                launch(800 + s)
+                runner.draft_phases(di1, b1, TEMPERATURE, 800 + s, D.DSPARK_PHASE_MERGE)
+            b1.x[:, 0].copy_(di1.anchor)
+            e0.record()
+            runner.draft_phases(di1, b1, TEMPERATURE, 800 + s, D.DSPARK_PHASE_STEPS,
+                                copy_anchor=False)
+            e1.record()
+            runner.draft_phases(di1, b1, TEMPERATURE, 800 + s, D.DSPARK_PHASE_MERGE)
+            torch.cuda.synchronize()
+            if s >= 2:
+                out[mode].append(e0.elapsed_time(e1) * 1e3)
+    del scratch, b1, di1
     return out
+
+
+def other_workloads(nb=10):
+    """The draft block at the other workload shapes (tokens/s, microseconds
+    per step, HBM fraction of the step), and the whole round with
+    verification at the 4B-shaped round workload (realised tau)."""
+    import torch
+    from semi_autoregressive_drafting_amd import dspark as D
+    from semi_autoregressive_drafting_amd import runner, synth
+    res = {}
+    for name, temps in (("qwen3_4b_r32_g7", (1.0,)), ("qwen3_14b_r512_g7", (0.0, 1.0)),
+                        ("round_4b_r128_g7", (1.0,))):
+        wl = synth.WORKLOADS[name]
+        inp = synth.generate(name, seed=0, target=wl.target)
+        di = runner.DeviceInputs.upload(inp)
+        buf = runner.RoundBuffers.allocate(di)
+        del inp
+        R, g, V, rank, d = di.R, di.gamma, di.V, di.rank, di.d
+        sb = draft_step_bytes(R, V, rank, d)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        for T in temps:
+            for s in range(3):
+                runner.draft(di, buf, T, 1000 + s)
+            steps_us, block_us = [], []
+            for s in range(nb):
+                buf.x[:, 0].copy_(di.anchor)
+                ev[0].record()
+                runner.draft_phases(di, buf, T, 1100 + s, D.DSPARK_PHASE_STEPS, copy_anchor=False)
+                ev[1].record()
+                runner.draft_phases(di, buf, T, 1100 + s, D.DSPARK_PHASE_MERGE)
+                ev[2].record()
+                torch.cuda.synchronize()
+                steps_us.append(ev[0].elapsed_time(ev[1]) * 1e3)
+                block_us.append(ev[0].elapsed_time(ev[2]) * 1e3)
+            st = float(np.median(steps_us)) / g
+            bl = float(np.median(block_us))
+            e = {"R": R, "gamma": g, "d": d, "temperature": T,
+                 "draft_tokens_per_s": round(R * g / (bl * 1e-6), 1),
+                 "block_us": round(bl, 2), "us_per_step": round(st, 2),
+                 "step_bytes": sb, "step_GBps": round(sb / st / 1e3, 1),
+                 "frac": round(sb / st / 1e3 / HBM_PEAK_GBS, 4)}
+            if wl.target:
+                r_us, taus = [], []
+                for s in range(nb + 2):
+                    ev[0].record()
+                    runner.draft(di, buf, T, 1200 + s)
+                    runner.schedule(di, buf)
+                    ev[1].record()
+                    runner.verify(di, buf, T, 1200 + s)
+                    ev[2].record()
+                    torch.cuda.synchronize()
+                    if s >= 2:
+                        r_us.append((ev[0].elapsed_time(ev[2]) * 1e3, ev[1].elapsed_time(ev[2]) * 1e3))
+                        taus.append(float(buf.tau_mean.item()))
+                rr = float(np.median([u[0] for u in r_us]))
+                vv = float(np.median([u[1] for u in r_us]))
+                vb = verify_bytes(R, V, rank, g)
+                e.update({"round_us": round(rr, 2),
+                          "round_draft_tokens_per_s": round(R * g / (rr * 1e-6), 1),
+                          "verify_us": round(vv, 2),
+                          "verify_frac": round(vb / vv / 1e3 / HBM_PEAK_GBS, 4),
+                          "tau_mean": round(float(np.mean(taus)), 4),
+                          "budget_last_round": int(buf.budget.item())})
+            res[f"{name}_T{T:g}"] = e
+        del di, buf
+        torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(inp, seed):
@@ -222,6 +392,9 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the read ceiling, cold steps, asynchronous scheduler and graph "
                          "replay (for counter-collection runs)")
+    ap.add_argument("--cold-only", action="store_true",
+                    help="only run single draft-step launches, each after a cache flush (so "
+                         "that a kernel trace shows the cold kernel alone)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (x4), so that "
                          "FETCH_SIZE / WRITE_SIZE counters can be scaled to bytes")
@@ -252,6 +425,13 @@ def main():
     print(f"# inputs ready in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
     R, g, V, rank, d = di.R, di.gamma, di.V, di.rank, di.d
     di_wl = inp.wl
+    if args.cold_only:
+        single = cold_single_steps(di, args.steps, modes=("cold",))
+        sb = draft_step_bytes(R, V, rank, d)
+        cm = float(np.median(single["cold"]))
+        print(json.dumps({"workload": WORKLOAD, "launches": args.steps + 2, "bytes_per_launch": sb,
+                          "cold_us_median_events": round(cm, 2)}), flush=True)
+        return
 
     def one_round(seed, ev=None):
         # the anchor copy and the gamma streaming steps, then the record merge;
@@ -405,27 +585,13 @@ def main():
                "round_draft_tokens_per_s": round(R * g / (rr_med * 1e-6), 1)}
         del rws, rstate, rrows
 
-    # Cold draft step: a 512 MB write evicts W2 and U from L2 and the MALL
-    # before each timed step (dspark_draft_step = step kernel + merge).
-    cold, warm = [float("nan")], [float("nan")]
-    scratch = torch.empty(512 << 20 if extras else 0, dtype=torch.uint8, device="cuda")
-    if extras:
-        cold, warm = [], []
-        buf.x[:, 0].copy_(di.anchor)
-    for s in range(6 if extras else 0):
-        for flush, acc in ((True, cold), (False, warm)):
-            if flush:
-                scratch.fill_(s & 0xFF)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            runner.draft_step(di, buf, 1 + s % g, TEMPERATURE, 700 + s)
-            e1.record()
-            torch.cuda.synchronize()
-            acc.append(e0.elapsed_time(e1) * 1e3)
-    del scratch
+    # One draft-step launch alone, after a flush of L2 and the MALL (cold)
+    # and with its inputs cached (hot).
+    single = cold_single_steps(di, 8) if extras else None
 
     sb = draft_step_bytes(R, V, rank, d)
     ceiling = read_ceiling(sb) if extras else None
+    others = other_workloads() if extras else None
 
     # The same round replayed from one captured HIP graph (no host launches).
     graph = None
@@ -475,6 +641,7 @@ def main():
 
     step_s = float(step_ms.mean()) * 1e-3
     achieved = sb / step_s / 1e9
+    cold_kernel_us = profiled_cold_us()
     vb = verify_bytes(R, V, rank, g)
     out = {
         "metric": "Markov-head draft tokens/s at R=128,γ=16,V=152k; % of HBM roofline",
@@ -500,10 +667,26 @@ def main():
                      "traffic": measured_traffic(), "bytes_per_launch": sb,
                      "avg_launch_us": round(step_s * 1e6, 2),
                      "frac_of_read_ceiling": (round(achieved / ceiling["rotating"]["GBps"], 4)
-                                              if ceiling else None)},
+                                              if ceiling else None),
+                     # cold: every byte from HBM (L2 and MALL flushed before the launch);
+                     # kernel-only from the committed kernel trace, and from HIP events
+                     # around one launch (launch latency included) measured here
+                     "frac_cold": (round(sb / cold_kernel_us / 1e3 / HBM_PEAK_GBS, 4)
+                                   if cold_kernel_us else None),
+                     "cold_kernel_us": cold_kernel_us,
+                     "frac_cold_events": (round(sb / float(np.median(single["cold"])) / 1e3
+                                                / HBM_PEAK_GBS, 4) if single else None),
+                     "cold_launch_us_events": (round(float(np.median(single["cold"])), 2)
+                                               if single else None)},
         "read_ceiling": ceiling,
-        "cold_step": {"step_plus_merge_us_cold": round(float(np.median(cold)), 2),
-                      "step_plus_merge_us_warm": round(float(np.median(warm)), 2)},
+        "single_step": ({"cold_us_median": round(float(np.median(single["cold"])), 2),
+                         "hot_us_median": round(float(np.median(single["hot"])), 2),
+                         "cold_us": [round(v, 2) for v in single["cold"]],
+                         "note": "one launch per event pair (launch latency included); a "
+                                 "cached 1 GiB read before each cold launch flushes L2 and "
+                                 "the MALL"}
+                        if single else None),
+        "other_workloads": others,
         "graph": graph,
         "breakdown_us": {"draft_step_mean": round(float(step_ms.mean()) * 1e3, 2),
                          "draft_step_median": round(float(np.median(step_ms)) * 1e3, 2),
