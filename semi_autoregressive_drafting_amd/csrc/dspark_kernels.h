@@ -10,10 +10,10 @@ namespace dspark {
 
 // Launch shape of one draft step (see markov_step.hip).
 struct StepPlan {
-  bool shared;        // 4 waves = 4 request tiles sharing an LDS W2t tile
   int grid_x, grid_y;
   int n_slabs;        // vocabulary slabs (workgroups) per request group
-  int n_groups;       // request groups (128 requests shared, 32 private)
+  int n_groups;       // request groups of 128 (4 waves = 4 request tiles sharing
+                      // an LDS W2t tile)
   int n_vtiles;       // 32-wide vocabulary tiles
   size_t rec_step;    // workspace: per-step record planes [gamma][n_slabs][5][R]
   size_t off_best;    //   then the winner words [gamma][R] (u64, kWinnerStride apart)

@@ -34,15 +34,16 @@
 //     x_k, p_k(x_k) = 2^(t_best - lse), lse_k.  It clears the atomic words it
 //     consumed, so the workspace stays zero between calls.
 //
-// Launch shapes of the streaming kernel (see mfma_stream.h):
-//   shared : R > 96.  A workgroup = 4 waves = 4 request tiles (a group of 128
-//            requests); each wave keeps its E fragments in VGPRs for the whole
-//            step and each W2t tile is staged once per workgroup in LDS.  W2t
-//            leaves HBM once per request group; the groups of one slab share an
-//            XCD (blockIdx % 8) so repeated W2t reads hit that XCD's L2.
-//   private: R <= 96.  A group = one request tile; the 4 waves of a workgroup
-//            stream interleaved tiles of the slab with W2t fragments loaded
-//            straight into VGPRs, then merge their records in LDS.
+// Launch shape of the streaming kernel (see mfma_stream.h): a workgroup = 4
+// waves = 4 request tiles (a group of 128 requests); each wave keeps its E
+// fragments in VGPRs for the whole step and each W2t tile is staged once per
+// workgroup in LDS.  W2t leaves HBM once per request group; the groups of one
+// slab share an XCD (blockIdx % 8) so repeated W2t reads hit that XCD's L2.
+// Batches below 128 requests run the same shape with the missing rows padded
+// (their lanes recompute row R-1 and store nothing): the bytes, not the
+// arithmetic, set the step's time, and a shape whose waves stream separate
+// tiles with W2t loaded straight into VGPRs measured slower at every batch
+// size from 1 to 96 requests.
 #include "dspark_kernels.h"
 #include "mfma_stream.h"
 
@@ -474,48 +475,6 @@ __global__ __launch_bounds__(kStreamThreads) void markov_step_shared(StepArgs a)
   finish_step<W>(a, a.k, a.prev_from_best, epi, slab, r0, nr, r, conf_pre, conf_tok, conf_red);
 }
 
-template <class W, int kKs, bool kGreedy, bool kDebug, bool kVec>
-__global__ __launch_bounds__(kStreamThreads) void markov_step_private(StepArgs a) {
-  __shared__ Rec srec[kWaves][kVTile];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int half = lane >> 5, col = lane & 31;
-  const int slab = blockIdx.x % a.n_slabs;
-  const int grp = blockIdx.x / a.n_slabs;  // request tile
-  const int r0 = grp * kVTile;
-  int t_begin, t_end;
-  slab_range(slab, a.n_slabs, a.n_vtiles, t_begin, t_end);
-
-  const int r = r0 + col;
-  const int rc = r < a.R ? r : a.R - 1;
-  __shared__ __align__(16) float patches[kVec ? kWaves : 1][kPatchFloats];
-  typename W::frag_t e[W::kMaxKs];
-  DraftEpi<kGreedy, kDebug, kVec> epi(a, a.k, r, rc, half, r0, patches[kVec ? wave : 0]);
-  WaveTokens toks;
-  if (!a.E_rows) toks.issue(a, a.k, a.prev_from_best, r0);
-  private_a_stream<W, kKs>(
-      a.W2t, a.V, a.rank, t_begin + wave, t_end, kWaves, e,
-      [&](typename W::frag_t(&ef)[W::kMaxKs]) {
-        const void* base = a.E_rows ? a.E_rows : a.W1;
-        const int row = a.E_rows ? rc : clamp_token(toks.token(), a.V);
-        if constexpr (std::is_same<W, WBf16>::value && kKs > 0 && kKs % 4 == 0 && kVec)
-          load_e_frags_lines<kKs>(ef, reinterpret_cast<const uint16_t*>(base), row,
-                                  patches[kVec ? wave : 0]);
-        else
-          load_e_frags<W, kKs>(ef, base, row, a.rank, a.E_rows ? a.R : a.V, half);
-      },
-      epi);
-
-  const Rec q = epi.row_record();
-  if (half == 0) srec[wave][col] = q;
-  __syncthreads();
-  if (wave == 0 && half == 0 && r < a.R) {
-    Rec m = srec[0][col];
-    for (int w = 1; w < kWaves; ++w) m = rec_merge(m, srec[w][col]);
-    publish(a, a.k, slab, r, m);
-  }
-  if (a.h != nullptr) step_confidence<W>(a, a.k, a.prev_from_best, slab, r0, min(kVTile, a.R - r0));
-}
-
 // ---------------------------------------------------------------------------
 // Merge of the records of step k = k0 + blockIdx.y for requests
 // r0 = 32 * blockIdx.x .. r0 + 31.  Wave w takes slabs [w * spw, (w+1) * spw);
@@ -599,14 +558,10 @@ __global__ __launch_bounds__(64 * kMergeWaves) void draft_merge(StepArgs a, int 
 
 template <class W, int kKs, bool kGreedy, bool kDebug, bool kVec>
 void launch_one(const StepArgs& a, const StepPlan& plan, hipStream_t stream) {
-  if (plan.shared)
-    hipLaunchKernelGGL((markov_step_shared<W, kKs, kGreedy, kDebug, kVec>), dim3(plan.grid_x),
-                       dim3(kStreamThreads),
-                       (draft_stream_lds<W, kKs>(a.rank) + kWaves * kPatchFloats * sizeof(float)),
-                       stream, a);
-  else
-    hipLaunchKernelGGL((markov_step_private<W, kKs, kGreedy, kDebug, kVec>), dim3(plan.grid_x),
-                       dim3(kStreamThreads), 0, stream, a);
+  hipLaunchKernelGGL((markov_step_shared<W, kKs, kGreedy, kDebug, kVec>), dim3(plan.grid_x),
+                     dim3(kStreamThreads),
+                     (draft_stream_lds<W, kKs>(a.rank) + kWaves * kPatchFloats * sizeof(float)),
+                     stream, a);
 }
 
 template <class W, int kKs, bool kGreedy>
@@ -645,21 +600,12 @@ StepPlan plan_draft_step(int R, int V, int gamma) {
   StepPlan p{};
   p.n_vtiles = (V + kVTile - 1) / kVTile;
   const int rt = (R + kVTile - 1) / kVTile;
-  if (rt >= 4) {
-    p.shared = true;
-    p.n_groups = (rt + kWaves - 1) / kWaves;
-    int slabs = kDraftWgs / p.n_groups;
-    if (p.n_groups > 1) slabs = (slabs / 8) * 8;
-    if (slabs < 8) slabs = 8;
-    p.n_slabs = slabs;
-  } else {
-    p.shared = false;
-    p.n_groups = rt;
-    int slabs = kDraftWgs / rt;
-    const int max_slabs = (p.n_vtiles + kWaves - 1) / kWaves;
-    if (slabs > max_slabs) slabs = max_slabs;
-    p.n_slabs = slabs;
-  }
+  p.n_groups = (rt + kWaves - 1) / kWaves;
+  // at most 4 groups (R <= 512), so a group never has more requests (128)
+  // than slabs (128 or more): one confidence head per workgroup at most
+  int slabs = kDraftWgs / p.n_groups;
+  if (p.n_groups > 1) slabs = (slabs / 8) * 8;
+  p.n_slabs = slabs;
   p.grid_x = p.n_slabs * p.n_groups;
   p.grid_y = 1;
   p.rec_step = align256((size_t)p.n_slabs * 5 * R * 4);

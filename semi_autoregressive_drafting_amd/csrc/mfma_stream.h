@@ -394,62 +394,6 @@ __device__ __forceinline__ void shared_a_stream_skew(const void* W2t, int V, int
   ss.run(t_begin, t_end, e, load_e, lds, epi);
 }
 
-// A single wave streams tiles t_begin, t_begin + t_stride, ... < t_end; the
-// W2t fragment goes straight from global memory into VGPRs.  The epilogue's
-// loads of the next tile are issued before the current tile's MFMAs.
-template <class W, int kKs, class LoadE, class Epi>
-__device__ __forceinline__ void private_a_stream(const void* W2t, int V, int rank, int t_begin,
-                                                 int t_end, int t_stride,
-                                                 typename W::frag_t (&e)[W::kMaxKs],
-                                                 LoadE&& load_e, Epi& epi) {
-  using store_t = typename W::store_t;
-  const int lane = threadIdx.x & 63;
-  const int half = lane >> 5;
-  const int nks = kKs > 0 ? kKs : rank / W::kKStep;
-  const int prow = tile_perm(lane & 31);
-  const int t_full = min(t_end, V / kVTile);
-  auto mma = [&](int vt, bool masked) {
-    const int vv = vt * kVTile + prow;
-    const bool ok = !masked || vv < V;
-    const store_t* wrow = reinterpret_cast<const store_t*>(W2t) + (size_t)(ok ? vv : 0) * rank;
-    f32x16_t acc = {};
-#pragma unroll
-    for (int ks = 0; ks < W::kMaxKs; ++ks) {
-      if (kKs > 0 ? ks < kKs : ks < nks) {
-        typename W::frag_t af = W::load(wrow, ks, half);
-        if (masked && !ok) af = W::zero();
-        acc = W::mma(af, e[ks], acc);
-      }
-    }
-    return acc;
-  };
-  auto body = [&](auto slot, int vt) {
-    constexpr int S = decltype(slot)::value;
-    const int nxt = vt + t_stride;
-    epi.template prefetch<(S + 1) % 2>(nxt < t_full ? nxt : -1);
-    const f32x16_t acc = mma(vt, false);
-    epi.template consume<S>(acc, vt);
-  };
-  int vt = t_begin;
-  if (vt < t_full) epi.template prefetch<0>(vt);
-  load_e(e);
-  wait_all_loads();
-  if (vt < t_full) {
-    for (;;) {
-      body(slot_t<0>{}, vt);
-      vt += t_stride;
-      if (vt >= t_full) break;
-      body(slot_t<1>{}, vt);
-      vt += t_stride;
-      if (vt >= t_full) break;
-    }
-  }
-  if (vt < t_end) {  // at most one partial tile remains (the last of the vocabulary)
-    const f32x16_t acc = mma(vt, true);
-    epi.tail(acc, vt);
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Rows of a vocabulary tile in fp32 (one wave: 32 rows x 32 entries = 4 KB per
 // array), read from global memory as whole 128-byte lines -- load instruction

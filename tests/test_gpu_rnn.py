@@ -22,8 +22,8 @@ from tests.gpu_parity import LSE_ATOL, NEAR_TIE, P_RTOL, Z_TOL, say
 
 pytestmark = pytest.mark.gpu
 
-# ragged vocabulary (V % 4 != 0) and request count with the smallest rank and
-# the private (R <= 32) / shared (R > 32) launch shapes
+# ragged vocabulary (V % 4 != 0) and request counts that leave part of a
+# request tile padded, with the smallest ranks
 synth.custom("rnn_v997_r37_g3", V=997, rank=32, d=48, gamma=3, R=37, dtype="bf16", peak="three")
 synth.custom("rnn_v4099_r20_g5", V=4099, rank=64, d=80, gamma=5, R=20, dtype="bf16", peak="three")
 # one request, a vocabulary below one MFMA tile pair, the smallest d
@@ -102,8 +102,8 @@ def test_rnn_draft_block_small(name, T):
 
 
 def test_rnn_draft_block_full_size_greedy():
-    """Greedy drafting with the RNN head at R = 32, gamma = 7 (the private launch
-    shape), full vocabulary, rank 256."""
+    """Greedy drafting with the RNN head at R = 32, gamma = 7 (one request group
+    with three padded request tiles), full vocabulary, rank 256."""
     name = "qwen3_4b_r32_g7"
     say(f"[rnn] {name} T=0")
     inp, gru, host, _ = _run(name, 0.0, 3)
