@@ -3,12 +3,10 @@
 //
 // One workgroup of 1024 threads:
 //   1. keys (~bits(a) << 32 | flat index) for the N = R*gamma candidates,
-//      padded to a power of two with all-ones keys, sorted ascending by a
-//      bitonic network: a descending, ties by flat index ascending.  Each
-//      thread keeps kPer consecutive keys in registers: compare-exchanges
-//      inside a thread need nothing, those between threads of one wave go
-//      through cross-lane shuffles, and only partners in different waves
-//      (stride >= 64 * kPer) go through LDS with workgroup barriers.
+//      sorted ascending by their high half (a descending) with a stable LDS
+//      radix sort (four passes of 8-bit digits, ranks from wave ballots and a
+//      workgroup scan of per-wave digit counts), so equal a keep flat index
+//      order.
 //   2. q_i = rint(a_i * 2^32) as int64 (exact scaling, round half to even);
 //      thread t owns a contiguous run of sorted positions, sums its q's, and a
 //      fixed-order scan over the 1024 run totals gives every prefix G_b exactly
@@ -27,76 +25,118 @@ namespace {
 constexpr int kMaxN = 8192;
 constexpr int kThreads = 1024;
 
-__device__ __forceinline__ unsigned long long shfl_xor64(unsigned long long v, int m) {
-  const uint32_t lo = __shfl_xor((uint32_t)v, m), hi = __shfl_xor((uint32_t)(v >> 32), m);
-  return ((unsigned long long)hi << 32) | lo;
+constexpr int kWavesS = kThreads / 64;
+constexpr int kDigits = 256;
+constexpr int kSlots = kMaxN / kThreads;  // items per lane at the largest N
+
+// Exclusive prefix sum of one value per thread over the whole workgroup, in
+// thread order; `tot` receives the sum over all threads.  Uses wsum[0..15].
+__device__ __forceinline__ int block_excl_scan(int v, int* wsum, int& tot) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  tot = 0;
+#pragma unroll
+  for (int w = 0; w < kWavesS; ++w) {
+    const int x = wsum[w];
+    before += w < wave ? x : 0;
+    tot += x;
+  }
+  __syncthreads();  // wsum may be reused after this
+  return before + incl - v;
 }
 
-// Bitonic network over n2 = kPer * kThreads * (1 or less) keys; thread t owns
-// positions t * kPer .. t * kPer + kPer - 1 in `k` (n2 / kThreads of them are
-// real when n2 < kPer * kThreads: the rest hold all-ones keys and stay last).
-template <int kPer>
-__device__ __forceinline__ void bitonic_sort(unsigned long long (&k)[kPer], unsigned long long* lds, int n2) {
-  const int t = threadIdx.x;
-  const int lane_bits = 6;  // 64 lanes
-  for (int size = 2; size <= n2; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      if (stride < kPer) {  // partners inside the thread (constant register indices)
+// Stable LSD radix sort of the N 64-bit keys in `src` by their high 32 bits,
+// four passes of 8-bit digits (ties keep their order, so keys that carry the
+// flat index in the low bits end up ordered by it).  Wave w owns items
+// w*C .. w*C + C - 1 (C = 64 * slots), lane l of slot j item w*C + 64 j + l,
+// so inside a wave the items run slot-major.  Per slot, the lanes holding one
+// digit find each other with eight ballots; their rank is the count of that
+// digit already seen by the wave (an LDS counter per wave and digit, advanced
+// by the lowest such lane) plus the matching lanes below.  A workgroup scan
+// over the counters in digit-major, wave-minor order then gives every
+// (wave, digit) its first output position.  The result ends in `src`.
+__device__ __forceinline__ void radix_sort(unsigned long long* src, unsigned long long* dst,
+                                           int* wcount, int* wsum, int N) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int slots = (N + kThreads - 1) / kThreads;
+  const int C = 64 * slots;
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 32 + 8 * pass;
+    for (int i = t; i < kWavesS * kDigits; i += kThreads) wcount[i] = 0;
+    __syncthreads();
+    int* wc = wcount + wave * kDigits;
+    unsigned long long v[kSlots];
+    int rank[kSlots], dig[kSlots];
 #pragma unroll
-        for (int cs = kPer / 2; cs > 0; cs >>= 1) {
-          if (cs != stride) continue;
+    for (int j = 0; j < kSlots; ++j) {
+      rank[j] = 0;
+      dig[j] = 0;
+      v[j] = 0ull;
+      if (j < slots) {
+        const int idx = wave * C + 64 * j + lane;
+        const bool valid = idx < N;
+        v[j] = valid ? src[idx] : 0ull;
+        const int d = (int)((v[j] >> shift) & 0xFFu);
+        // lanes of this slot holding digit d: agree with d on all 8 bits
+        unsigned long long peers = __ballot(valid);
 #pragma unroll
-          for (int j = 0; j < kPer; ++j) {
-            if ((j & cs) != 0) continue;  // i & cs == j & cs since t * kPer is a multiple of kPer
-            const int i = t * kPer + j;
-            const bool asc = (i & size) == 0;
-            const unsigned long long x = k[j], y = k[j + cs];
-            const bool sw = (x > y) == asc;
-            k[j] = sw ? y : x;
-            k[j + cs] = sw ? x : y;
-          }
+        for (int bit = 0; bit < 8; ++bit) {
+          const unsigned long long b = (d >> bit) & 1;
+          peers &= __ballot(b != 0) ^ (b - 1ull);  // the ballot itself, or its complement
         }
-      } else if (stride < (kPer << lane_bits)) {  // partners in the same wave
-        const int m = stride / kPer;  // lane distance
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-          const int i = t * kPer + j;
-          const unsigned long long o = shfl_xor64(k[j], m);
-          const bool lower = (i & stride) == 0;
-          const bool asc = (i & size) == 0;
-          // the lower position keeps the smaller key when ascending
-          const bool keep_min = lower == asc;
-          k[j] = keep_min ? (o < k[j] ? o : k[j]) : (o > k[j] ? o : k[j]);
+        dig[j] = d;
+        if (valid) {
+          const int seen = wc[d];
+          const unsigned long long below = peers & lt;
+          rank[j] = seen + __popcll(below);
+          if (below == 0ull) wc[d] = seen + __popcll(peers);
         }
-      } else {  // partners in other waves: through LDS
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) lds[t * kPer + j] = k[j];
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-          const int i = t * kPer + j;
-          const unsigned long long o = lds[i ^ stride];
-          const bool lower = (i & stride) == 0;
-          const bool asc = (i & size) == 0;
-          const bool keep_min = lower == asc;
-          k[j] = keep_min ? (o < k[j] ? o : k[j]) : (o > k[j] ? o : k[j]);
-        }
-        __syncthreads();
       }
     }
+    __syncthreads();
+    // first output position of every (wave, digit): thread t takes digit t/4
+    // and waves 4(t%4) .. 4(t%4)+3
+    {
+      const int d = t >> 2, w0 = (t & 3) * 4;
+      int c[4], sum = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        c[i] = wcount[(w0 + i) * kDigits + d];
+        sum += c[i];
+      }
+      int tot;
+      int base = block_excl_scan(sum, wsum, tot);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        wcount[(w0 + i) * kDigits + d] = base;
+        base += c[i];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kSlots; ++j) {
+      if (j < slots) {
+        const int idx = wave * C + 64 * j + lane;
+        if (idx < N) {
+          const int pos = wc[dig[j]] + rank[j];
+          if (pos < N) dst[pos] = v[j];
+        }
+      }
+    }
+    __syncthreads();
+    unsigned long long* tmp = src;
+    src = dst;
+    dst = tmp;
   }
-}
-
-// The network on the first P of the kPer register keys.
-template <int P, int kPer>
-__device__ __forceinline__ void sort_prefix(unsigned long long (&k)[kPer], unsigned long long* lds,
-                                            int n2) {
-  unsigned long long kk[P];
-#pragma unroll
-  for (int j = 0; j < P; ++j) kk[j] = k[j];
-  bitonic_sort<P>(kk, lds, n2);
-#pragma unroll
-  for (int j = 0; j < P; ++j) k[j] = kk[j];
 }
 
 // Sort the N = R * gamma candidates of `a` into `key` (ascending; see the
@@ -113,36 +153,26 @@ __device__ __forceinline__ long long q_of(unsigned long long key) {
   return (long long)rint((double)v * 4294967296.0);
 }
 
-__device__ __forceinline__ Runs sort_and_scan(const float* a, int N, unsigned long long* key, long long* wsum) {
+// Length of thread t's run of sorted positions, [t * per, t * per + per)
+// clipped to N (per = ceil(N / kThreads) <= kSlots).
+__device__ __forceinline__ int run_length(int N) {
+  const int per = (N + kThreads - 1) / kThreads;
+  const int b0 = min(N, (int)threadIdx.x * per);
+  return min(N, b0 + per) - b0;
+}
+
+__device__ __forceinline__ Runs sort_and_scan(const float* a, int N, unsigned long long* key,
+                                              unsigned long long* tmp, int* wcount, int* wsum,
+                                              long long* lsum) {
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
-  int n2 = kThreads;  // at least one key per thread so every thread runs the network
-  while (n2 < N) n2 <<= 1;
-  constexpr int kPer = kMaxN / kThreads;
-  const int per2 = n2 / kThreads;  // keys per thread actually in the network
-  unsigned long long k[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int i = t * per2 + j;
-    unsigned long long v = ~0ull;
-    if (j < per2 && i < N) {
-      const float f = a[i];
-      const uint32_t bits = (f > 0.0f) ? __float_as_uint(f) : 0u;  // NaN / <= 0 sort as 0
-      v = ((unsigned long long)(~bits) << 32) | (uint32_t)i;
-    }
-    k[j] = v;
-  }
-  switch (per2) {  // the network over n2 keys, per2 in registers per thread
-    case 1: sort_prefix<1>(k, key, n2); break;
-    case 2: sort_prefix<2>(k, key, n2); break;
-    case 4: sort_prefix<4>(k, key, n2); break;
-    default: bitonic_sort<kPer>(k, key, n2); break;
+  for (int i = t; i < N; i += kThreads) {
+    const float f = a[i];
+    const uint32_t bits = (f > 0.0f) ? __float_as_uint(f) : 0u;  // NaN / <= 0 sort as 0
+    key[i] = ((unsigned long long)(~bits) << 32) | (uint32_t)i;
   }
   __syncthreads();
-#pragma unroll
-  for (int j = 0; j < kPer; ++j)
-    if (j < per2) key[t * per2 + j] = k[j];
-  __syncthreads();
+  radix_sort(key, tmp, wcount, wsum, N);
 
   Runs u;
   const int per = (N + kThreads - 1) / kThreads;
@@ -158,20 +188,23 @@ __device__ __forceinline__ Runs sort_and_scan(const float* a, int N, unsigned lo
     const long long v = (long long)(((unsigned long long)hi << 32) | lo);
     if (lane >= off) incl += v;
   }
-  if (lane == 63) wsum[wave] = incl;
+  if (lane == 63) lsum[wave] = incl;
   __syncthreads();
   long long before = 0;
-  for (int w = 0; w < wave; ++w) before += wsum[w];
+  for (int w = 0; w < wave; ++w) before += lsum[w];
   u.total = 0;
-  for (int w = 0; w < kThreads / 64; ++w) u.total += wsum[w];
+  for (int w = 0; w < kThreads / 64; ++w) u.total += lsum[w];
   u.base = before + incl - own;  // G at position b0
-  __syncthreads();               // wsum and key may be reused after this
+  __syncthreads();               // lsum and key may be reused after this
   return u;
 }
 
 __global__ __launch_bounds__(kThreads) void schedule_kernel(SchedArgs a) {
   __shared__ unsigned long long key[kMaxN];
-  __shared__ long long wsum[kThreads / 64];
+  __shared__ unsigned long long tmp[kMaxN];
+  __shared__ int wcount[kWavesS * kDigits];
+  __shared__ int wsum[kWavesS];
+  __shared__ long long lsum[kWavesS];
   __shared__ int ell_s[512];
   __shared__ int stop_s;
   __shared__ double theta_s;
@@ -179,29 +212,47 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(SchedArgs a) {
   const int N = a.R * a.gamma;
   for (int i = t; i < a.R; i += kThreads) ell_s[i] = 0;
   if (t == 0) stop_s = N;
-  const Runs u = sort_and_scan(a.a, N, key, wsum);
+  // this thread's SPS entries R + b0 .. R + b1 (b1 - b0 <= kSlots), loaded
+  // before the sort so that their latency hides behind it
+  double sp[kSlots + 1];
+  const int nb = run_length(N);
+  {
+    const double* sps = a.sps + a.R + min(N, t * ((N + kThreads - 1) / kThreads));
+#pragma unroll
+    for (int j = 0; j <= kSlots; ++j) sp[j] = j <= nb ? sps[j] : 0.0;
+  }
+  const Runs u = sort_and_scan(a.a, N, key, tmp, wcount, wsum, lsum);
   const long long tau0 = (long long)a.R << 32;
 
   long long G = u.base;
-  for (int i = u.b0; i < u.b1; ++i) {
-    const long long Gn = G + q_of(key[i]);
-    const double th = (double)(tau0 + G) * a.sps[a.R + i];
-    const double thn = (double)(tau0 + Gn) * a.sps[a.R + i + 1];
-    if (!(thn > th)) {
-      atomicMin(&stop_s, i);
-      break;
+  bool stopped = false;
+#pragma unroll
+  for (int j = 0; j < kSlots; ++j) {
+    if (j < nb && !stopped) {
+      const int i = u.b0 + j;
+      const long long Gn = G + q_of(key[i]);
+      const double th = (double)(tau0 + G) * sp[j];
+      const double thn = (double)(tau0 + Gn) * sp[j + 1];
+      if (!(thn > th)) {
+        atomicMin(&stop_s, i);
+        stopped = true;
+      }
+      G = Gn;
     }
-    G = Gn;
   }
   __syncthreads();
   const int bstar = stop_s;
 
   G = u.base;
-  for (int i = u.b0; i < u.b1; ++i) {
-    if (i == bstar) theta_s = (double)(tau0 + G) * a.sps[a.R + i];
-    if (i < bstar) {
-      atomicAdd(&ell_s[(int)(key[i] & 0xFFFFFFFFu) / a.gamma], 1);
-      G += q_of(key[i]);
+#pragma unroll
+  for (int j = 0; j < kSlots; ++j) {
+    if (j < nb) {
+      const int i = u.b0 + j;
+      if (i == bstar) theta_s = (double)(tau0 + G) * sp[j];
+      if (i < bstar) {
+        atomicAdd(&ell_s[(int)(key[i] & 0xFFFFFFFFu) / a.gamma], 1);
+        G += q_of(key[i]);
+      }
     }
   }
   if (bstar == N && t == kThreads - 1) theta_s = (double)(tau0 + u.total) * a.sps[a.R + N];
@@ -220,7 +271,10 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(SchedArgs a) {
 // (a_cur, same key order) are admitted.
 __global__ __launch_bounds__(kThreads) void schedule_async_kernel(SchedAsyncArgs a) {
   __shared__ unsigned long long key[kMaxN];
-  __shared__ long long wsum[kThreads / 64];
+  __shared__ unsigned long long tmp[kMaxN];
+  __shared__ int wcount[kWavesS * kDigits];
+  __shared__ int wsum[kWavesS];
+  __shared__ long long lsum[kWavesS];
   __shared__ int ell_s[512];
   __shared__ double red_v[kThreads / 64];
   __shared__ int red_b[kThreads / 64];
@@ -232,7 +286,14 @@ __global__ __launch_bounds__(kThreads) void schedule_async_kernel(SchedAsyncArgs
 
   // 1. K from the lagged survival: thread t scores b = i + 1 for i in its run
   //    (thread 0 also b = 0); the best (Theta, smallest b) wins.
-  const Runs u = sort_and_scan(a.a_lag, N, key, wsum);
+  double sp[kSlots + 1];
+  const int nb = run_length(N);
+  {
+    const double* sps = a.sps + a.R + min(N, t * ((N + kThreads - 1) / kThreads));
+#pragma unroll
+    for (int j = 0; j <= kSlots; ++j) sp[j] = j <= nb ? sps[j] : 0.0;
+  }
+  const Runs u = sort_and_scan(a.a_lag, N, key, tmp, wcount, wsum, lsum);
   double bv = -1.0;
   int bb = 0x7fffffff;
   if (t == 0) {
@@ -240,12 +301,16 @@ __global__ __launch_bounds__(kThreads) void schedule_async_kernel(SchedAsyncArgs
     bb = 0;
   }
   long long G = u.base;
-  for (int i = u.b0; i < u.b1; ++i) {
-    G += q_of(key[i]);
-    const double th = (double)(tau0 + G) * a.sps[a.R + i + 1];
-    if (th > bv) {  // positions rise within the run: strict '>' keeps the smallest b
-      bv = th;
-      bb = i + 1;
+#pragma unroll
+  for (int j = 0; j < kSlots; ++j) {
+    if (j < nb) {
+      const int i = u.b0 + j;
+      G += q_of(key[i]);
+      const double th = (double)(tau0 + G) * sp[j + 1];
+      if (th > bv) {  // positions rise within the run: strict '>' keeps the smallest b
+        bv = th;
+        bb = i + 1;
+      }
     }
   }
   for (int off = 32; off > 0; off >>= 1) {
@@ -271,7 +336,7 @@ __global__ __launch_bounds__(kThreads) void schedule_async_kernel(SchedAsyncArgs
   __syncthreads();  // the key buffer is reused below
 
   // 2. top-K of the current survival
-  const Runs c = sort_and_scan(a.a_cur, N, key, wsum);
+  const Runs c = sort_and_scan(a.a_cur, N, key, tmp, wcount, wsum, lsum);
   for (int i = c.b0; i < c.b1; ++i)
     if (i < K) atomicAdd(&ell_s[(int)(key[i] & 0xFFFFFFFFu) / a.gamma], 1);
   __syncthreads();
