@@ -16,7 +16,10 @@
  *   - Arguments are validated on the host before any HIP call; a failed check
  *     returns an error status and enqueues nothing.  Launch failures return
  *     DSPARK_ERR_LAUNCH.  Faults inside kernels surface at the caller's next
- *     synchronisation.  Device data (token ids, NaNs) is not checked.
+ *     synchronisation.  Device data is not validated on the host: a token id
+ *     outside [0, V) that a kernel uses to gather a W1 row is clamped into
+ *     range (so the gather stays in bounds) and recorded in the GPU's
+ *     token-error word (see dspark_token_errors); NaNs are not checked.
  *   - Outputs are overwritten; outputs must not alias inputs.
  *   - Layouts are row-major and dense:
  *       W1   [V][rank]       Markov embedding table (P1 §2.3, W1 in R^{V x r})
@@ -85,6 +88,22 @@ size_t dspark_workspace_bytes(int op, int R, int V, int rank, int gamma);
 
 /* Human-readable name of a status code (static string). Host-only. */
 const char* dspark_status_string(int status);
+
+/*
+ * The token-error word of the current device (not a method step: a guard
+ * for corrupted device data).  Every kernel that gathers a W1 row by a token
+ * id read from device memory -- the anchor and drafted columns of x in the
+ * draft step, the confidence head and verification, x* in training, the
+ * winner of the previous step inside a block -- stores 1 into the word when
+ * the id lies outside [0, V), clamps the id into range and carries on.  The
+ * word is shared by all calls on the device and stays set until cleared.
+ * *flag (HOST pointer) receives the word; clear = 1 then resets it to 0,
+ * clear = 0 leaves it.  Synchronous (blocking copies): call it after the
+ * streams that ran the kernels have been synchronised.  flag NULL ->
+ * DSPARK_ERR_NULL; clear outside {0, 1} -> DSPARK_ERR_VALUE; no device or a
+ * failed copy -> DSPARK_ERR_LAUNCH.
+ */
+dspark_status dspark_token_errors(uint32_t* flag, int clear);
 
 /*
  * One sequential draft step k (1 <= k <= gamma) for all R requests

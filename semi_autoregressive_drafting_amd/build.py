@@ -90,5 +90,45 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     return LIB
 
 
+HOSTSAN_LIB = os.path.join(BUILD, "libdspark_hostsan.so")
+HOST_SANITIZERS = ["-fno-omit-frame-pointer", "-g",
+                   "-Xarch_host", "-fsanitize=address",
+                   "-Xarch_host", "-fsanitize=undefined",
+                   "-Xarch_host", "-fno-sanitize-recover=undefined"]
+
+
+def asan_runtime() -> str | None:
+    """The ASan runtime of the ROCm clang that built the library (it also
+    carries the UBSan handlers), or None."""
+    import glob
+    hits = sorted(glob.glob(os.path.join(os.path.dirname(os.path.dirname(_hipcc())), "llvm", "lib",
+                                         "clang", "*", "lib", "linux",
+                                         "libclang_rt.asan-x86_64.so")))
+    return hits[-1] if hits else None
+
+
+def build_host_sanitized() -> str:
+    """libdspark.so with its host layer (dspark_api.hip: argument validation,
+    workspace sizing, launch planning) compiled with AddressSanitizer and
+    UndefinedBehaviorSanitizer; the kernels' objects are the normal build's
+    (build() must have run).  Load it with the ASan runtime preloaded
+    (asan_runtime()) and DSPARK_LIB pointing at it."""
+    os.makedirs(os.path.join(BUILD, "hostsan"), exist_ok=True)
+    src = os.path.join(CSRC, "dspark_api.hip")
+    obj = os.path.join(BUILD, "hostsan", "dspark_api.o")
+    flags = [f for f in HIPCC_FLAGS if f != "-O3"] + ["-O1"]
+    res = subprocess.run([_hipcc(), *flags, *HOST_SANITIZERS, "-c", src, "-o", obj],
+                         capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed on dspark_api.hip (sanitized):\n" + res.stderr)
+    others = [os.path.join(BUILD, os.path.basename(s)[:-4] + ".o") for s in sources()
+              if os.path.basename(s) != "dspark_api.hip"]
+    missing = [o for o in others if not os.path.exists(o)]
+    if missing:
+        raise RuntimeError(f"build() first: {missing[0]} is missing")
+    _link(others + [obj], HOSTSAN_LIB)
+    return HOSTSAN_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

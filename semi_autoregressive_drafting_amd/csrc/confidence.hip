@@ -20,7 +20,7 @@ __global__ __launch_bounds__(256) void confidence_kernel(ConfArgs a) {
   float run = 1.0f;
   for (int k = 1; k <= a.gamma; ++k) {
     const size_t o = (size_t)r * a.gamma + (k - 1);
-    const int xp = clamp_token(a.x[(size_t)r * (a.gamma + 1) + (k - 1)], a.V);
+    const int xp = checked_token(a.x[(size_t)r * (a.gamma + 1) + (k - 1)], a.V, a.err);
     const store_t* hrow = reinterpret_cast<const store_t*>(a.h) + o * a.d;
     const store_t* erow = reinterpret_cast<const store_t*>(a.W1) + (size_t)xp * a.rank;
     const float c = sigmoid_f32(conf_dot_wg<W>(hrow, erow, a.w, a.d, a.rank, red));

@@ -23,6 +23,12 @@ using namespace dspark;
 constexpr size_t kNoAllocScratchBytes = (size_t)22 << 20;
 static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
+// The token-error word of this GPU: every kernel that gathers a W1 row by a
+// token id read from device memory stores 1 here when the id lies outside
+// [0, V).  Kernels receive its device address (token_error_address); the host
+// reads and clears it through dspark_token_errors.
+static __device__ __align__(256) uint32_t token_error[64];
+
 namespace {
 
 constexpr int kMaxR = 512;
@@ -90,6 +96,25 @@ dspark_status scratch_address(void** out) {
     g_scratch_addr[dev] = ptr;
   }
   *out = g_scratch_addr[dev];
+  return DSPARK_OK;
+}
+
+std::mutex g_err_mu;
+uint32_t* g_err_addr[kMaxDevices] = {};
+
+// Device address of the token-error word on the current device (looked up
+// once per device).
+dspark_status token_error_address(uint32_t** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DSPARK_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_err_mu);
+  if (g_err_addr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(token_error)) != hipSuccess || ptr == nullptr)
+      return DSPARK_ERR_LAUNCH;
+    g_err_addr[dev] = static_cast<uint32_t*>(ptr);
+  }
+  *out = g_err_addr[dev];
   return DSPARK_OK;
 }
 
@@ -232,6 +257,7 @@ dspark_status verify_common(int R, int V, int rank, int gamma, int dt, const voi
   args.tau = tau;
   args.tau_mean = tau_mean;
   args.ws = static_cast<unsigned char*>(ws);
+  if (token_error_address(&args.err) != DSPARK_OK) return DSPARK_ERR_LAUNCH;
   if (launch_verify(args, plan, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return DSPARK_ERR_LAUNCH;
   return DSPARK_OK;
@@ -253,6 +279,7 @@ dspark_status dspark_draft_step(int R, int V, int rank, int d, int gamma, int k,
   const dspark_status s = check_draft(R, V, rank, d, gamma, k, dt, W1, W2t, U, h, w, temperature,
                                       seed, x, p, lse, c, a, z_debug, ws, ws_bytes, args, plan);
   if (s != DSPARK_OK) return s;
+  if (token_error_address(&args.err) != DSPARK_OK) return DSPARK_ERR_LAUNCH;
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (launch_draft_step(args, plan, st) != hipSuccess ||
       launch_draft_finalize(args, plan, k, 1, st) != hipSuccess)
@@ -272,6 +299,7 @@ dspark_status dspark_draft_block_phases(int R, int V, int rank, int d, int gamma
   const dspark_status s = check_draft(R, V, rank, d, gamma, 0, dt, W1, W2t, U, h, w, temperature,
                                       seed, x, p, lse, c, a, nullptr, ws, ws_bytes, args, plan);
   if (s != DSPARK_OK) return s;
+  if (token_error_address(&args.err) != DSPARK_OK) return DSPARK_ERR_LAUNCH;
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (phases & DSPARK_PHASE_STEPS) {
     if (launch_draft_steps(args, plan, st) != hipSuccess) return DSPARK_ERR_LAUNCH;
@@ -301,6 +329,7 @@ dspark_status dspark_draft_block_noalloc(int R, int V, int rank, int d, int gamm
   void* ws = nullptr;
   const dspark_status t = scratch_address(&ws);
   if (t != DSPARK_OK) return t;
+  if (token_error_address(&args.err) != DSPARK_OK) return DSPARK_ERR_LAUNCH;
   args.rec = static_cast<float*>(ws);
   args.best =
       reinterpret_cast<unsigned long long*>(static_cast<unsigned char*>(ws) + plan.off_best);
@@ -343,6 +372,7 @@ dspark_status dspark_draft_block_rnn(int R, int V, int rank, int d, int gamma, i
   if (s != DSPARK_OK) return s;
   const RnnPlan rp = plan_rnn(R, V, rank, gamma);
   if (ws_bytes < rp.ws_bytes) return DSPARK_ERR_WORKSPACE;
+  if (token_error_address(&args.err) != DSPARK_OK) return DSPARK_ERR_LAUNCH;
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   unsigned char* wsb = static_cast<unsigned char*>(ws);
   RnnArgs ra{};
@@ -358,6 +388,7 @@ dspark_status dspark_draft_block_rnn(int R, int V, int rank, int d, int gamma, i
   ra.b_hh = b_hh;
   ra.h = static_cast<const uint16_t*>(h);
   ra.x = x;
+  ra.err = args.err;
   ra.best = args.best;
   ra.P = reinterpret_cast<float*>(wsb + rp.off_P);
   ra.Pk = reinterpret_cast<float*>(wsb + rp.off_Pk);
@@ -390,7 +421,8 @@ dspark_status dspark_confidence(int R, int gamma, int d, int rank, int V, int dt
     return DSPARK_ERR_SHAPE;
   dspark_status s = check_rank(dt, rank);
   if (s != DSPARK_OK) return s;
-  ConfArgs args{R, gamma, d, rank, V, dt == DSPARK_BF16, h, W1, x, w, c, a};
+  ConfArgs args{R, gamma, d, rank, V, dt == DSPARK_BF16, h, W1, x, w, c, a, nullptr};
+  if (token_error_address(&args.err) != DSPARK_OK) return DSPARK_ERR_LAUNCH;
   if (launch_confidence(args, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return DSPARK_ERR_LAUNCH;
   return DSPARK_OK;
@@ -491,7 +523,8 @@ dspark_status train_common(int R, int V, int rank, int d, int gamma, int dt, con
   float* c = reinterpret_cast<float*>(wsb + tplan.off_c);
   float* surv = reinterpret_cast<float*>(wsb + tplan.off_surv);
   // c_k = sigma(w . [h_k; W1[x*_{k-1}]]) with the target block as the Markov input
-  ConfArgs cargs{R, gamma, d, rank, V, dt == DSPARK_BF16, h, W1, x_star, w, c, surv};
+  ConfArgs cargs{R, gamma, d, rank, V, dt == DSPARK_BF16, h, W1, x_star, w, c, surv, nullptr};
+  if (token_error_address(&cargs.err) != DSPARK_OK) return DSPARK_ERR_LAUNCH;
   if (launch_confidence(cargs, st) != hipSuccess) return DSPARK_ERR_LAUNCH;
 
   VerifyArgs args{};
@@ -506,6 +539,7 @@ dspark_status train_common(int R, int V, int rank, int d, int gamma, int dt, con
   args.U = U;
   args.target = target;
   args.x = x_star;
+  args.err = cargs.err;
   args.kscale = kscale_of(temperature);
   args.ws = wsb;
   TrainArgs targs{};
@@ -558,6 +592,21 @@ dspark_status dspark_train_loss_grad(int R, int V, int rank, int d, int gamma, i
   return train_common(R, V, rank, d, gamma, dt, W1, W2t, U, h, w, target, x_star, temperature,
                       lambda, alpha_ce, alpha_tv, alpha_conf, terms, sums, &g, ws, ws_bytes,
                       stream);
+}
+
+dspark_status dspark_token_errors(uint32_t* flag, int clear) {
+  if (!flag) return DSPARK_ERR_NULL;
+  if (clear != 0 && clear != 1) return DSPARK_ERR_VALUE;
+  uint32_t* word = nullptr;
+  if (token_error_address(&word) != DSPARK_OK) return DSPARK_ERR_LAUNCH;
+  if (hipMemcpy(flag, word, sizeof(uint32_t), hipMemcpyDeviceToHost) != hipSuccess)
+    return DSPARK_ERR_LAUNCH;
+  if (clear) {
+    const uint32_t zero = 0u;
+    if (hipMemcpy(word, &zero, sizeof(uint32_t), hipMemcpyHostToDevice) != hipSuccess)
+      return DSPARK_ERR_LAUNCH;
+  }
+  return DSPARK_OK;
 }
 
 }  // extern "C"

@@ -271,7 +271,16 @@ struct ConfPreload {
 
 __device__ __forceinline__ float sigmoid_f32(float x) { return 1.0f / (1.0f + expf(-x)); }
 
-__device__ __forceinline__ int clamp_token(int x, int V) { return x < 0 ? 0 : (x >= V ? V - 1 : x); }
+// A token id read from device memory, clamped into [0, V) so that the row
+// gather it drives stays inside W1.  An id outside [0, V) (a corrupted anchor
+// or block, or a step that found no winner) also sets the library's
+// token-error word to 1 with a plain store (the host reads it back with
+// dspark_token_errors); nothing traps.
+__device__ __forceinline__ int checked_token(int x, int V, uint32_t* err) {
+  if (x >= 0 && x < V) return x;
+  if (err != nullptr) *err = 1u;
+  return x < 0 ? 0 : V - 1;
+}
 
 // Winner words of the draft steps: one 64-bit word per (step, request), each
 // alone in its 128-byte line.  Every workgroup of a step publishes into the

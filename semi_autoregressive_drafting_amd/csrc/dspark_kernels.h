@@ -42,6 +42,7 @@ struct StepArgs {
   size_t rec_step_f;         // floats per step plane
   unsigned long long* best;  // winner words [gamma][R], kWinnerStride apart
   int n_vtiles, n_slabs, n_groups;
+  uint32_t* err;  // token-error word (checked_token)
 };
 
 StepPlan plan_draft_step(int R, int V, int gamma);
@@ -71,6 +72,7 @@ struct RnnArgs {
   float* Pk;              // their sums, step-major [gamma][R][3 rank]
   uint16_t* rows_out;     // optional: bf16(s_k) of every position [R][gamma][rank]
   uint16_t* E;            // bf16(s_k) [R][rank], the step's bias rows
+  uint32_t* err;  // token-error word (checked_token)
 };
 hipError_t launch_rnn_input_proj(const RnnArgs& a, hipStream_t stream);
 hipError_t launch_rnn_state_step(const RnnArgs& a, int k, const float* s_prev, float* s_next,
@@ -85,6 +87,7 @@ struct ConfArgs {
   const float* w;
   float* c;
   float* a;
+  uint32_t* err;  // token-error word (checked_token)
 };
 hipError_t launch_confidence(const ConfArgs& a, hipStream_t stream);
 
@@ -143,6 +146,7 @@ struct VerifyArgs {
   int32_t* tau;
   float* tau_mean;
   unsigned char* ws;
+  uint32_t* err;  // token-error word (checked_token)
 };
 
 VerifyPlan plan_verify(int R, int V, int gamma);

@@ -362,7 +362,7 @@ __device__ __forceinline__ void step_confidence(const StepArgs& a, int k, bool p
   for (int q = slab; q < nr; q += a.n_slabs) {
     const int r = r0 + q;
     const size_t o = (size_t)r * a.gamma + (k - 1);
-    const int xp = clamp_token(prev_token(a, k, pfb, r), a.V);
+    const int xp = checked_token(prev_token(a, k, pfb, r), a.V, a.err);
     const store_t* hrow = reinterpret_cast<const store_t*>(a.h) + o * a.d;
     const store_t* erow = reinterpret_cast<const store_t*>(a.W1) + (size_t)xp * a.rank;
     const float c = sigmoid_f32(conf_dot_wg<W>(hrow, erow, a.w, a.d, a.rank, red));
@@ -459,7 +459,7 @@ __global__ __launch_bounds__(kStreamThreads) void markov_step_shared(StepArgs a)
   const bool conf_pre = conf_preloadable<W>(a, slab, nr);
   auto gather = [&](typename W::frag_t(&ef)[W::kMaxKs]) {
     const void* base = a.E_rows ? a.E_rows : a.W1;
-    const int row = a.E_rows ? rc : clamp_token(toks.token(), a.V);
+    const int row = a.E_rows ? rc : checked_token(toks.token(), a.V, a.err);
     if (conf_pre && wave == (slab >> 5) && lane == (slab & 31)) conf_tok = row;
     if constexpr (std::is_same<W, WBf16>::value && kKs > 0 && kKs % 4 == 0 && kVec)
       load_e_frags_lines<kKs>(ef, reinterpret_cast<const uint16_t*>(base), row, patch);

@@ -222,7 +222,7 @@ __device__ __forceinline__ void state_step_body(const RnnArgs& a, int k, const f
     }
   }
   int tok = k > 1 ? winner_id(a.best[winner_index(k - 2, a.R, mc)]) : a.x[(size_t)mc * (a.gamma + 1)];
-  tok = clamp_token(tok, a.V);
+  tok = checked_token(tok, a.V, a.err);
   const uint16_t* erow = a.W1 + (size_t)tok * H + 8 * half;
 #pragma unroll
   for (int j = 0; j < kStateMaxSteps; ++j)

@@ -45,6 +45,7 @@ struct GradArgs {
   const uint16_t* h;
   const float* w;
   const int32_t* x;  // x* [R][gamma + 1]
+  uint32_t* err;     // token-error word (checked_token)
   const float* dz;   // [n_rows][V]
   const float* dl;   // [n_rows]
   uint16_t* w2;      // W2t transposed, chunk-major [vp / 64][rank][64]
@@ -59,7 +60,7 @@ struct GradArgs {
 
 __device__ __forceinline__ int row_token(const GradArgs& g, int row) {
   const int r = row / g.gamma, k = row % g.gamma;  // position k+1 reads x*_k
-  return clamp_token(g.x[(size_t)r * (g.gamma + 1) + k], g.V);
+  return checked_token(g.x[(size_t)r * (g.gamma + 1) + k], g.V, g.err);
 }
 
 // bf16 of an fp32 value, round to nearest even (values here are finite).
@@ -420,6 +421,7 @@ hipError_t launch_train_grad_rest(const VerifyArgs& a, const TrainArgs& ta, cons
   g.h = static_cast<const uint16_t*>(ta.h);
   g.w = ta.w;
   g.x = a.x;
+  g.err = a.err;
   g.dz = ta.dU;
   g.dl = reinterpret_cast<const float*>(a.ws + tp.off_dl);
   g.w2 = reinterpret_cast<uint16_t*>(a.ws + tp.off_w2);

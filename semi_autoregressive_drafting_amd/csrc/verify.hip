@@ -172,7 +172,7 @@ __global__ __launch_bounds__(kAcceptThreads) void verify_accept(VerifyArgs a, Ve
     const int r = row / a.gamma, j = row - r * a.gamma + 1;  // drafted position j = k
     const float* q = lp + (size_t)row * p.lse_chunks * 2;
     const int xraw = a.x[(size_t)r * (a.gamma + 1) + j];
-    const int xj = clamp_token(xraw, a.V);
+    const int xj = checked_token(xraw, a.V, a.err);
     bool ok;
     if (a.greedy) {
       float m = -INFINITY;
@@ -253,7 +253,9 @@ __device__ __forceinline__ void verify_gather(typename W::frag_t (&ef)[W::kMaxKs
   if (a.E_rows)
     load_e_frags<W, kKs>(ef, a.E_rows, r * a.gamma + (k - 1), a.rank, a.R * a.gamma, half);
   else
-    load_e_frags<W, kKs>(ef, a.W1, a.x[(size_t)r * (a.gamma + 1) + (k - 1)], a.rank, a.V, half);
+    load_e_frags<W, kKs>(ef, a.W1,
+                         checked_token(a.x[(size_t)r * (a.gamma + 1) + (k - 1)], a.V, a.err),
+                         a.rank, a.V, half);
 }
 
 // Map blockIdx to (slab, group); the groups of one slab share an XCD.
@@ -727,7 +729,9 @@ __global__ __launch_bounds__(kTvThreads) void train_draft_lse(VerifyArgs a, Veri
   epi.tx = -INFINITY;
   epi.xs = a.x[(size_t)r * (a.gamma + 1) + k];
   auto gather = [&](typename W::frag_t(&ef)[W::kMaxKs]) {
-    load_e_frags<W, kKs>(ef, a.W1, a.x[(size_t)r * (a.gamma + 1) + (k - 1)], a.rank, a.V, half);
+    load_e_frags<W, kKs>(ef, a.W1,
+                         checked_token(a.x[(size_t)r * (a.gamma + 1) + (k - 1)], a.V, a.err),
+                         a.rank, a.V, half);
   };
   shared_a_stream<W, kKs, kVerifyDist, kTvThreads>(a.W2t, a.V, a.rank, t_begin, t_end, e, gather,
                                                    lds, epi);
@@ -938,7 +942,9 @@ __global__ __launch_bounds__(kTvThreads) void train_grad_logits(VerifyArgs a, Ve
   for (int q = 0; q < 4; ++q)
     epi.line_ok[q] = (grp * kTvWaves + wave) * kVTile + 8 * q + (lane >> 3) < p.n_rows;
   auto gather = [&](typename W::frag_t(&ef)[W::kMaxKs]) {
-    load_e_frags<W, kKs>(ef, a.W1, a.x[(size_t)r * (a.gamma + 1) + (k - 1)], a.rank, a.V, half);
+    load_e_frags<W, kKs>(ef, a.W1,
+                         checked_token(a.x[(size_t)r * (a.gamma + 1) + (k - 1)], a.V, a.err),
+                         a.rank, a.V, half);
   };
   shared_a_stream<W, kKs, kVerifyDist, kTvThreads>(a.W2t, a.V, a.rank, t_begin, t_end, e, gather,
                                                    lds, epi);

@@ -12,7 +12,9 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libdspark.so")
+# DSPARK_LIB selects another build of the same library (e.g. the one whose
+# host layer is built with sanitizers, build.build_host_sanitized()).
+LIB_PATH = os.environ.get("DSPARK_LIB") or os.path.join(_HERE, "libdspark.so")
 
 DSPARK_OK, DSPARK_ERR_NULL, DSPARK_ERR_SHAPE, DSPARK_ERR_DTYPE, DSPARK_ERR_VALUE, \
     DSPARK_ERR_WORKSPACE, DSPARK_ERR_LAUNCH = range(7)
@@ -24,7 +26,8 @@ DSPARK_PHASE_STEPS, DSPARK_PHASE_MERGE = 1, 2
 EXPORTS = ("dspark_workspace_bytes", "dspark_status_string", "dspark_draft_step",
            "dspark_draft_block", "dspark_draft_block_phases", "dspark_confidence", "dspark_schedule", "dspark_schedule_async",
            "dspark_verify", "dspark_train_loss", "dspark_train_loss_grad",
-           "dspark_draft_block_rnn", "dspark_verify_rnn", "dspark_draft_block_noalloc")
+           "dspark_draft_block_rnn", "dspark_verify_rnn", "dspark_draft_block_noalloc",
+           "dspark_token_errors")
 
 _lib = None
 
@@ -49,6 +52,8 @@ def load():
     L.dspark_workspace_bytes.restype = SZ
     L.dspark_status_string.argtypes = [I]
     L.dspark_status_string.restype = ctypes.c_char_p
+    L.dspark_token_errors.argtypes = [ctypes.POINTER(ctypes.c_uint32), I]
+    L.dspark_token_errors.restype = I
     L.dspark_draft_step.argtypes = [I, I, I, I, I, I, I, P, P, P, P, P, F, U64,
                                     P, P, P, P, P, P, P, SZ, P]
     L.dspark_draft_step.restype = I
@@ -120,6 +125,15 @@ def _call(fn, *args):
 
 def dspark_workspace_bytes(op, R, V, rank, gamma) -> int:
     return int(load().dspark_workspace_bytes(op, R, V, rank, gamma))
+
+
+def dspark_token_errors(clear=False) -> int:
+    """The current device's token-error word (1 if some kernel met a token id
+    outside [0, V) since the last clear); clear=True resets it.  Synchronise
+    the streams that ran the kernels first."""
+    flag = ctypes.c_uint32(0)
+    _call("dspark_token_errors", ctypes.byref(flag), 1 if clear else 0)
+    return int(flag.value)
 
 
 def dspark_draft_step(R, V, rank, d, gamma, k, dt, W1, W2t, U, h, w, temperature, seed,

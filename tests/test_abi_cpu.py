@@ -320,3 +320,23 @@ def test_bench_refuses_several_gpus():
                        capture_output=True, text=True, timeout=60)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_token_errors_query_plumbing():
+    """The token-error query checks its arguments before any HIP call, and
+    without a usable GPU reports a launch error (leaving *flag alone) instead
+    of crashing; the Python wrapper raises on that status."""
+    import ctypes
+    f = D.load().dspark_token_errors
+    flag = ctypes.c_uint32(12345)
+    assert f(None, 0) == D.DSPARK_ERR_NULL
+    assert f(ctypes.byref(flag), 2) == D.DSPARK_ERR_VALUE
+    assert f(ctypes.byref(flag), -1) == D.DSPARK_ERR_VALUE
+    assert flag.value == 12345
+    import torch
+    if not torch.cuda.is_available():
+        assert f(ctypes.byref(flag), 0) == D.DSPARK_ERR_LAUNCH
+        assert f(ctypes.byref(flag), 1) == D.DSPARK_ERR_LAUNCH
+        assert flag.value == 12345
+        with pytest.raises(D.DsparkError):
+            D.dspark_token_errors()
