@@ -392,6 +392,9 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the read ceiling, cold steps, asynchronous scheduler and graph "
                          "replay (for counter-collection runs)")
+    ap.add_argument("--train-only", action="store_true",
+                    help="only run the training losses with every gradient (K times, the "
+                         "drafted block standing in for x*), for counter collection")
     ap.add_argument("--cold-only", action="store_true",
                     help="only run single draft-step launches, each after a cache flush (so "
                          "that a kernel trace shows the cold kernel alone)")
@@ -425,6 +428,17 @@ def main():
     print(f"# inputs ready in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
     R, g, V, rank, d = di.R, di.gamma, di.V, di.rank, di.d
     di_wl = inp.wl
+    if args.train_only:
+        runner.draft(di, buf, TEMPERATURE, 1)
+        x_star = buf.x.clone()
+        gws = torch.empty(D.dspark_workspace_bytes(D.DSPARK_OP_TRAIN_GRAD, R, V, rank, g),
+                          dtype=torch.uint8, device="cuda")
+        for _ in range(args.steps):
+            gout = runner.train_loss_grad(di, x_star, ws=gws)
+            del gout
+        torch.cuda.synchronize()
+        print(json.dumps({"workload": WORKLOAD, "train_loss_grad_calls": args.steps}), flush=True)
+        return
     if args.cold_only:
         single = cold_single_steps(di, args.steps, modes=("cold",))
         sb = draft_step_bytes(R, V, rank, d)

@@ -69,12 +69,6 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
-__device__ __forceinline__ bf16x8_t pack_bf16(const float (&v)[8]) {
-  bf16x8_t r;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) r[j] = __builtin_bit_cast(__bf16, bf16_rne(v[j]));
-  return r;
-}
 
 // ---------------------------------------------------------------------------
 // G2 / G3: 64 x 64 tiles through LDS, read along rank and written along K
@@ -164,35 +158,49 @@ __device__ __forceinline__ void mma_chunk(f32x16_t (&acc)[NC], const bf16x8_t (&
   }
 }
 
-// Chunk loop over [c_begin, c_end) (at least one chunk).  load_a(a, chunk)
-// fills a wave's A values; B comes from the chunk-major copy `bsrc`.
-template <int NC, class LoadA>
-__device__ __forceinline__ void contract(f32x16_t (&acc)[NC], const uint16_t* bsrc, int c_begin,
-                                         int c_end, uint16_t* lds, LoadA load_a) {
+// Chunk loop over [c_begin, c_end) (at least one chunk), B from the
+// chunk-major copy `bsrc`, the A operand staged like B: load_raw(ch) issues a
+// wave's global loads of chunk ch (whole 128-byte lines), put_raw() rounds
+// them to bf16 and writes them into the wave's A patch (32 rows of 64 K values,
+// kLdsRow apart, the layout of the B chunk), from which every lane reads its
+// MFMA operands.  In the lane layout itself a load instruction would touch 32
+// different lines; the patch lets each instruction read whole lines.
+template <int NC, class LoadRaw, class PutRaw>
+__device__ __forceinline__ void contract_staged(f32x16_t (&acc)[NC], const uint16_t* bsrc,
+                                                int c_begin, int c_end, uint16_t* lds,
+                                                const uint16_t* apatch, LoadRaw load_raw,
+                                                PutRaw put_raw) {
   constexpr size_t kChunkElems = (size_t)NC * 32 * kChunk;
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5, col = lane & 31;
   BChunk<NC> b;
-  float nxt[4][8];
-  bf16x8_t cur[4];  // the current chunk's A operands, rounded to bf16 on arrival
   b.load(bsrc + c_begin * kChunkElems);
-  load_a(nxt, c_begin);
-#pragma unroll
-  for (int s = 0; s < 4; ++s) cur[s] = pack_bf16(nxt[s]);
+  load_raw(c_begin);
   b.store(lds);
+  put_raw();
   lds_barrier();
   for (int ch = c_begin; ch < c_end; ++ch) {
-    // the next chunk (the last one again at the end: loads stay unconditional)
     const int cn = ch + 1 < c_end ? ch + 1 : ch;
     b.load(bsrc + cn * kChunkElems);
-    load_a(nxt, cn);
+    load_raw(cn);
+    // keep the next chunk's loads ahead of this chunk's MFMAs (the scheduler
+    // would otherwise sink them next to their use, leaving the latency bare)
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8_t cur[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      cur[s] = *reinterpret_cast<const bf16x8_t*>(apatch + col * kLdsRow + 16 * s + 8 * half);
     mma_chunk<NC>(acc, cur, lds, col, half);
     lds_barrier();  // every wave is past its reads of this chunk
     b.store(lds);
+    put_raw();
     lds_barrier();
-#pragma unroll
-    for (int s = 0; s < 4; ++s) cur[s] = pack_bf16(nxt[s]);
   }
+}
+
+__device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) {
+  return make_uint2((uint32_t)bf16_rne(a) | ((uint32_t)bf16_rne(b) << 16),
+                    (uint32_t)bf16_rne(c) | ((uint32_t)bf16_rne(d) << 16));
 }
 
 // G4: wave q of workgroup (group, slab) owns rows 32 (4 group + q) .. +31;
@@ -200,6 +208,7 @@ __device__ __forceinline__ void contract(f32x16_t (&acc)[NC], const uint16_t* bs
 template <int NC, bool kVec>
 __global__ __launch_bounds__(kGThreads) void grad_e_partial(GradArgs g) {
   __shared__ __align__(16) uint16_t lds[NC * 32 * kLdsRow];
+  __shared__ __align__(16) uint16_t apatch[4][32 * kLdsRow];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = lane >> 5, col = lane & 31;
   // blockIdx -> (group, slab): workgroups are dealt to the 8 XCDs in turn, so
@@ -215,34 +224,51 @@ __global__ __launch_bounds__(kGThreads) void grad_e_partial(GradArgs g) {
     slab = blockIdx.x / g.e_groups;
   }
   const int rt = grp * 4 + wave;
-  const int row = rt * 32 + col;
-  const int rowc = row < g.n_rows ? row : g.n_rows - 1;
-  const float* zrow = g.dz + (size_t)rowc * g.V;
   int c_begin, c_end;
   slab_range(slab, g.e_slabs, g.vp / kChunk, c_begin, c_end);
+
+  // load instruction q of a chunk, lane l: the wave's row 4q + l/16 (rows past
+  // n_rows read row n_rows - 1; their results are never used), entries
+  // 4 (l%16) .. +3 of the chunk (zeros past V)
+  const int lrow = lane >> 4, lk = 4 * (lane & 15);
+  const float* zq[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int row = min(rt * 32 + 4 * q + lrow, g.n_rows - 1);
+    zq[q] = g.dz + (size_t)row * g.V + lk;
+  }
+  // With V % 4 == 0 a lane's 4 entries are all inside V or all past it: the
+  // loads go unconditionally to an in-bounds address and the entries past V
+  // become zeros when they are written to the patch (a select right after a
+  // load would make the wave wait for it).
+  f32x4_t raw[8];
+  bool kin = true;
+  uint16_t* ap = apatch[wave];
+  auto load_raw = [&](int ch) {
+    const int vb = ch * kChunk + lk;
+    if constexpr (kVec) {
+      kin = vb < g.V;
+      const int off = kin ? ch * kChunk : 0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) raw[q] = *reinterpret_cast<const f32x4_t*>(zq[q] + off);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) raw[q][j] = vb + j < g.V ? zq[q][ch * kChunk + j] : 0.0f;
+    }
+  };
+  auto put_raw = [&]() {
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      *reinterpret_cast<uint2*>(ap + (4 * q + lrow) * kLdsRow + lk) =
+          kin ? pack4_bf16(raw[q][0], raw[q][1], raw[q][2], raw[q][3]) : make_uint2(0u, 0u);
+  };
 
   f32x16_t acc[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) acc[c] = f32x16_t{};
-  auto load_a = [&](float (&a)[4][8], int ch) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int vb = ch * kChunk + 16 * s + 8 * half;
-      if (kVec && vb + 8 <= g.V) {
-        const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(zrow + vb);
-        const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(zrow + vb + 4);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          a[s][j] = lo[j];
-          a[s][4 + j] = hi[j];
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) a[s][j] = vb + j < g.V ? zrow[vb + j] : 0.0f;
-      }
-    }
-  };
-  contract<NC>(acc, g.w2, c_begin, c_end, lds, load_a);
+  contract_staged<NC>(acc, g.w2, c_begin, c_end, lds, ap, load_raw, put_raw);
   // accumulator i of lane l: row 8 (i/4) + 4 half + i%4 of the tile, rank c*32 + l%32
   float* out = g.dep + (size_t)slab * g.n_pad * g.rank;
 #pragma unroll
@@ -265,32 +291,65 @@ __global__ __launch_bounds__(kGThreads) void grad_e_reduce(GradArgs g) {
 }
 
 // G6: wave q of workgroup b owns vocabulary tile vt = 4 b + q (entries past V
-// read as zero and are not written); K = all rows, B = et.  A values are
-// dz[row k][32 vt + m]: 8 rows per lane and step, 128 contiguous bytes per
-// row across the 32 lanes of a half.
-template <int NC>
+// read as zero and are not written); K = all rows, B = et.  The wave's A patch
+// holds the tile transposed, [entry][row]: lane l loads rows 32 g + 4 (l/8)
+// + j (g = 0, 1; j = 0..3) at entries 4 (l%8) .. +3 of the tile, so each load
+// instruction reads 8 whole 128-byte row segments, and writes, per entry, its
+// 4 consecutive rows as one 8-byte piece.
+template <int NC, bool kVec>
 __global__ __launch_bounds__(kGThreads) void grad_w2t(GradArgs g) {
   __shared__ __align__(16) uint16_t lds[NC * 32 * kLdsRow];
+  __shared__ __align__(16) uint16_t apatch[4][32 * kLdsRow];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = lane >> 5, col = lane & 31;
   const int vt = blockIdx.x * 4 + wave;
-  const int v = vt * 32 + col;
-  const bool vin = v < g.V;
-  const float* zcol = g.dz + (vin ? v : 0);
+  const int le = 4 * (lane & 7), lr = 4 * (lane >> 3);
+  const int v0 = vt * 32 + le;  // this lane's first entry
+  const bool vin = v0 < g.V;  // with V % 4 == 0: all 4 entries or none
+  const float* zc = g.dz + (vin ? v0 : 0);
+  // loads go unconditionally to in-bounds rows (row n_rows - 1 past the end);
+  // rows past n_rows and entries past V become zeros in the patch
+  f32x4_t raw[2][4];
+  unsigned rin = 0u;  // bit 4 gg + j: row 32 gg + lr + j of the chunk exists
+  uint16_t* ap = apatch[wave];
+  auto load_raw = [&](int ch) {
+    rin = 0u;
+#pragma unroll
+    for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rr = ch * kChunk + 32 * gg + lr + j;
+        rin |= (rr < g.n_rows ? 1u : 0u) << (4 * gg + j);
+        if constexpr (kVec) {
+          raw[gg][j] = *reinterpret_cast<const f32x4_t*>(zc + (size_t)min(rr, g.n_rows - 1) * g.V);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            raw[gg][j][e] = (rr < g.n_rows && v0 + e < g.V) ? zc[(size_t)rr * g.V + e] : 0.0f;
+        }
+      }
+  };
+  auto put_raw = [&]() {
+#pragma unroll
+    for (int gg = 0; gg < 2; ++gg) {
+      float v[4][4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool ok = (!kVec || vin) && ((rin >> (4 * gg + j)) & 1u);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[j][e] = ok ? raw[gg][j][e] : 0.0f;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        *reinterpret_cast<uint2*>(ap + (le + e) * kLdsRow + 32 * gg + lr) =
+            pack4_bf16(v[0][e], v[1][e], v[2][e], v[3][e]);
+    }
+  };
 
   f32x16_t acc[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) acc[c] = f32x16_t{};
-  auto load_a = [&](float (&a)[4][8], int ch) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int rr = ch * kChunk + 16 * s + 8 * half + j;
-        a[s][j] = (vin && rr < g.n_rows) ? zcol[(size_t)rr * g.V] : 0.0f;
-      }
-  };
-  contract<NC>(acc, g.et, 0, g.n_pad / kChunk, lds, load_a);
+  contract_staged<NC>(acc, g.et, 0, g.n_pad / kChunk, lds, ap, load_raw, put_raw);
 #pragma unroll
   for (int c = 0; c < NC; ++c)
 #pragma unroll
@@ -396,7 +455,10 @@ hipError_t launch_gemms(const GradArgs& g, bool vec, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_vt = (g.V + 31) / 32;
-  hipLaunchKernelGGL((grad_w2t<NC>), dim3((n_vt + 3) / 4), dim3(kGThreads), 0, stream, g);
+  if (vec)
+    hipLaunchKernelGGL((grad_w2t<NC, true>), dim3((n_vt + 3) / 4), dim3(kGThreads), 0, stream, g);
+  else
+    hipLaunchKernelGGL((grad_w2t<NC, false>), dim3((n_vt + 3) / 4), dim3(kGThreads), 0, stream, g);
   return hipGetLastError();
 }
 
