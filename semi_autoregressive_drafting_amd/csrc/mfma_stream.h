@@ -194,6 +194,9 @@ __device__ __forceinline__ void shared_a_stream(const void* W2t, int V, int rank
   auto body = [&](auto slot, int vt) {
     constexpr int S = decltype(slot)::value;
     fetch(slot_t<(S + kDist) % P>{}, vt + kDist);
+    // the prefetch goes out before this tile's MFMAs (the scheduler would
+    // otherwise spread its loads among them, later than they can be issued)
+    __builtin_amdgcn_sched_barrier(0);
     const f32x16_t acc = mma(lds + S * tile_lds);
     epi.template consume<S>(acc, vt);
     stash(slot_t<(S + 1) % P>{});
