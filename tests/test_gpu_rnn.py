@@ -178,7 +178,7 @@ def test_rnn_round_verifies_against_its_own_rows(name, V, R, gamma):
     ok = ((g["n_accept"] == res["n_accept"]) & (g["next_token"] == res["next_token"])
           & (g["tau"] == res["tau"]))
     assert np.all(ok | near), np.nonzero(~ok & ~near)
-    # with the Markov rows the verdict would be different: the rows matter
+    # with the Markov rows the acceptance outcome would differ: the rows matter
     res_m = O.verify(inp.U, inp.target, W1, W2t, x, g["ell"], T, seed, np.arange(wl.R))
     assert np.abs(res_m["c_star"] - cs_o).max() > 1e-3
     say(f"  ok: budget {g['ell'].sum()}, tau mean {g['tau'].mean():.3f}")
