@@ -4,7 +4,7 @@ TEST INFRASTRUCTURE.  Only the test suite, the package smoke check and the
 benchmark's CPU-baseline leg may import or run this module.  The product path
 never does, and this module shares no code with it (no kernels, headers,
 helpers, tables or constants): it is a plain, slow, obviously correct fp64
-restatement of what the pages define, used to judge the HIP path.
+restatement of what the pages define, used to check the HIP path.
 
 Sources, cited by page title and section (no other source defines the method):
   [P1] "DSpark" -- rainlin-net.pages.dev/llm-inference/dspark (sections 1-9).
