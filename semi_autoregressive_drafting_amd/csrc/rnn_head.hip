@@ -165,16 +165,23 @@ __global__ __launch_bounds__(256) void rnn_proj_reduce(RnnArgs a) {
 //   A  e:  W1[x_{k-1}[m]][k ..]       s:  hi / lo bf16 terms of s_{k-1}[m][k ..]
 //   B  W_ih[g rank + n][k ..] (the e columns), W_hh[g rank + n][k ..]
 // The kernel is bound by dependent memory round trips (a few microseconds
-// each here), so every wave issues all of its loads at the start and only the
-// e rows wait for the token.  The quarters meet in LDS in a fixed order, the
+// each here) and by one CU's load pipeline (32 workgroups on 32 CUs), so every
+// wave issues all of its loads at the start, only the e rows wait for the
+// token, and s_{k-1} is read once per workgroup as whole rows into LDS rather
+// than once per gate wave in the MFMA lane layout.  The quarters meet in LDS in a fixed order, the
 // first one bringing the input projection and the recurrent bias; waves 0 .. 3
 // then form s_k, four of each lane's 16 entries each.
 constexpr int kStateQ = 4;       // K quarters
 constexpr int kStateMaxSteps = 4;  // K steps per quarter at rank 256
 
+// s_{k-1} rows of the workgroup's 32 requests, staged once in LDS (row
+// stride kSRow floats) instead of once per gate wave in the lane layout.
+constexpr int kSRow = 256 + 4;
+
 template <bool kRec>
 __device__ __forceinline__ void state_step_body(const RnnArgs& a, int k, const float* s_prev,
-                                                float* s_next, float (*red)[3][2][16][64]) {
+                                                float* s_next, float (*red)[3][2][16][64],
+                                                float (*sl)[kSRow]) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = w / kStateQ, q = w % kStateQ;
   const int half = lane >> 5, col = lane & 31;
@@ -186,8 +193,6 @@ __device__ __forceinline__ void state_step_body(const RnnArgs& a, int k, const f
   const int n = jb * 32 + col;
   const uint16_t* wi = a.W_ih + (size_t)(g * H + n) * (H + a.d) + 8 * half;
   const uint16_t* wh = a.W_hh + (size_t)(g * H + n) * H + 8 * half;
-  const float* srow = s_prev + (size_t)mc * H + 8 * half;
-
   // loads that do not depend on the token
   bf16x8_t wiv[kStateMaxSteps], whv[kStateMaxSteps], ev[kStateMaxSteps];
   f32x4_t sv[kStateMaxSteps][2];
@@ -195,10 +200,20 @@ __device__ __forceinline__ void state_step_body(const RnnArgs& a, int k, const f
   for (int j = 0; j < kStateMaxSteps; ++j) {
     const int k0 = 16 * min(s_begin + j, KS - 1);
     wiv[j] = *reinterpret_cast<const bf16x8_t*>(wi + k0);
-    if constexpr (kRec) {
-      whv[j] = *reinterpret_cast<const bf16x8_t*>(wh + k0);
-      sv[j][0] = *reinterpret_cast<const f32x4_t*>(srow + k0);
-      sv[j][1] = *reinterpret_cast<const f32x4_t*>(srow + k0 + 4);
+    if constexpr (kRec) whv[j] = *reinterpret_cast<const bf16x8_t*>(wh + k0);
+  }
+  // s_{k-1} of the 32 requests (rows past R repeat row R - 1): whole rows,
+  // 16 bytes per thread and piece, into LDS
+  constexpr int kPieces = 32 * 256 / 4;
+  f32x4_t spc[(kPieces + 64 * 3 * kStateQ - 1) / (64 * 3 * kStateQ)];
+  const int pieces = 32 * H / 4;
+  if constexpr (kRec) {
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(spc) / sizeof(spc[0])); ++i) {
+      const int pc = threadIdx.x + i * 64 * 3 * kStateQ;
+      const int row = pc / (H / 4), c4 = pc % (H / 4);
+      const int rr = min(rt * 32 + row, a.R - 1);
+      if (pc < pieces) spc[i] = *reinterpret_cast<const f32x4_t*>(s_prev + (size_t)rr * H + 4 * c4);
     }
   }
   // waves 0 .. 3 each blend 4 of the 16 accumulator entries at the end, and
@@ -227,6 +242,24 @@ __device__ __forceinline__ void state_step_body(const RnnArgs& a, int k, const f
 #pragma unroll
   for (int j = 0; j < kStateMaxSteps; ++j)
     ev[j] = *reinterpret_cast<const bf16x8_t*>(erow + 16 * min(s_begin + j, KS - 1));
+
+  if constexpr (kRec) {
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(spc) / sizeof(spc[0])); ++i) {
+      const int pc = threadIdx.x + i * 64 * 3 * kStateQ;
+      if (pc < pieces) {
+        const int row = pc / (H / 4), c4 = pc % (H / 4);
+        *reinterpret_cast<f32x4_t*>(&sl[row][4 * c4]) = spc[i];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kStateMaxSteps; ++j) {
+      const int k0 = 16 * min(s_begin + j, KS - 1) + 8 * half;
+      sv[j][0] = *reinterpret_cast<const f32x4_t*>(&sl[col][k0]);
+      sv[j][1] = *reinterpret_cast<const f32x4_t*>(&sl[col][k0 + 4]);
+    }
+  }
 
   f32x16_t gi = f32x16_t{}, gh = f32x16_t{};
 #pragma unroll
@@ -295,10 +328,11 @@ __global__ __launch_bounds__(64 * 3 * kStateQ) void rnn_state_step(RnnArgs a, in
                                                                    const float* s_prev,
                                                                    float* s_next) {
   __shared__ float red[2][3][2][16][64];  // slot, gate, input / recurrent part
+  __shared__ __align__(16) float sl[32][kSRow];
   if (k > 1)
-    state_step_body<true>(a, k, s_prev, s_next, red);
+    state_step_body<true>(a, k, s_prev, s_next, red, sl);
   else
-    state_step_body<false>(a, k, s_prev, s_next, red);  // s_0 = 0
+    state_step_body<false>(a, k, s_prev, s_next, red, sl);  // s_0 = 0
 }
 
 }  // namespace
