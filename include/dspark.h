@@ -247,7 +247,12 @@ dspark_status dspark_confidence(int R, int gamma, int d, int rank, int V, int dt
  *   may be NULL).
  * sps: fp64 [sps_len], steps/s at B verified tokens, B = 0..R*(1+gamma)
  * (sps_len >= R*(1+gamma)+1).  a: fp32 [R][gamma], values in [0, 1].
- * One workgroup; R*gamma <= 8192.
+ * R*gamma <= 8192.  ws: dspark_workspace_bytes(DSPARK_OP_SCHEDULE, R, V, rank,
+ * gamma) bytes (V and rank are ignored), 16-byte aligned, ZERO-FILLED before
+ * its first use: it holds the prefix sums and requests by sorted position and
+ * the counters of finished workgroups, which every call leaves at zero again.
+ * Calls that overlap in time need workspaces of their own; a workspace sized
+ * for one R*gamma serves every smaller call.
  */
 dspark_status dspark_schedule(int R, int gamma, const float* a, const double* sps, int sps_len,
                               int32_t* ell, int32_t* budget, double* theta, void* ws,
@@ -267,13 +272,13 @@ dspark_status dspark_schedule(int R, int gamma, const float* a, const double* sp
  * Outputs (device): ell[R] = admitted positions of request r (a prefix when
  * the rows of a_cur are non-increasing), *budget = K, *theta =
  * Theta_fix(K) * 2^-32 (the lagged estimate; may be NULL).
- * a_lag, a_cur: fp32 [R][gamma], values in [0, 1]; sps as for
- * dspark_schedule.  One workgroup; R*gamma <= 8192.  ell depends on a_lag
- * only through K.
+ * a_lag, a_cur: fp32 [R][gamma], values in [0, 1]; sps and ws as for
+ * dspark_schedule; R*gamma <= 8192.  ell depends on a_lag only through K.
  */
 dspark_status dspark_schedule_async(int R, int gamma, const float* a_lag, const float* a_cur,
                                     const double* sps, int sps_len, int32_t* ell,
-                                    int32_t* budget, double* theta, dspark_stream_t stream);
+                                    int32_t* budget, double* theta, void* ws, size_t ws_bytes,
+                                    dspark_stream_t stream);
 
 /*
  * Verification of drafted blocks against target logits [P1 §3.1 eq. c*;

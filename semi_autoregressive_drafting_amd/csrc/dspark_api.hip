@@ -139,7 +139,9 @@ size_t dspark_workspace_bytes(int op, int R, int V, int rank, int gamma) {
   if (R < 1 || R > kMaxR || V < 2 || V > kMaxV || gamma < 1 || gamma > kMaxGamma) return 0;
   switch (op) {
     case DSPARK_OP_DRAFT_STEP: return plan_draft_step(R, V, gamma).ws_bytes;
-    case DSPARK_OP_SCHEDULE: return 0;
+    case DSPARK_OP_SCHEDULE:
+      if (R * gamma > kMaxSched) return 0;
+      return sched_ws_bytes(R * gamma);
     case DSPARK_OP_VERIFY: return plan_verify(R, V, gamma).ws_bytes;
     case DSPARK_OP_TRAIN_LOSS: return plan_train(R, V, rank < 1 ? 1 : rank, 1, gamma).ws_bytes;
     case DSPARK_OP_DRAFT_RNN:
@@ -260,6 +262,16 @@ dspark_status verify_common(int R, int V, int rank, int gamma, int dt, const voi
   if (token_error_address(&args.err) != DSPARK_OK) return DSPARK_ERR_LAUNCH;
   if (launch_verify(args, plan, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return DSPARK_ERR_LAUNCH;
+  return DSPARK_OK;
+}
+
+// Validation shared by the two schedulers (pointers were checked by the caller).
+dspark_status check_schedule(int R, int gamma, int sps_len, const void* ws, size_t ws_bytes) {
+  if (R < 1 || R > kMaxR || gamma < 1 || gamma > kMaxGamma || R * gamma > kMaxSched)
+    return DSPARK_ERR_SHAPE;
+  if (sps_len < R * (1 + gamma) + 1) return DSPARK_ERR_SHAPE;
+  if (!ws || ws_bytes < sched_ws_bytes(R * gamma) || (reinterpret_cast<uintptr_t>(ws) & 15u))
+    return DSPARK_ERR_WORKSPACE;
   return DSPARK_OK;
 }
 
@@ -431,27 +443,45 @@ dspark_status dspark_confidence(int R, int gamma, int d, int rank, int V, int dt
 dspark_status dspark_schedule(int R, int gamma, const float* a, const double* sps, int sps_len,
                               int32_t* ell, int32_t* budget, double* theta, void* ws,
                               size_t ws_bytes, dspark_stream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
   if (!a || !sps || !ell || !budget) return DSPARK_ERR_NULL;
-  if (R < 1 || R > kMaxR || gamma < 1 || gamma > kMaxGamma || R * gamma > kMaxSched)
-    return DSPARK_ERR_SHAPE;
-  if (sps_len < R * (1 + gamma) + 1) return DSPARK_ERR_SHAPE;
-  SchedArgs args{R, gamma, a, sps, ell, budget, theta};
-  if (launch_schedule(args, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+  const dspark_status s = check_schedule(R, gamma, sps_len, ws, ws_bytes);
+  if (s != DSPARK_OK) return s;
+  SchedRankArgs args{};
+  args.R = R;
+  args.gamma = gamma;
+  args.N = R * gamma;
+  args.async = false;
+  args.a = a;
+  args.sps = sps;
+  args.ell = ell;
+  args.budget = budget;
+  args.theta = theta;
+  sched_ws_layout(args, ws);
+  if (launch_schedule_ranked(args, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return DSPARK_ERR_LAUNCH;
   return DSPARK_OK;
 }
 
 dspark_status dspark_schedule_async(int R, int gamma, const float* a_lag, const float* a_cur,
                                     const double* sps, int sps_len, int32_t* ell,
-                                    int32_t* budget, double* theta, dspark_stream_t stream) {
+                                    int32_t* budget, double* theta, void* ws, size_t ws_bytes,
+                                    dspark_stream_t stream) {
   if (!a_lag || !a_cur || !sps || !ell || !budget) return DSPARK_ERR_NULL;
-  if (R < 1 || R > kMaxR || gamma < 1 || gamma > kMaxGamma || R * gamma > kMaxSched)
-    return DSPARK_ERR_SHAPE;
-  if (sps_len < R * (1 + gamma) + 1) return DSPARK_ERR_SHAPE;
-  SchedAsyncArgs args{R, gamma, a_lag, a_cur, sps, ell, budget, theta};
-  if (launch_schedule_async(args, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+  const dspark_status s = check_schedule(R, gamma, sps_len, ws, ws_bytes);
+  if (s != DSPARK_OK) return s;
+  SchedRankArgs args{};
+  args.R = R;
+  args.gamma = gamma;
+  args.N = R * gamma;
+  args.async = true;
+  args.a = a_lag;
+  args.a_cur = a_cur;
+  args.sps = sps;
+  args.ell = ell;
+  args.budget = budget;
+  args.theta = theta;
+  sched_ws_layout(args, ws);
+  if (launch_schedule_ranked(args, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return DSPARK_ERR_LAUNCH;
   return DSPARK_OK;
 }

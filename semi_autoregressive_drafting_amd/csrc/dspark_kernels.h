@@ -91,26 +91,29 @@ struct ConfArgs {
 };
 hipError_t launch_confidence(const ConfArgs& a, hipStream_t stream);
 
-struct SchedArgs {
-  int R, gamma;
+// Prefix scheduler (see schedule.hip): one launch over the grid; the last
+// workgroup to finish applies the early stop.  The workspace carries, by
+// sorted position, the prefix sums G and the candidates' requests, and the
+// finishing counters (zero before the first call; every call leaves them zero).
+struct SchedRankArgs {
+  int R, gamma, N;      // N = R * gamma
+  bool async;           // asynchronous variant: a = a_lag (budget), a_cur (selection)
   const float* a;
+  const float* a_cur;
   const double* sps;
   int32_t* ell;
   int32_t* budget;
   double* theta;
+  // workspace (sched_ws_layout)
+  int n_wgs;            // workgroups per key array
+  unsigned* done;       // finishing counters
+  int32_t* req;         // [N] request of the candidate at each sorted position (a_cur when async)
+  double* gpos;         // [N + 1] G_b, the exact sum of q over the first b candidates
+                        // (of a_lag when async)
 };
-hipError_t launch_schedule(const SchedArgs& a, hipStream_t stream);
-
-struct SchedAsyncArgs {
-  int R, gamma;
-  const float* a_lag;  // survival probabilities two steps earlier (budget only)
-  const float* a_cur;  // current survival probabilities (selection)
-  const double* sps;
-  int32_t* ell;
-  int32_t* budget;
-  double* theta;
-};
-hipError_t launch_schedule_async(const SchedAsyncArgs& a, hipStream_t stream);
+size_t sched_ws_bytes(int N);
+void sched_ws_layout(SchedRankArgs& a, void* ws);
+hipError_t launch_schedule_ranked(const SchedRankArgs& a, hipStream_t stream);
 
 // Verification (see verify.hip).
 struct VerifyPlan {

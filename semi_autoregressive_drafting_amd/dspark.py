@@ -70,7 +70,7 @@ def load():
     L.dspark_confidence.restype = I
     L.dspark_schedule.argtypes = [I, I, P, P, I, P, P, P, P, SZ, P]
     L.dspark_schedule.restype = I
-    L.dspark_schedule_async.argtypes = [I, I, P, P, P, I, P, P, P, P]
+    L.dspark_schedule_async.argtypes = [I, I, P, P, P, I, P, P, P, P, SZ, P]
     L.dspark_schedule_async.restype = I
     L.dspark_verify.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, F, U64,
                                 P, P, P, P, P, P, SZ, P]
@@ -175,16 +175,20 @@ def dspark_confidence(R, gamma, d, rank, V, dt, h, W1, x, w, c, a, stream=None):
           _ptr(c), _ptr(a), _stream(stream))
 
 
-def dspark_schedule(R, gamma, a, sps, sps_len, ell, budget, theta, ws=None, ws_bytes=0,
+def dspark_schedule(R, gamma, a, sps, sps_len, ell, budget, theta, ws, ws_bytes=None,
                     stream=None):
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
     _call("dspark_schedule", R, gamma, _ptr(a), _ptr(sps), int(sps_len), _ptr(ell),
           _ptr(budget), _ptr(theta), _ptr(ws), int(ws_bytes), _stream(stream))
 
 
-def dspark_schedule_async(R, gamma, a_lag, a_cur, sps, sps_len, ell, budget, theta,
-                          stream=None):
+def dspark_schedule_async(R, gamma, a_lag, a_cur, sps, sps_len, ell, budget, theta, ws,
+                          ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
     _call("dspark_schedule_async", R, gamma, _ptr(a_lag), _ptr(a_cur), _ptr(sps), int(sps_len),
-          _ptr(ell), _ptr(budget), _ptr(theta), _stream(stream))
+          _ptr(ell), _ptr(budget), _ptr(theta), _ptr(ws), int(ws_bytes), _stream(stream))
 
 
 def dspark_verify(R, V, rank, gamma, dt, W1, W2t, U, target, x, lse_d, p_d_x, ell,

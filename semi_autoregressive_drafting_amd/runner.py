@@ -65,6 +65,7 @@ class RoundBuffers:
     tau: torch.Tensor
     tau_mean: torch.Tensor
     vws: torch.Tensor      # verify workspace
+    sws: torch.Tensor      # scheduler workspace
 
     @staticmethod
     def allocate(di: DeviceInputs, device="cuda") -> "RoundBuffers":
@@ -73,6 +74,7 @@ class RoundBuffers:
         i32 = dict(dtype=torch.int32, device=device)
         ws = D.dspark_workspace_bytes(D.DSPARK_OP_DRAFT_STEP, R, di.V, di.rank, g)
         vws = D.dspark_workspace_bytes(D.DSPARK_OP_VERIFY, R, di.V, di.rank, g)
+        sws = D.dspark_workspace_bytes(D.DSPARK_OP_SCHEDULE, R, di.V, di.rank, g)
         return RoundBuffers(
             x=torch.zeros((R, g + 1), **i32), p=torch.zeros((R, g), **f32),
             lse=torch.zeros((R, g), **f32), c=torch.zeros((R, g), **f32),
@@ -83,7 +85,8 @@ class RoundBuffers:
             c_star=torch.zeros((R, g), **f32), n_accept=torch.zeros(R, **i32),
             next_token=torch.zeros(R, **i32), tau=torch.zeros(R, **i32),
             tau_mean=torch.zeros(1, **f32),
-            vws=torch.empty(max(vws, 16), dtype=torch.uint8, device=device))
+            vws=torch.empty(max(vws, 16), dtype=torch.uint8, device=device),
+            sws=torch.zeros(max(sws, 16), dtype=torch.uint8, device=device))  # zero-filled once
 
 
 def draft_step(di: DeviceInputs, buf: RoundBuffers, k: int, temperature: float, seed: int,
@@ -116,14 +119,14 @@ def draft_phases(di: DeviceInputs, buf: RoundBuffers, temperature: float, seed: 
 
 def schedule(di: DeviceInputs, buf: RoundBuffers):
     D.dspark_schedule(di.R, di.gamma, buf.a, di.sps, di.sps.numel(), buf.ell, buf.budget,
-                      buf.theta)
+                      buf.theta, buf.sws)
 
 
 def schedule_async(di: DeviceInputs, buf: RoundBuffers, a_lag: torch.Tensor):
     """Asynchronous scheduling: budget from a_lag (survival two steps old),
     selection from buf.a."""
     D.dspark_schedule_async(di.R, di.gamma, a_lag, buf.a, di.sps, di.sps.numel(), buf.ell,
-                            buf.budget, buf.theta)
+                            buf.budget, buf.theta, buf.sws)
 
 
 def verify(di: DeviceInputs, buf: RoundBuffers, temperature: float, seed: int):

@@ -51,7 +51,7 @@ def test_workspace_sizes():
     assert f(D.DSPARK_OP_DRAFT_STEP, 513, 1024, 32, 4) == 0
     assert f(D.DSPARK_OP_DRAFT_STEP, 4, 1, 32, 4) == 0
     assert f(D.DSPARK_OP_DRAFT_STEP, 4, 1024, 32, 17) == 0
-    assert f(D.DSPARK_OP_SCHEDULE, 128, 151936, 256, 16) == 0
+    assert f(D.DSPARK_OP_SCHEDULE, 128, 151936, 256, 16) > 0
     assert f(99, 4, 1024, 32, 4) == 0
     # at least one 5-field record per request and slab; 256-byte aligned regions
     w128 = f(D.DSPARK_OP_DRAFT_STEP, 128, 151936, 256, 16)
@@ -158,6 +158,24 @@ def test_schedule_validation():
     assert f(4, 4, FAKE, FAKE, 20, FAKE, FAKE, FAKE, None, 0, None) == D.DSPARK_ERR_SHAPE
     assert f(512, 17, FAKE, FAKE, 10 ** 6, FAKE, FAKE, FAKE, None, 0, None) == D.DSPARK_ERR_SHAPE
     assert f(600, 4, FAKE, FAKE, 10 ** 6, FAKE, FAKE, FAKE, None, 0, None) == D.DSPARK_ERR_SHAPE
+    need = D.dspark_workspace_bytes(D.DSPARK_OP_SCHEDULE, 4, 2, 16, 4)
+    assert f(4, 4, FAKE, FAKE, 21, FAKE, FAKE, FAKE, None, need, None) == D.DSPARK_ERR_WORKSPACE
+    assert f(4, 4, FAKE, FAKE, 21, FAKE, FAKE, FAKE, FAKE, need - 1, None) == \
+        D.DSPARK_ERR_WORKSPACE
+    assert f(4, 4, FAKE, FAKE, 21, FAKE, FAKE, FAKE, FAKE + 8, need, None) == \
+        D.DSPARK_ERR_WORKSPACE
+
+
+def test_schedule_workspace_size():
+    """The scheduler's workspace grows with R*gamma and covers the sorted
+    positions (int32) and the prefix sums G at every position 0..N (fp64);
+    beyond 8192 candidates there is no size."""
+    ws = lambda R, g: D.dspark_workspace_bytes(D.DSPARK_OP_SCHEDULE, R, 2, 16, g)
+    assert ws(1, 1) > 0
+    assert ws(128, 16) >= 128 * 16 * 4 + (128 * 16 + 1) * 8
+    assert ws(512, 16) > ws(128, 16) > ws(4, 4)
+    assert ws(512, 16) <= 160 << 10
+    assert ws(600, 16) == 0 and ws(512, 17) == 0
 
 
 def test_draft_block_phases_validation():
@@ -264,12 +282,19 @@ def test_verify_rnn_validation():
 
 def test_schedule_async_validation():
     f = D.load().dspark_schedule_async
-    assert f(4, 4, None, FAKE, FAKE, 21, FAKE, FAKE, FAKE, None) == D.DSPARK_ERR_NULL
-    assert f(4, 4, FAKE, None, FAKE, 21, FAKE, FAKE, FAKE, None) == D.DSPARK_ERR_NULL
-    assert f(4, 4, FAKE, FAKE, FAKE, 21, FAKE, None, FAKE, None) == D.DSPARK_ERR_NULL
-    assert f(4, 4, FAKE, FAKE, FAKE, 20, FAKE, FAKE, FAKE, None) == D.DSPARK_ERR_SHAPE
-    assert f(0, 4, FAKE, FAKE, FAKE, 10 ** 6, FAKE, FAKE, FAKE, None) == D.DSPARK_ERR_SHAPE
-    assert f(512, 17, FAKE, FAKE, FAKE, 10 ** 6, FAKE, FAKE, FAKE, None) == D.DSPARK_ERR_SHAPE
+    need = D.dspark_workspace_bytes(D.DSPARK_OP_SCHEDULE, 4, 2, 16, 4)
+    assert f(4, 4, None, FAKE, FAKE, 21, FAKE, FAKE, FAKE, FAKE, need, None) == D.DSPARK_ERR_NULL
+    assert f(4, 4, FAKE, None, FAKE, 21, FAKE, FAKE, FAKE, FAKE, need, None) == D.DSPARK_ERR_NULL
+    assert f(4, 4, FAKE, FAKE, FAKE, 21, FAKE, None, FAKE, FAKE, need, None) == D.DSPARK_ERR_NULL
+    assert f(4, 4, FAKE, FAKE, FAKE, 20, FAKE, FAKE, FAKE, FAKE, need, None) == D.DSPARK_ERR_SHAPE
+    assert f(0, 4, FAKE, FAKE, FAKE, 10 ** 6, FAKE, FAKE, FAKE, FAKE, need, None) == \
+        D.DSPARK_ERR_SHAPE
+    assert f(512, 17, FAKE, FAKE, FAKE, 10 ** 6, FAKE, FAKE, FAKE, FAKE, need, None) == \
+        D.DSPARK_ERR_SHAPE
+    assert f(4, 4, FAKE, FAKE, FAKE, 21, FAKE, FAKE, FAKE, None, need, None) == \
+        D.DSPARK_ERR_WORKSPACE
+    assert f(4, 4, FAKE, FAKE, FAKE, 21, FAKE, FAKE, FAKE, FAKE, need - 1, None) == \
+        D.DSPARK_ERR_WORKSPACE
 
 
 def test_confidence_validation():

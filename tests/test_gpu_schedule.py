@@ -1,5 +1,6 @@
-"""GPU parity of the single-workgroup prefix scheduler: budgets, admitted
-prefixes and Theta must equal the oracle's bit for bit on identical a."""
+"""GPU parity of the prefix schedulers (rank launch + finishing workgroup):
+budgets, admitted prefixes and Theta must equal the oracle's bit for bit on
+identical a."""
 import numpy as np
 import pytest
 import torch
@@ -11,21 +12,35 @@ from tests.gpu_parity import say
 
 pytestmark = pytest.mark.gpu
 
+COUNTER_BYTES = 17 * 128
 
-def gpu_schedule(a, sps):
+
+def workspace(R, g):
+    """The scheduler's workspace: zero-filled before its first use, and left
+    with its finishing counters (the first 17 128-byte lines) at zero by
+    every call.  The rest is filled with junk, which no call may depend on."""
+    n = D.dspark_workspace_bytes(D.DSPARK_OP_SCHEDULE, R, 2, 16, g)
+    assert n > COUNTER_BYTES
+    ws = torch.full((n,), 0xA5, dtype=torch.uint8, device="cuda")
+    ws[:COUNTER_BYTES].zero_()
+    return ws
+
+
+def gpu_schedule(a, sps, ws=None):
     R, g = a.shape
     ta = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
     ts = torch.from_numpy(np.ascontiguousarray(sps, dtype=np.float64)).cuda()
     ell = torch.full((R,), -7, dtype=torch.int32, device="cuda")
     budget = torch.full((1,), -7, dtype=torch.int32, device="cuda")
     theta = torch.zeros(1, dtype=torch.float64, device="cuda")
-    D.dspark_schedule(R, g, ta, ts, ts.numel(), ell, budget, theta)
+    D.dspark_schedule(R, g, ta, ts, ts.numel(), ell, budget, theta,
+                      workspace(R, g) if ws is None else ws)
     torch.cuda.synchronize()
     return ell.cpu().numpy(), int(budget.item()), float(theta.item())
 
 
-def assert_same(a, sps, tag=""):
-    ell_g, b_g, th_g = gpu_schedule(a, sps)
+def assert_same(a, sps, tag="", ws=None):
+    ell_g, b_g, th_g = gpu_schedule(a, sps, ws)
     ell_o, b_o, th_o, _, _ = O.schedule(a, sps)
     assert b_g == b_o, (tag, b_g, b_o)
     np.testing.assert_array_equal(ell_g, ell_o)
@@ -53,6 +68,29 @@ def test_schedule_random(R, g):
         for name, sps in _tables(rng, R, g):
             assert_same(a, sps, f"{R}x{g} {name} #{trial}")
     say(f"[schedule] {R}x{g} ok")
+
+
+def test_schedule_workspace_reused_across_sizes():
+    """One workspace sized for the largest call serves smaller calls after it,
+    whatever the previous call left in it."""
+    ws = workspace(512, 16)
+    rng = np.random.default_rng(11)
+    for R, g in [(512, 16), (37, 3), (128, 16), (1, 1), (300, 9)]:
+        c = rng.uniform(0.0, 1.0, (R, g)).astype(np.float32)
+        assert_same(O.survival(c), synth.sps_table(R, g), f"{R}x{g} reused", ws=ws)
+        assert int(ws[:COUNTER_BYTES].count_nonzero().item()) == 0  # counters left at zero
+
+
+def test_schedule_zero_survival():
+    """Zero survival (+0 and -0 alike) sorts after every positive value, in
+    flat-index order."""
+    rng = np.random.default_rng(12)
+    a = O.survival(rng.uniform(0.3, 1.0, (24, 6)).astype(np.float32))
+    a[3, 2:] = 0.0
+    a[7, 4:] = -0.0
+    a[9, 5] = 0.0
+    for sps in (synth.sps_table(24, 6), np.ones(24 * 7 + 1)):
+        assert_same(a, sps, "zero")
 
 
 def test_schedule_all_equal_keys():
@@ -88,13 +126,14 @@ def test_schedule_on_the_plan_demo_setting():
 # ---------------------------------------------------------------------------
 def gpu_schedule_async(a_lag, a_cur, sps):
     R, g = a_cur.shape
+    ws = workspace(R, g)
     tl = torch.from_numpy(np.ascontiguousarray(a_lag, dtype=np.float32)).cuda()
     tc = torch.from_numpy(np.ascontiguousarray(a_cur, dtype=np.float32)).cuda()
     ts = torch.from_numpy(np.ascontiguousarray(sps, dtype=np.float64)).cuda()
     ell = torch.full((R,), -7, dtype=torch.int32, device="cuda")
     budget = torch.full((1,), -7, dtype=torch.int32, device="cuda")
     theta = torch.zeros(1, dtype=torch.float64, device="cuda")
-    D.dspark_schedule_async(R, g, tl, tc, ts, ts.numel(), ell, budget, theta)
+    D.dspark_schedule_async(R, g, tl, tc, ts, ts.numel(), ell, budget, theta, ws)
     torch.cuda.synchronize()
     return ell.cpu().numpy(), int(budget.item()), float(theta.item())
 
