@@ -66,7 +66,7 @@ PROFILE_COUNTERS = os.path.join(os.path.dirname(os.path.abspath(__file__)), "pro
 
 # Sources the draft step kernel is compiled from (the counters go stale when
 # any of them changes).
-DRAFT_KERNEL_SOURCES = ("markov_step.hip", "mfma_stream.h", "dspark_device.h", "dspark_kernels.h")
+DRAFT_KERNEL_SOURCES = ("markov_step.hip", "mfma_stream.h", "dspark_device.h", "draft_step.h")
 
 
 def sources_sha256():

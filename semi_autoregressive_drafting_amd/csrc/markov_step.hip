@@ -44,7 +44,7 @@
 // arithmetic, set the step's time, and a shape whose waves stream separate
 // tiles with W2t loaded straight into VGPRs measured slower at every batch
 // size from 1 to 96 requests.
-#include "dspark_kernels.h"
+#include "draft_step.h"
 #include "mfma_stream.h"
 
 namespace dspark {
