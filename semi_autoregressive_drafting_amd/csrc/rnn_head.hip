@@ -172,6 +172,13 @@ __global__ __launch_bounds__(256) void rnn_proj_reduce(RnnArgs a) {
 // first one bringing the input projection and the recurrent bias; waves 0 .. 3
 // then form s_k, four of each lane's 16 entries each.
 constexpr int kStateQ = 4;       // K quarters
+
+// winner_id of a winner word from its low 32 bits alone (~id; an empty word
+// gives -1 either way), so the load fills one register and nothing reuses a
+// half of it while it is in flight.
+__device__ __forceinline__ int winner_id_low(const unsigned long long* w) {
+  return (int)~*reinterpret_cast<const uint32_t*>(w);
+}
 constexpr int kStateMaxSteps = 4;  // K steps per quarter at rank 256
 
 // s_{k-1} rows of the workgroup's 32 requests, staged once in LDS (row
@@ -193,6 +200,11 @@ __device__ __forceinline__ void state_step_body(const RnnArgs& a, int k, const f
   const int n = jb * 32 + col;
   const uint16_t* wi = a.W_ih + (size_t)(g * H + n) * (H + a.d) + 8 * half;
   const uint16_t* wh = a.W_hh + (size_t)(g * H + n) * H + 8 * half;
+  // The token first: vector loads return in order, so its wait below leaves
+  // every later load in flight and the row gather goes out a round trip after
+  // the start instead of after all of the workgroup's bulk loads.
+  int tok = k > 1 ? winner_id_low(a.best + winner_index(k - 2, a.R, mc))
+                   : a.x[(size_t)mc * (a.gamma + 1)];
   // loads that do not depend on the token
   bf16x8_t wiv[kStateMaxSteps], whv[kStateMaxSteps], ev[kStateMaxSteps];
   f32x4_t sv[kStateMaxSteps][2];
@@ -236,12 +248,14 @@ __device__ __forceinline__ void state_step_body(const RnnArgs& a, int k, const f
       pre[i] = a.Pk[((size_t)(k - 1) * a.R + r) * (3 * H) + g * H + n];
     }
   }
-  int tok = k > 1 ? winner_id(a.best[winner_index(k - 2, a.R, mc)]) : a.x[(size_t)mc * (a.gamma + 1)];
+  const float bh = a.b_hh[g * H + n];
+  __builtin_amdgcn_sched_barrier(0);  // every load above is issued before the token is used
   tok = checked_token(tok, a.V, a.err);
   const uint16_t* erow = a.W1 + (size_t)tok * H + 8 * half;
 #pragma unroll
   for (int j = 0; j < kStateMaxSteps; ++j)
     ev[j] = *reinterpret_cast<const bf16x8_t*>(erow + 16 * min(s_begin + j, KS - 1));
+  __builtin_amdgcn_sched_barrier(0);  // the row loads go out together, before any is used
 
   if constexpr (kRec) {
 #pragma unroll
@@ -286,7 +300,6 @@ __device__ __forceinline__ void state_step_body(const RnnArgs& a, int k, const f
   // quarters in a fixed order over two LDS slots: slot 0 = (q0 + input
   // projection) + q2, slot 1 = q1 + q3 (the recurrent part likewise, with its
   // bias in q0), and the gate input is slot 0 + slot 1
-  const float bh = a.b_hh[g * H + n];
   if (q < 2) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {

@@ -191,6 +191,10 @@ __device__ __forceinline__ void contract_staged(f32x16_t (&acc)[NC], const uint1
     for (int s = 0; s < 4; ++s)
       cur[s] = *reinterpret_cast<const bf16x8_t*>(apatch + col * kLdsRow + 16 * s + 8 * half);
     mma_chunk<NC>(acc, cur, lds, col, half);
+    // and keep put_raw's selects on the loaded values (rows and entries past
+    // the end become zeros) behind the MFMAs: hoisted above them, they made
+    // the wave wait for the next chunk's loads before this chunk's MFMAs
+    __builtin_amdgcn_sched_barrier(0);
     lds_barrier();  // every wave is past its reads of this chunk
     b.store(lds);
     put_raw();
