@@ -159,19 +159,25 @@ __global__ __launch_bounds__(256) void rnn_proj_reduce(RnnArgs a) {
   a.Pk[i] = v;
 }
 
-// R2: workgroup (jb, rt) owns requests 32 rt .. +31 and state entries
-// 32 jb .. +31, with 12 waves: wave w computes gate g = w / 4 (reset, update,
-// new) over the K quarter q = w % 4.  MFMA M = requests, N = state entries:
+// R2: workgroup (eb, rt) owns requests 32 rt .. +31 and state entries
+// 8 eb .. +7, with 4 waves, wave q taking K quarter q.  MFMA M = requests,
+// N = (gate, entry) pairs: column c = 8 g + j holds gate g (reset, update,
+// new) of entry 8 eb + j; columns 24 .. 31 are zero.
 //   A  e:  W1[x_{k-1}[m]][k ..]       s:  hi / lo bf16 terms of s_{k-1}[m][k ..]
 //   B  W_ih[g rank + n][k ..] (the e columns), W_hh[g rank + n][k ..]
-// The kernel is bound by dependent memory round trips (a few microseconds
-// each here) and by one CU's load pipeline (32 workgroups on 32 CUs), so every
-// wave issues all of its loads at the start, only the e rows wait for the
-// token, and s_{k-1} is read once per workgroup as whole rows into LDS rather
-// than once per gate wave in the MFMA lane layout.  The quarters meet in LDS in a fixed order, the
-// first one bringing the input projection and the recurrent bias; waves 0 .. 3
-// then form s_k, four of each lane's 16 entries each.
-constexpr int kStateQ = 4;       // K quarters
+// Each output keeps its operands, its K quarters and their fixed reduction
+// order whatever column it sits in, so the entry-group width only decides
+// how the work spreads: 8 entries per workgroup put the update on 4x as many
+// CUs as 32 would, and a CU's loads (the W slices of its entries, the e and
+// s_{k-1} rows of its requests, the input projections) are what bound the
+// kernel.  Every wave issues its loads at the start, the token first, so
+// that only the row gather waits for it; s_{k-1} is read once per workgroup
+// as whole rows into LDS.  The quarters meet in LDS in a fixed order, the
+// first one bringing the input projection and the recurrent bias; then each
+// of the 256 threads forms s_k for one (request, entry).
+constexpr int kStateQ = 4;         // K quarters = waves
+constexpr int kStateEnt = 8;       // state entries per workgroup
+constexpr int kStateMaxSteps = 4;  // K steps per quarter at rank 256
 
 // winner_id of a winner word from its low 32 bits alone (~id; an empty word
 // gives -1 either way), so the load fills one register and nothing reuses a
@@ -179,32 +185,34 @@ constexpr int kStateQ = 4;       // K quarters
 __device__ __forceinline__ int winner_id_low(const unsigned long long* w) {
   return (int)~*reinterpret_cast<const uint32_t*>(w);
 }
-constexpr int kStateMaxSteps = 4;  // K steps per quarter at rank 256
 
 // s_{k-1} rows of the workgroup's 32 requests, staged once in LDS (row
-// stride kSRow floats) instead of once per gate wave in the lane layout.
+// stride kSRow floats).
 constexpr int kSRow = 256 + 4;
 
 template <bool kRec>
 __device__ __forceinline__ void state_step_body(const RnnArgs& a, int k, const float* s_prev,
-                                                float* s_next, float (*red)[3][2][16][64],
+                                                float* s_next, float (*red)[2][16][64],
                                                 float (*sl)[kSRow]) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int g = w / kStateQ, q = w % kStateQ;
+  const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
   const int half = lane >> 5, col = lane & 31;
-  const int jb = blockIdx.x, rt = blockIdx.y;
+  const int eb = blockIdx.x, rt = blockIdx.y;
   const int H = a.rank, KS = H / 16;
   const int kq = (KS + kStateQ - 1) / kStateQ;
   const int s_begin = min(KS, q * kq), s_end = min(KS, s_begin + kq);
   const int mc = min(rt * 32 + col, a.R - 1);
-  const int n = jb * 32 + col;
-  const uint16_t* wi = a.W_ih + (size_t)(g * H + n) * (H + a.d) + 8 * half;
-  const uint16_t* wh = a.W_hh + (size_t)(g * H + n) * H + 8 * half;
+  // column col: gate cg, entry n (columns past 3 kStateEnt read a valid row
+  // and are zeroed before the MFMAs)
+  const bool cin = col < 3 * kStateEnt;
+  const int cg = cin ? col / kStateEnt : 0;
+  const int n = eb * kStateEnt + (cin ? col % kStateEnt : 0);
+  const uint16_t* wi = a.W_ih + (size_t)(cg * H + n) * (H + a.d) + 8 * half;
+  const uint16_t* wh = a.W_hh + (size_t)(cg * H + n) * H + 8 * half;
   // The token first: vector loads return in order, so its wait below leaves
   // every later load in flight and the row gather goes out a round trip after
   // the start instead of after all of the workgroup's bulk loads.
   int tok = k > 1 ? winner_id_low(a.best + winner_index(k - 2, a.R, mc))
-                   : a.x[(size_t)mc * (a.gamma + 1)];
+                  : a.x[(size_t)mc * (a.gamma + 1)];
   // loads that do not depend on the token
   bf16x8_t wiv[kStateMaxSteps], whv[kStateMaxSteps], ev[kStateMaxSteps];
   f32x4_t sv[kStateMaxSteps][2];
@@ -217,38 +225,30 @@ __device__ __forceinline__ void state_step_body(const RnnArgs& a, int k, const f
   // s_{k-1} of the 32 requests (rows past R repeat row R - 1): whole rows,
   // 16 bytes per thread and piece, into LDS
   constexpr int kPieces = 32 * 256 / 4;
-  f32x4_t spc[(kPieces + 64 * 3 * kStateQ - 1) / (64 * 3 * kStateQ)];
+  constexpr int kThreads = 64 * kStateQ;
+  f32x4_t spc[kPieces / kThreads];
   const int pieces = 32 * H / 4;
   if constexpr (kRec) {
 #pragma unroll
-    for (int i = 0; i < (int)(sizeof(spc) / sizeof(spc[0])); ++i) {
-      const int pc = threadIdx.x + i * 64 * 3 * kStateQ;
+    for (int i = 0; i < kPieces / kThreads; ++i) {
+      const int pc = threadIdx.x + i * kThreads;
       const int row = pc / (H / 4), c4 = pc % (H / 4);
       const int rr = min(rt * 32 + row, a.R - 1);
       if (pc < pieces) spc[i] = *reinterpret_cast<const f32x4_t*>(s_prev + (size_t)rr * H + 4 * c4);
     }
   }
-  // waves 0 .. 3 each blend 4 of the 16 accumulator entries at the end, and
-  // keep s_{k-1} of those entries
-  float sp[4];
-  if (kRec && w < 4) {
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const int i = 4 * w + ii;
-      const int r = min(rt * 32 + 8 * (i >> 2) + 4 * half + (i & 3), a.R - 1);
-      sp[ii] = s_prev[(size_t)r * H + n];
-    }
-  }
-  // the first quarter also brings the input projection of step k
+  // the first quarter also brings the input projection of step k and the
+  // recurrent bias of its columns
   float pre[16];
+  float bh = 0.0f;
   if (q == 0) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int r = min(rt * 32 + 8 * (i >> 2) + 4 * half + (i & 3), a.R - 1);
-      pre[i] = a.Pk[((size_t)(k - 1) * a.R + r) * (3 * H) + g * H + n];
+      pre[i] = a.Pk[((size_t)(k - 1) * a.R + r) * (3 * H) + cg * H + n];
     }
+    bh = a.b_hh[cg * H + n];
   }
-  const float bh = a.b_hh[g * H + n];
   __builtin_amdgcn_sched_barrier(0);  // every load above is issued before the token is used
   tok = checked_token(tok, a.V, a.err);
   const uint16_t* erow = a.W1 + (size_t)tok * H + 8 * half;
@@ -259,14 +259,16 @@ __device__ __forceinline__ void state_step_body(const RnnArgs& a, int k, const f
 
   if constexpr (kRec) {
 #pragma unroll
-    for (int i = 0; i < (int)(sizeof(spc) / sizeof(spc[0])); ++i) {
-      const int pc = threadIdx.x + i * 64 * 3 * kStateQ;
+    for (int i = 0; i < kPieces / kThreads; ++i) {
+      const int pc = threadIdx.x + i * kThreads;
       if (pc < pieces) {
         const int row = pc / (H / 4), c4 = pc % (H / 4);
         *reinterpret_cast<f32x4_t*>(&sl[row][4 * c4]) = spc[i];
       }
     }
-    __syncthreads();
+  }
+  __syncthreads();  // s_{k-1} rows in LDS (read below and by the blend)
+  if constexpr (kRec) {
 #pragma unroll
     for (int j = 0; j < kStateMaxSteps; ++j) {
       const int k0 = 16 * min(s_begin + j, KS - 1) + 8 * half;
@@ -279,8 +281,10 @@ __device__ __forceinline__ void state_step_body(const RnnArgs& a, int k, const f
 #pragma unroll
   for (int j = 0; j < kStateMaxSteps; ++j) {
     if (s_begin + j >= s_end) break;
-    gi = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ev[j], wiv[j], gi, 0, 0, 0);
+    const bf16x8_t wij = cin ? wiv[j] : bf16x8_t{};
+    gi = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ev[j], wij, gi, 0, 0, 0);
     if constexpr (kRec) {
+      const bf16x8_t whj = cin ? whv[j] : bf16x8_t{};
       float hi[8], lo[8];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -293,8 +297,8 @@ __device__ __forceinline__ void state_step_body(const RnnArgs& a, int k, const f
         hi[t] = bf16_value(bf16_bits_rne(v));
         lo[t] = v - hi[t];
       }
-      gh = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf16x8_of(hi), whv[j], gh, 0, 0, 0);
-      gh = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf16x8_of(lo), whv[j], gh, 0, 0, 0);
+      gh = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf16x8_of(hi), whj, gh, 0, 0, 0);
+      gh = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf16x8_of(lo), whj, gh, 0, 0, 0);
     }
   }
   // quarters in a fixed order over two LDS slots: slot 0 = (q0 + input
@@ -303,44 +307,43 @@ __device__ __forceinline__ void state_step_body(const RnnArgs& a, int k, const f
   if (q < 2) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      red[q][g][0][i][lane] = q == 0 ? gi[i] + pre[i] : gi[i];
-      red[q][g][1][i][lane] = q == 0 ? gh[i] + bh : gh[i];
+      red[q][0][i][lane] = q == 0 ? gi[i] + pre[i] : gi[i];
+      red[q][1][i][lane] = q == 0 ? gh[i] + bh : gh[i];
     }
   }
   __syncthreads();
   if (q >= 2) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      red[q - 2][g][0][i][lane] += gi[i];
-      red[q - 2][g][1][i][lane] += gh[i];
+      red[q - 2][0][i][lane] += gi[i];
+      red[q - 2][1][i][lane] += gh[i];
     }
   }
   __syncthreads();
-  if (w >= 4) return;
-  // accumulator i: request 32 rt + 8 (i/4) + 4 half + i%4, state entry n;
-  // wave w blends i = 4 w .. 4 w + 3
-#pragma unroll
-  for (int ii = 0; ii < 4; ++ii) {
-    const int i = 4 * w + ii;
-    const int r = rt * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-    if (r >= a.R) continue;
-    auto part = [&](int gate, int which) {
-      return red[0][gate][which][i][lane] + red[1][gate][which][i][lane];
-    };
-    const float rg = 1.0f / (1.0f + expf(-(part(0, 0) + part(0, 1))));
-    const float zg = 1.0f / (1.0f + expf(-(part(1, 0) + part(1, 1))));
-    const float ng = tanhf(part(2, 0) + rg * part(2, 1));
-    const float s = (1.0f - zg) * ng + zg * (kRec ? sp[ii] : 0.0f);
-    s_next[(size_t)r * H + n] = s;
-    a.E[(size_t)r * H + n] = bf16_bits_rne(s);
-    if (a.rows_out) a.rows_out[((size_t)r * a.gamma + (k - 1)) * H + n] = bf16_bits_rne(s);
-  }
+  // thread t forms s_k of request 32 rt + m and entry 8 eb + j (m = t / 8,
+  // j = t % 8); accumulator i of lane l holds request 8 (i/4) + 4 (l/32) + i%4
+  // of column l%32
+  const int m = threadIdx.x / kStateEnt, j = threadIdx.x % kStateEnt;
+  const int r = rt * 32 + m;
+  if (m >= 32 || r >= a.R) return;
+  const int i = 4 * (m >> 3) + (m & 3), ll = 32 * ((m >> 2) & 1);
+  auto part = [&](int gate, int which) {
+    return red[0][which][i][ll + gate * kStateEnt + j] + red[1][which][i][ll + gate * kStateEnt + j];
+  };
+  const int nn = eb * kStateEnt + j;
+  const float rg = 1.0f / (1.0f + expf(-(part(0, 0) + part(0, 1))));
+  const float zg = 1.0f / (1.0f + expf(-(part(1, 0) + part(1, 1))));
+  const float ng = tanhf(part(2, 0) + rg * part(2, 1));
+  const float s = (1.0f - zg) * ng + zg * (kRec ? sl[m][nn] : 0.0f);
+  s_next[(size_t)r * H + nn] = s;
+  a.E[(size_t)r * H + nn] = bf16_bits_rne(s);
+  if (a.rows_out) a.rows_out[((size_t)r * a.gamma + (k - 1)) * H + nn] = bf16_bits_rne(s);
 }
 
-__global__ __launch_bounds__(64 * 3 * kStateQ) void rnn_state_step(RnnArgs a, int k,
-                                                                   const float* s_prev,
-                                                                   float* s_next) {
-  __shared__ float red[2][3][2][16][64];  // slot, gate, input / recurrent part
+__global__ __launch_bounds__(64 * kStateQ) void rnn_state_step(RnnArgs a, int k,
+                                                               const float* s_prev,
+                                                               float* s_next) {
+  __shared__ float red[2][2][16][64];  // slot, input / recurrent part
   __shared__ __align__(16) float sl[32][kSRow];
   if (k > 1)
     state_step_body<true>(a, k, s_prev, s_next, red, sl);
@@ -365,7 +368,7 @@ hipError_t launch_rnn_input_proj(const RnnArgs& a, hipStream_t stream) {
 
 hipError_t launch_rnn_state_step(const RnnArgs& a, int k, const float* s_prev, float* s_next,
                                  hipStream_t stream) {
-  hipLaunchKernelGGL(rnn_state_step, dim3(a.rank / 32, (a.R + 31) / 32), dim3(64 * 3 * kStateQ), 0,
+  hipLaunchKernelGGL(rnn_state_step, dim3(a.rank / kStateEnt, (a.R + 31) / 32), dim3(64 * kStateQ), 0,
                      stream, a, k, s_prev, s_next);
   return hipGetLastError();
 }
