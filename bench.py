@@ -136,7 +136,7 @@ def read_ceiling(nbytes, launches=20):
     slots = 12
     pool = torch.empty(nbytes * slots, dtype=torch.uint8, device="cuda")
     pool.fill_(1)
-    grids = (512, 1024, 2048, 4096)
+    grids = (256, 512, 1024, 2048, 4096)
     sink = torch.zeros(max(grids), dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
 
