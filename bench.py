@@ -570,15 +570,18 @@ def main():
                           dtype=torch.uint8, device="cuda")
         for s in range(3):
             runner.draft_rnn(di, buf, rw, TEMPERATURE, 600 + s, rstate, rws)
-        er = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        r_us = []
+        # back-to-back blocks with an event between each, as for the Markov
+        # block (draft_block_with_copy_and_merge), so that neither figure
+        # carries the launch latency of an idle queue
+        erb = [torch.cuda.Event(enable_timing=True) for _ in range(nb + 1)]
+        erb[0].record()
         for s in range(nb):
-            er[0].record()
             runner.draft_rnn(di, buf, rw, TEMPERATURE, 610 + s, rstate, rws)
-            er[1].record()
-            torch.cuda.synchronize()
-            r_us.append(er[0].elapsed_time(er[1]) * 1e3)
+            erb[s + 1].record()
+        torch.cuda.synchronize()
+        r_us = [erb[s].elapsed_time(erb[s + 1]) * 1e3 for s in range(nb)]
         r_med = float(np.median(r_us))
+        er = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         # the RNN head's whole round: its block (bias rows written out),
         # schedule, and verification with those rows
         rrows = torch.empty((R, g, rank), dtype=torch.int16, device="cuda")
@@ -594,6 +597,7 @@ def main():
                 rr_us.append(er[0].elapsed_time(er[1]) * 1e3)
         rr_med = float(np.median(rr_us))
         rnn = {"block_us": round(r_med, 2), "us_per_step": round(r_med / g, 2),
+               "vs_markov_block": round(r_med / float(block_ms.mean() * 1e3), 3),
                "draft_tokens_per_s": round(R * g / (r_med * 1e-6), 1),
                "round_us": round(rr_med, 2),
                "round_draft_tokens_per_s": round(R * g / (rr_med * 1e-6), 1)}
