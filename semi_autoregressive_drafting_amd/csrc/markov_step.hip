@@ -39,6 +39,12 @@
 // fragments in VGPRs for the whole step and each W2t tile is staged once per
 // workgroup in LDS.  W2t leaves HBM once per request group; the groups of one
 // slab share an XCD (blockIdx % 8) so repeated W2t reads hit that XCD's L2.
+// Odd steps walk each slab's tiles upward and even steps downward, so a step
+// starts on the W2t tiles the previous step read last.  The L2 does not keep
+// them across the launch (the L2 misses per step stay the same); the most
+// recently read tiles are the likeliest to be served by the memory-side cache
+// (MALL) rather than by DRAM, and the step is faster this way.  The races
+// break ties by id, so the visiting order changes no tie.
 // Batches below 128 requests run the same shape with the missing rows padded
 // (their lanes recompute row R-1 and store nothing): the bytes, not the
 // arithmetic, set the step's time, and a shape whose waves stream separate
@@ -147,12 +153,20 @@ struct DraftEpi {
   template <bool kMasked>
   __device__ __forceinline__ void fold(const float (&z)[16], int vb) {
     if constexpr (kGreedy) {
+      // the tile's best (ids rise inside it, so strict > keeps the lowest id
+      // among equal logits), then merged into the running best with the same
+      // rule whatever order the tiles come in
+      float zt = -INFINITY;
+      int it = -1;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const bool win = (!kMasked || vb + i < V) && (z[i] > st.bE);
-        st.bE = win ? z[i] : st.bE;
-        st.bV = win ? vb + i : st.bV;
+        const bool w = (!kMasked || vb + i < V) && z[i] > zt;
+        zt = w ? z[i] : zt;
+        it = w ? vb + i : it;
       }
+      const bool win = it >= 0 && (zt > st.bE || (zt == st.bE && it < st.bV));
+      st.bE = win ? zt : st.bE;
+      st.bV = win ? it : st.bV;
     } else {
       float zm = -INFINITY;
 #pragma unroll
@@ -174,8 +188,10 @@ struct DraftEpi {
       st.S += sb;
       const float ln = fast_log2(
           bits_to_uniform(rxs_m_xs(state_row + (uint32_t)(vb / kDraftBlock) * kLcgMul)));
-      // sb / L > bE / bL  <=>  sb * bLn < bE * ln     (L = -ln > 0)
-      const bool win = sb * st.bLn < st.bE * ln;
+      // sb / L > bE / bL  <=>  sb * bLn < bE * ln     (L = -ln > 0); on equal
+      // keys the lower block, whatever order the tiles come in
+      const float lhs = sb * st.bLn, rhs = st.bE * ln;
+      const bool win = lhs < rhs || (lhs == rhs && st.bV >= 0 && vb < st.bV);
       st.bE = win ? sb : st.bE;
       st.bLn = win ? ln : st.bLn;
       st.bV = win ? vb : st.bV;
@@ -467,7 +483,8 @@ __global__ __launch_bounds__(kStreamThreads) void markov_step_shared(StepArgs a)
       load_e_frags<W, kKs>(ef, base, row, a.rank, a.E_rows ? a.R : a.V, half);
   };
   if constexpr (kKs > 0)
-    shared_a_stream_skew<W, kKs>(a.W2t, a.V, t_begin, t_end, e, gather, lds, epi);
+    shared_a_stream_skew<W, kKs>(a.W2t, a.V, t_begin, t_end, e, gather, lds, epi,
+                                 (a.k & 1) == 0);
   else
     shared_a_stream<W, kKs, draft_dist<W>()>(a.W2t, a.V, a.rank, t_begin, t_end, e, gather, lds,
                                              epi);

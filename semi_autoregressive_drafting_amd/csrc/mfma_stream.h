@@ -259,6 +259,11 @@ __device__ __forceinline__ void shared_a_stream(const void* W2t, int V, int rank
 //   f. issue the epilogue's loads of tile i+2 into slot S (tile i is folded).
 // A partial last tile of the vocabulary is handled after the loop.
 //
+// With rev the full tiles are visited from the top of the range down (tile
+// t_full - 1 - (i - t_begin) at iteration i).  A caller that alternates the
+// direction from one launch to the next starts each launch on the W2t tiles
+// the previous one read last.
+//
 // SkewStream holds the stream's per-thread offsets and W2t register buffers;
 // shared_a_stream_skew is its plain use.
 template <class W, int kKs, int kThreads = kStreamThreads>
@@ -275,6 +280,7 @@ struct SkewStream {
 
   const unsigned char* wbase;
   int V, t_full;
+  int mrev = -1;  // rev: t_begin + t_full - 1
   int coff[kPer], loff[kPer];
   u32x4_t wreg[2][kPer];
 
@@ -288,9 +294,11 @@ struct SkewStream {
       loff[j] = row * kRs + (c - row * kCpr) * 16;
     }
   }
+  // Tile visited at iteration i (i in [t_begin, t_full)).
+  __device__ __forceinline__ int tile_at(int i) const { return mrev >= 0 ? mrev - i : i; }
   template <int S>
-  __device__ __forceinline__ void fetch_w(int vt) {
-    const unsigned char* tile = wbase + (vt < t_full ? (size_t)vt * kChunks * 16 : 0);
+  __device__ __forceinline__ void fetch_w(int i) {
+    const unsigned char* tile = wbase + (i < t_full ? (size_t)tile_at(i) * kChunks * 16 : 0);
 #pragma unroll
     for (int j = 0; j < kPer; ++j) wreg[S][j] = *reinterpret_cast<const u32x4_t*>(tile + coff[j]);
   }
@@ -319,7 +327,8 @@ struct SkewStream {
   // depends on a token id read from memory) overlaps them.
   template <class LoadE, class Epi>
   __device__ __forceinline__ void run(int t_begin, int t_end, typename W::frag_t (&e)[W::kMaxKs],
-                                      LoadE&& load_e, unsigned char* lds, Epi& epi) {
+                                      LoadE&& load_e, unsigned char* lds, Epi& epi, bool rev) {
+    if (rev) mrev = t_begin + t_full - 1;
     // Scheduler groups for one iteration body: the first kAhead A reads, then
     // per MFMA one more read and a share of the epilogue's VALU work.
     constexpr int kAhead = 4;
@@ -343,22 +352,22 @@ struct SkewStream {
       lds_barrier();
       fetch_w<S>(vt + 2);
       const f32x16_t acc_next = mma(lds + (S ^ 1) * kTileLds, e);
-      epi.template consume<S>(acc_cur, vt);
-      epi.template prefetch<S>(vt + 2 < t_full ? vt + 2 : -1);
+      epi.template consume<S>(acc_cur, tile_at(vt));
+      epi.template prefetch<S>(vt + 2 < t_full ? tile_at(vt + 2) : -1);
       pin();
       acc_cur = acc_next;
     };
 
     if (t_begin < t_full) {
       fetch_w<0>(t_begin);
-      epi.template prefetch<0>(t_begin);
+      epi.template prefetch<0>(tile_at(t_begin));
     }
     load_e(e);
     wait_all_loads();  // the E fragments never stay pending into the loop
     if (t_begin < t_full) {
       stash<0>(lds);
       fetch_w<1>(t_begin + 1);
-      epi.template prefetch<1>(t_begin + 1 < t_full ? t_begin + 1 : -1);
+      epi.template prefetch<1>(t_begin + 1 < t_full ? tile_at(t_begin + 1) : -1);
       lds_barrier();
       acc_cur = mma(lds, e);
       int vt = t_begin;
@@ -392,9 +401,9 @@ __device__ __forceinline__ void shared_a_stream_skew(const void* W2t, int V, int
                                                      int t_end,
                                                      typename W::frag_t (&e)[W::kMaxKs],
                                                      LoadE&& load_e, unsigned char* lds,
-                                                     Epi& epi) {
+                                                     Epi& epi, bool rev = false) {
   SkewStream<W, kKs, kThreads> ss(W2t, V, t_end);
-  ss.run(t_begin, t_end, e, load_e, lds, epi);
+  ss.run(t_begin, t_end, e, load_e, lds, epi, rev);
 }
 
 // ---------------------------------------------------------------------------
